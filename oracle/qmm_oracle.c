@@ -1,0 +1,526 @@
+/*
+ * qmm_oracle.c -- plain, slow CPU oracle for the quantized mul_mat.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark; never by the product path.  It includes no
+ * header of the GPU library and the GPU library includes nothing from here.
+ *
+ * Every function follows a passage of the pages (cited per function).  Where
+ * the pages leave a step open, the reading taken is stated at the function.
+ * Floating point: single IEEE binary32 operations where the encoders fix the
+ * precision (no contraction: built with -ffp-contract=off), fp64 for results.
+ */
+#include "qmm_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define QK4_0 32
+#define QK8_0 32
+#define QK_K 256
+
+int orc_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int pick_threads(int nthreads) {
+    int mx = orc_max_threads();
+    if (nthreads <= 0 || nthreads > mx) return mx;
+    return nthreads;
+}
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16.  Written from the format's definition: 1 sign bit,     */
+/* 5 exponent bits (bias 15), 10 fraction bits, subnormals below 2^-14.      */
+/* Rounding is to nearest, ties to even.  (The pages only say "ggml_half",   */
+/* i.e. FP16: P1 "最基础的两块:Q4_0 与 Q8_0".)                               */
+/* ------------------------------------------------------------------------ */
+uint16_t orc_f32_to_f16(float x) {
+    uint32_t bits;
+    memcpy(&bits, &x, 4);
+    uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    if (isnan(x)) return (uint16_t)(sign | 0x7e00u);
+    double a = fabs((double)x);
+    if (isinf(x) || a >= 65520.0) return (uint16_t)(sign | 0x7c00u); /* rounds past 65504 */
+    if (a == 0.0) return sign;
+    /* quantum of the binade that a falls in (subnormal quantum 2^-24) */
+    int e;
+    frexp(a, &e);              /* a = f * 2^e, f in [0.5, 1) -> binade exponent e-1 */
+    int E = e - 1;
+    if (E < -14) E = -14;      /* subnormal range shares the quantum of 2^-14's binade */
+    double quantum = ldexp(1.0, E - 10);
+    double n = nearbyint(a / quantum);   /* exact division by a power of two; RNE */
+    double v = n * quantum;
+    if (v >= 65536.0) return (uint16_t)(sign | 0x7c00u);
+    if (v < ldexp(1.0, -14)) {           /* subnormal: fraction = v / 2^-24 */
+        return (uint16_t)(sign | (uint16_t)(v / ldexp(1.0, -24)));
+    }
+    frexp(v, &e);
+    int Ev = e - 1;                      /* v = (1 + frac/1024) * 2^Ev */
+    double frac = (v / ldexp(1.0, Ev) - 1.0) * 1024.0;
+    return (uint16_t)(sign | (uint16_t)((Ev + 15) << 10) | (uint16_t)frac);
+}
+
+float orc_f16_to_f32(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int E = (h >> 10) & 0x1f;
+    int F = h & 0x3ff;
+    double v;
+    if (E == 0)
+        v = ldexp((double)F, -24);
+    else if (E == 31)
+        v = F ? NAN : INFINITY;
+    else
+        v = ldexp(1.0 + F / 1024.0, E - 15);
+    return (float)(sign ? -v : v);
+}
+
+static float rd_f16(const uint8_t *p) {
+    return orc_f16_to_f32((uint16_t)(p[0] | (p[1] << 8)));
+}
+static void wr_f16(uint8_t *p, uint16_t h) {
+    p[0] = (uint8_t)(h & 0xff);
+    p[1] = (uint8_t)(h >> 8);
+}
+static float rd_f32(const uint8_t *p) {
+    float f;
+    memcpy(&f, p, 4);
+    return f;
+}
+static int16_t rd_i16(const uint8_t *p) {
+    return (int16_t)(uint16_t)(p[0] | (p[1] << 8));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q4_K 12-byte scale field.  P1 "6-bit 参数是怎么塞进 12 字节的": the decode  */
+/* rule there fixes all 96 bits.  Sub-blocks j<4: s_j = low 6 bits of byte j, */
+/* m_j = low 6 bits of byte j+4.  j>=4: the low 4 bits of s_j / m_j are the  */
+/* low / high nibble of byte j+4, their top 2 bits sit in the top 2 bits of  */
+/* byte j-4 (for s_j) and byte j (for m_j).  (The prose of that section puts */
+/* the two nibbles the other way round; the decode rule is followed.)        */
+/* ------------------------------------------------------------------------ */
+void orc_q4_K_get_scale_min(const uint8_t *q, int j, uint8_t *s, uint8_t *m) {
+    if (j < 4) {
+        *s = q[j] & 63;
+        *m = q[j + 4] & 63;
+    } else {
+        *s = (uint8_t)((q[j + 4] & 0x0f) | ((q[j - 4] >> 6) << 4));
+        *m = (uint8_t)((q[j + 4] >> 4) | ((q[j] >> 6) << 4));
+    }
+}
+
+void orc_q4_K_pack_scales(const uint8_t s[8], const uint8_t m[8], uint8_t out[12]) {
+    memset(out, 0, 12);
+    for (int j = 0; j < 4; ++j) {
+        out[j] = (uint8_t)(s[j] & 63);
+        out[j + 4] = (uint8_t)(m[j] & 63);
+    }
+    for (int j = 4; j < 8; ++j) {
+        out[j + 4] = (uint8_t)((s[j] & 0x0f) | ((m[j] & 0x0f) << 4));
+        out[j - 4] |= (uint8_t)(((s[j] >> 4) & 3) << 6);
+        out[j] |= (uint8_t)(((m[j] >> 4) & 3) << 6);
+    }
+}
+
+static int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/* ------------------------------------------------------------------------ */
+/* Q4_0 encoder (input generator).  P1 "最基础的两块:Q4_0 与 Q8_0": per 32    */
+/* weights, d = -xmax/8 with xmax the signed element of largest magnitude,   */
+/* w ~ d*(q-8).  Readings: first index wins a tie in |x|; q = rint(x/d)+8    */
+/* computed as x*(1/d) in fp32, ties to even, clamped to [0,15]; the high   */
+/* nibble of byte l holds element l+16 (the split-half order the K-quant     */
+/* section uses).                                                           */
+/* ------------------------------------------------------------------------ */
+void orc_quantize_q4_0(const float *x, int64_t rows, int64_t K, uint8_t *out) {
+    const int64_t nb = K / QK4_0;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *xb = x + r * K + b * QK4_0;
+            uint8_t *blk = out + (r * nb + b) * ORC_Q4_0_BYTES;
+            float amax = 0.0f, xmax = 0.0f;
+            for (int i = 0; i < QK4_0; ++i) {
+                float a = fabsf(xb[i]);
+                if (a > amax) { amax = a; xmax = xb[i]; }
+            }
+            float d = 0.0f - xmax / 8.0f;   /* +0 for an all-zero block */
+            float id = d != 0.0f ? 1.0f / d : 0.0f;
+            uint8_t q[QK4_0];
+            for (int i = 0; i < QK4_0; ++i) {
+                float t = xb[i] * id;
+                q[i] = (uint8_t)clampi((int)rintf(t) + 8, 0, 15);
+            }
+            wr_f16(blk, orc_f32_to_f16(d));
+            for (int l = 0; l < 16; ++l)
+                blk[2 + l] = (uint8_t)(q[l] | (q[l + 16] << 4));
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q4_K encoder (input generator).  P1 "K-quant:为什么需要超级块" fixes the   */
+/* decoded value w = d*s_j*q - dmin*m_j with q in [0,15] and 6-bit s_j, m_j; */
+/* the nibble order comes from "正确性:缩放系数可以提到求和号外面" (byte l of  */
+/* 64-element group g holds element l low, element l+32 high).  The pages do */
+/* not give the scale search; the plain min/max reading is taken:            */
+/*   lo_j = min(0, min x), hi_j = max x, sc_j = (hi_j - lo_j)/15, mn_j = -lo_j */
+/*   d = max sc_j / 63, dmin = max mn_j / 63                                 */
+/*   s_j = rint(sc_j/d), m_j = rint(mn_j/dmin), clamped to [0,63]             */
+/*   with D_j = f16(d)*s_j, M_j = f16(dmin)*m_j: q = rint((x+M_j)/D_j) in [0,15] */
+/* ------------------------------------------------------------------------ */
+void orc_quantize_q4_K(const float *x, int64_t rows, int64_t K, uint8_t *out) {
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *xb = x + r * K + b * QK_K;
+            uint8_t *blk = out + (r * nb + b) * ORC_Q4_K_BYTES;
+            float sc[8], mn[8];
+            float maxsc = 0.0f, maxmn = 0.0f;
+            for (int j = 0; j < 8; ++j) {
+                const float *xs = xb + 32 * j;
+                float lo = xs[0], hi = xs[0];
+                for (int i = 1; i < 32; ++i) {
+                    if (xs[i] < lo) lo = xs[i];
+                    if (xs[i] > hi) hi = xs[i];
+                }
+                if (!(lo < 0.0f)) lo = 0.0f;
+                sc[j] = (hi - lo) / 15.0f;
+                mn[j] = 0.0f - lo;
+                if (sc[j] > maxsc) maxsc = sc[j];
+                if (mn[j] > maxmn) maxmn = mn[j];
+            }
+            float d = maxsc / 63.0f;
+            float dmin = maxmn / 63.0f;
+            uint8_t s[8], m[8];
+            for (int j = 0; j < 8; ++j) {
+                s[j] = (uint8_t)(d > 0.0f ? clampi((int)rintf(sc[j] / d), 0, 63) : 0);
+                m[j] = (uint8_t)(dmin > 0.0f ? clampi((int)rintf(mn[j] / dmin), 0, 63) : 0);
+            }
+            uint16_t dh = orc_f32_to_f16(d), dmh = orc_f32_to_f16(dmin);
+            float df = orc_f16_to_f32(dh), dmf = orc_f16_to_f32(dmh);
+            uint8_t q[QK_K];
+            for (int j = 0; j < 8; ++j) {
+                float Dj = df * (float)s[j];
+                float Mj = dmf * (float)m[j];
+                for (int i = 0; i < 32; ++i) {
+                    int k = 32 * j + i;
+                    q[k] = (uint8_t)(Dj > 0.0f ? clampi((int)rintf((xb[k] + Mj) / Dj), 0, 15) : 0);
+                }
+            }
+            wr_f16(blk, dh);
+            wr_f16(blk + 2, dmh);
+            orc_q4_K_pack_scales(s, m, blk + 4);
+            for (int g = 0; g < 4; ++g)
+                for (int l = 0; l < 32; ++l)
+                    blk[16 + 32 * g + l] = (uint8_t)(q[64 * g + l] | (q[64 * g + 32 + l] << 4));
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activation encoders.  P1 "最基础的两块:Q4_0 与 Q8_0" (Q8_0: symmetric      */
+/* int8, fp16 d, 32 values) and "更低的比特" (Q8_K: fp32 d, 256 int8 and      */
+/* int16 bsums, each the sum of 16 consecutive values; also "正确性" where   */
+/* bsums are said to be filled while quantizing).  The formula is not on the */
+/* pages; reading: amax = max|x|, d = amax/127, id = d ? 1/d : 0,            */
+/* y = rint(x*id) (one fp32 multiply, ties to even) clamped to [-127,127].   */
+/* Q8_0 computes y from the fp32 d and stores f16(d).                        */
+/* ------------------------------------------------------------------------ */
+static void q8_block(const float *xb, int n, float *d_out, int8_t *q) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(xb[i]);
+        if (a > amax) amax = a;
+    }
+    float d = amax / 127.0f;
+    float id = d != 0.0f ? 1.0f / d : 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float t = xb[i] * id;
+        q[i] = (int8_t)clampi((int)rintf(t), -127, 127);
+    }
+    *d_out = d;
+}
+
+void orc_quantize_q8_0(const float *x, int64_t rows, int64_t K, uint8_t *out) {
+    const int64_t nb = K / QK8_0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            uint8_t *blk = out + (r * nb + b) * ORC_Q8_0_BYTES;
+            float d;
+            int8_t q[QK8_0];
+            q8_block(x + r * K + b * QK8_0, QK8_0, &d, q);
+            wr_f16(blk, orc_f32_to_f16(d));
+            memcpy(blk + 2, q, QK8_0);
+        }
+}
+
+void orc_quantize_q8_K(const float *x, int64_t rows, int64_t K, uint8_t *out) {
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            uint8_t *blk = out + (r * nb + b) * ORC_Q8_K_BYTES;
+            float d;
+            int8_t q[QK_K];
+            q8_block(x + r * K + b * QK_K, QK_K, &d, q);
+            memcpy(blk, &d, 4);
+            memcpy(blk + 4, q, QK_K);
+            for (int g = 0; g < 16; ++g) {
+                int s = 0;
+                for (int i = 0; i < 16; ++i) s += q[16 * g + i];
+                uint16_t u = (uint16_t)(int16_t)s;
+                blk[260 + 2 * g] = (uint8_t)(u & 0xff);
+                blk[260 + 2 * g + 1] = (uint8_t)(u >> 8);
+            }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decoders.  Q4_0: w = d*(q-8); Q4_K: w = d*s_j*q - dmin*m_j; Q8: a = d*y.   */
+/* (P1 "最基础的两块" and "K-quant:为什么需要超级块".)  All products are exact  */
+/* in fp64 (at most 11+6+4 significant bits).                                */
+/* ------------------------------------------------------------------------ */
+static int q4_0_nibble(const uint8_t *qs, int i) {
+    return i < 16 ? (qs[i] & 0x0f) : (qs[i - 16] >> 4);
+}
+static int q4_K_nibble(const uint8_t *qs, int k) {
+    int g = k / 64, r = k % 64;
+    uint8_t byte = qs[32 * g + (r % 32)];
+    return r < 32 ? (byte & 0x0f) : (byte >> 4);
+}
+
+void orc_dequantize_q4_0(const uint8_t *w, int64_t rows, int64_t K, double *out) {
+    const int64_t nb = K / QK4_0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = w + (r * nb + b) * ORC_Q4_0_BYTES;
+            double d = rd_f16(blk);
+            for (int i = 0; i < QK4_0; ++i)
+                out[r * K + b * QK4_0 + i] = d * (q4_0_nibble(blk + 2, i) - 8);
+        }
+}
+
+void orc_dequantize_q4_K(const uint8_t *w, int64_t rows, int64_t K, double *out) {
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = w + (r * nb + b) * ORC_Q4_K_BYTES;
+            double d = rd_f16(blk), dmin = rd_f16(blk + 2);
+            for (int k = 0; k < QK_K; ++k) {
+                uint8_t s, m;
+                orc_q4_K_get_scale_min(blk + 4, k / 32, &s, &m);
+                out[r * K + b * QK_K + k] = d * s * q4_K_nibble(blk + 16, k) - dmin * m;
+            }
+        }
+}
+
+void orc_dequantize_q8_0(const uint8_t *y, int64_t rows, int64_t K, double *out) {
+    const int64_t nb = K / QK8_0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = y + (r * nb + b) * ORC_Q8_0_BYTES;
+            double d = rd_f16(blk);
+            for (int i = 0; i < QK8_0; ++i)
+                out[r * K + b * QK8_0 + i] = d * (int8_t)blk[2 + i];
+        }
+}
+
+void orc_dequantize_q8_K(const uint8_t *y, int64_t rows, int64_t K, double *out) {
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = y + (r * nb + b) * ORC_Q8_K_BYTES;
+            double d = rd_f32(blk);
+            for (int i = 0; i < QK_K; ++i)
+                out[r * K + b * QK_K + i] = d * (int8_t)blk[4 + i];
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* The plain definition C[m,n] = sum_k A[m,k] W[n,k] (P3 "从数学表达式到真实 */
+/* 存储:混合精度 GEMM 的计算对象"), in fp64 on decoded values.                */
+/* ------------------------------------------------------------------------ */
+void orc_brute_force(const double *w, const double *a, int64_t M, int64_t N,
+                     int64_t K, double *out, double *terms) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0, t = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = w[n * K + k] * a[m * K + k];
+                s += p;
+                t += fabs(p);
+            }
+            out[m * N + n] = s;
+            if (terms) terms[m * N + n] = t;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Integer path.  P1 "正确性:缩放系数可以提到求和号外面": for one sub-block,    */
+/* sum w_i a_i = d*d_a*s*sum q_i y_i - dmin*d_a*m*sum y_i, with sum y_i taken */
+/* from bsums (two 16-element sums per 32-element sub-block, "min 项与最终归 */
+/* 约").  Per super-block: P_j (int32), S = sum_j s_j P_j, Mn = sum_j m_j Y_j,*/
+/* contribution d_a*(d*S - dmin*Mn); accumulated in fp64.                    */
+/* Q4_0 x Q8_0: P_b = sum (q_i-8) y_i, contribution d_w*d_a*P_b.             */
+/* ------------------------------------------------------------------------ */
+static double q4_K_row_dot(const uint8_t *wrow, const uint8_t *yrow, int64_t nb,
+                           int32_t *P_out, double *terms) {
+    double acc = 0.0, tacc = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *wb = wrow + b * ORC_Q4_K_BYTES;
+        const uint8_t *yb = yrow + b * ORC_Q8_K_BYTES;
+        float d = rd_f16(wb), dmin = rd_f16(wb + 2), da = rd_f32(yb);
+        int32_t S = 0, Mn = 0;
+        for (int j = 0; j < 8; ++j) {
+            uint8_t s, m;
+            orc_q4_K_get_scale_min(wb + 4, j, &s, &m);
+            int32_t P = 0;
+            for (int i = 0; i < 32; ++i) {
+                int k = 32 * j + i;
+                int q = q4_K_nibble(wb + 16, k);
+                int y = (int8_t)yb[4 + k];
+                P += q * y;
+                if (terms) tacc += fabs(((double)d * s * q - (double)dmin * m) * ((double)da * y));
+            }
+            if (P_out) P_out[b * 8 + j] = P;
+            int32_t Y = rd_i16(yb + 260 + 4 * j) + rd_i16(yb + 260 + 4 * j + 2);
+            S += (int32_t)s * P;
+            Mn += (int32_t)m * Y;
+        }
+        acc += (double)da * ((double)d * S - (double)dmin * Mn);
+    }
+    if (terms) *terms = tacc;
+    return acc;
+}
+
+static double q4_0_row_dot(const uint8_t *wrow, const uint8_t *yrow, int64_t nb,
+                           int32_t *P_out, double *terms) {
+    double acc = 0.0, tacc = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *wb = wrow + b * ORC_Q4_0_BYTES;
+        const uint8_t *yb = yrow + b * ORC_Q8_0_BYTES;
+        double dw = rd_f16(wb), da = rd_f16(yb);
+        int32_t P = 0;
+        for (int i = 0; i < QK4_0; ++i) {
+            int q = q4_0_nibble(wb + 2, i) - 8;
+            int y = (int8_t)yb[2 + i];
+            P += q * y;
+            if (terms) tacc += fabs(dw * q * da * y);
+        }
+        if (P_out) P_out[b] = P;
+        acc += dw * da * P;
+    }
+    if (terms) *terms = tacc;
+    return acc;
+}
+
+void orc_mul_mat_q4_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                           int64_t N, int64_t K, double *out, int nthreads) {
+    const int64_t nb = K / QK_K;
+    const int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            out[m * N + n] = q4_K_row_dot(w + n * nb * ORC_Q4_K_BYTES,
+                                          y + m * nb * ORC_Q8_K_BYTES, nb, NULL, NULL);
+}
+
+void orc_mul_mat_q4_0_q8_0(const uint8_t *w, const uint8_t *y, int64_t M,
+                           int64_t N, int64_t K, double *out, int nthreads) {
+    const int64_t nb = K / QK4_0;
+    const int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            out[m * N + n] = q4_0_row_dot(w + n * nb * ORC_Q4_0_BYTES,
+                                          y + m * nb * ORC_Q8_0_BYTES, nb, NULL, NULL);
+}
+
+void orc_q4_K_subblock_sums(const uint8_t *w, const uint8_t *y, int64_t M,
+                            int64_t N, int64_t K, int32_t *P) {
+    const int64_t nb = K / QK_K;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            (void)q4_K_row_dot(w + n * nb * ORC_Q4_K_BYTES, y + m * nb * ORC_Q8_K_BYTES,
+                               nb, P + (m * N + n) * (K / 32), NULL);
+}
+
+void orc_q4_0_block_sums(const uint8_t *w, const uint8_t *y, int64_t M,
+                         int64_t N, int64_t K, int32_t *P) {
+    const int64_t nb = K / QK4_0;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            (void)q4_0_row_dot(w + n * nb * ORC_Q4_0_BYTES, y + m * nb * ORC_Q8_0_BYTES,
+                               nb, P + (m * N + n) * nb, NULL);
+}
+
+void orc_sample_q4_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                          int64_t N, int64_t K, const int64_t *ms,
+                          const int64_t *ns, int64_t count, double *out,
+                          double *terms) {
+    const int64_t nb = K / QK_K;
+    (void)M; (void)N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = q4_K_row_dot(w + ns[i] * nb * ORC_Q4_K_BYTES,
+                              y + ms[i] * nb * ORC_Q8_K_BYTES, nb, NULL, &terms[i]);
+}
+
+void orc_sample_q4_0_q8_0(const uint8_t *w, const uint8_t *y, int64_t M,
+                          int64_t N, int64_t K, const int64_t *ms,
+                          const int64_t *ns, int64_t count, double *out,
+                          double *terms) {
+    const int64_t nb = K / QK4_0;
+    (void)M; (void)N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = q4_0_row_dot(w + ns[i] * nb * ORC_Q4_0_BYTES,
+                              y + ms[i] * nb * ORC_Q8_0_BYTES, nb, NULL, &terms[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Load-time layouts.  P3 "Ladder Permutation" describes an offline,        */
+/* lossless permutation of static weights into the order the kernel reads.   */
+/* The layouts below are this project's own; this is their definition as an */
+/* index map, written independently of the GPU repack kernels.               */
+/* ------------------------------------------------------------------------ */
+int64_t orc_repacked_bytes_q4_K(int64_t N, int64_t K) {
+    return N * (K / QK_K) * ORC_Q4_K_BYTES;
+}
+
+int64_t orc_repacked_bytes_q4_0(int64_t N, int64_t K) {
+    int64_t nblk = N * (K / QK4_0);
+    int64_t dsec = (2 * nblk + 255) / 256 * 256;
+    return dsec + 16 * nblk;
+}
+
+void orc_repack_q4_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out) {
+    const int64_t nb = K / QK_K;
+    const int64_t pay0 = 16 * N * nb;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *src = canon + (n * nb + b) * ORC_Q4_K_BYTES;
+            memcpy(out + 16 * (n * nb + b), src, 16);
+            memcpy(out + pay0 + 128 * (n * nb + b), src + 16, 128);
+        }
+}
+
+void orc_repack_q4_0(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out) {
+    const int64_t nblk = N * (K / QK4_0);
+    const int64_t dsec = (2 * nblk + 255) / 256 * 256;
+    memset(out, 0, (size_t)dsec);
+    for (int64_t i = 0; i < nblk; ++i) {
+        const uint8_t *src = canon + i * ORC_Q4_0_BYTES;
+        memcpy(out + 2 * i, src, 2);
+        memcpy(out + dsec + 16 * i, src + 2, 16);
+    }
+}
