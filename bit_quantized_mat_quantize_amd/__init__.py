@@ -1,0 +1,10 @@
+"""Quantized mul_mat (Q4_0 / Q4_K weights x Q8_0 / Q8_K activations) on MI355X.
+
+The computation lives in ``libqmm.so`` (hand-written HIP kernels for gfx950
+behind the C ABI of ``include/qmm.h``); this package is its thin binding.
+"""
+from ._binding import (  # noqa: F401
+    ALGO_AUTO, ALGO_GEMV, ALGO_MFMA, CANONICAL, LIB_PATH, Q4_0, Q4_K, Q8_0, Q8_K, REPACKED,
+    QmmError, act_bytes, debug_block_sums, load, mul_mat_q4_0, mul_mat_q4_K, quantize_row_q8,
+    quantize_weights, repack_weights, version, weight_bytes,
+)

@@ -1,0 +1,182 @@
+"""ctypes binding of libqmm (include/qmm.h): argument marshalling only.
+
+Every computation runs in the HIP kernels of ``libqmm.so``; this module checks
+that it was handed torch tensors on the GPU, passes their device pointers and
+the current HIP stream, and turns a non-zero status into :class:`QmmError`.
+There is no fallback: if ``libqmm.so`` is missing, importing the entry points
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqmm.so")
+
+# enums of include/qmm.h
+Q8_0, Q8_K = 0, 1
+Q4_0, Q4_K = 0, 1
+CANONICAL, REPACKED = 0, 1
+ALGO_AUTO, ALGO_GEMV, ALGO_MFMA = 0, 1, 2
+STATUS = {0: "QMM_OK", 1: "QMM_EINVAL", 2: "QMM_EALIGN", 3: "QMM_EUNSUPPORTED", 4: "QMM_EDEVICE"}
+
+_ACT = {"q8_0": Q8_0, "q8_K": Q8_K}
+_WEIGHT = {"q4_0": Q4_0, "q4_K": Q4_K}
+_LAYOUT = {"canonical": CANONICAL, "repacked": REPACKED}
+_ALGO = {"auto": ALGO_AUTO, "gemv": ALGO_GEMV, "mfma": ALGO_MFMA}
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libqmm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m bit_quantized_mat_quantize_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    sigs = {
+        "qmm_act_bytes": (SZ, [I, I64, I64]),
+        "qmm_weight_bytes": (SZ, [I, I, I64, I64]),
+        "qmm_quantize_row_q8": (I, [I, P, I64, I64, P, SZ, P]),
+        "qmm_quantize_weights": (I, [I, P, I64, I64, P, SZ, P]),
+        "qmm_repack_weights": (I, [I, P, I64, I64, P, SZ, P]),
+        "qmm_mul_mat_q4_0": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
+        "qmm_mul_mat_q4_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
+        "qmm_mul_mat_q4_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
+        "qmm_debug_block_sums": (I, [I, P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
+        "qmm_status_string": (ctypes.c_char_p, [I]),
+        "qmm_last_error": (ctypes.c_char_p, []),
+        "qmm_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise QmmError(status, where, load().qmm_last_error().decode())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size()
+
+
+def act_bytes(fmt: str, M: int, K: int) -> int:
+    return int(load().qmm_act_bytes(_ACT[fmt], M, K))
+
+
+def weight_bytes(fmt: str, layout: str, N: int, K: int) -> int:
+    return int(load().qmm_weight_bytes(_WEIGHT[fmt], _LAYOUT[layout], N, K))
+
+
+def quantize_row_q8(x, fmt: str = "q8_K", out=None, stream=None):
+    """fp32 [M, K] GPU tensor -> uint8 activation blocks (bit-exact Q8_0/Q8_K)."""
+    import torch
+    M, K = x.shape
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32")
+    if out is None:
+        out = torch.empty(max(act_bytes(fmt, M, K), 1), dtype=torch.uint8, device=x.device)
+    px, _ = _dev(x, "x")
+    py, ny = _dev(out, "y")
+    _check(load().qmm_quantize_row_q8(_ACT[fmt], px, M, K, py, ny, _stream(stream)),
+           "qmm_quantize_row_q8")
+    return out
+
+
+def quantize_weights(w, fmt: str = "q4_K", out=None, stream=None):
+    """fp32 [N, K] GPU tensor -> canonical uint8 weight blocks."""
+    import torch
+    N, K = w.shape
+    if w.dtype != torch.float32:
+        raise ValueError("w must be float32")
+    if out is None:
+        out = torch.empty(max(weight_bytes(fmt, "canonical", N, K), 1), dtype=torch.uint8,
+                          device=w.device)
+    pw, _ = _dev(w, "w")
+    po, no = _dev(out, "out")
+    _check(load().qmm_quantize_weights(_WEIGHT[fmt], pw, N, K, po, no, _stream(stream)),
+           "qmm_quantize_weights")
+    return out
+
+
+def repack_weights(w, fmt: str, N: int, K: int, out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty(max(weight_bytes(fmt, "repacked", N, K), 1), dtype=torch.uint8,
+                          device=w.device)
+    pw, _ = _dev(w, "w_canon")
+    po, no = _dev(out, "w_repacked")
+    _check(load().qmm_repack_weights(_WEIGHT[fmt], pw, N, K, po, no, _stream(stream)),
+           "qmm_repack_weights")
+    return out
+
+
+def mul_mat_q4_0(w, y, M: int, N: int, K: int, layout: str = "canonical", out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=y.device)
+    pw, nw = _dev(w, "w")
+    py, ny = _dev(y, "y")
+    po, no = _dev(out, "out")
+    _check(load().qmm_mul_mat_q4_0(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
+                                   _stream(stream)), "qmm_mul_mat_q4_0")
+    return out
+
+
+def mul_mat_q4_K(w, y, M: int, N: int, K: int, layout: str = "canonical", algo: str = "auto",
+                 out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=y.device)
+    pw, nw = _dev(w, "w")
+    py, ny = _dev(y, "y")
+    po, no = _dev(out, "out")
+    _check(load().qmm_mul_mat_q4_K_ex(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
+                                      _ALGO[algo], _stream(stream)), "qmm_mul_mat_q4_K")
+    return out
+
+
+def debug_block_sums(wfmt: str, w, y, M: int, N: int, K: int, layout: str = "canonical",
+                     out=None, stream=None):
+    """int32 [M, N, K/32] per-sub-block (Q4_K) or per-block (Q4_0) sums."""
+    import torch
+    if out is None:
+        out = torch.empty((M, N, K // 32), dtype=torch.int32, device=y.device)
+    pw, nw = _dev(w, "w")
+    py, ny = _dev(y, "y")
+    po, no = _dev(out, "P")
+    _check(load().qmm_debug_block_sums(_WEIGHT[wfmt], pw, nw, _LAYOUT[layout], py, ny, po, no,
+                                       M, N, K, _stream(stream)), "qmm_debug_block_sums")
+    return out
+
+
+def version() -> str:
+    return load().qmm_version().decode()

@@ -1,0 +1,247 @@
+// api.hip -- the extern "C" entry points of libqmm (declared in include/qmm.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so a bad call returns an error code, enqueues nothing and needs
+// no GPU to be tested.  Valid calls dispatch to the kernel families in
+// quantize.hip, repack.hip, gemv.hip and gemm.hip.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/qmm.h"
+#include "qmm_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qmm_status fail(qmm_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+constexpr int64_t kMaxRows = int64_t(1) << 24;
+constexpr int64_t kMaxK = int64_t(1) << 20;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int act_qk(qmm_act_type t) { return t == QMM_Q8_0 ? 32 : (t == QMM_Q8_K ? 256 : 0); }
+int act_bytes_per_block(qmm_act_type t) { return t == QMM_Q8_0 ? 34 : 292; }
+int w_qk(qmm_weight_type t) { return t == QMM_Q4_0 ? 32 : (t == QMM_Q4_K ? 256 : 0); }
+int w_bytes_per_block(qmm_weight_type t) { return t == QMM_Q4_0 ? 18 : 144; }
+
+qmm_status check_rows(const char *name, int64_t v) {
+    if (v < 0) return fail(QMM_EINVAL, "%s = %lld is negative", name, (long long)v);
+    if (v > kMaxRows)
+        return fail(QMM_EUNSUPPORTED, "%s = %lld exceeds the limit %lld", name, (long long)v,
+                    (long long)kMaxRows);
+    return QMM_OK;
+}
+
+qmm_status check_k(int64_t K, int qk) {
+    if (K <= 0 || K % qk != 0)
+        return fail(QMM_EUNSUPPORTED, "K = %lld must be a positive multiple of %d", (long long)K, qk);
+    if (K > kMaxK)
+        return fail(QMM_EUNSUPPORTED, "K = %lld exceeds the limit %lld", (long long)K, (long long)kMaxK);
+    return QMM_OK;
+}
+
+qmm_status check_ptr(const char *name, const void *p) {
+    if (!p) return fail(QMM_EINVAL, "%s is NULL", name);
+    if (!aligned16(p)) return fail(QMM_EALIGN, "%s = %p is not 16-byte aligned", name, p);
+    return QMM_OK;
+}
+
+qmm_status check_size(const char *name, size_t have, size_t need) {
+    if (have < need)
+        return fail(QMM_EINVAL, "%s holds %zu bytes, %zu needed", name, have, need);
+    return QMM_OK;
+}
+
+qmm_status device_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return QMM_OK;
+    return fail(QMM_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define QMM_TRY(expr)                        \
+    do {                                     \
+        const qmm_status st_ = (expr);       \
+        if (st_ != QMM_OK) return st_;       \
+    } while (0)
+
+qmm_status mul_mat_common(qmm_weight_type wt, const void *w, size_t w_bytes, qmm_layout l,
+                          const void *y, size_t y_bytes, const float *out, size_t out_bytes,
+                          int64_t M, int64_t N, int64_t K) {
+    if (l != QMM_LAYOUT_CANONICAL && l != QMM_LAYOUT_REPACKED)
+        return fail(QMM_EUNSUPPORTED, "unknown layout %d", (int)l);
+    QMM_TRY(check_rows("M", M));
+    QMM_TRY(check_rows("N", N));
+    QMM_TRY(check_k(K, w_qk(wt)));
+    if (M == 0 || N == 0) return QMM_OK;
+    QMM_TRY(check_ptr("w", w));
+    QMM_TRY(check_ptr("y", y));
+    QMM_TRY(check_ptr("out", out));
+    QMM_TRY(check_size("w", w_bytes, qmm_weight_bytes(wt, l, N, K)));
+    const qmm_act_type at = wt == QMM_Q4_0 ? QMM_Q8_0 : QMM_Q8_K;
+    QMM_TRY(check_size("y", y_bytes, qmm_act_bytes(at, M, K)));
+    QMM_TRY(check_size("out", out_bytes, (size_t)(M * N) * sizeof(float)));
+    return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qmm_act_bytes(qmm_act_type t, int64_t M, int64_t K) {
+    const int qk = act_qk(t);
+    if (!qk || M < 0 || K < 0 || K % qk) return 0;
+    return (size_t)(M * (K / qk) * act_bytes_per_block(t));
+}
+
+size_t qmm_weight_bytes(qmm_weight_type t, qmm_layout l, int64_t N, int64_t K) {
+    const int qk = w_qk(t);
+    if (!qk || N < 0 || K < 0 || K % qk) return 0;
+    if (l != QMM_LAYOUT_CANONICAL && l != QMM_LAYOUT_REPACKED) return 0;
+    if (t == QMM_Q4_0 && l == QMM_LAYOUT_REPACKED) return (size_t)qmm::repacked_bytes_q4_0(N, K);
+    return (size_t)(N * (K / qk) * w_bytes_per_block(t));
+}
+
+qmm_status qmm_quantize_row_q8(qmm_act_type t, const float *x, int64_t M, int64_t K, void *y,
+                               size_t y_bytes, void *stream) {
+    const int qk = act_qk(t);
+    if (!qk) return fail(QMM_EUNSUPPORTED, "unknown activation type %d", (int)t);
+    QMM_TRY(check_rows("M", M));
+    QMM_TRY(check_k(K, qk));
+    if (M == 0) return QMM_OK;
+    QMM_TRY(check_ptr("x", x));
+    QMM_TRY(check_ptr("y", y));
+    QMM_TRY(check_size("y", y_bytes, qmm_act_bytes(t, M, K)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *yo = static_cast<uint8_t *>(y);
+    return device_status(t == QMM_Q8_K ? qmm::launch_quantize_q8_K(x, yo, M, K, s)
+                                       : qmm::launch_quantize_q8_0(x, yo, M, K, s),
+                         "quantize_row_q8 launch");
+}
+
+qmm_status qmm_quantize_weights(qmm_weight_type t, const float *w, int64_t N, int64_t K, void *out,
+                                size_t out_bytes, void *stream) {
+    const int qk = w_qk(t);
+    if (!qk) return fail(QMM_EUNSUPPORTED, "unknown weight type %d", (int)t);
+    QMM_TRY(check_rows("N", N));
+    QMM_TRY(check_k(K, qk));
+    if (N == 0) return QMM_OK;
+    QMM_TRY(check_ptr("w", w));
+    QMM_TRY(check_ptr("out", out));
+    QMM_TRY(check_size("out", out_bytes, qmm_weight_bytes(t, QMM_LAYOUT_CANONICAL, N, K)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *o = static_cast<uint8_t *>(out);
+    return device_status(t == QMM_Q4_K ? qmm::launch_encode_q4_K(w, o, N, K, s)
+                                       : qmm::launch_encode_q4_0(w, o, N, K, s),
+                         "quantize_weights launch");
+}
+
+qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N, int64_t K,
+                              void *w_repacked, size_t out_bytes, void *stream) {
+    const int qk = w_qk(t);
+    if (!qk) return fail(QMM_EUNSUPPORTED, "unknown weight type %d", (int)t);
+    QMM_TRY(check_rows("N", N));
+    QMM_TRY(check_k(K, qk));
+    if (N == 0) return QMM_OK;
+    QMM_TRY(check_ptr("w_canon", w_canon));
+    QMM_TRY(check_ptr("w_repacked", w_repacked));
+    const size_t need = qmm_weight_bytes(t, QMM_LAYOUT_REPACKED, N, K);
+    QMM_TRY(check_size("w_repacked", out_bytes, need));
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(w_canon);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(w_repacked);
+    const size_t in_bytes = qmm_weight_bytes(t, QMM_LAYOUT_CANONICAL, N, K);
+    if (a0 < b0 + need && b0 < a0 + in_bytes)
+        return fail(QMM_EINVAL, "w_canon and w_repacked overlap");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t *in = static_cast<const uint8_t *>(w_canon);
+    uint8_t *o = static_cast<uint8_t *>(w_repacked);
+    return device_status(t == QMM_Q4_K ? qmm::launch_repack_q4_K(in, o, N, K, s)
+                                       : qmm::launch_repack_q4_0(in, o, N, K, s),
+                         "repack_weights launch");
+}
+
+qmm_status qmm_mul_mat_q4_0(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                            size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                            int64_t K, void *stream) {
+    QMM_TRY(mul_mat_common(QMM_Q4_0, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
+    if (M == 0 || N == 0) return QMM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool rep = l == QMM_LAYOUT_REPACKED;
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const uint8_t *yb = static_cast<const uint8_t *>(y);
+    // groups of up to 8 activation rows per GEMV launch
+    for (int64_t m0 = 0; m0 < M; m0 += qmm::kGemvMaxM) {
+        const int64_t mm = M - m0 < qmm::kGemvMaxM ? M - m0 : qmm::kGemvMaxM;
+        QMM_TRY(device_status(qmm::launch_gemv_q4_0(wb, rep, yb + m0 * (K / 32) * 34, out + m0 * N,
+                                                    mm, N, K, s),
+                              "mul_mat_q4_0 launch"));
+    }
+    return QMM_OK;
+}
+
+qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                               size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                               int64_t K, qmm_algo algo, void *stream) {
+    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
+        return fail(QMM_EUNSUPPORTED, "unknown algo %d", (int)algo);
+    QMM_TRY(mul_mat_common(QMM_Q4_K, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
+    if (algo == QMM_ALGO_GEMV && M > qmm::kGemvMaxM)
+        return fail(QMM_EUNSUPPORTED, "GEMV path takes M <= %d (M = %lld)", qmm::kGemvMaxM,
+                    (long long)M);
+    if (M == 0 || N == 0) return QMM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool rep = l == QMM_LAYOUT_REPACKED;
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const uint8_t *yb = static_cast<const uint8_t *>(y);
+    const bool gemv = algo == QMM_ALGO_GEMV || (algo == QMM_ALGO_AUTO && M <= qmm::kGemvMaxM);
+    if (gemv)
+        return device_status(qmm::launch_gemv_q4_K(wb, rep, yb, out, M, N, K, s), "mul_mat_q4_K gemv launch");
+    return device_status(qmm::launch_gemm_q4_K(wb, rep, yb, out, M, N, K, s), "mul_mat_q4_K gemm launch");
+}
+
+qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                            size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                            int64_t K, void *stream) {
+    return qmm_mul_mat_q4_K_ex(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, QMM_ALGO_AUTO,
+                               stream);
+}
+
+qmm_status qmm_debug_block_sums(qmm_weight_type t, const void *w, size_t w_bytes, qmm_layout l,
+                                const void *y, size_t y_bytes, int32_t *P, size_t p_bytes,
+                                int64_t M, int64_t N, int64_t K, void *stream) {
+    if (!w_qk(t)) return fail(QMM_EUNSUPPORTED, "unknown weight type %d", (int)t);
+    QMM_TRY(mul_mat_common(t, w, w_bytes, l, y, y_bytes, reinterpret_cast<const float *>(P),
+                           p_bytes, M, N, K));
+    if (M == 0 || N == 0) return QMM_OK;
+    QMM_TRY(check_size("P", p_bytes, (size_t)(M * N * (K / 32)) * sizeof(int32_t)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool rep = l == QMM_LAYOUT_REPACKED;
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const uint8_t *yb = static_cast<const uint8_t *>(y);
+    return device_status(t == QMM_Q4_K ? qmm::launch_block_sums_q4_K(wb, rep, yb, P, M, N, K, s)
+                                       : qmm::launch_block_sums_q4_0(wb, rep, yb, P, M, N, K, s),
+                         "debug_block_sums launch");
+}
+
+const char *qmm_status_string(qmm_status s) {
+    switch (s) {
+        case QMM_OK: return "ok";
+        case QMM_EINVAL: return "invalid argument";
+        case QMM_EALIGN: return "pointer not 16-byte aligned";
+        case QMM_EUNSUPPORTED: return "unsupported shape or option";
+        case QMM_EDEVICE: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *qmm_last_error(void) { return g_err; }
+
+const char *qmm_version(void) { return "qmm 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,297 @@
+// gemv.hip -- memory-bound quantized GEMV (M <= 8) for gfx950.
+//
+// Decode is bound by the weight stream (ggml-cpu mul_mat page, "先把账算清楚":
+// at M = 1 the time per token is the weight bytes over the bandwidth), so the
+// kernel is shaped around HBM: one wavefront per R output rows, each lane owns
+// one 16-byte piece of a block payload per step, consecutive lanes read
+// consecutive pieces (a wavefront step reads 1 KiB per row, coalesced), and the
+// nibbles are unpacked in registers with two masks and a shift, never written
+// back to memory (same section; "正确性:缩放系数可以提到求和号外面" for the
+// byte order).  The int8 products use v_dot4_i32_i8 (4 MACs per lane per
+// instruction), the block scales are applied once per 16-element piece, and
+// the per-lane fp32 partials are reduced across the wavefront at the end.
+//
+// Q4_K piece c of block b (c = 2g + h, g = 64-element group, h = half):
+//   payload bytes 32g+16h .. +15 -> low nibbles  = elements 64g+16h+i    (sub-block 2g)
+//                                   high nibbles = elements 64g+32+16h+i (sub-block 2g+1)
+//   activation codes qs[64g+16h ..], qs[64g+32+16h ..], bsums[4g+h], bsums[4g+2+h]
+//   partial = d_a * (d * (s_2g*P_lo + s_2g+1*P_hi) - dmin * (m_2g*B_lo + m_2g+1*B_hi))
+// Summed over the 8 pieces of a block this is d_a*(d*S - dmin*Mn) of the
+// ggml-cpu page ("正确性" and "min 项与最终归约").
+#include "qmm_device.h"
+#include "qmm_launch.h"
+
+namespace qmm {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+template <bool REPACKED>
+struct Q4KAddr {
+    const uint8_t *W;
+    int64_t N, nb;
+    __device__ __forceinline__ const uint8_t *header(int64_t n, int64_t b) const {
+        return REPACKED ? W + 16 * (n * nb + b) : W + kQ4_KBytes * (n * nb + b);
+    }
+    __device__ __forceinline__ const uint8_t *piece(int64_t n, int64_t b, int c) const {
+        return REPACKED ? W + 16 * N * nb + 128 * (n * nb + b) + 16 * c
+                        : W + kQ4_KBytes * (n * nb + b) + 16 + 16 * c;
+    }
+};
+
+// MODE 0: out[m*N+n] fp32.  MODE 1: int32 sub-block sums P[m][n][K/32].
+template <int M, int R, bool REPACKED, int MODE>
+__global__ __launch_bounds__(256) void k_gemv_q4_K(const uint8_t *__restrict__ W,
+                                                   const uint8_t *__restrict__ Y,
+                                                   void *__restrict__ dst, int64_t N, int64_t K) {
+    const int64_t nb = K / QK_K;
+    const int nchunk = (int)(nb * 8);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t n0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * R;
+    if (n0 >= N) return;  // uniform per wavefront
+    const Q4KAddr<REPACKED> A{W, N, nb};
+
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+    for (int c = lane; c < nchunk; c += kWave) {
+        const int b = c >> 3, cc = c & 7, g = cc >> 1, h = cc & 1;
+        uint4 pw[R], hw[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t n = n0 + r < N ? n0 + r : N - 1;
+            hw[r] = ld16(A.header(n, b));
+            pw[r] = ld16(A.piece(n, b, cc));
+        }
+        uint4 ylo[M], yhi[M];
+        float da[M];
+        int bs_lo[M], bs_hi[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint8_t *yb = Y + ((int64_t)m * nb + b) * kQ8_KBytes;
+            ylo[m] = ld_align4<uint4>(yb + 4 + 64 * g + 16 * h);
+            yhi[m] = ld_align4<uint4>(yb + 4 + 64 * g + 32 + 16 * h);
+            da[m] = ld_align4<float>(yb);
+            bs_lo[m] = *reinterpret_cast<const int16_t *>(yb + 260 + 2 * (4 * g + h));
+            bs_hi[m] = *reinterpret_cast<const int16_t *>(yb + 260 + 2 * (4 * g + 2 + h));
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const Q4KScales sc = unpack_scales(hw[r].y, hw[r].z, hw[r].w);
+            const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
+            const uint32_t mw = g < 2 ? sc.m_lo : sc.m_hi;
+            const int sh = (g & 1) * 16;
+            const int s0 = (sw >> sh) & 0xff, s1 = (sw >> (sh + 8)) & 0xff;
+            const int m0 = (mw >> sh) & 0xff, m1 = (mw >> (sh + 8)) & 0xff;
+            const float d = f16_bits_to_f32(hw[r].x & 0xffff);
+            const float dmin = f16_bits_to_f32(hw[r].x >> 16);
+            const uint32_t l0 = pw[r].x & 0x0f0f0f0fu, l1 = pw[r].y & 0x0f0f0f0fu;
+            const uint32_t l2 = pw[r].z & 0x0f0f0f0fu, l3 = pw[r].w & 0x0f0f0f0fu;
+            const uint32_t h0 = (pw[r].x >> 4) & 0x0f0f0f0fu, h1 = (pw[r].y >> 4) & 0x0f0f0f0fu;
+            const uint32_t h2 = (pw[r].z >> 4) & 0x0f0f0f0fu, h3 = (pw[r].w >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                int plo = dot4(l0, ylo[m].x, 0);
+                plo = dot4(l1, ylo[m].y, plo);
+                plo = dot4(l2, ylo[m].z, plo);
+                plo = dot4(l3, ylo[m].w, plo);
+                int phi = dot4(h0, yhi[m].x, 0);
+                phi = dot4(h1, yhi[m].y, phi);
+                phi = dot4(h2, yhi[m].z, phi);
+                phi = dot4(h3, yhi[m].w, phi);
+                if (MODE == 0) {
+                    const int S = s0 * plo + s1 * phi;
+                    const int Mn = m0 * bs_lo[m] + m1 * bs_hi[m];
+                    const float t = fmaf(d, (float)S, -dmin * (float)Mn);
+                    acc[r][m] = fmaf(da[m], t, acc[r][m]);
+                } else {
+                    // full sub-block sums: the two halves sit in lanes c and c^1
+                    const int plo_all = plo + __shfl_xor(plo, 1, kWave);
+                    const int phi_all = phi + __shfl_xor(phi, 1, kWave);
+                    if (h == 0 && n0 + r < N) {
+                        int32_t *P = reinterpret_cast<int32_t *>(dst) +
+                                     ((int64_t)m * N + n0 + r) * (K / 32) + 8 * b + 2 * g;
+                        P[0] = plo_all;
+                        P[1] = phi_all;
+                    }
+                }
+            }
+        }
+    }
+    if (MODE == 0) {
+        float *out = reinterpret_cast<float *>(dst);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float v = wave_sum(acc[r][m]);
+                if (lane == 0 && n0 + r < N) out[(int64_t)m * N + n0 + r] = v;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q4_0 x Q8_0: one lane per 32-element block (16-byte payload).  Canonical
+// blocks are 18 B and Q8_0 blocks 34 B, so both are read with 2-byte loads;
+// the repacked weight payload is read with one aligned 16-byte load.
+// P_b = sum (q-8)*y = sum q*y - 8*sum y; partial = d_w*d_a*P_b.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ld_u32_a2(const uint8_t *p) {
+    const uint16_t *q = reinterpret_cast<const uint16_t *>(p);
+    return (uint32_t)q[0] | ((uint32_t)q[1] << 16);
+}
+
+template <int M, bool REPACKED, int MODE>
+__global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ W,
+                                                   const uint8_t *__restrict__ Y,
+                                                   void *__restrict__ dst, int64_t N, int64_t K,
+                                                   int64_t dsec) {
+    const int64_t nb = K / QK4_0;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (n >= N) return;  // uniform per wavefront
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    for (int64_t b = lane; b < nb; b += kWave) {
+        uint32_t w[4];
+        float dw;
+        if (REPACKED) {
+            const uint4 v = ld16(W + dsec + 16 * (n * nb + b));
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            dw = f16_bits_to_f32(ld_u16(W + 2 * (n * nb + b)));
+        } else {
+            const uint8_t *blk = W + kQ4_0Bytes * (n * nb + b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = ld_u32_a2(blk + 2 + 4 * i);
+            dw = f16_bits_to_f32(ld_u16(blk));
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint8_t *yb = Y + ((int64_t)m * nb + b) * kQ8_0Bytes;
+            const float da = f16_bits_to_f32(ld_u16(yb));
+            int p = 0, ys = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t ya = ld_u32_a2(yb + 2 + 4 * i);        // elements 4i..4i+3
+                const uint32_t yc = ld_u32_a2(yb + 2 + 16 + 4 * i);   // elements 16+4i..
+                p = dot4(w[i] & 0x0f0f0f0fu, ya, p);
+                p = dot4((w[i] >> 4) & 0x0f0f0f0fu, yc, p);
+                ys = dot4(0x01010101u, ya, ys);
+                ys = dot4(0x01010101u, yc, ys);
+            }
+            p -= 8 * ys;
+            if (MODE == 0) {
+                acc[m] = fmaf(dw * da, (float)p, acc[m]);
+            } else {
+                reinterpret_cast<int32_t *>(dst)[((int64_t)m * N + n) * nb + b] = p;
+            }
+        }
+    }
+    if (MODE == 0) {
+        float *out = reinterpret_cast<float *>(dst);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float v = wave_sum(acc[m]);
+            if (lane == 0) out[(int64_t)m * N + n] = v;
+        }
+    }
+}
+
+template <int MODE>
+hipError_t dispatch_q4_K(const uint8_t *w, bool rep, const uint8_t *y, void *dst, int64_t M,
+                         int64_t N, int64_t K, hipStream_t s) {
+#define QMM_GEMV_K(MM, RR)                                                                       \
+    do {                                                                                         \
+        const int64_t rows_per_block = (int64_t)kWavesPerBlock * (RR);                           \
+        const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block));                  \
+        if (rep)                                                                                 \
+            hipLaunchKernelGGL((k_gemv_q4_K<MM, RR, true, MODE>), grid, dim3(256), 0, s, w, y,    \
+                               dst, N, K);                                                       \
+        else                                                                                     \
+            hipLaunchKernelGGL((k_gemv_q4_K<MM, RR, false, MODE>), grid, dim3(256), 0, s, w, y,   \
+                               dst, N, K);                                                       \
+    } while (0)
+    switch (M) {
+        case 1: QMM_GEMV_K(1, 1); break;
+        case 2: QMM_GEMV_K(2, 2); break;
+        case 3: QMM_GEMV_K(3, 2); break;
+        case 4: QMM_GEMV_K(4, 2); break;
+        case 5: QMM_GEMV_K(5, 2); break;
+        case 6: QMM_GEMV_K(6, 2); break;
+        case 7: QMM_GEMV_K(7, 2); break;
+        case 8: QMM_GEMV_K(8, 2); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef QMM_GEMV_K
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t dispatch_q4_0(const uint8_t *w, bool rep, const uint8_t *y, void *dst, int64_t M,
+                         int64_t N, int64_t K, hipStream_t s) {
+    const int64_t dsec = repacked_bytes_q4_0(N, K) - 16 * N * (K / QK4_0);
+    const dim3 grid((unsigned)((N + kWavesPerBlock - 1) / kWavesPerBlock));
+#define QMM_GEMV_0(MM)                                                                            \
+    do {                                                                                          \
+        if (rep)                                                                                  \
+            hipLaunchKernelGGL((k_gemv_q4_0<MM, true, MODE>), grid, dim3(256), 0, s, w, y, dst, N, \
+                               K, dsec);                                                          \
+        else                                                                                      \
+            hipLaunchKernelGGL((k_gemv_q4_0<MM, false, MODE>), grid, dim3(256), 0, s, w, y, dst,   \
+                               N, K, dsec);                                                       \
+    } while (0)
+    switch (M) {
+        case 1: QMM_GEMV_0(1); break;
+        case 2: QMM_GEMV_0(2); break;
+        case 3: QMM_GEMV_0(3); break;
+        case 4: QMM_GEMV_0(4); break;
+        case 5: QMM_GEMV_0(5); break;
+        case 6: QMM_GEMV_0(6); break;
+        case 7: QMM_GEMV_0(7); break;
+        case 8: QMM_GEMV_0(8); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef QMM_GEMV_0
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    return dispatch_q4_K<0>(w, repacked, y, out, M, N, K, s);
+}
+
+hipError_t launch_block_sums_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    // the sums path is launched per group of up to 8 activation rows
+    for (int64_t m0 = 0; m0 < M; m0 += kGemvMaxM) {
+        const int64_t mm = M - m0 < kGemvMaxM ? M - m0 : kGemvMaxM;
+        hipError_t e = dispatch_q4_K<1>(w, repacked, y + m0 * (K / QK_K) * kQ8_KBytes,
+                                        P + m0 * N * (K / 32), mm, N, K, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_gemv_q4_0(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    return dispatch_q4_0<0>(w, repacked, y, out, M, N, K, s);
+}
+
+hipError_t launch_block_sums_q4_0(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    for (int64_t m0 = 0; m0 < M; m0 += kGemvMaxM) {
+        const int64_t mm = M - m0 < kGemvMaxM ? M - m0 : kGemvMaxM;
+        hipError_t e = dispatch_q4_0<1>(w, repacked, y + m0 * (K / QK4_0) * kQ8_0Bytes,
+                                        P + m0 * N * (K / 32), mm, N, K, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace qmm

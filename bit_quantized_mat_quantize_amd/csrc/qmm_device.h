@@ -1,0 +1,75 @@
+// qmm_device.h -- device-side helpers shared by the libqmm kernels (gfx950).
+//
+// Byte formats are those of include/qmm.h.  Everything here is written for
+// CDNA4: 64-lane wavefronts, int8 dot products (v_dot4_i32_i8), MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+constexpr int kWave = 64;
+constexpr int QK4_0 = 32;
+constexpr int QK_K = 256;
+constexpr int kQ4_0Bytes = 18;
+constexpr int kQ8_0Bytes = 34;
+constexpr int kQ4_KBytes = 144;
+constexpr int kQ8_KBytes = 292;
+
+// ---- fp16 <-> fp32 (hardware conversions; fp32 -> fp16 rounds to nearest even)
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    _Float16 v;
+    uint16_t b = (uint16_t)h;
+    __builtin_memcpy(&v, &b, 2);
+    return (float)v;
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    _Float16 v = (_Float16)f;
+    uint16_t b;
+    __builtin_memcpy(&b, &v, 2);
+    return b;
+}
+
+// ---- loads with the alignment the formats guarantee
+template <typename T>
+__device__ __forceinline__ T ld_align4(const void *p) {
+    T v;
+    __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), sizeof(T));
+    return v;
+}
+__device__ __forceinline__ uint4 ld16(const void *p) {   // 16-byte aligned
+    return *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ uint32_t ld_u16(const void *p) {
+    return *reinterpret_cast<const uint16_t *>(p);
+}
+
+// ---- wavefront reductions (all 64 lanes hold the result)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// ---- int8 dot product of 4 packed bytes, accumulated (v_dot4_i32_i8)
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// ---- Q4_K 12-byte scale field, word-parallel: from the three little-endian
+// words w1 = scales[0..3], w2 = scales[4..7], w3 = scales[8..11] build four
+// words whose bytes are s_0..s_3, m_0..m_3, s_4..s_7, m_4..m_7.
+struct Q4KScales {
+    uint32_t s_lo, m_lo, s_hi, m_hi;
+};
+__device__ __forceinline__ Q4KScales unpack_scales(uint32_t w1, uint32_t w2, uint32_t w3) {
+    Q4KScales r;
+    r.s_lo = w1 & 0x3f3f3f3fu;
+    r.m_lo = w2 & 0x3f3f3f3fu;
+    r.s_hi = (w3 & 0x0f0f0f0fu) | ((w1 >> 2) & 0x30303030u);
+    r.m_hi = ((w3 >> 4) & 0x0f0f0f0fu) | ((w2 >> 2) & 0x30303030u);
+    return r;
+}
+
+}  // namespace qmm

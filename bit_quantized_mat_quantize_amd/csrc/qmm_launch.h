@@ -1,0 +1,37 @@
+// qmm_launch.h -- internal host launchers (called by api.hip after validation).
+// Arguments are already checked: sizes in range, K a multiple of the block,
+// pointers non-null and 16-byte aligned.  Each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+hipError_t launch_quantize_q8_0(const float *x, uint8_t *y, int64_t M, int64_t K, hipStream_t s);
+hipError_t launch_quantize_q8_K(const float *x, uint8_t *y, int64_t M, int64_t K, hipStream_t s);
+hipError_t launch_encode_q4_0(const float *w, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_encode_q4_K(const float *w, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
+
+int64_t repacked_bytes_q4_0(int64_t N, int64_t K);
+hipError_t launch_repack_q4_0(const uint8_t *in, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_repack_q4_K(const uint8_t *in, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
+
+// GEMV family: M <= 8.  `repacked` selects the weight layout.
+hipError_t launch_gemv_q4_0(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemv_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
+// int32 per-(sub-)block sums with the GEMV decode path (verification aid).
+hipError_t launch_block_sums_q4_0(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_block_sums_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+// MFMA GEMM family (any M >= 1).
+hipError_t launch_gemm_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+constexpr int kGemvMaxM = 8;
+
+}  // namespace qmm

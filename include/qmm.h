@@ -1,0 +1,162 @@
+/*
+ * qmm.h -- C ABI of libqmm: quantized mul_mat (Q4_0 / Q4_K weights times
+ * Q8_0 / Q8_K activations) on AMD Instinct MI355X (gfx950).
+ *
+ * Operation (BitBLAS page, "从数学表达式到真实存储:混合精度 GEMM 的计算对象";
+ * ggml-cpu mul_mat page, "mul_mat:一次矩阵乘被切成什么样"):
+ *     out[m*N + n] = sum_k  deq(A)[m,k] * deq(W)[n,k]
+ * with W an [N, K] matrix of packed 4-bit weight blocks (row n = output channel,
+ * K contiguous) and A an [M, K] matrix of int8 activation blocks, computed
+ * without expanding W: per block, integer dot products of the codes with the
+ * block scales pulled out of the sum (ggml-cpu mul_mat page,
+ * "正确性:缩放系数可以提到求和号外面").
+ *
+ * Byte formats (little-endian), as the ggml-cpu mul_mat page defines them:
+ *   Q4_0  18 B / 32:  fp16 d; qs[16], byte l = element l (low nibble) |
+ *                     element l+16 (high nibble); w = d*(q-8)
+ *   Q8_0  34 B / 32:  fp16 d; int8 qs[32]; a = d*y
+ *   Q4_K 144 B / 256: fp16 d; fp16 dmin; scales[12]; qs[128]
+ *                     w = d*s_j*q - dmin*m_j for element k in sub-block j = k/32;
+ *                     qs byte 32g+l = element 64g+l (low) | element 64g+32+l (high)
+ *                     scales[12] bit layout (section "6-bit 参数是怎么塞进 12 字节的"):
+ *                       j<4 : s_j = byte j & 63,  m_j = byte j+4 & 63
+ *                       j>=4: s_j = (byte j+4 & 15) | (byte j-4 >> 6) << 4
+ *                             m_j = (byte j+4 >> 4) | (byte j   >> 6) << 4
+ *   Q8_K 292 B / 256: fp32 d; int8 qs[256]; int16 bsums[16] (sum of qs[16g..16g+15])
+ *   Rows are arrays of blocks: row r of a [R, K] matrix starts at r * (K/QK) * bytes.
+ *
+ * Load-time layout QMM_LAYOUT_REPACKED (a lossless byte permutation of the
+ * canonical matrix, BitBLAS page "Ladder Permutation"; produced by
+ * qmm_repack_weights):
+ *   Q4_K: [N*nb headers of 16 B: d, dmin, scales[12]] then
+ *         [N*nb payloads of 128 B: qs], block (n,b) at index n*nb+b
+ *   Q4_0: [N*nb fp16 d, zero-padded to a multiple of 256 B] then
+ *         [N*nb payloads of 16 B: qs]
+ *   (nb = blocks per row).  The payload stream is 16-byte aligned, which lets a
+ *   wavefront read weights with coalesced 16-byte loads.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers (hipMalloc / torch CUDA tensors)
+ *     owned by the caller and 16-byte aligned; the library never allocates,
+ *     frees or synchronizes; work is enqueued on `stream` (a hipStream_t; NULL
+ *     is the legacy default stream) and runs asynchronously.
+ *   - Arguments are validated on the host before any HIP call; on failure the
+ *     call returns a non-zero qmm_status, enqueues nothing and leaves a
+ *     message for qmm_last_error().  M or N equal to 0 is a valid empty call.
+ *   - K must be a positive multiple of the block length (32 for Q4_0/Q8_0,
+ *     256 for Q4_K/Q8_K), else QMM_EUNSUPPORTED.  Sizes are limited to
+ *     M, N <= 2^24 and K <= 2^20 (QMM_EUNSUPPORTED beyond).
+ *   - `*_bytes` arguments give the size of the caller's buffer; a buffer
+ *     smaller than the corresponding qmm_*_bytes() value gives QMM_EINVAL.
+ *   - A failed kernel launch gives QMM_EDEVICE.
+ *   - Functions are thread-safe (the error message is thread-local).
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QMM_OK = 0,
+    QMM_EINVAL = 1,        /* bad argument (null pointer, negative size, small buffer) */
+    QMM_EALIGN = 2,        /* pointer not 16-byte aligned */
+    QMM_EUNSUPPORTED = 3,  /* K not a multiple of the block, size limit, unknown enum */
+    QMM_EDEVICE = 4        /* HIP runtime error while enqueueing */
+} qmm_status;
+
+typedef enum { QMM_Q8_0 = 0, QMM_Q8_K = 1 } qmm_act_type;
+typedef enum { QMM_Q4_0 = 0, QMM_Q4_K = 1 } qmm_weight_type;
+typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
+
+/* Kernel family for a mul_mat call.  AUTO picks the GEMV path for small M
+ * and the MFMA GEMM path otherwise (Q4_K only; Q4_0 always uses GEMV). */
+typedef enum { QMM_ALGO_AUTO = 0, QMM_ALGO_GEMV = 1, QMM_ALGO_MFMA = 2 } qmm_algo;
+
+/* Bytes of an [M, K] activation matrix in format t: M*K/32*34 or M*K/256*292.
+ * Returns 0 for invalid arguments. */
+size_t qmm_act_bytes(qmm_act_type t, int64_t M, int64_t K);
+
+/* Bytes of an [N, K] weight matrix in format t and layout l.  Canonical:
+ * N*K/32*18 or N*K/256*144.  Repacked Q4_0 adds the padding of its scale
+ * section (at most 254 B).  Returns 0 for invalid arguments. */
+size_t qmm_weight_bytes(qmm_weight_type t, qmm_layout l, int64_t N, int64_t K);
+
+/* Quantize fp32 activations x [M, K] (row-major) to int8 blocks y [M, K/QK]
+ * (ggml-cpu mul_mat page, "第一步:激活得先变成 Q8_K": activations are
+ * converted once per mul_mat and shared by all output tiles).
+ * Per block: amax = max|x|, d = amax/127, y = rint(x * (1/d)) (ties to even),
+ * d = 0 and y = 0 for an all-zero block; Q8_0 stores fp16(d), Q8_K stores the
+ * fp32 d and the 16 bsums.  The result is bit-identical to the reference
+ * encoder.  x: device fp32, M*K elements; y: device, y_bytes >= qmm_act_bytes. */
+qmm_status qmm_quantize_row_q8(qmm_act_type t, const float *x, int64_t M, int64_t K,
+                               void *y, size_t y_bytes, void *stream);
+
+/* Encode fp32 weights w [N, K] into canonical blocks (offline; the pages give
+ * the decoded form, the scale search is this library's reading):
+ *   Q4_0: d = -xmax/8 (xmax = signed element of largest |x|, first wins),
+ *         q = clamp(rint(x*(1/d)) + 8, 0, 15)
+ *   Q4_K: per sub-block lo = min(0, min x), sc = (max x - lo)/15, mn = -lo;
+ *         d = max sc/63, dmin = max mn/63; s_j = rint(sc/d), m_j = rint(mn/dmin)
+ *         (clamped to 63); q = clamp(rint((x + f16(dmin)*m_j)/(f16(d)*s_j)), 0, 15)
+ * out: device, out_bytes >= qmm_weight_bytes(t, CANONICAL, N, K). */
+qmm_status qmm_quantize_weights(qmm_weight_type t, const float *w, int64_t N, int64_t K,
+                                void *out, size_t out_bytes, void *stream);
+
+/* Permute canonical weight blocks into QMM_LAYOUT_REPACKED (load time, once
+ * per weight matrix; the canonical bytes stay the source of truth).
+ * w_canon and w_repacked must not overlap. */
+qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N, int64_t K,
+                              void *w_repacked, size_t out_bytes, void *stream);
+
+/* out[m*N+n] = sum over blocks b of d_w*d_a*sum_i (q_i-8)*y_i  (fp32 output,
+ * overwritten).  w: Q4_0 [N,K] in layout l; y: Q8_0 [M,K] from
+ * qmm_quantize_row_q8. */
+qmm_status qmm_mul_mat_q4_0(const void *w, size_t w_bytes, qmm_layout l,
+                            const void *y, size_t y_bytes,
+                            float *out, size_t out_bytes,
+                            int64_t M, int64_t N, int64_t K, void *stream);
+
+/* out[m*N+n] = sum over super-blocks b of d_a*(d*S - dmin*Mn) with
+ * S = sum_j s_j*P_j, P_j = sum_{i in j} q_i*y_i, Mn = sum_j m_j*(bsums[2j]+bsums[2j+1])
+ * (ggml-cpu mul_mat page, "正确性" and "min 项与最终归约").  fp32 output,
+ * overwritten.  w: Q4_K [N,K] in layout l; y: Q8_K [M,K]. */
+qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l,
+                            const void *y, size_t y_bytes,
+                            float *out, size_t out_bytes,
+                            int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Same as qmm_mul_mat_q4_K with an explicit kernel family (for measuring the
+ * GEMV / GEMM crossover).  QMM_ALGO_GEMV requires M <= 8. */
+qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l,
+                               const void *y, size_t y_bytes,
+                               float *out, size_t out_bytes,
+                               int64_t M, int64_t N, int64_t K, qmm_algo algo,
+                               void *stream);
+
+/* Verification aid: the int32 per-sub-block (Q4_K) or per-block (Q4_0) sums
+ * P[m][n][K/32] = sum_{i in block} q_i*y_i  (Q4_0: (q_i-8)*y_i), computed by
+ * the same decode and int8 dot-product code the GEMV kernels use.
+ * P: device int32, p_bytes >= M*N*(K/32)*4. */
+qmm_status qmm_debug_block_sums(qmm_weight_type t, const void *w, size_t w_bytes,
+                                qmm_layout l, const void *y, size_t y_bytes,
+                                int32_t *P, size_t p_bytes,
+                                int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Static description of a status code. */
+const char *qmm_status_string(qmm_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *qmm_last_error(void);
+
+/* Library version string. */
+const char *qmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMM_H */

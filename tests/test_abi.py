@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: every symbol declared in include/qmm.h is exported
+by libqmm.so, the size helpers agree with the formats, and every validation
+error is returned by the host before any HIP call (the pointers below are never
+dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+OK, EINVAL, EALIGN, EUNSUP = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_quantized_mat_quantize_amd import _binding
+    return _binding.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[A-Za-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported(lib):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    # the exports are exactly the declared entry points (no stray C symbols)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if re.search(r" T qmm_", l)})
+    assert exported == names
+
+
+def test_size_helpers(lib):
+    assert lib.qmm_act_bytes(0, 3, 64) == 3 * 2 * 34
+    assert lib.qmm_act_bytes(1, 3, 512) == 3 * 2 * 292
+    assert lib.qmm_act_bytes(1, 3, 500) == 0
+    assert lib.qmm_weight_bytes(1, 0, 5, 512) == 5 * 2 * 144
+    assert lib.qmm_weight_bytes(1, 1, 5, 512) == 5 * 2 * 144
+    assert lib.qmm_weight_bytes(0, 0, 5, 64) == 5 * 2 * 18
+    # repacked Q4_0: scale section padded to 256 B, then 16 B per block
+    assert lib.qmm_weight_bytes(0, 1, 5, 64) == 256 + 5 * 2 * 16
+    assert lib.qmm_weight_bytes(0, 1, 256, 1024) == (2 * 256 * 32 + 255) // 256 * 256 + 16 * 256 * 32
+    assert lib.qmm_weight_bytes(7, 0, 5, 64) == 0
+
+
+def _last(lib):
+    return lib.qmm_last_error().decode()
+
+
+A = 0x10000  # a 16-byte-aligned fake address, never dereferenced
+
+
+def test_quantize_validation(lib):
+    q = lib.qmm_quantize_row_q8
+    assert q(1, A, 2, 300, A, 10**6, None) == EUNSUP and "multiple of 256" in _last(lib)
+    assert q(0, A, 2, 48, A, 10**6, None) == EUNSUP
+    assert q(1, A, 2, 0, A, 10**6, None) == EUNSUP
+    assert q(1, A, -1, 256, A, 10**6, None) == EINVAL
+    assert q(1, A, 2**24 + 1, 256, A, 10**9, None) == EUNSUP
+    assert q(1, A, 2, 2**21, A, 10**9, None) == EUNSUP
+    assert q(1, None, 2, 256, A, 10**6, None) == EINVAL and "x is NULL" in _last(lib)
+    assert q(1, A + 4, 2, 256, A, 10**6, None) == EALIGN
+    assert q(1, A, 2, 256, A + 8, 10**6, None) == EALIGN
+    assert q(1, A, 2, 256, A, 2 * 292 - 1, None) == EINVAL and "needed" in _last(lib)
+    assert q(5, A, 2, 256, A, 10**6, None) == EUNSUP
+    # empty is a valid no-op (nothing is launched, pointers may be NULL)
+    assert q(1, None, 0, 256, None, 0, None) == OK
+
+
+def test_mul_mat_validation(lib):
+    f = lib.qmm_mul_mat_q4_K_ex
+    big = 10**9
+    args = dict(w=A, wb=big, l=0, y=A, yb=big, o=A, ob=big, M=4, N=8, K=512, algo=0)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["w"], a["wb"], a["l"], a["y"], a["yb"], a["o"], a["ob"], a["M"], a["N"], a["K"],
+                 a["algo"], None)
+
+    assert call(K=384) == EUNSUP
+    assert call(l=2) == EUNSUP
+    assert call(algo=9) == EUNSUP
+    assert call(M=-1) == EINVAL
+    assert call(N=-3) == EINVAL
+    assert call(w=None) == EINVAL
+    assert call(y=A + 2) == EALIGN
+    assert call(o=A + 4) == EALIGN
+    assert call(wb=8 * 2 * 144 - 1) == EINVAL
+    assert call(yb=4 * 2 * 292 - 1) == EINVAL
+    assert call(ob=4 * 8 * 4 - 1) == EINVAL
+    assert call(M=9, algo=1) == EUNSUP and "M <= 8" in _last(lib)
+    assert call(M=0, w=None, y=None, o=None) == OK
+    assert call(N=0) == OK
+    g = lib.qmm_mul_mat_q4_0
+    assert g(A, big, 0, A, big, A, big, 1, 256, 1000, None) == EUNSUP
+    assert g(A, 18 * 32 * 256 - 1, 0, A, big, A, big, 1, 256, 1024, None) == EINVAL
+    # repacked Q4_0 needs the padded size
+    need = lib.qmm_weight_bytes(0, 1, 3, 64)
+    assert g(A, need - 1, 1, A, big, A, big, 1, 3, 64, None) == EINVAL
+
+
+def test_other_validation(lib):
+    assert lib.qmm_quantize_weights(1, A, 4, 100, A, 10**6, None) == EUNSUP
+    assert lib.qmm_quantize_weights(0, A, 4, 64, A, 4 * 2 * 18 - 1, None) == EINVAL
+    assert lib.qmm_quantize_weights(3, A, 4, 64, A, 10**6, None) == EUNSUP
+    assert lib.qmm_repack_weights(1, A, 4, 256, A + 4 * 144 - 16, 10**6, None) == EINVAL  # overlap
+    assert "overlap" in _last(lib)
+    assert lib.qmm_repack_weights(1, A, 4, 256, A + 10**6, 4 * 144 - 1, None) == EINVAL
+    assert lib.qmm_debug_block_sums(1, A, 10**9, 0, A, 10**9, A, 4 * 8 * 16 * 4 - 1,
+                                    4, 8, 512, None) == EINVAL
+    assert lib.qmm_debug_block_sums(2, A, 10**9, 0, A, 10**9, A, 10**9, 4, 8, 512, None) == EUNSUP
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.qmm_status_string(s)
+    assert lib.qmm_version().startswith(b"qmm")
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from bit_quantized_mat_quantize_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _binding.load()
+
+
+def test_product_path_does_not_import_oracle():
+    """The product package must not reach the oracle (test infrastructure)."""
+    pkg = os.path.join(ROOT, "bit_quantized_mat_quantize_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert not re.search(r"\bimport oracle\b|from oracle\b|qmm_oracle", txt), fn

@@ -1,0 +1,87 @@
+"""GPU encoders against the oracle: bytes must be identical."""
+import numpy as np
+import pytest
+
+import oracle
+import bit_quantized_mat_quantize_amd as qmm
+from bit_quantized_mat_quantize_amd.inputs import activations, weights_normal, weights_t4_skewed
+from gpu_helpers import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _special_rows(K, rng):
+    """Rows that exercise the rounding and clamping decisions."""
+    rows = []
+    z = np.zeros(K, np.float32)
+    rows.append(z)                                       # all-zero blocks
+    t = np.zeros(K, np.float32)
+    t[::256] = 127.0
+    t[1::256] = 2.5
+    t[2::256] = -2.5
+    t[3::256] = 0.5
+    t[4:256:256] = 126.5
+    rows.append(t)                                       # exact .5 ties at d = 1
+    rows.append(np.full(K, -3.0, np.float32))            # constant negative blocks
+    rows.append((rng.standard_normal(K) * 1e-30).astype(np.float32))   # tiny scales
+    rows.append((rng.standard_normal(K) * 1e30).astype(np.float32))    # huge scales
+    sp = np.zeros(K, np.float32)
+    sp[rng.choice(K, K // 50, replace=False)] = rng.standard_normal(K // 50).astype(np.float32)
+    rows.append(sp)                                      # sparse
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("fmt,K", [("q8_K", 256), ("q8_K", 4096), ("q8_K", 14336),
+                                   ("q8_0", 32), ("q8_0", 1024), ("q8_0", 4096)])
+@pytest.mark.parametrize("M", [1, 3, 37])
+def test_quantize_row_q8_bit_exact(fmt, K, M):
+    x = activations([200, M, K], M, K, outlier_frac=0.01)
+    if M == 37:
+        x = np.concatenate([x[:-6], _special_rows(K, np.random.default_rng(M))])
+    want = oracle.quantize(fmt, x)
+    got = to_host(qmm.quantize_row_q8(to_dev(x), fmt))
+    assert got.size == want.size
+    assert np.array_equal(got, want.reshape(-1)), \
+        f"first mismatch at byte {np.flatnonzero(got != want.reshape(-1))[:8]}"
+
+
+def test_quantize_row_q8_large_bit_exact():
+    """Prefill-sized activations with outlier channels (2048 x 8192)."""
+    M, K = 2048, 8192
+    x = activations([105, M], M, K, outlier_frac=0.01)
+    want = oracle.quantize("q8_K", x)
+    got = to_host(qmm.quantize_row_q8(to_dev(x), "q8_K"))
+    assert np.array_equal(got, want.reshape(-1))
+
+
+@pytest.mark.parametrize("fmt,N,K", [("q4_K", 7, 256), ("q4_K", 33, 2048), ("q4_K", 300, 4096),
+                                     ("q4_0", 5, 32), ("q4_0", 256, 1024), ("q4_0", 61, 4096)])
+def test_quantize_weights_bit_exact(fmt, N, K):
+    w = weights_t4_skewed([300, N, K], N, K) if fmt == "q4_K" else weights_normal([301, N, K], N, K)
+    if N >= 7:
+        sp = _special_rows(K, np.random.default_rng(N))
+        w[:sp.shape[0]] = sp
+    want = oracle.quantize(fmt, w)
+    got = to_host(qmm.quantize_weights(to_dev(w), fmt))
+    assert np.array_equal(got, want.reshape(-1)), \
+        f"first mismatch at byte {np.flatnonzero(got != want.reshape(-1))[:8]}"
+
+
+@pytest.mark.parametrize("fmt,N,K", [("q4_K", 1, 256), ("q4_K", 37, 1024), ("q4_0", 3, 64),
+                                     ("q4_0", 129, 1024)])
+def test_repack_bit_exact(fmt, N, K):
+    w = oracle.quantize(fmt, weights_normal([302, N], N, K))
+    want = oracle.repack(fmt, w, N, K)
+    got = to_host(qmm.repack_weights(to_dev(w.reshape(-1)), fmt, N, K))
+    assert np.array_equal(got, want)
+
+
+def test_empty_calls_are_noops():
+    import torch
+    x = torch.zeros((0, 256), dtype=torch.float32, device="cuda")
+    y = qmm.quantize_row_q8(x, "q8_K")
+    assert y.numel() == 1  # placeholder buffer, nothing written
+    w = torch.zeros(144, dtype=torch.uint8, device="cuda")
+    out = torch.full((0, 1), 7.0, device="cuda")
+    qmm.mul_mat_q4_K(w, y, 0, 1, 256, out=out)
+    torch.cuda.synchronize()
