@@ -21,14 +21,27 @@
 // |bsums| <= 2032 is exact in fp16 and -dmin*m_j (17 significant bits) is the
 // exact sum of two fp16 values, so only the fp32 accumulation rounds.
 //
-// Workgroup: 256 threads = 4 wavefronts; tile 128 (M) x 128 (N); wavefront w
-// owns columns 32w..32w+31 for all 128 rows (4 MFMA tiles of 32 x 32), so each
-// weight column is decoded by exactly one wavefront.  One super-block per K
-// step is staged through LDS:
-//   sA  int8 codes   [128][256 + 16]  row stride 272 B: conflict-free 16-byte reads
-//   sB  Q4_K blocks  [128][144]       header + payload, stride 144 B: conflict-free
-//   sBs bsums, fp16  [128][24]        stride 48 B
-//   sDa d_a          [128]
+// Workgroup: 256 threads = 4 wavefronts, one per SIMD (all 512 registers of
+// the lane are available); tile 128 (M) x 256 (N); wavefront w owns columns
+// 64w..64w+63 (two 32-column tiles) for all 128 rows (four 32-row tiles), so
+// each weight column is decoded by exactly one wavefront and each activation
+// operand read from LDS feeds four MFMAs.  K advances one
+// 256-element super-block per step through two LDS buffers: while step b is
+// computed from one buffer, the codes of step b+1 stream into the other with
+// direct global->LDS loads (global_load_lds_dwordx4, no registers involved);
+// bsums and d_a of step b+1 travel through registers (they are converted to
+// fp16 on the way).  One barrier per step.  Per buffer:
+//   A   int8 codes   [128][256]  16-byte piece p of row r at position p ^ (r & 15)
+//   HDR Q4_K headers [256][16]   d, dmin, scales[12] per column
+//   PAY Q4_K payload [256][128]  16-byte piece p of column c at position p ^ ((c >> 1) & 7)
+//   BS  bsums, fp16  [128][24]   stride 48 B
+//   DA  d_a          [128]
+// (the XOR placements make the 16-byte reads down 16 consecutive rows or
+// columns hit distinct banks).  Each wavefront decodes the eight sub-block
+// planes of its two column tiles into registers once per step, then walks the
+// eight (row tile, column tile) pairs software-pipelined: the MFMAs of pair
+// p+1 are issued before the fp32 epilogue of pair p, so the vector ALU work
+// runs in the matrix core's shadow.
 //
 // MFMA operand convention (v_mfma_*_32x32xK): lane l supplies row (A) or
 // column (B) l % 32 and the K-slice selected by l / 32; A and B use the same
@@ -47,15 +60,25 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, MT = BM / 32;
-constexpr int SA_STRIDE = 272;
-constexpr int SB_STRIDE = 144;
-constexpr int SBS_STRIDE = 48;
-constexpr int SA_BYTES = BM * SA_STRIDE;
-constexpr int SB_BYTES = BN * SB_STRIDE;
-constexpr int SBS_BYTES = BM * SBS_STRIDE;
-constexpr int SDA_BYTES = BM * 4;
-constexpr int LDS_BYTES = SA_BYTES + SB_BYTES + SBS_BYTES + SDA_BYTES;
+constexpr int BM = 128, BN = 256, MT = BM / 32, NWAVE = 4, NTHR = 64 * NWAVE;
+constexpr int CT = BN / 32 / NWAVE;  // column tiles per wavefront
+constexpr int A_OFF = 0, A_BYTES = BM * 256;
+constexpr int H_OFF = A_OFF + A_BYTES, H_BYTES = BN * 16;
+constexpr int P_OFF = H_OFF + H_BYTES, P_BYTES = BN * 128;
+constexpr int BS_OFF = P_OFF + P_BYTES, BS_STRIDE = 48, BS_BYTES = BM * BS_STRIDE;
+constexpr int DA_OFF = BS_OFF + BS_BYTES, DA_BYTES = BM * 4;
+constexpr int BUF_BYTES = DA_OFF + DA_BYTES;
+constexpr int LDS_BYTES = 2 * BUF_BYTES;
+constexpr int A_INSTR = A_BYTES / 1024;  // 64-lane x 16-byte loads per buffer
+constexpr int H_INSTR = H_BYTES / 1024;
+constexpr int P_INSTR = P_BYTES / 1024;
+constexpr int A_PER_WAVE = A_INSTR / NWAVE;
+constexpr int P_PER_WAVE = P_INSTR / NWAVE;
+static_assert(A_INSTR % NWAVE == 0 && P_INSTR % NWAVE == 0 && H_INSTR <= NWAVE,
+              "staging must split evenly over the wavefronts");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ uint32_t h2_bits(int lo, int hi) {
     return f32_to_f16_bits((float)lo) | (f32_to_f16_bits((float)hi) << 16);
@@ -67,16 +90,28 @@ __device__ __forceinline__ int plane(uint32_t q4, uint32_t digit_pair) {
     return (int)__builtin_bit_cast(uint32_t, p);
 }
 
+// 16 bytes per lane from `src` into LDS at lds_base + 16 * lane (lds_base is
+// wavefront-uniform)
+__device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
+}
+
+// A pointer the compiler must treat as wavefront-uniform and opaque, so that
+// base + 32-bit lane offset stays a scalar base plus a vector offset instead
+// of being re-associated into per-lane 64-bit addresses kept across the loop.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+}
+
 template <bool REPACKED>
-__global__ __launch_bounds__(256, 2) void k_gemm_q4_K(const uint8_t *__restrict__ W,
-                                                      const uint8_t *__restrict__ Y,
-                                                      float *__restrict__ out, int64_t M, int64_t N,
-                                                      int64_t K, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict__ W,
+                                                       const uint8_t *__restrict__ Y,
+                                                       float *__restrict__ out, int64_t M, int64_t N,
+                                                       int64_t K, int tiles_m, int tiles_n) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    uint8_t *sA = lds;
-    uint8_t *sB = lds + SA_BYTES;
-    uint8_t *sBs = sB + SB_BYTES;
-    float *sDa = reinterpret_cast<float *>(sBs + SBS_BYTES);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -92,180 +127,234 @@ __global__ __launch_bounds__(256, 2) void k_gemm_q4_K(const uint8_t *__restrict_
     const int64_t nb = K / QK_K;
 
     // ---- staging sources.  Rows past M and columns past N are clamped to the
-    // last valid one (their results are never stored), so no load is predicated.
-    // Workgroup bases are uniform; per-thread offsets fit in 32 bits.
+    // last valid one (their results are never stored), so every load is in
+    // bounds and none is predicated.  Bases are uniform, offsets 32-bit.
     const int m_last = (int)(M - 1 - m_base < BM - 1 ? M - 1 - m_base : BM - 1);
     const int n_last = (int)(N - 1 - n_base < BN - 1 ? N - 1 - n_base : BN - 1);
     const uint32_t a_rowstride = (uint32_t)(nb * kQ8_KBytes);
     const uint8_t *a_base = Y + m_base * nb * kQ8_KBytes;
-    // activation codes: rows (tid>>4) + 16 i, 16-byte piece tid & 15
-    const int a_p = tid & 15, a_r0 = tid >> 4;
-    uint32_t a_off[8];
+    uint32_t a_goff[A_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = a_r0 + 16 * i < m_last ? a_r0 + 16 * i : m_last;
-        a_off[i] = (uint32_t)r * a_rowstride + 4 + 16 * a_p;
+    for (int t = 0; t < A_PER_WAVE; ++t) {
+        const int row = (wave * A_PER_WAVE + t) * 4 + (lane >> 4);
+        const int gp = (lane & 15) ^ (row & 15);  // global piece stored at position lane & 15
+        const int rr = row < m_last ? row : m_last;
+        a_goff[t] = (uint32_t)rr * a_rowstride + 4 + 16 * gp;
     }
-    // weights: headers by threads 0..127, payload pieces (tid>>3) + 32 i, piece tid & 7
     const uint32_t hdr_step = REPACKED ? 16 : kQ4_KBytes, pay_step = REPACKED ? 128 : kQ4_KBytes;
-    const uint8_t *h_base = W + (REPACKED ? 16 : kQ4_KBytes) * (n_base * nb);
+    const uint8_t *h_base = W + (int64_t)hdr_step * (n_base * nb);
     const uint8_t *p_base = REPACKED ? W + 16 * N * nb + 128 * (n_base * nb)
                                      : W + kQ4_KBytes * (n_base * nb) + 16;
-    const int h_row = tid < BN ? (tid < n_last ? tid : n_last) : 0;
-    const uint32_t h_off = (uint32_t)h_row * (uint32_t)nb * hdr_step;
-    const int p_c = tid & 7, p_r0 = tid >> 3;
-    uint32_t p_off[4];
+    // headers: wavefront w < H_INSTR loads columns 64w + lane
+    const int h_col = wave * 64 + lane;
+    const uint32_t h_goff = (uint32_t)(h_col < n_last ? h_col : n_last) * (uint32_t)nb * hdr_step;
+    // payload: load t of wavefront w covers columns 8*(w*P_PER_WAVE + t) + lane/8,
+    // position lane & 7 holds piece (lane & 7) ^ ((col >> 1) & 7)
+    uint32_t p_goff[P_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = p_r0 + 32 * i < n_last ? p_r0 + 32 * i : n_last;
-        p_off[i] = (uint32_t)r * (uint32_t)nb * pay_step + 16 * p_c;
+    for (int t = 0; t < P_PER_WAVE; ++t) {
+        const int c = (wave * P_PER_WAVE + t) * 8 + (lane >> 3);
+        const int piece = (lane & 7) ^ ((c >> 1) & 7);
+        const int cc = c < n_last ? c : n_last;
+        p_goff[t] = (uint32_t)cc * (uint32_t)nb * pay_step + 16 * piece;
     }
-    // bsums and d_a: row tid>>1, half tid&1
-    const int s_row = tid >> 1, s_half = tid & 1;
-    const uint32_t s_off = (uint32_t)(s_row < m_last ? s_row : m_last) * a_rowstride;
+    // bsums: row tid>>1, 16-byte half tid&1; d_a: row tid (threads < 128)
+    const int s_row = tid >> 1;
+    const uint32_t s_off = (uint32_t)(s_row < m_last ? s_row : m_last) * a_rowstride + 260 + 16 * (tid & 1);
+    const uint32_t d_off = (uint32_t)((tid & (BM - 1)) < m_last ? (tid & (BM - 1)) : m_last) * a_rowstride;
 
-    float acc[MT][16];
+    auto issue = [&](int64_t b, uint8_t *buf) {
+        const uint8_t *ab = uniform_ptr(a_base + b * kQ8_KBytes);
+#pragma unroll
+        for (int t = 0; t < A_PER_WAVE; ++t)
+            dma16(ab + a_goff[t], buf + A_OFF + (wave * A_PER_WAVE + t) * 1024);
+        const uint8_t *pb = uniform_ptr(p_base + b * pay_step);
+#pragma unroll
+        for (int t = 0; t < P_PER_WAVE; ++t)
+            dma16(pb + p_goff[t], buf + P_OFF + (wave * P_PER_WAVE + t) * 1024);
+        if (wave < H_INSTR)
+            dma16(uniform_ptr(h_base + b * hdr_step) + h_goff, buf + H_OFF + wave * 1024);
+    };
+    auto prefetch = [&](int64_t b, uint4 &raw, uint32_t &draw) {
+        const uint8_t *yb = uniform_ptr(a_base + b * kQ8_KBytes);
+        raw = ld_align4<uint4>(yb + s_off);
+        if (tid < BM) draw = ld_align4<uint32_t>(yb + d_off);
+    };
+    auto commit = [&](const uint4 &raw, uint32_t draw, uint8_t *buf) {
+        const uint4 hv = make_uint4(h2_bits((int16_t)(raw.x & 0xffff), (int16_t)(raw.x >> 16)),
+                                    h2_bits((int16_t)(raw.y & 0xffff), (int16_t)(raw.y >> 16)),
+                                    h2_bits((int16_t)(raw.z & 0xffff), (int16_t)(raw.z >> 16)),
+                                    h2_bits((int16_t)(raw.w & 0xffff), (int16_t)(raw.w >> 16)));
+        *reinterpret_cast<uint4 *>(buf + BS_OFF + s_row * BS_STRIDE + 16 * (tid & 1)) = hv;
+        if (tid < BM) *reinterpret_cast<uint32_t *>(buf + DA_OFF + 4 * tid) = draw;
+    };
+
+    float acc[MT][CT][16];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][c][r] = 0.0f;
 
-    const int col = wave * 32 + l32;  // this lane's column within the tile
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    uint32_t draw = 0;
+    issue(0, lds);
+    prefetch(0, raw, draw);
 
     for (int64_t b = 0; b < nb; ++b) {
-        // ---------------- stage super-block b
-        __syncthreads();
-        {
-            const uint8_t *ab = a_base + b * kQ8_KBytes;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint4 val = ld_align4<uint4>(ab + a_off[i]);
-                *reinterpret_cast<uint4 *>(sA + (a_r0 + 16 * i) * SA_STRIDE + 16 * a_p) = val;
-            }
-            const uint8_t *pb = p_base + b * pay_step;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 val = ld16(pb + p_off[i]);
-                *reinterpret_cast<uint4 *>(sB + (p_r0 + 32 * i) * SB_STRIDE + 16 + 16 * p_c) = val;
-            }
-            if (tid < BN) {
-                const uint4 val = ld16(h_base + b * hdr_step + h_off);
-                *reinterpret_cast<uint4 *>(sB + tid * SB_STRIDE) = val;
-            }
-            const uint8_t *yb = ab + s_off;  // block start of this row
-            const uint4 raw = ld_align4<uint4>(yb + 260 + 16 * s_half);
-            const uint4 hv = make_uint4(h2_bits((int16_t)(raw.x & 0xffff), (int16_t)(raw.x >> 16)),
-                                        h2_bits((int16_t)(raw.y & 0xffff), (int16_t)(raw.y >> 16)),
-                                        h2_bits((int16_t)(raw.z & 0xffff), (int16_t)(raw.z >> 16)),
-                                        h2_bits((int16_t)(raw.w & 0xffff), (int16_t)(raw.w >> 16)));
-            *reinterpret_cast<uint4 *>(sBs + s_row * SBS_STRIDE + 16 * s_half) = hv;
-            if (s_half == 0) sDa[s_row] = ld_align4<float>(yb);
+        uint8_t *buf = lds + (b & 1) * BUF_BYTES;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of step b
+        commit(raw, draw, buf);
+        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
+        if (b + 1 < nb) {
+            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
+            prefetch(b + 1, raw, draw);
         }
-        __syncthreads();
 
-        // ---------------- this lane's column: header
-        const uint4 hdr = *reinterpret_cast<const uint4 *>(sB + col * SB_STRIDE);
-        const float dcol = f16_bits_to_f32(hdr.x & 0xffff);
-        const float dmcol = f16_bits_to_f32(hdr.x >> 16);
-        const Q4KScales sc = unpack_scales(hdr.y, hdr.z, hdr.w);
-
-        v16i acc_hi[MT], acc_lo[MT];
+        // ---------------- this lane's two columns: header and the 8 sub-block planes
+        float dcol[CT];
+        v4i bhi[CT][8], blo[CT][8];
+        v8h bmh[CT], bml[CT];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const uint4 pw = *reinterpret_cast<const uint4 *>(sB + col * SB_STRIDE + 16 + 32 * g + 16 * hh);
-            const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
+        for (int c = 0; c < CT; ++c) {
+            const int col = wave * (32 * CT) + 32 * c + l32;
+            const uint4 hdr = *reinterpret_cast<const uint4 *>(buf + H_OFF + 16 * col);
+            dcol[c] = f16_bits_to_f32(hdr.x & 0xffff);
+            const float dmcol = f16_bits_to_f32(hdr.x >> 16);
+            const Q4KScales sc = unpack_scales(hdr.y, hdr.z, hdr.w);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {  // t = 0: low nibbles (sub-block 2g), 1: high (2g+1)
-                const int j = 2 * g + t;
-                const int shift = t * 4;
-                const uint32_t q0 = (pw.x >> shift) & 0x0f0f0f0fu, q1 = (pw.y >> shift) & 0x0f0f0f0fu;
-                const uint32_t q2 = (pw.z >> shift) & 0x0f0f0f0fu, q3 = (pw.w >> shift) & 0x0f0f0f0fu;
-                const uint32_t s = (sw >> (8 * (j & 3))) & 0xff;
-                const uint32_t hi2 = (s >> 3) * 0x00010001u, lo2 = (s & 7) * 0x00010001u;
-                const v4i bhi = v4i{plane(q0, hi2), plane(q1, hi2), plane(q2, hi2), plane(q3, hi2)};
-                const v4i blo = v4i{plane(q0, lo2), plane(q1, lo2), plane(q2, lo2), plane(q3, lo2)};
+            for (int g = 0; g < 4; ++g) {
+                const int piece = 2 * g + hh;  // this lane's K-slice of sub-blocks 2g, 2g+1
+                const uint4 pw = *reinterpret_cast<const uint4 *>(buf + P_OFF + 128 * col +
+                                                                  16 * (piece ^ ((col >> 1) & 7)));
+                const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
 #pragma unroll
-                for (int i = 0; i < MT; ++i) {
-                    const uint4 a = *reinterpret_cast<const uint4 *>(sA + (i * 32 + l32) * SA_STRIDE + 32 * j + 16 * hh);
-                    const v4i va = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-                    if (j == 0) {
-                        const v16i zero = {};
-                        acc_hi[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, bhi, zero, 0, 0, 0);
-                        acc_lo[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, blo, zero, 0, 0, 0);
-                    } else {
-                        acc_hi[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, bhi, acc_hi[i], 0, 0, 0);
-                        acc_lo[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, blo, acc_lo[i], 0, 0, 0);
-                    }
+                for (int t = 0; t < 2; ++t) {  // t = 0: low nibbles (sub-block 2g), 1: high (2g+1)
+                    const int j = 2 * g + t;
+                    const int shift = t * 4;
+                    const uint32_t q0 = (pw.x >> shift) & 0x0f0f0f0fu, q1 = (pw.y >> shift) & 0x0f0f0f0fu;
+                    const uint32_t q2 = (pw.z >> shift) & 0x0f0f0f0fu, q3 = (pw.w >> shift) & 0x0f0f0f0fu;
+                    const uint32_t sj = (sw >> (8 * (j & 3))) & 0xff;
+                    const uint32_t hi2 = (sj >> 3) * 0x00010001u, lo2 = (sj & 7) * 0x00010001u;
+                    bhi[c][j] = v4i{plane(q0, hi2), plane(q1, hi2), plane(q2, hi2), plane(q3, hi2)};
+                    blo[c][j] = v4i{plane(q0, lo2), plane(q1, lo2), plane(q2, lo2), plane(q3, lo2)};
                 }
             }
+            // min-term operand: -dmin*m_j has at most 17 significant bits, so it is
+            // the exact sum of two fp16 values (hi = fp16(-dmin*m), lo = remainder);
+            // two fp16 MFMAs against the exact fp16 bsums give -dmin*Mn with fp32
+            // rounding only.
+            const uint32_t mw = hh == 0 ? sc.m_lo : sc.m_hi;  // m_{4hh .. 4hh+3}
+            uint32_t bh[4], bl[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float vv = -dmcol * (float)((mw >> (8 * e)) & 0xff);  // exact in fp32
+                const uint32_t hb = f32_to_f16_bits(vv);
+                const uint32_t lb = f32_to_f16_bits(vv - f16_bits_to_f32(hb));
+                bh[e] = hb | (hb << 16);
+                bl[e] = lb | (lb << 16);
+            }
+            __builtin_memcpy(&bmh[c], bh, 16);
+            __builtin_memcpy(&bml[c], bl, 16);
         }
+        const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
 
-        // ---------------- min term and the fp32 block-scale epilogue.
-        // -dmin*m_j has at most 17 significant bits: it is the exact sum of two
-        // fp16 values (hi = fp16(-dmin*m), lo = remainder), so two fp16 MFMAs
-        // against the exact fp16 bsums give -dmin*Mn with fp32 rounding only.
-        const uint32_t mw = hh == 0 ? sc.m_lo : sc.m_hi;  // m_{4hh .. 4hh+3}
-        uint32_t bh[4], bl[4];
+        // ---------------- eight (row tile, column tile) pairs, software-pipelined
+        v4i a_op[8];
+        v8h a_bs;
+        float dav[16];
+        v16i ah[2], al[2];
+        v16f mn[2];
+        auto load_rows = [&](int i) {
+            const int row = i * 32 + l32;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float v = -dmcol * (float)((mw >> (8 * e)) & 0xff);  // exact in fp32
-            const uint32_t hb = f32_to_f16_bits(v);
-            const uint32_t lb = f32_to_f16_bits(v - f16_bits_to_f32(hb));
-            bh[e] = hb | (hb << 16);
-            bl[e] = lb | (lb << 16);
-        }
-        v8h bmh, bml;
-        __builtin_memcpy(&bmh, bh, 16);
-        __builtin_memcpy(&bml, bl, 16);
+            for (int j = 0; j < 8; ++j) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * 256 +
+                                                                 16 * ((2 * j + hh) ^ (row & 15)));
+                a_op[j] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+            }
+            const uint4 au = *reinterpret_cast<const uint4 *>(buf + BS_OFF + row * BS_STRIDE + 16 * hh);
+            __builtin_memcpy(&a_bs, &au, 16);
+        };
+        auto mfma_pair = [&](int c, int set) {
+            const v16i zero = {};
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const uint4 au = *reinterpret_cast<const uint4 *>(sBs + (i * 32 + l32) * SBS_STRIDE + 16 * hh);
-            v8h abs_;
-            __builtin_memcpy(&abs_, &au, 16);
+            for (int j = 0; j < 8; ++j) {
+                ah[set] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[j], bhi[c][j], j ? ah[set] : zero, 0, 0, 0);
+                al[set] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[j], blo[c][j], j ? al[set] : zero, 0, 0, 0);
+            }
             const v16f zf = {};
-            v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(abs_, bmh, zf, 0, 0, 0);
-            mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(abs_, bml, mn, 0, 0, 0);
+            mn[set] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmh[c], zf, 0, 0, 0);
+            mn[set] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bml[c], mn[set], 0, 0, 0);
+        };
+        auto load_da = [&](int i) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float4 da4 = *reinterpret_cast<const float4 *>(sDa + i * 32 + 8 * q + 4 * hh);
-                const float dav[4] = {da4.x, da4.y, da4.z, da4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * q + e;
-                    const int S = (acc_hi[i][r] << 3) + acc_lo[i][r];
-                    const float t = fmaf(dcol, (float)S, mn[r]);
-                    acc[i][r] = fmaf(dav[e], t, acc[i][r]);
-                }
+                const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
+                dav[4 * q + 0] = d4.x; dav[4 * q + 1] = d4.y; dav[4 * q + 2] = d4.z; dav[4 * q + 3] = d4.w;
             }
+        };
+        auto epilogue = [&](int i, int c, int set) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int S = (ah[set][r] << 3) + al[set][r];
+                const float t = fmaf(dcol[c], (float)S, mn[set][r]);
+                acc[i][c][r] = fmaf(dav[r], t, acc[i][c][r]);
+            }
+        };
+        load_rows(0);
+        mfma_pair(0, 0);
+#pragma unroll
+        for (int p = 0; p < MT * CT; ++p) {
+            const int i = p / CT, c = p % CT;
+            if (p + 1 < MT * CT) {
+                const int i1 = (p + 1) / CT, c1 = (p + 1) % CT;
+                if (c1 == 0) load_rows(i1);
+                mfma_pair(c1, (p + 1) & 1);
+            }
+            if (c == 0) load_da(i);
+            epilogue(i, c, p & 1);
         }
     }
 
     // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
-    const int64_t n = n_base + col;
-    if (n < N) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+    for (int c = 0; c < CT; ++c) {
+        const int64_t n = n_base + wave * (32 * CT) + 32 * c + l32;
+        if (n < N) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m_base + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (m < M) out[m * N + n] = acc[i][r];
-            }
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = m_base + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (m < M) out[m * N + n] = acc[i][c][r];
+                }
+        }
     }
+}
+
+template <bool REPACKED>
+hipError_t launch(const uint8_t *w, const uint8_t *y, float *out, int64_t M, int64_t N, int64_t K,
+                  hipStream_t s) {
+    static bool attr_set = false;  // the LDS budget above 64 KiB must be opted into once
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_q4_K<REPACKED>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    hipLaunchKernelGGL(k_gemm_q4_K<REPACKED>, dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR),
+                       LDS_BYTES, s, w, y, out, M, N, K, tiles_m, tiles_n);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s) {
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    const dim3 grid((unsigned)(tiles_m * tiles_n));
-    if (repacked)
-        hipLaunchKernelGGL(k_gemm_q4_K<true>, grid, dim3(256), LDS_BYTES, s, w, y, out, M, N, K,
-                           tiles_m, tiles_n);
-    else
-        hipLaunchKernelGGL(k_gemm_q4_K<false>, grid, dim3(256), LDS_BYTES, s, w, y, out, M, N, K,
-                           tiles_m, tiles_n);
-    return hipGetLastError();
+    return repacked ? launch<true>(w, y, out, M, N, K, s) : launch<false>(w, y, out, M, N, K, s);
 }
 
 }  // namespace qmm
