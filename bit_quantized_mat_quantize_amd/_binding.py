@@ -55,6 +55,7 @@ def load() -> ctypes.CDLL:
         "qmm_mul_mat_q4_0": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_mul_mat_q4_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_mul_mat_q4_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
+        "qmm_quantize_mul_mat": (I, [I, P, SZ, I, P, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_debug_block_sums": (I, [I, P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_status_string": (ctypes.c_char_p, [I]),
         "qmm_last_error": (ctypes.c_char_p, []),
@@ -162,6 +163,30 @@ def mul_mat_q4_K(w, y, M: int, N: int, K: int, layout: str = "canonical", algo: 
     _check(load().qmm_mul_mat_q4_K_ex(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
                                       _ALGO[algo], _stream(stream)), "qmm_mul_mat_q4_K")
     return out
+
+
+def quantize_mul_mat(wfmt: str, w, x, N: int, layout: str = "canonical", y=None, out=None,
+                     stream=None):
+    """out = mul_mat(w, quantize_row_q8(x)) in one call; returns (out, y).
+
+    x: fp32 [M, K] GPU tensor; y receives the Q8 activation bytes.  For Q4_K
+    and M == 1 the quantization runs inside the GEMV launch."""
+    import torch
+    M, K = x.shape
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32")
+    afmt = "q8_K" if wfmt == "q4_K" else "q8_0"
+    if y is None:
+        y = torch.empty(max(act_bytes(afmt, M, K), 1), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    pw, nw = _dev(w, "w")
+    px, _ = _dev(x, "x")
+    py, ny = _dev(y, "y")
+    po, no = _dev(out, "out")
+    _check(load().qmm_quantize_mul_mat(_WEIGHT[wfmt], pw, nw, _LAYOUT[layout], px, py, ny, po, no,
+                                       M, N, K, _stream(stream)), "qmm_quantize_mul_mat")
+    return out, y
 
 
 def debug_block_sums(wfmt: str, w, y, M: int, N: int, K: int, layout: str = "canonical",

@@ -212,6 +212,39 @@ qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l, const v
                                stream);
 }
 
+qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes, qmm_layout l,
+                                const float *x, void *y, size_t y_bytes, float *out,
+                                size_t out_bytes, int64_t M, int64_t N, int64_t K, void *stream) {
+    if (!w_qk(t)) return fail(QMM_EUNSUPPORTED, "unknown weight type %d", (int)t);
+    if (l != QMM_LAYOUT_CANONICAL && l != QMM_LAYOUT_REPACKED)
+        return fail(QMM_EUNSUPPORTED, "unknown layout %d", (int)l);
+    const qmm_act_type at = t == QMM_Q4_0 ? QMM_Q8_0 : QMM_Q8_K;
+    QMM_TRY(check_rows("M", M));
+    QMM_TRY(check_rows("N", N));
+    QMM_TRY(check_k(K, w_qk(t)));
+    if (M == 0) return QMM_OK;
+    QMM_TRY(check_ptr("x", x));
+    QMM_TRY(check_ptr("y", y));
+    QMM_TRY(check_size("y", y_bytes, qmm_act_bytes(at, M, K)));
+    if (N > 0) {
+        QMM_TRY(check_ptr("w", w));
+        QMM_TRY(check_ptr("out", out));
+        QMM_TRY(check_size("w", w_bytes, qmm_weight_bytes(t, l, N, K)));
+        QMM_TRY(check_size("out", out_bytes, (size_t)(M * N) * sizeof(float)));
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *yb = static_cast<uint8_t *>(y);
+    if (t == QMM_Q4_K && M == 1 && N > 0 && K <= qmm::gemv1_fused_max_k())
+        return device_status(qmm::launch_gemv1_fused_q4_K(static_cast<const uint8_t *>(w),
+                                                          l == QMM_LAYOUT_REPACKED, x, yb, out, N,
+                                                          K, s),
+                             "quantize_mul_mat fused launch");
+    QMM_TRY(qmm_quantize_row_q8(at, x, M, K, y, y_bytes, stream));
+    if (N == 0) return QMM_OK;
+    return t == QMM_Q4_K ? qmm_mul_mat_q4_K(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream)
+                         : qmm_mul_mat_q4_0(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream);
+}
+
 qmm_status qmm_debug_block_sums(qmm_weight_type t, const void *w, size_t w_bytes, qmm_layout l,
                                 const void *y, size_t y_bytes, int32_t *P, size_t p_bytes,
                                 int64_t M, int64_t N, int64_t K, void *stream) {

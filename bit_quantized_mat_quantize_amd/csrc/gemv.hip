@@ -134,6 +134,205 @@ __global__ __launch_bounds__(256) void k_gemv_q4_K(const uint8_t *__restrict__ W
 }
 
 // ---------------------------------------------------------------------------
+// M = 1 variant: one wavefront per output row.  Every lane first issues the
+// loads of all its weight pieces of the row (up to kNit per pass) together
+// with the workgroup's share of the activation row, so one memory round trip
+// covers the whole row; the activation row (shared by the 4 rows of the
+// workgroup) is staged in LDS with its 16-byte pieces aligned:
+//   qs [K] int8 | d [nb] fp32 (padded to 16 B) | bsums [nb][16] int16
+// ---------------------------------------------------------------------------
+
+__host__ __device__ constexpr int64_t gemv1_lds_bytes(int64_t K) {
+    return K + ((K / QK_K) * 4 + 15) / 16 * 16 + (K / QK_K) * 32;
+}
+
+// Issue the loads of this lane's weight pieces c = base + lane + 64*it of row nn.
+template <bool REPACKED, int kNit>
+__device__ __forceinline__ void gemv1_load(const Q4KAddr<REPACKED> &A, int64_t nn, int base,
+                                           int nchunk, int lane, uint4 (&hw)[kNit],
+                                           uint4 (&pw)[kNit]) {
+#pragma unroll
+    for (int it = 0; it < kNit; ++it) {
+        const int c = base + lane + 64 * it;
+        if (c < nchunk) {
+            hw[it] = ld16(A.header(nn, c >> 3));
+            pw[it] = ld16(A.piece(nn, c >> 3, c & 7));
+        }
+    }
+}
+
+// Integer dot products of the loaded pieces with the activation row in LDS:
+// piece cc = 2g+h of super-block b holds bytes 16h..16h+15 of the 32-byte
+// group g, i.e. elements 64g+16h.. (low nibbles, sub-block 2g) and
+// 64g+32+16h.. (high nibbles, sub-block 2g+1).  Per piece:
+//   acc += d_a * (d * (s_2g*P_lo + s_2g+1*P_hi) - dmin * (m_2g*Y_lo + m_2g+1*Y_hi))
+// where Y are the matching 16-element activation sums (bsums).
+template <int kNit>
+__device__ __forceinline__ float gemv1_accumulate(const uint4 (&hw)[kNit], const uint4 (&pw)[kNit],
+                                                  int base, int nchunk, int lane,
+                                                  const uint8_t *s_qs, const int16_t *s_bs,
+                                                  const float *s_d, float acc) {
+#pragma unroll
+    for (int it = 0; it < kNit; ++it) {
+        const int c = base + lane + 64 * it;
+        if (c < nchunk) {
+            const int b = c >> 3, cc = c & 7, g = cc >> 1, h = cc & 1;
+            const Q4KScales sc = unpack_scales(hw[it].y, hw[it].z, hw[it].w);
+            const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
+            const uint32_t mw = g < 2 ? sc.m_lo : sc.m_hi;
+            const int sh = (g & 1) * 16;
+            const int s0 = (sw >> sh) & 0xff, s1 = (sw >> (sh + 8)) & 0xff;
+            const int m0 = (mw >> sh) & 0xff, m1 = (mw >> (sh + 8)) & 0xff;
+            const float d = f16_bits_to_f32(hw[it].x & 0xffff);
+            const float dmin = f16_bits_to_f32(hw[it].x >> 16);
+            const uint4 ylo = *reinterpret_cast<const uint4 *>(s_qs + b * QK_K + 64 * g + 16 * h);
+            const uint4 yhi = *reinterpret_cast<const uint4 *>(s_qs + b * QK_K + 64 * g + 32 + 16 * h);
+            const int blo = s_bs[16 * b + 4 * g + h], bhi = s_bs[16 * b + 4 * g + 2 + h];
+            const uint4 q = pw[it];
+            int plo = dot4(q.x & 0x0f0f0f0fu, ylo.x, 0);
+            plo = dot4(q.y & 0x0f0f0f0fu, ylo.y, plo);
+            plo = dot4(q.z & 0x0f0f0f0fu, ylo.z, plo);
+            plo = dot4(q.w & 0x0f0f0f0fu, ylo.w, plo);
+            int phi = dot4((q.x >> 4) & 0x0f0f0f0fu, yhi.x, 0);
+            phi = dot4((q.y >> 4) & 0x0f0f0f0fu, yhi.y, phi);
+            phi = dot4((q.z >> 4) & 0x0f0f0f0fu, yhi.z, phi);
+            phi = dot4((q.w >> 4) & 0x0f0f0f0fu, yhi.w, phi);
+            const int S = s0 * plo + s1 * phi;
+            const int Mn = m0 * blo + m1 * bhi;
+            const float t = fmaf(d, (float)S, -dmin * (float)Mn);
+            acc = fmaf(s_d[b], t, acc);
+        }
+    }
+    return acc;
+}
+
+template <bool REPACKED, int kNit>
+__global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ W,
+                                                    const uint8_t *__restrict__ Y,
+                                                    float *__restrict__ out, int64_t N, int64_t K) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t ys[];
+    const int64_t nb = K / QK_K;
+    const int nchunk = (int)(nb * 8);
+    uint8_t *s_qs = ys;
+    float *s_d = reinterpret_cast<float *>(ys + K);
+    int16_t *s_bs = reinterpret_cast<int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const int64_t nn = n < N ? n : N - 1;  // a tail wavefront loads a valid row, stores nothing
+    const Q4KAddr<REPACKED> A{W, N, nb};
+
+    float acc = 0.0f;
+    for (int base = 0; base < nchunk; base += 64 * kNit) {
+        // activation row -> registers (first pass only), then this row's weights
+        const int nq = (int)(K / 16), nbs = (int)(nb * 2);
+        uint4 yq[4], yb = make_uint4(0, 0, 0, 0);
+        float yd = 0.0f;
+        if (base == 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int pc = tid + 256 * t;
+                if (pc < nq) yq[t] = ld_align4<uint4>(Y + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
+            }
+            if (tid < nbs) yb = ld_align4<uint4>(Y + (tid >> 1) * kQ8_KBytes + 260 + 16 * (tid & 1));
+            if (tid < nb) yd = ld_align4<float>(Y + tid * kQ8_KBytes);
+        }
+        uint4 pw[kNit], hw[kNit];
+        gemv1_load<REPACKED, kNit>(A, nn, base, nchunk, lane, hw, pw);
+        if (base == 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int pc = tid + 256 * t;
+                if (pc < nq) *reinterpret_cast<uint4 *>(s_qs + 16 * pc) = yq[t];
+            }
+            if (tid < nbs) *reinterpret_cast<uint4 *>(s_bs + 8 * tid) = yb;
+            if (tid < nb) s_d[tid] = yd;
+            // rows longer than 1024 pieces: the rest of the activation row
+            for (int pc = tid + 1024; pc < nq; pc += 256)
+                *reinterpret_cast<uint4 *>(s_qs + 16 * pc) =
+                    ld_align4<uint4>(Y + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
+            for (int q = tid + 256; q < nbs; q += 256)
+                *reinterpret_cast<uint4 *>(s_bs + 8 * q) =
+                    ld_align4<uint4>(Y + (q >> 1) * kQ8_KBytes + 260 + 16 * (q & 1));
+            for (int q = tid + 256; q < nb; q += 256) s_d[q] = ld_align4<float>(Y + q * kQ8_KBytes);
+            __syncthreads();
+        }
+        acc = gemv1_accumulate<kNit>(hw, pw, base, nchunk, lane, s_qs, s_bs, s_d, acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0 && n < N) out[n] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Fused M = 1 path: the fp32 activation row is quantized to Q8_K inside the
+// GEMV, straight into LDS, so one launch covers quantize + mul_mat.  Eight
+// wavefronts (eight output rows) per workgroup share the quantized row.  Each
+// wavefront first issues the fp32 loads of up to kXB of its activation blocks
+// (b = wave + 8i) and the loads of its row's weight pieces, then quantizes
+// while the weights are in flight (further blocks of long rows follow).  Workgroup 0 also stores the Q8_K bytes to
+// Yq, byte-identical to the stand-alone quantizer (same device routine), so
+// another projection of the same input can reuse them.
+// ---------------------------------------------------------------------------
+constexpr int kFusedWaves = 8;
+
+template <bool REPACKED, int kNit, int kXB>
+__global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
+    const uint8_t *__restrict__ W, const float *__restrict__ X, uint8_t *__restrict__ Yq,
+    float *__restrict__ out, int64_t N, int64_t K) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t ys[];
+    const int64_t nb = K / QK_K;
+    const int nchunk = (int)(nb * 8);
+    uint8_t *s_qs = ys;
+    float *s_d = reinterpret_cast<float *>(ys + K);
+    int16_t *s_bs = reinterpret_cast<int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t n = (int64_t)blockIdx.x * kFusedWaves + wave;
+    const int64_t nn = n < N ? n : N - 1;  // a tail wavefront loads a valid row, stores nothing
+    const Q4KAddr<REPACKED> A{W, N, nb};
+    const bool store_q = blockIdx.x == 0;
+
+    // one 256-value block per wavefront and step: quantize, write LDS (+ Yq)
+    auto quantize_block = [&](const float4 v, int b) {
+        const Q8KLane r = q8K_quantize_lane(v);
+        const uint32_t packed = pack4_i8(r.q[0], r.q[1], r.q[2], r.q[3]);
+        *reinterpret_cast<uint32_t *>(s_qs + b * QK_K + 4 * lane) = packed;
+        if ((lane & 3) == 0) s_bs[16 * b + (lane >> 2)] = (int16_t)r.bsum;
+        if (lane == 0) s_d[b] = r.d;
+        if (store_q) {
+            uint8_t *o = Yq + (int64_t)b * kQ8_KBytes;
+            *reinterpret_cast<uint32_t *>(o + 4 + 4 * lane) = packed;
+            if ((lane & 3) == 0) *reinterpret_cast<int16_t *>(o + 260 + 2 * (lane >> 2)) = (int16_t)r.bsum;
+            if (lane == 0) *reinterpret_cast<float *>(o) = r.d;
+        }
+    };
+
+    float4 xv[kXB];
+#pragma unroll
+    for (int i = 0; i < kXB; ++i) {
+        const int b = wave + kFusedWaves * i;  // uniform per wavefront
+        if (b < nb) xv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane);
+    }
+    float acc = 0.0f;
+    for (int base = 0; base < nchunk; base += 64 * kNit) {
+        uint4 pw[kNit], hw[kNit];
+        gemv1_load<REPACKED, kNit>(A, nn, base, nchunk, lane, hw, pw);
+        if (base == 0) {
+#pragma unroll
+            for (int i = 0; i < kXB; ++i) {
+                const int b = wave + kFusedWaves * i;
+                if (b < nb) quantize_block(xv[i], b);
+            }
+            // rows longer than 8 * kXB blocks: the remaining blocks
+            for (int b = wave + kFusedWaves * kXB; b < nb; b += kFusedWaves)
+                quantize_block(*reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane), b);
+            __syncthreads();
+        }
+        acc = gemv1_accumulate<kNit>(hw, pw, base, nchunk, lane, s_qs, s_bs, s_d, acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0 && n < N) out[n] = acc;
+}
+
+// ---------------------------------------------------------------------------
 // Q4_0 x Q8_0: one lane per 32-element block (16-byte payload).  Canonical
 // blocks are 18 B and Q8_0 blocks 34 B, so both are read with 2-byte loads;
 // the repacked weight payload is read with one aligned 16-byte load.
@@ -263,7 +462,54 @@ hipError_t dispatch_q4_0(const uint8_t *w, bool rep, const uint8_t *y, void *dst
 
 hipError_t launch_gemv_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t lds = gemv1_lds_bytes(K);
+    const int64_t nit = (K / QK_K * 8 + 63) / 64;  // 16-byte pieces per lane for one row
+    if (M == 1 && lds <= 60 * 1024) {
+        const dim3 grid((unsigned)((N + kWavesPerBlock - 1) / kWavesPerBlock));
+#define QMM_GEMV1(NIT)                                                                                     \
+    do {                                                                                                   \
+        if (repacked)                                                                                      \
+            hipLaunchKernelGGL((k_gemv1_q4_K<true, NIT>), grid, dim3(256), (unsigned)lds, s, w, y, out, N, K);  \
+        else                                                                                               \
+            hipLaunchKernelGGL((k_gemv1_q4_K<false, NIT>), grid, dim3(256), (unsigned)lds, s, w, y, out, N, K); \
+    } while (0)
+        if (nit <= 1) QMM_GEMV1(1);
+        else if (nit <= 2) QMM_GEMV1(2);
+        else if (nit <= 4) QMM_GEMV1(4);
+        else QMM_GEMV1(8);
+#undef QMM_GEMV1
+        return hipGetLastError();
+    }
     return dispatch_q4_K<0>(w, repacked, y, out, M, N, K, s);
+}
+
+int64_t gemv1_fused_max_k() {
+    // largest K whose activation row fits the 60 KB LDS budget
+    int64_t k = 0;
+    while (gemv1_lds_bytes(k + QK_K) <= 60 * 1024) k += QK_K;
+    return k;
+}
+
+hipError_t launch_gemv1_fused_q4_K(const uint8_t *w, bool repacked, const float *x, uint8_t *yq,
+                                   float *out, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t lds = gemv1_lds_bytes(K);
+    const int64_t nit = (K / QK_K * 8 + 63) / 64;
+    const dim3 grid((unsigned)((N + kFusedWaves - 1) / kFusedWaves)), block(kFusedWaves * 64);
+#define QMM_FUSED1(NIT)                                                                                 \
+    do {                                                                                                \
+        if (repacked)                                                                                   \
+            hipLaunchKernelGGL((k_gemv1_fused_q4_K<true, NIT, (NIT < 4 ? NIT : 4)>), grid, block,       \
+                               (unsigned)lds, s, w, x, yq, out, N, K);                                  \
+        else                                                                                            \
+            hipLaunchKernelGGL((k_gemv1_fused_q4_K<false, NIT, (NIT < 4 ? NIT : 4)>), grid, block,      \
+                               (unsigned)lds, s, w, x, yq, out, N, K);                                  \
+    } while (0)
+    if (nit <= 1) QMM_FUSED1(1);
+    else if (nit <= 2) QMM_FUSED1(2);
+    else if (nit <= 4) QMM_FUSED1(4);
+    else QMM_FUSED1(8);
+#undef QMM_FUSED1
+    return hipGetLastError();
 }
 
 hipError_t launch_block_sums_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,

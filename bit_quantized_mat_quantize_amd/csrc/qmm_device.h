@@ -72,4 +72,38 @@ __device__ __forceinline__ Q4KScales unpack_scales(uint32_t w1, uint32_t w2, uin
     return r;
 }
 
+// ---- Q8_K quantization of one 256-value block held by a wavefront, four
+// consecutive values per lane (lane l holds elements 4l..4l+3).  Per block:
+// amax = max|x|, d = amax/127, id = d ? 1/d : 0, y = rint(x*id) clamped to
+// [-127, 127] (single IEEE fp32 operations; the library is built without FMA
+// contraction), bsum of 16 values = sum over lanes 4k..4k+3 (valid on lane 4k).
+// Every caller goes through this routine, so all paths produce identical bytes.
+struct Q8KLane {
+    int q[4];
+    float d;
+    int bsum;
+};
+__device__ __forceinline__ int clamp127(int v) { return v < -127 ? -127 : (v > 127 ? 127 : v); }
+__device__ __forceinline__ Q8KLane q8K_quantize_lane(const float4 v) {
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+    Q8KLane r;
+    r.d = a / 127.0f;
+    const float id = r.d != 0.0f ? 1.0f / r.d : 0.0f;
+    r.q[0] = clamp127((int)rintf(v.x * id));
+    r.q[1] = clamp127((int)rintf(v.y * id));
+    r.q[2] = clamp127((int)rintf(v.z * id));
+    r.q[3] = clamp127((int)rintf(v.w * id));
+    int s = r.q[0] + r.q[1] + r.q[2] + r.q[3];
+    s += __shfl_xor(s, 1, kWave);
+    s += __shfl_xor(s, 2, kWave);
+    r.bsum = s;
+    return r;
+}
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
 }  // namespace qmm

@@ -22,6 +22,11 @@ hipError_t launch_gemv_q4_0(const uint8_t *w, bool repacked, const uint8_t *y, f
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemv_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
+// Fused M = 1 quantize + GEMV: x is one fp32 row of K values; yq receives its
+// Q8_K bytes.  Valid for K <= gemv1_fused_max_k().
+int64_t gemv1_fused_max_k();
+hipError_t launch_gemv1_fused_q4_K(const uint8_t *w, bool repacked, const float *x, uint8_t *yq,
+                                   float *out, int64_t N, int64_t K, hipStream_t s);
 // int32 per-(sub-)block sums with the GEMV decode path (verification aid).
 hipError_t launch_block_sums_q4_0(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
                                   int64_t M, int64_t N, int64_t K, hipStream_t s);

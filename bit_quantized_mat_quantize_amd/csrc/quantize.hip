@@ -15,11 +15,6 @@ namespace {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
-    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
-           ((uint32_t)(d & 0xff) << 24);
-}
-
 // ---------------------------------------------------------------------------
 // Q8_K: one wavefront per 256-value block, 4 consecutive values per lane
 // (one 16-byte load).  Block bytes: fp32 d | int8 qs[256] | int16 bsums[16]
@@ -34,22 +29,11 @@ __global__ __launch_bounds__(256) void k_quantize_q8_K(const float *__restrict__
     const int lane = threadIdx.x & 63;
     const int64_t row = blk / nb_row, b = blk - row * nb_row;
     const float4 v = *reinterpret_cast<const float4 *>(x + row * K + b * QK_K + lane * 4);
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
-    const float d = a / 127.0f;
-    const float id = d != 0.0f ? 1.0f / d : 0.0f;
-    const int q0 = clampi((int)rintf(v.x * id), -127, 127);
-    const int q1 = clampi((int)rintf(v.y * id), -127, 127);
-    const int q2 = clampi((int)rintf(v.z * id), -127, 127);
-    const int q3 = clampi((int)rintf(v.w * id), -127, 127);
+    const Q8KLane r = q8K_quantize_lane(v);
     uint8_t *out = y + blk * kQ8_KBytes;
-    *reinterpret_cast<uint32_t *>(out + 4 + lane * 4) = pack4_i8(q0, q1, q2, q3);
-    int s = q0 + q1 + q2 + q3;
-    s += __shfl_xor(s, 1, kWave);
-    s += __shfl_xor(s, 2, kWave);
-    if ((lane & 3) == 0) *reinterpret_cast<int16_t *>(out + 260 + (lane >> 2) * 2) = (int16_t)s;
-    if (lane == 0) *reinterpret_cast<float *>(out) = d;
+    *reinterpret_cast<uint32_t *>(out + 4 + lane * 4) = pack4_i8(r.q[0], r.q[1], r.q[2], r.q[3]);
+    if ((lane & 3) == 0) *reinterpret_cast<int16_t *>(out + 260 + (lane >> 2) * 2) = (int16_t)r.bsum;
+    if (lane == 0) *reinterpret_cast<float *>(out) = r.d;
 }
 
 // ---------------------------------------------------------------------------

@@ -138,6 +138,25 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l,
                                int64_t M, int64_t N, int64_t K, qmm_algo algo,
                                void *stream);
 
+/* Quantize-and-multiply in one call: y = quantize_row_q8(x) (Q8_0 for t = Q4_0,
+ * Q8_K for t = Q4_K), then out = mul_mat(w, y).  The ggml-cpu mul_mat page
+ * ("激活量化重复与融合") notes that quantizing the activations once at the
+ * start of a fused node saves both the launch and the repeated conversion;
+ * here, for Q4_K with M == 1 and K <= 53760, the quantization runs inside the
+ * GEMV launch itself (one kernel), otherwise the two steps are enqueued back to
+ * back.  Projections that share one input are handled by concatenating their
+ * canonical weight rows along N before the repack (gate||up: N = 2*14336),
+ * or by passing the returned y to qmm_mul_mat_q4_* for the other projections.
+ * x: device fp32 [M, K]; y: device, y_bytes >= qmm_act_bytes(t's activation
+ * type, M, K), always fully written (byte-identical to qmm_quantize_row_q8);
+ * w, out as in qmm_mul_mat_q4_*.  x, y, w and out must not overlap.  N == 0
+ * quantizes only (w and out are not read).  Results are identical to
+ * qmm_quantize_row_q8 followed by qmm_mul_mat_q4_* (same rounding). */
+qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes,
+                                qmm_layout l, const float *x, void *y, size_t y_bytes,
+                                float *out, size_t out_bytes,
+                                int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Verification aid: the int32 per-sub-block (Q4_K) or per-block (Q4_0) sums
  * P[m][n][K/32] = sum_{i in block} q_i*y_i  (Q4_0: (q_i-8)*y_i), computed by
  * the same decode and int8 dot-product code the GEMV kernels use.

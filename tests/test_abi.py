@@ -108,6 +108,35 @@ def test_mul_mat_validation(lib):
     assert g(A, need - 1, 1, A, big, A, big, 1, 3, 64, None) == EINVAL
 
 
+def test_quantize_mul_mat_validation(lib):
+    f = lib.qmm_quantize_mul_mat
+    big = 10**9
+    args = dict(t=1, w=A, wb=big, l=1, x=A, y=A, yb=big, o=A, ob=big, M=1, N=8, K=512)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["t"], a["w"], a["wb"], a["l"], a["x"], a["y"], a["yb"], a["o"], a["ob"],
+                 a["M"], a["N"], a["K"], None)
+
+    assert call(t=4) == EUNSUP
+    assert call(l=3) == EUNSUP
+    assert call(K=300) == EUNSUP
+    assert call(t=0, K=48) == EUNSUP
+    assert call(M=-2) == EINVAL
+    assert call(N=-1) == EINVAL
+    assert call(x=None) == EINVAL and "x is NULL" in _last(lib)
+    assert call(x=A + 4) == EALIGN
+    assert call(y=None) == EINVAL
+    assert call(yb=2 * 292 - 1) == EINVAL and "needed" in _last(lib)
+    assert call(t=0, yb=16 * 34 - 1) == EINVAL
+    assert call(w=None) == EINVAL
+    assert call(o=A + 8) == EALIGN
+    assert call(wb=8 * 2 * 144 - 1) == EINVAL
+    assert call(ob=8 * 4 - 1) == EINVAL
+    # w and out are not checked when N == 0 would only quantize; M == 0 is empty
+    assert call(M=0, x=None, y=None, w=None, o=None) == OK
+
+
 def test_other_validation(lib):
     assert lib.qmm_quantize_weights(1, A, 4, 100, A, 10**6, None) == EUNSUP
     assert lib.qmm_quantize_weights(0, A, 4, 64, A, 4 * 2 * 18 - 1, None) == EINVAL
