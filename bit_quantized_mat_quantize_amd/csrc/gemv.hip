@@ -139,25 +139,31 @@ __global__ __launch_bounds__(256) void k_gemv_q4_K(const uint8_t *__restrict__ W
 // with the workgroup's share of the activation row, so one memory round trip
 // covers the whole row; the activation row (shared by the 4 rows of the
 // workgroup) is staged in LDS with its 16-byte pieces aligned:
-//   qs [K] int8 | d [nb] fp32 (padded to 16 B) | bsums [nb][16] int16
+//   qs [K] int8 | d [nb] fp32 (padded to 16 B) | bsums [nb][16] int16 | 16 B
+// The last 16 bytes take the stores of threads without a piece to stage, so
+// loads and stores need no branches (a load whose only use sits in a branch
+// is sunk past the weight loads by the compiler, which then has to wait for
+// every weight before staging the activations).
 // ---------------------------------------------------------------------------
 
 __host__ __device__ constexpr int64_t gemv1_lds_bytes(int64_t K) {
-    return K + ((K / QK_K) * 4 + 15) / 16 * 16 + (K / QK_K) * 32;
+    return K + ((K / QK_K) * 4 + 15) / 16 * 16 + (K / QK_K) * 32 + 16;
 }
 
 // Issue the loads of this lane's weight pieces c = base + lane + 64*it of row nn.
+// Pieces past the row end load the last piece again (unused): the loads stay
+// branch-free, so the compiler can wait for older loads (the activations)
+// while these are still in flight.
 template <bool REPACKED, int kNit>
 __device__ __forceinline__ void gemv1_load(const Q4KAddr<REPACKED> &A, int64_t nn, int base,
                                            int nchunk, int lane, uint4 (&hw)[kNit],
                                            uint4 (&pw)[kNit]) {
 #pragma unroll
     for (int it = 0; it < kNit; ++it) {
-        const int c = base + lane + 64 * it;
-        if (c < nchunk) {
-            hw[it] = ld16(A.header(nn, c >> 3));
-            pw[it] = ld16(A.piece(nn, c >> 3, c & 7));
-        }
+        const int c0 = base + lane + 64 * it;
+        const int c = c0 < nchunk ? c0 : nchunk - 1;
+        hw[it] = ld16(A.header(nn, c >> 3));
+        pw[it] = ld16(A.piece(nn, c >> 3, c & 7));
     }
 }
 
@@ -210,52 +216,55 @@ template <bool REPACKED, int kNit>
 __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ W,
                                                     const uint8_t *__restrict__ Y,
                                                     float *__restrict__ out, int64_t N, int64_t K) {
+    // 16-byte activation pieces per thread loaded up front (K <= 4096 * kYT)
+    constexpr int kYT = kNit >= 8 ? 4 : (kNit + 1) / 2;
     extern __shared__ __attribute__((aligned(16))) uint8_t ys[];
     const int64_t nb = K / QK_K;
     const int nchunk = (int)(nb * 8);
     uint8_t *s_qs = ys;
     float *s_d = reinterpret_cast<float *>(ys + K);
     int16_t *s_bs = reinterpret_cast<int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
+    uint8_t *s_trash = ys + K + (nb * 4 + 15) / 16 * 16 + nb * 32;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     const int64_t nn = n < N ? n : N - 1;  // a tail wavefront loads a valid row, stores nothing
     const Q4KAddr<REPACKED> A{W, N, nb};
+    const int nq = (int)(K / 16), nbs = (int)(nb * 2);
 
-    float acc = 0.0f;
-    for (int base = 0; base < nchunk; base += 64 * kNit) {
-        // activation row -> registers (first pass only), then this row's weights
-        const int nq = (int)(K / 16), nbs = (int)(nb * 2);
-        uint4 yq[4], yb = make_uint4(0, 0, 0, 0);
-        float yd = 0.0f;
-        if (base == 0) {
+    // activation row -> registers (indices clamped: branch-free loads), then
+    // the first pass of this row's weights, then the row -> LDS
+    uint4 yq[kYT];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int pc = tid + 256 * t;
-                if (pc < nq) yq[t] = ld_align4<uint4>(Y + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
-            }
-            if (tid < nbs) yb = ld_align4<uint4>(Y + (tid >> 1) * kQ8_KBytes + 260 + 16 * (tid & 1));
-            if (tid < nb) yd = ld_align4<float>(Y + tid * kQ8_KBytes);
-        }
-        uint4 pw[kNit], hw[kNit];
+    for (int t = 0; t < kYT; ++t) {
+        const int pc = tid + 256 * t < nq ? tid + 256 * t : nq - 1;
+        yq[t] = ld_align4<uint4>(Y + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
+    }
+    const int qb = tid < nbs ? tid : nbs - 1, qd = tid < nb ? tid : (int)nb - 1;
+    const uint4 yb = ld_align4<uint4>(Y + (qb >> 1) * kQ8_KBytes + 260 + 16 * (qb & 1));
+    const float yd = ld_align4<float>(Y + qd * kQ8_KBytes);
+    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
+    uint4 pw[kNit], hw[kNit];
+    gemv1_load<REPACKED, kNit>(A, nn, 0, nchunk, lane, hw, pw);
+#pragma unroll
+    for (int t = 0; t < kYT; ++t) {
+        const int pc = tid + 256 * t;
+        *reinterpret_cast<uint4 *>(pc < nq ? s_qs + 16 * pc : s_trash) = yq[t];
+    }
+    *reinterpret_cast<uint4 *>(tid < nbs ? reinterpret_cast<uint8_t *>(s_bs + 8 * tid) : s_trash) = yb;
+    *reinterpret_cast<float *>(tid < nb ? reinterpret_cast<uint8_t *>(s_d + tid) : s_trash) = yd;
+    // rows longer than 256 * kYT pieces: the rest of the activation row
+    for (int pc = tid + 256 * kYT; pc < nq; pc += 256)
+        *reinterpret_cast<uint4 *>(s_qs + 16 * pc) =
+            ld_align4<uint4>(Y + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
+    for (int q = tid + 256; q < nbs; q += 256)
+        *reinterpret_cast<uint4 *>(s_bs + 8 * q) =
+            ld_align4<uint4>(Y + (q >> 1) * kQ8_KBytes + 260 + 16 * (q & 1));
+    for (int q = tid + 256; q < nb; q += 256) s_d[q] = ld_align4<float>(Y + q * kQ8_KBytes);
+    __syncthreads();
+
+    float acc = gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, 0.0f);
+    for (int base = 64 * kNit; base < nchunk; base += 64 * kNit) {
         gemv1_load<REPACKED, kNit>(A, nn, base, nchunk, lane, hw, pw);
-        if (base == 0) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int pc = tid + 256 * t;
-                if (pc < nq) *reinterpret_cast<uint4 *>(s_qs + 16 * pc) = yq[t];
-            }
-            if (tid < nbs) *reinterpret_cast<uint4 *>(s_bs + 8 * tid) = yb;
-            if (tid < nb) s_d[tid] = yd;
-            // rows longer than 1024 pieces: the rest of the activation row
-            for (int pc = tid + 1024; pc < nq; pc += 256)
-                *reinterpret_cast<uint4 *>(s_qs + 16 * pc) =
-                    ld_align4<uint4>(Y + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
-            for (int q = tid + 256; q < nbs; q += 256)
-                *reinterpret_cast<uint4 *>(s_bs + 8 * q) =
-                    ld_align4<uint4>(Y + (q >> 1) * kQ8_KBytes + 260 + 16 * (q & 1));
-            for (int q = tid + 256; q < nb; q += 256) s_d[q] = ld_align4<float>(Y + q * kQ8_KBytes);
-            __syncthreads();
-        }
         acc = gemv1_accumulate<kNit>(hw, pw, base, nchunk, lane, s_qs, s_bs, s_d, acc);
     }
     acc = wave_sum(acc);
@@ -264,15 +273,20 @@ __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ 
 
 // ---------------------------------------------------------------------------
 // Fused M = 1 path: the fp32 activation row is quantized to Q8_K inside the
-// GEMV, straight into LDS, so one launch covers quantize + mul_mat.  Eight
-// wavefronts (eight output rows) per workgroup share the quantized row.  Each
-// wavefront first issues the fp32 loads of up to kXB of its activation blocks
-// (b = wave + 8i) and the loads of its row's weight pieces, then quantizes
-// while the weights are in flight (further blocks of long rows follow).  Workgroup 0 also stores the Q8_K bytes to
-// Yq, byte-identical to the stand-alone quantizer (same device routine), so
-// another projection of the same input can reuse them.
+// GEMV, straight into LDS, so one launch covers quantize + mul_mat.
+// Quantization costs vector-ALU work that every workgroup repeats, so the
+// grid holds at most one 16-wavefront workgroup per CU and each workgroup
+// loops over rows (wavefront w of workgroup g takes rows g*16 + w, then
+// + 16*gridDim.x, ...).  A wavefront first issues the fp32 loads of up to kXB
+// of its activation blocks (b = wave + 16i) and the loads of its first row,
+// then quantizes while the weights are in flight; in the row loop the next
+// row's pieces are loaded before the current row is reduced when the row
+// takes at most two pieces per lane (longer rows load it right after).  Rows
+// are one pass: K <= 8192, at most four pieces per lane.  Workgroup 0 also stores the Q8_K bytes to Yq, byte-identical to the
+// stand-alone quantizer (same device routine), so another projection of the
+// same input can reuse them.
 // ---------------------------------------------------------------------------
-constexpr int kFusedWaves = 8;
+constexpr int kFusedWaves = 16;
 
 template <bool REPACKED, int kNit, int kXB>
 __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
@@ -284,20 +298,25 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
     uint8_t *s_qs = ys;
     float *s_d = reinterpret_cast<float *>(ys + K);
     int16_t *s_bs = reinterpret_cast<int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
+    uint8_t *s_trash = ys + K + (nb * 4 + 15) / 16 * 16 + nb * 32;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int64_t n = (int64_t)blockIdx.x * kFusedWaves + wave;
-    const int64_t nn = n < N ? n : N - 1;  // a tail wavefront loads a valid row, stores nothing
+    const int64_t stride = (int64_t)gridDim.x * kFusedWaves;
+    int64_t row = (int64_t)blockIdx.x * kFusedWaves + wave;  // uniform per wavefront
     const Q4KAddr<REPACKED> A{W, N, nb};
     const bool store_q = blockIdx.x == 0;
 
-    // one 256-value block per wavefront and step: quantize, write LDS (+ Yq)
+    // one 256-value block per wavefront and step: quantize, write LDS (+ Yq);
+    // an invalid block (b >= nb) is quantized too and stored to the trash slot
     auto quantize_block = [&](const float4 v, int b) {
+        const bool valid = b < nb;
         const Q8KLane r = q8K_quantize_lane(v);
         const uint32_t packed = pack4_i8(r.q[0], r.q[1], r.q[2], r.q[3]);
-        *reinterpret_cast<uint32_t *>(s_qs + b * QK_K + 4 * lane) = packed;
-        if ((lane & 3) == 0) s_bs[16 * b + (lane >> 2)] = (int16_t)r.bsum;
-        if (lane == 0) s_d[b] = r.d;
-        if (store_q) {
+        *reinterpret_cast<uint32_t *>(valid ? s_qs + b * QK_K + 4 * lane : s_trash) = packed;
+        if ((lane & 3) == 0)
+            *reinterpret_cast<int16_t *>(valid ? reinterpret_cast<uint8_t *>(s_bs + 16 * b + (lane >> 2))
+                                               : s_trash) = (int16_t)r.bsum;
+        if (lane == 0) *reinterpret_cast<float *>(valid ? reinterpret_cast<uint8_t *>(s_d + b) : s_trash) = r.d;
+        if (store_q && valid) {
             uint8_t *o = Yq + (int64_t)b * kQ8_KBytes;
             *reinterpret_cast<uint32_t *>(o + 4 + 4 * lane) = packed;
             if ((lane & 3) == 0) *reinterpret_cast<int16_t *>(o + 260 + 2 * (lane >> 2)) = (int16_t)r.bsum;
@@ -305,31 +324,42 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
         }
     };
 
+    // the launcher guarantees nb <= 16 * kXB; block indices past the row end
+    // load the last block again (branch-free loads)
     float4 xv[kXB];
 #pragma unroll
     for (int i = 0; i < kXB; ++i) {
-        const int b = wave + kFusedWaves * i;  // uniform per wavefront
-        if (b < nb) xv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane);
+        const int b0 = wave + kFusedWaves * i;  // uniform per wavefront
+        const int b = b0 < nb ? b0 : (int)nb - 1;
+        xv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane);
     }
-    float acc = 0.0f;
-    for (int base = 0; base < nchunk; base += 64 * kNit) {
-        uint4 pw[kNit], hw[kNit];
-        gemv1_load<REPACKED, kNit>(A, nn, base, nchunk, lane, hw, pw);
-        if (base == 0) {
+    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
+    uint4 pw[kNit], hw[kNit];
+    // a wavefront without rows loads a valid row and stores nothing
+    gemv1_load<REPACKED, kNit>(A, row < N ? row : N - 1, 0, nchunk, lane, hw, pw);
 #pragma unroll
-            for (int i = 0; i < kXB; ++i) {
-                const int b = wave + kFusedWaves * i;
-                if (b < nb) quantize_block(xv[i], b);
+    for (int i = 0; i < kXB; ++i) quantize_block(xv[i], wave + kFusedWaves * i);
+    __syncthreads();
+
+    for (; row < N; row += stride) {
+        const bool more = row + stride < N;
+        float acc = 0.0f;
+        if constexpr (kNit <= 2) {  // rows of one pass; registers for a second row
+            uint4 pn[kNit], hn[kNit];
+            if (more) gemv1_load<REPACKED, kNit>(A, row + stride, 0, nchunk, lane, hn, pn);
+            acc = gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, acc);
+#pragma unroll
+            for (int it = 0; it < kNit; ++it) {
+                hw[it] = hn[it];
+                pw[it] = pn[it];
             }
-            // rows longer than 8 * kXB blocks: the remaining blocks
-            for (int b = wave + kFusedWaves * kXB; b < nb; b += kFusedWaves)
-                quantize_block(*reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane), b);
-            __syncthreads();
+        } else {
+            acc = gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, acc);
+            if (more) gemv1_load<REPACKED, kNit>(A, row + stride, 0, nchunk, lane, hw, pw);
         }
-        acc = gemv1_accumulate<kNit>(hw, pw, base, nchunk, lane, s_qs, s_bs, s_d, acc);
+        acc = wave_sum(acc);
+        if (lane == 0) out[row] = acc;
     }
-    acc = wave_sum(acc);
-    if (lane == 0 && n < N) out[n] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -484,30 +514,45 @@ hipError_t launch_gemv_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, f
 }
 
 int64_t gemv1_fused_max_k() {
-    // largest K whose activation row fits the 60 KB LDS budget
-    int64_t k = 0;
-    while (gemv1_lds_bytes(k + QK_K) <= 60 * 1024) k += QK_K;
-    return k;
+    // rows of up to four 16-byte pieces per lane (K <= 8192): longer rows
+    // need more registers than a 16-wavefront workgroup leaves per lane, and
+    // their weight stream is long enough to hide a separate quantize launch
+    return 4 * 64 / 8 * QK_K;
+}
+
+int cu_count() {
+    static int cached[64];  // per device; 0 = not queried yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+    }
+    return v;
 }
 
 hipError_t launch_gemv1_fused_q4_K(const uint8_t *w, bool repacked, const float *x, uint8_t *yq,
                                    float *out, int64_t N, int64_t K, hipStream_t s) {
     const int64_t lds = gemv1_lds_bytes(K);
     const int64_t nit = (K / QK_K * 8 + 63) / 64;
-    const dim3 grid((unsigned)((N + kFusedWaves - 1) / kFusedWaves)), block(kFusedWaves * 64);
-#define QMM_FUSED1(NIT)                                                                                 \
-    do {                                                                                                \
-        if (repacked)                                                                                   \
-            hipLaunchKernelGGL((k_gemv1_fused_q4_K<true, NIT, (NIT < 4 ? NIT : 4)>), grid, block,       \
-                               (unsigned)lds, s, w, x, yq, out, N, K);                                  \
-        else                                                                                            \
-            hipLaunchKernelGGL((k_gemv1_fused_q4_K<false, NIT, (NIT < 4 ? NIT : 4)>), grid, block,      \
-                               (unsigned)lds, s, w, x, yq, out, N, K);                                  \
+    const int64_t groups = (N + kFusedWaves - 1) / kFusedWaves;
+    const int64_t cus = cu_count();
+    const dim3 grid((unsigned)(groups < cus ? groups : cus)), block(kFusedWaves * 64);
+#define QMM_FUSED1(NIT, XB)                                                                        \
+    do {                                                                                           \
+        if (repacked)                                                                              \
+            hipLaunchKernelGGL((k_gemv1_fused_q4_K<true, NIT, XB>), grid, block, (unsigned)lds, s, \
+                               w, x, yq, out, N, K);                                               \
+        else                                                                                       \
+            hipLaunchKernelGGL((k_gemv1_fused_q4_K<false, NIT, XB>), grid, block, (unsigned)lds,   \
+                               s, w, x, yq, out, N, K);                                            \
     } while (0)
-    if (nit <= 1) QMM_FUSED1(1);
-    else if (nit <= 2) QMM_FUSED1(2);
-    else if (nit <= 4) QMM_FUSED1(4);
-    else QMM_FUSED1(8);
+    // kXB = activation blocks per wavefront: ceil(nb / 16) (nb <= 8 * kNit <= 16 * kXB)
+    if (nit <= 1) QMM_FUSED1(1, 1);
+    else if (nit <= 2) QMM_FUSED1(2, 1);
+    else QMM_FUSED1(4, 2);
 #undef QMM_FUSED1
     return hipGetLastError();
 }

@@ -45,10 +45,45 @@ __device__ __forceinline__ uint32_t ld_u16(const void *p) {
     return *reinterpret_cast<const uint16_t *>(p);
 }
 
-// ---- wavefront reductions (all 64 lanes hold the result)
+// ---- cross-lane moves.  DPP moves within rows of 16 lanes (gfx9 DPP control
+// codes: quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140), then v_readlane across the
+// four rows: no LDS round trips.  All 64 lanes must be active.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over the 64 lanes (every lane gets the same value; a fixed tree order).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x141>(v);
+    v += dpp_f32<0x140>(v);
+    return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
+// Max over the 64 lanes (exact; every lane gets the value).
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+                 fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
+// Sum over each group of 4 consecutive lanes (lanes 4k..4k+3 all get it).
+__device__ __forceinline__ int quad_sum(int v) {
+    v += dpp_i32<0xB1>(v);
+    v += dpp_i32<0x4E>(v);
     return v;
 }
 
@@ -76,7 +111,8 @@ __device__ __forceinline__ Q4KScales unpack_scales(uint32_t w1, uint32_t w2, uin
 // consecutive values per lane (lane l holds elements 4l..4l+3).  Per block:
 // amax = max|x|, d = amax/127, id = d ? 1/d : 0, y = rint(x*id) clamped to
 // [-127, 127] (single IEEE fp32 operations; the library is built without FMA
-// contraction), bsum of 16 values = sum over lanes 4k..4k+3 (valid on lane 4k).
+// contraction), bsum of 16 values = sum over lanes 4k..4k+3.  All 64 lanes
+// must be active.
 // Every caller goes through this routine, so all paths produce identical bytes.
 struct Q8KLane {
     int q[4];
@@ -85,9 +121,7 @@ struct Q8KLane {
 };
 __device__ __forceinline__ int clamp127(int v) { return v < -127 ? -127 : (v > 127 ? 127 : v); }
 __device__ __forceinline__ Q8KLane q8K_quantize_lane(const float4 v) {
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+    const float a = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     Q8KLane r;
     r.d = a / 127.0f;
     const float id = r.d != 0.0f ? 1.0f / r.d : 0.0f;
@@ -95,10 +129,7 @@ __device__ __forceinline__ Q8KLane q8K_quantize_lane(const float4 v) {
     r.q[1] = clamp127((int)rintf(v.y * id));
     r.q[2] = clamp127((int)rintf(v.z * id));
     r.q[3] = clamp127((int)rintf(v.w * id));
-    int s = r.q[0] + r.q[1] + r.q[2] + r.q[3];
-    s += __shfl_xor(s, 1, kWave);
-    s += __shfl_xor(s, 2, kWave);
-    r.bsum = s;
+    r.bsum = quad_sum(r.q[0] + r.q[1] + r.q[2] + r.q[3]);
     return r;
 }
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {

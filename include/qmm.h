@@ -142,7 +142,7 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l,
  * Q8_K for t = Q4_K), then out = mul_mat(w, y).  The ggml-cpu mul_mat page
  * ("激活量化重复与融合") notes that quantizing the activations once at the
  * start of a fused node saves both the launch and the repeated conversion;
- * here, for Q4_K with M == 1 and K <= 53760, the quantization runs inside the
+ * here, for Q4_K with M == 1 and K <= 8192, the quantization runs inside the
  * GEMV launch itself (one kernel), otherwise the two steps are enqueued back to
  * back.  Projections that share one input are handled by concatenating their
  * canonical weight rows along N before the repack (gate||up: N = 2*14336),
