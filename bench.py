@@ -50,7 +50,16 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--all", action="store_true", help="report every workload")
     ap.add_argument("--prefill-only", action="store_true", help="measure only the prefill GEMM")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps eagerly instead of replaying a HIP graph "
+                         "(for profilers that count per dispatch)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run plain device copies of 256 MiB (a known byte count for "
+                         "scaling the HBM read/write counters)")
     return ap.parse_args()
+
+
+GRAPH = True
 
 
 class Prepared:
@@ -121,38 +130,59 @@ class Prepared:
                                          out=m["out"])
 
     @property
-    def launches_per_step(self) -> int:
+    def calls_per_step(self) -> int:
+        """mul_mat (or quantize_mul_mat) calls per step."""
         return sum(len(it["mats"]) for it in self.items)
 
 
 def time_graph(prep: Prepared, steps: int, only=None, reps: int = 1):
-    """Capture `steps` steps in one HIP graph, replay it, return ms per step."""
+    """Capture `steps` steps in one HIP graph, replay it, return ms per step
+    (with GRAPH off: launch the steps eagerly and time them with events)."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for i in range(3):                  # warm the kernels on the capture stream
+        for i in range(3):                  # warm the kernels on the timing stream
             prep.step(i, only)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        for i in range(steps):
-            prep.step(i, only)
-    g.replay()                               # untimed replay
-    torch.cuda.synchronize()
+    g = None
+    if GRAPH:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                prep.step(i, only)
+        g.replay()                           # untimed replay
+        torch.cuda.synchronize()
     best = None
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        e0.record()
-        g.replay()
-        e1.record()
+        with torch.cuda.stream(s):           # events on the stream the kernels run on
+            e0.record()
+            if g is not None:
+                g.replay()
+            else:
+                for i in range(steps):
+                    prep.step(i, only)
+            e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
         best = ms if best is None else min(best, ms)
     del g
     return best
+
+
+def calibrate_copy():
+    """Plain device copies of a known size (read 256 MiB, write 256 MiB)."""
+    import torch
+    n = (256 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return {"bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4, "copies": 3}
 
 
 def cpu_baseline(key: str, seconds: float):
@@ -204,7 +234,7 @@ def measure_decode(key: str, layout: str, steps: int, warmup: int):
         ms_step = time_graph(prep, steps, reps=3)
         tag = "fused" if fused else "unfused"
         res[tag] = dict(ms_per_step=ms_step, value=wbytes / (ms_step * 1e-3) / 1e9,
-                        launches_per_step=prep.launches_per_step)
+                        calls_per_step=prep.calls_per_step)
         if not fused:
             res[tag]["mul_mat_us"] = time_graph(prep, steps, only="mul_mat", reps=3) * 1e3
             res[tag]["quantize_us"] = time_graph(prep, steps, only="quantize", reps=3) * 1e3
@@ -214,14 +244,43 @@ def measure_decode(key: str, layout: str, steps: int, warmup: int):
     return res
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemv1_q4_K_c2.md")
+TRAFFIC_SOURCES = ("bit_quantized_mat_quantize_amd/csrc/gemv.hip",
+                   "bit_quantized_mat_quantize_amd/csrc/qmm_device.h")
+
+
+def profiled_traffic(kernel: str, key: str):
+    """HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters
+    (scaled by a plain copy of known size), or None when no measurement exists
+    for this kernel and workload or the kernel sources changed since."""
+    import hashlib
+    import re
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    sha = h.hexdigest()[:16]
+    pat = re.compile(r"traffic kernel=(\S+) workload=(\S+) bytes_per_launch=(\d+) sources_sha256_16=(\w+)")
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            m = pat.search(line)
+            if m and m.group(1) == kernel and m.group(2) == key and m.group(4) == sha:
+                return int(m.group(3))
+    return None
+
+
 def roofline_of(res: dict, path: str) -> dict:
     """Roofline of the dominant kernel: weight bytes per launch / launch time."""
     r = res[path]
-    n = r["launches_per_step"]
+    n = r["calls_per_step"]
     ms = r["ms_per_step"] if path == "fused" else r["mul_mat_us"] * 1e-3
     achieved = res["weight_bytes"] / n / (ms / n * 1e-3) / 1e9
+    kernel = "k_gemv1_fused_q4_K" if path == "fused" else "k_gemv1_q4_K"
+    traffic = profiled_traffic(kernel, res["key"]) if n == 1 else None
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
 
 def measure_prefill(key: str, layout: str, steps: int):
@@ -248,6 +307,8 @@ def main():
         sys.exit(2)
     import torch
     import bit_quantized_mat_quantize_amd as qmm
+    global GRAPH
+    GRAPH = not a.no_graph
     qmm.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
@@ -305,6 +366,10 @@ def main():
     }
     if extra:
         line["other_workloads"] = extra
+    if not GRAPH:
+        line["timing"] = "eager launches (--no-graph)"
+    if a.calibrate_copy:
+        line["copy_calibration"] = calibrate_copy()
     print(json.dumps(line), flush=True)
 
 
