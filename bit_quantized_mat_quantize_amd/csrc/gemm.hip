@@ -60,8 +60,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 256, MT = BM / 32, NWAVE = 4, NTHR = 64 * NWAVE;
-constexpr int CT = BN / 32 / NWAVE;  // column tiles per wavefront
+constexpr int BM = 128, BN = 256, MT = BM / 32, NWAVE = 8, NTHR = 64 * NWAVE;
+constexpr int CT = BN / 32 / NWAVE;  // column tiles per wavefront (one)
 constexpr int A_OFF = 0, A_BYTES = BM * 256;
 constexpr int H_OFF = A_OFF + A_BYTES, H_BYTES = BN * 16;
 constexpr int P_OFF = H_OFF + H_BYTES, P_BYTES = BN * 128;
@@ -77,6 +77,7 @@ constexpr int P_PER_WAVE = P_INSTR / NWAVE;
 static_assert(A_INSTR % NWAVE == 0 && P_INSTR % NWAVE == 0 && H_INSTR <= NWAVE,
               "staging must split evenly over the wavefronts");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
+static_assert(CT == 1 && 2 * BM <= NTHR, "one column tile per wavefront; bsums staged by 2*BM threads");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -90,20 +91,22 @@ __device__ __forceinline__ int plane(uint32_t q4, uint32_t digit_pair) {
     return (int)__builtin_bit_cast(uint32_t, p);
 }
 
-// 16 bytes per lane from `src` into LDS at lds_base + 16 * lane (lds_base is
-// wavefront-uniform)
-__device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
+// Staging goes through buffer resources: a scalar base and byte count per
+// source (the tile's first activation row, first header, first payload) and
+// 32-bit per-lane offsets, with the super-block step in the scalar offset.
+// Loads past the byte count return zero instead of faulting.  Plain global
+// pointers would need 64-bit per-lane addresses, and a generic (flat) load
+// would make the compiler wait for every outstanding global->LDS transfer.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t *base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, (int)(uint32_t)n,
+                                             0x00020000);  // raw dword access (gfx9 family)
 }
-
-// A pointer the compiler must treat as wavefront-uniform and opaque, so that
-// base + 32-bit lane offset stays a scalar base plus a vector offset instead
-// of being re-associated into per-lane 64-bit addresses kept across the loop.
-__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+// 16 bytes per lane into LDS at lds_base + 16 * lane (lds_base wavefront-uniform)
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, voff, soff, 0, 0);
 }
 
 template <bool REPACKED>
@@ -116,23 +119,30 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs; give
-    // each XCD a contiguous range of tiles (M-tile fastest) so the tiles that
-    // share weight columns and activation rows meet in the same L2.
+    // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
+    // each XCD gets a contiguous range of the index v; v walks groups of GM
+    // row tiles with the row tile fastest, so the 32 workgroups an XCD runs
+    // at once cover GM row tiles x 32/GM column tiles and share both their
+    // activation and weight tiles through that XCD's L2.
+    constexpr int GM = 4;
     const int nwg = tiles_m * tiles_n;
     const int bid = blockIdx.x;
     const int v = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
-    const int tile_m = v % tiles_m, tile_n = v / tiles_m;
+    const int group = v / (GM * tiles_n), first_m = group * GM;
+    const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;
+    const int in_group = v - group * GM * tiles_n;
+    const int tile_m = first_m + in_group % gm, tile_n = in_group / gm;
     const int64_t m_base = (int64_t)tile_m * BM, n_base = (int64_t)tile_n * BN;
     const int64_t nb = K / QK_K;
 
     // ---- staging sources.  Rows past M and columns past N are clamped to the
     // last valid one (their results are never stored), so every load is in
-    // bounds and none is predicated.  Bases are uniform, offsets 32-bit.
+    // bounds and none is predicated.
     const int m_last = (int)(M - 1 - m_base < BM - 1 ? M - 1 - m_base : BM - 1);
     const int n_last = (int)(N - 1 - n_base < BN - 1 ? N - 1 - n_base : BN - 1);
     const uint32_t a_rowstride = (uint32_t)(nb * kQ8_KBytes);
-    const uint8_t *a_base = Y + m_base * nb * kQ8_KBytes;
+    const int64_t a_first = m_base * nb * kQ8_KBytes;
+    const int64_t a_bytes = M * nb * kQ8_KBytes - a_first;
     uint32_t a_goff[A_PER_WAVE];
 #pragma unroll
     for (int t = 0; t < A_PER_WAVE; ++t) {
@@ -142,9 +152,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
         a_goff[t] = (uint32_t)rr * a_rowstride + 4 + 16 * gp;
     }
     const uint32_t hdr_step = REPACKED ? 16 : kQ4_KBytes, pay_step = REPACKED ? 128 : kQ4_KBytes;
-    const uint8_t *h_base = W + (int64_t)hdr_step * (n_base * nb);
-    const uint8_t *p_base = REPACKED ? W + 16 * N * nb + 128 * (n_base * nb)
-                                     : W + kQ4_KBytes * (n_base * nb) + 16;
+    const int64_t w_bytes = N * nb * kQ4_KBytes;
+    const int64_t h_first = (int64_t)hdr_step * (n_base * nb);
+    const int64_t p_first = REPACKED ? 16 * N * nb + 128 * (n_base * nb) : kQ4_KBytes * (n_base * nb) + 16;
+    // (the resources are built where they are used: a resource held across the
+    // lambdas below would be treated as divergent and waterfall-looped)
     // headers: wavefront w < H_INSTR loads columns 64w + lane
     const int h_col = wave * 64 + lane;
     const uint32_t h_goff = (uint32_t)(h_col < n_last ? h_col : n_last) * (uint32_t)nb * hdr_step;
@@ -158,34 +170,42 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
         const int cc = c < n_last ? c : n_last;
         p_goff[t] = (uint32_t)cc * (uint32_t)nb * pay_step + 16 * piece;
     }
-    // bsums: row tid>>1, 16-byte half tid&1; d_a: row tid (threads < 128)
-    const int s_row = tid >> 1;
+    // bsums: row tid>>1, 16-byte half tid&1 (threads < 256); d_a: row tid (threads < 128)
+    const int s_row = (tid >> 1) & (BM - 1);
     const uint32_t s_off = (uint32_t)(s_row < m_last ? s_row : m_last) * a_rowstride + 260 + 16 * (tid & 1);
     const uint32_t d_off = (uint32_t)((tid & (BM - 1)) < m_last ? (tid & (BM - 1)) : m_last) * a_rowstride;
 
     auto issue = [&](int64_t b, uint8_t *buf) {
-        const uint8_t *ab = uniform_ptr(a_base + b * kQ8_KBytes);
+        const rsrc_t ra = make_rsrc(Y + a_first, a_bytes);
+        const rsrc_t rp = make_rsrc(W + p_first, w_bytes - p_first);
+        const rsrc_t rh = make_rsrc(W + h_first, w_bytes - h_first);
+        const uint32_t sa = (uint32_t)b * kQ8_KBytes;
 #pragma unroll
         for (int t = 0; t < A_PER_WAVE; ++t)
-            dma16(ab + a_goff[t], buf + A_OFF + (wave * A_PER_WAVE + t) * 1024);
-        const uint8_t *pb = uniform_ptr(p_base + b * pay_step);
+            dma16(ra, a_goff[t], sa, buf + A_OFF + (wave * A_PER_WAVE + t) * 1024);
+        const uint32_t sp = (uint32_t)b * pay_step;
 #pragma unroll
         for (int t = 0; t < P_PER_WAVE; ++t)
-            dma16(pb + p_goff[t], buf + P_OFF + (wave * P_PER_WAVE + t) * 1024);
-        if (wave < H_INSTR)
-            dma16(uniform_ptr(h_base + b * hdr_step) + h_goff, buf + H_OFF + wave * 1024);
+            dma16(rp, p_goff[t], sp, buf + P_OFF + (wave * P_PER_WAVE + t) * 1024);
+        if (wave < H_INSTR) dma16(rh, h_goff, (uint32_t)b * hdr_step, buf + H_OFF + wave * 1024);
     };
     auto prefetch = [&](int64_t b, uint4 &raw, uint32_t &draw) {
-        const uint8_t *yb = uniform_ptr(a_base + b * kQ8_KBytes);
-        raw = ld_align4<uint4>(yb + s_off);
-        if (tid < BM) draw = ld_align4<uint32_t>(yb + d_off);
+        const rsrc_t ra = make_rsrc(Y + a_first, a_bytes);
+        const uint32_t sa = (uint32_t)b * kQ8_KBytes;
+        if (tid < 2 * BM) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, s_off, sa, 0);
+            raw = make_uint4(v.x, v.y, v.z, v.w);
+        }
+        if (tid < BM) draw = __builtin_amdgcn_raw_buffer_load_b32(ra, d_off, sa, 0);
     };
     auto commit = [&](const uint4 &raw, uint32_t draw, uint8_t *buf) {
-        const uint4 hv = make_uint4(h2_bits((int16_t)(raw.x & 0xffff), (int16_t)(raw.x >> 16)),
-                                    h2_bits((int16_t)(raw.y & 0xffff), (int16_t)(raw.y >> 16)),
-                                    h2_bits((int16_t)(raw.z & 0xffff), (int16_t)(raw.z >> 16)),
-                                    h2_bits((int16_t)(raw.w & 0xffff), (int16_t)(raw.w >> 16)));
-        *reinterpret_cast<uint4 *>(buf + BS_OFF + s_row * BS_STRIDE + 16 * (tid & 1)) = hv;
+        if (tid < 2 * BM) {
+            const uint4 hv = make_uint4(h2_bits((int16_t)(raw.x & 0xffff), (int16_t)(raw.x >> 16)),
+                                        h2_bits((int16_t)(raw.y & 0xffff), (int16_t)(raw.y >> 16)),
+                                        h2_bits((int16_t)(raw.z & 0xffff), (int16_t)(raw.z >> 16)),
+                                        h2_bits((int16_t)(raw.w & 0xffff), (int16_t)(raw.w >> 16)));
+            *reinterpret_cast<uint4 *>(buf + BS_OFF + s_row * BS_STRIDE + 16 * (tid & 1)) = hv;
+        }
         if (tid < BM) *reinterpret_cast<uint32_t *>(buf + DA_OFF + 4 * tid) = draw;
     };
 
@@ -212,39 +232,37 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
             prefetch(b + 1, raw, draw);
         }
 
-        // ---------------- this lane's two columns: header and the 8 sub-block planes
-        float dcol[CT];
-        v4i bhi[CT][8], blo[CT][8];
-        v8h bmh[CT], bml[CT];
+        // ---------------- this lane's column: header and the 8 sub-block planes
+        const int col = wave * 32 + l32;
+        const uint4 hdr = *reinterpret_cast<const uint4 *>(buf + H_OFF + 16 * col);
+        const float dcol = f16_bits_to_f32(hdr.x & 0xffff);
+        const float dmcol = f16_bits_to_f32(hdr.x >> 16);
+        const Q4KScales sc = unpack_scales(hdr.y, hdr.z, hdr.w);
+        v4i bhi[8], blo[8];
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            const int col = wave * (32 * CT) + 32 * c + l32;
-            const uint4 hdr = *reinterpret_cast<const uint4 *>(buf + H_OFF + 16 * col);
-            dcol[c] = f16_bits_to_f32(hdr.x & 0xffff);
-            const float dmcol = f16_bits_to_f32(hdr.x >> 16);
-            const Q4KScales sc = unpack_scales(hdr.y, hdr.z, hdr.w);
+        for (int g = 0; g < 4; ++g) {
+            const int piece = 2 * g + hh;  // this lane's K-slice of sub-blocks 2g, 2g+1
+            const uint4 pw = *reinterpret_cast<const uint4 *>(buf + P_OFF + 128 * col +
+                                                              16 * (piece ^ ((col >> 1) & 7)));
+            const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int piece = 2 * g + hh;  // this lane's K-slice of sub-blocks 2g, 2g+1
-                const uint4 pw = *reinterpret_cast<const uint4 *>(buf + P_OFF + 128 * col +
-                                                                  16 * (piece ^ ((col >> 1) & 7)));
-                const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {  // t = 0: low nibbles (sub-block 2g), 1: high (2g+1)
-                    const int j = 2 * g + t;
-                    const int shift = t * 4;
-                    const uint32_t q0 = (pw.x >> shift) & 0x0f0f0f0fu, q1 = (pw.y >> shift) & 0x0f0f0f0fu;
-                    const uint32_t q2 = (pw.z >> shift) & 0x0f0f0f0fu, q3 = (pw.w >> shift) & 0x0f0f0f0fu;
-                    const uint32_t sj = (sw >> (8 * (j & 3))) & 0xff;
-                    const uint32_t hi2 = (sj >> 3) * 0x00010001u, lo2 = (sj & 7) * 0x00010001u;
-                    bhi[c][j] = v4i{plane(q0, hi2), plane(q1, hi2), plane(q2, hi2), plane(q3, hi2)};
-                    blo[c][j] = v4i{plane(q0, lo2), plane(q1, lo2), plane(q2, lo2), plane(q3, lo2)};
-                }
+            for (int t = 0; t < 2; ++t) {  // t = 0: low nibbles (sub-block 2g), 1: high (2g+1)
+                const int j = 2 * g + t;
+                const int shift = t * 4;
+                const uint32_t q0 = (pw.x >> shift) & 0x0f0f0f0fu, q1 = (pw.y >> shift) & 0x0f0f0f0fu;
+                const uint32_t q2 = (pw.z >> shift) & 0x0f0f0f0fu, q3 = (pw.w >> shift) & 0x0f0f0f0fu;
+                const uint32_t sj = (sw >> (8 * (j & 3))) & 0xff;
+                const uint32_t hi2 = (sj >> 3) * 0x00010001u, lo2 = (sj & 7) * 0x00010001u;
+                bhi[j] = v4i{plane(q0, hi2), plane(q1, hi2), plane(q2, hi2), plane(q3, hi2)};
+                blo[j] = v4i{plane(q0, lo2), plane(q1, lo2), plane(q2, lo2), plane(q3, lo2)};
             }
-            // min-term operand: -dmin*m_j has at most 17 significant bits, so it is
-            // the exact sum of two fp16 values (hi = fp16(-dmin*m), lo = remainder);
-            // two fp16 MFMAs against the exact fp16 bsums give -dmin*Mn with fp32
-            // rounding only.
+        }
+        // min-term operand: -dmin*m_j has at most 17 significant bits, so it is
+        // the exact sum of two fp16 values (hi = fp16(-dmin*m), lo = remainder);
+        // two fp16 MFMAs against the exact fp16 bsums give -dmin*Mn with fp32
+        // rounding only.
+        v8h bmh, bml;
+        {
             const uint32_t mw = hh == 0 ? sc.m_lo : sc.m_hi;  // m_{4hh .. 4hh+3}
             uint32_t bh[4], bl[4];
 #pragma unroll
@@ -255,73 +273,61 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
                 bh[e] = hb | (hb << 16);
                 bl[e] = lb | (lb << 16);
             }
-            __builtin_memcpy(&bmh[c], bh, 16);
-            __builtin_memcpy(&bml[c], bl, 16);
+            __builtin_memcpy(&bmh, bh, 16);
+            __builtin_memcpy(&bml, bl, 16);
         }
         const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
 
-        // ---------------- eight (row tile, column tile) pairs, software-pipelined
-        v4i a_op[8];
-        v8h a_bs;
-        float dav[16];
-        v16i ah[2], al[2];
-        v16f mn[2];
-        auto load_rows = [&](int i) {
+        // ---------------- the four row tiles of this column tile
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
             const int row = i * 32 + l32;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * 256 +
-                                                                 16 * ((2 * j + hh) ^ (row & 15)));
-                a_op[j] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-            }
-            const uint4 au = *reinterpret_cast<const uint4 *>(buf + BS_OFF + row * BS_STRIDE + 16 * hh);
-            __builtin_memcpy(&a_bs, &au, 16);
-        };
-        auto mfma_pair = [&](int c, int set) {
             const v16i zero = {};
+            v16i ah, al;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                ah[set] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[j], bhi[c][j], j ? ah[set] : zero, 0, 0, 0);
-                al[set] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[j], blo[c][j], j ? al[set] : zero, 0, 0, 0);
+            for (int half = 0; half < 2; ++half) {
+                v4i a_op[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = 4 * half + jj;
+                    const uint4 a = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * 256 +
+                                                                     16 * ((2 * j + hh) ^ (row & 15)));
+                    a_op[jj] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = 4 * half + jj;
+                    ah = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[jj], bhi[j], j ? ah : zero, 0, 0, 0);
+                    al = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[jj], blo[j], j ? al : zero, 0, 0, 0);
+                }
+            }
+            v8h a_bs;
+            {
+                const uint4 au = *reinterpret_cast<const uint4 *>(buf + BS_OFF + row * BS_STRIDE + 16 * hh);
+                __builtin_memcpy(&a_bs, &au, 16);
             }
             const v16f zf = {};
-            mn[set] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmh[c], zf, 0, 0, 0);
-            mn[set] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bml[c], mn[set], 0, 0, 0);
-        };
-        auto load_da = [&](int i) {
+            v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmh, zf, 0, 0, 0);
+            mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bml, mn, 0, 0, 0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
-                dav[4 * q + 0] = d4.x; dav[4 * q + 1] = d4.y; dav[4 * q + 2] = d4.z; dav[4 * q + 3] = d4.w;
-            }
-        };
-        auto epilogue = [&](int i, int c, int set) {
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int S = (ah[set][r] << 3) + al[set][r];
-                const float t = fmaf(dcol[c], (float)S, mn[set][r]);
-                acc[i][c][r] = fmaf(dav[r], t, acc[i][c][r]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q + e;
+                    const int S = (ah[r] << 3) + al[r];
+                    const float t = fmaf(dcol, (float)S, mn[r]);
+                    acc[i][0][r] = fmaf(dv[e], t, acc[i][0][r]);
+                }
             }
-        };
-        load_rows(0);
-        mfma_pair(0, 0);
-#pragma unroll
-        for (int p = 0; p < MT * CT; ++p) {
-            const int i = p / CT, c = p % CT;
-            if (p + 1 < MT * CT) {
-                const int i1 = (p + 1) / CT, c1 = (p + 1) % CT;
-                if (c1 == 0) load_rows(i1);
-                mfma_pair(c1, (p + 1) & 1);
-            }
-            if (c == 0) load_da(i);
-            epilogue(i, c, p & 1);
         }
     }
 
     // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-        const int64_t n = n_base + wave * (32 * CT) + 32 * c + l32;
+        const int64_t n = n_base + wave * 32 + l32;
         if (n < N) {
 #pragma unroll
             for (int i = 0; i < MT; ++i)
