@@ -18,13 +18,13 @@ LIB_PATH = os.path.join(PKG, "libqmm.so")
 Q8_0, Q8_K = 0, 1
 Q4_0, Q4_K = 0, 1
 CANONICAL, REPACKED = 0, 1
-ALGO_AUTO, ALGO_GEMV, ALGO_MFMA = 0, 1, 2
+ALGO_AUTO, ALGO_GEMV, ALGO_MFMA, ALGO_SKINNY = 0, 1, 2, 3
 STATUS = {0: "QMM_OK", 1: "QMM_EINVAL", 2: "QMM_EALIGN", 3: "QMM_EUNSUPPORTED", 4: "QMM_EDEVICE"}
 
 _ACT = {"q8_0": Q8_0, "q8_K": Q8_K}
 _WEIGHT = {"q4_0": Q4_0, "q4_K": Q4_K}
 _LAYOUT = {"canonical": CANONICAL, "repacked": REPACKED}
-_ALGO = {"auto": ALGO_AUTO, "gemv": ALGO_GEMV, "mfma": ALGO_MFMA}
+_ALGO = {"auto": ALGO_AUTO, "gemv": ALGO_GEMV, "mfma": ALGO_MFMA, "skinny": ALGO_SKINNY}
 
 
 class QmmError(RuntimeError):

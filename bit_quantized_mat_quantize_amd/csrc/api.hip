@@ -188,20 +188,35 @@ qmm_status qmm_mul_mat_q4_0(const void *w, size_t w_bytes, qmm_layout l, const v
 qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,
                                size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
                                int64_t K, qmm_algo algo, void *stream) {
-    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
+    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA &&
+        algo != QMM_ALGO_SKINNY)
         return fail(QMM_EUNSUPPORTED, "unknown algo %d", (int)algo);
     QMM_TRY(mul_mat_common(QMM_Q4_K, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
     if (algo == QMM_ALGO_GEMV && M > qmm::kGemvMaxM)
         return fail(QMM_EUNSUPPORTED, "GEMV path takes M <= %d (M = %lld)", qmm::kGemvMaxM,
                     (long long)M);
+    // the small-batch kernel addresses both matrices with 32-bit offsets
+    const bool skinny_ok = M <= qmm::skinny_max_m() &&
+                           qmm_weight_bytes(QMM_Q4_K, l, N, K) < (size_t(1) << 32) &&
+                           qmm_act_bytes(QMM_Q8_K, M, K) < (size_t(1) << 32);
+    if (algo == QMM_ALGO_SKINNY && !skinny_ok)
+        return fail(QMM_EUNSUPPORTED,
+                    "SKINNY path takes M <= %lld and matrices below 4 GiB (M = %lld)",
+                    (long long)qmm::skinny_max_m(), (long long)M);
     if (M == 0 || N == 0) return QMM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool rep = l == QMM_LAYOUT_REPACKED;
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
-    const bool gemv = algo == QMM_ALGO_GEMV || (algo == QMM_ALGO_AUTO && M <= qmm::kGemvMaxM);
-    if (gemv)
+    qmm_algo a = algo;
+    if (a == QMM_ALGO_AUTO)
+        a = M == 1 ? QMM_ALGO_GEMV : (skinny_ok ? QMM_ALGO_SKINNY
+                                                : (M <= qmm::kGemvMaxM ? QMM_ALGO_GEMV : QMM_ALGO_MFMA));
+    if (a == QMM_ALGO_GEMV)
         return device_status(qmm::launch_gemv_q4_K(wb, rep, yb, out, M, N, K, s), "mul_mat_q4_K gemv launch");
+    if (a == QMM_ALGO_SKINNY)
+        return device_status(qmm::launch_skinny_q4_K(wb, rep, yb, out, M, N, K, s),
+                             "mul_mat_q4_K skinny launch");
     return device_status(qmm::launch_gemm_q4_K(wb, rep, yb, out, M, N, K, s), "mul_mat_q4_K gemm launch");
 }
 

@@ -33,6 +33,12 @@ hipError_t launch_block_sums_q4_0(const uint8_t *w, bool repacked, const uint8_t
 hipError_t launch_block_sums_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
                                   int64_t M, int64_t N, int64_t K, hipStream_t s);
 
+// Small-batch MFMA family: M <= skinny_max_m(), weight and activation
+// matrices below 4 GiB (32-bit buffer offsets).
+int64_t skinny_max_m();
+hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                              int64_t M, int64_t N, int64_t K, hipStream_t s);
+
 // MFMA GEMM family (any M >= 1).
 hipError_t launch_gemm_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);

@@ -1,0 +1,250 @@
+// skinny.hip -- quantized mul_mat for small batches (2 <= M <= 32) on int8 MFMA, gfx950.
+//
+// A batch of a few activation rows still reads every weight once, so the
+// operation stays bound by the weight stream (BitBLAS page, "调度与自动调优":
+// small-M shapes sit on the memory side of the roofline), but the per-row
+// vector dot products of the GEMV grow with M.  Here the contraction runs on
+// the matrix cores instead: the (at most 32) activation rows are one MFMA row
+// tile, so every weight column is decoded once per super-block and then costs
+// a handful of v_mfma_i32_32x32x32_i8 no matter how many rows there are.
+//
+// Arithmetic (ggml-cpu mul_mat page, "正确性:缩放系数可以提到求和号外面" and
+// "min 项与最终归约"), per super-block b and output (m, n):
+//     S  = sum_j s_j P_j,  P_j = sum_{k in j} q_k y_k    (int32, exact)
+//     Mn = sum_g m_{g/2} bsums[g]
+//     out += d_a (d S - dmin Mn)                         (fp32)
+// with the 6-bit s_j folded into two int8 digit planes (s = 8 hi + lo, every
+// plane value <= 105) so that S = 8 (Y x hiQ) + (Y x loQ) on the MFMA, and
+// -dmin m_j split into two fp16 values for an exact fp16 MFMA against the
+// fp16 bsums (|bsums| <= 2032).
+//
+// Workgroup: 8 wavefronts (two per SIMD) own one 32-column tile of the output;
+// wavefront w takes the super-blocks b = w, w + 8, ... (a split of K), and the
+// eight partial tiles are summed through LDS at the end.  Each wavefront
+// streams its columns' weights straight from memory into registers (no LDS
+// staging: every byte is used by exactly one wavefront) and reads the
+// activation operands from L2, where all workgroups share them.  The weight
+// loads of super-block b + 8 are issued before b is computed.
+//
+// MFMA operand convention (v_mfma_*_32x32xK): lane l supplies row (A) or
+// column (B) l % 32 and the K-slice selected by l / 32; the result register r
+// of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+#include "qmm_device.h"
+#include "qmm_launch.h"
+
+namespace qmm {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int SK_WAVES = 8, SK_THREADS = 64 * SK_WAVES;
+constexpr int SK_MAX_M = 32;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t *base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, (int)(uint32_t)n,
+                                             0x00020000);  // raw dword access (gfx9 family)
+}
+__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+// packed per-byte product of four codes (each <= 15) with a scale digit (<= 7)
+__device__ __forceinline__ int plane(uint32_t q4, uint32_t digit_pair) {
+    const us2 p = __builtin_bit_cast(us2, q4) * __builtin_bit_cast(us2, digit_pair);
+    return (int)__builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ uint32_t h2_bits(int lo, int hi) {
+    return f32_to_f16_bits((float)lo) | (f32_to_f16_bits((float)hi) << 16);
+}
+
+// The weight side of one super-block in this lane's registers (loaded one
+// step ahead), plus the row's bsums and d_a.
+struct Stage {
+    uint4 hdr;      // Q4_K header of column l%32
+    uint4 pay[4];   // payload pieces 2g + l/32, g = 0..3
+    uint4 bs;       // bsums 8*(l/32)..+7 of row l%32
+    uint32_t da;    // d_a of row l%32
+};
+
+template <bool REPACKED>
+__global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__restrict__ W,
+                                                             const uint8_t *__restrict__ Y,
+                                                             float *__restrict__ out, int64_t M,
+                                                             int64_t N, int64_t K) {
+    __shared__ __attribute__((aligned(16))) float red[SK_WAVES][16][64];  // partial tiles
+    __shared__ __attribute__((aligned(16))) float s_da[SK_WAVES][32];      // d_a of the step
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wavefront-uniform, and known to be: the super-block index derived from it
+    // goes into the scalar offset of the buffer loads
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int64_t nb = K / QK_K;
+    const int64_t n_base = (int64_t)blockIdx.x * 32;
+    const int64_t col = n_base + l32 < N ? n_base + l32 : N - 1;  // clamped: loads stay in bounds
+    const int64_t row = l32 < M ? l32 : M - 1;
+
+    // weights: this lane's column; offsets relative to the matrix start
+    // (buffer resources are built where they are used: one held across the
+    // lambda below would be treated as divergent and waterfall-looped)
+    const int64_t w_bytes = N * nb * kQ4_KBytes, y_bytes = M * nb * kQ8_KBytes;
+    const uint32_t hdr_step = REPACKED ? 16 : kQ4_KBytes, pay_step = REPACKED ? 128 : kQ4_KBytes;
+    const uint32_t h_off = (uint32_t)(col * nb) * hdr_step;
+    const uint32_t p_off = REPACKED ? (uint32_t)(16 * N * nb + 128 * col * nb) + 16 * hh
+                                    : (uint32_t)(kQ4_KBytes * col * nb) + 16 + 16 * hh;
+    // activations: row l%32 (clamped to M - 1)
+    const uint32_t y_off = (uint32_t)(row * nb * kQ8_KBytes);
+
+    auto load = [&](int64_t b, Stage &st) {
+        const rsrc_t rw = make_rsrc(W, w_bytes), ry = make_rsrc(Y, y_bytes);
+        st.hdr = bld16(rw, h_off, (uint32_t)b * hdr_step);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) st.pay[g] = bld16(rw, p_off + 32 * g, (uint32_t)b * pay_step);
+        const uint32_t sy = (uint32_t)b * kQ8_KBytes;
+        st.bs = bld16(ry, y_off + 260 + 16 * hh, sy);
+        st.da = __builtin_amdgcn_raw_buffer_load_b32(ry, y_off, sy, 0);
+    };
+
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+
+    // Loads are never predicated (a branch around a load makes the compiler
+    // wait for every outstanding load before the next use): a wavefront without
+    // super-blocks loads block nb - 1 and skips the loop; the step after its
+    // last one loads that block again (from L2) and leaves it unused.
+    // One step: this step's activation operands first, then the next step's
+    // weights into the other stage (waiting for the activations leaves that
+    // prefetch in flight), then decode, contraction and epilogue.  Two stages
+    // alternate (the loop is unrolled by two) so no register copy forces a
+    // wait for the prefetch.
+    auto step = [&](int64_t b, const Stage &cur, Stage &nxt) {
+        uint4 act[8];
+        const rsrc_t ry = make_rsrc(Y, y_bytes);
+        const uint32_t sy = (uint32_t)b * kQ8_KBytes;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) act[j] = bld16(ry, y_off + 4 + 32 * j + 16 * hh, sy);
+        load(b + SK_WAVES < nb ? b + SK_WAVES : b, nxt);
+
+        // d_a of the 32 rows, shared through this wavefront's LDS slot
+        if (hh == 0) s_da[wave][l32] = __uint_as_float(cur.da);
+
+        // ---- decode: 8 sub-block digit planes of this lane's K-slice
+        const float dcol = f16_bits_to_f32(cur.hdr.x & 0xffff);
+        const float dmcol = f16_bits_to_f32(cur.hdr.x >> 16);
+        const Q4KScales sc = unpack_scales(cur.hdr.y, cur.hdr.z, cur.hdr.w);
+        v4i bhi[8], blo[8];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint4 pw = cur.pay[g];
+            const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {  // t = 0: low nibbles (sub-block 2g), 1: high (2g+1)
+                const int j = 2 * g + t;
+                const int shift = t * 4;
+                const uint32_t q0 = (pw.x >> shift) & 0x0f0f0f0fu, q1 = (pw.y >> shift) & 0x0f0f0f0fu;
+                const uint32_t q2 = (pw.z >> shift) & 0x0f0f0f0fu, q3 = (pw.w >> shift) & 0x0f0f0f0fu;
+                const uint32_t sj = (sw >> (8 * (j & 3))) & 0xff;
+                const uint32_t hi2 = (sj >> 3) * 0x00010001u, lo2 = (sj & 7) * 0x00010001u;
+                bhi[j] = v4i{plane(q0, hi2), plane(q1, hi2), plane(q2, hi2), plane(q3, hi2)};
+                blo[j] = v4i{plane(q0, lo2), plane(q1, lo2), plane(q2, lo2), plane(q3, lo2)};
+            }
+        }
+        // min-term operands: -dmin*m_j = hi + lo exactly in fp16; bsums exact in fp16
+        v8h bmh, bml, a_bs;
+        {
+            const uint32_t mw = hh == 0 ? sc.m_lo : sc.m_hi;  // m_{4hh .. 4hh+3}
+            uint32_t bh[4], bl[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float vv = -dmcol * (float)((mw >> (8 * e)) & 0xff);  // exact in fp32
+                const uint32_t hb = f32_to_f16_bits(vv);
+                const uint32_t lb = f32_to_f16_bits(vv - f16_bits_to_f32(hb));
+                bh[e] = hb | (hb << 16);
+                bl[e] = lb | (lb << 16);
+            }
+            __builtin_memcpy(&bmh, bh, 16);
+            __builtin_memcpy(&bml, bl, 16);
+            const uint4 r = cur.bs;
+            const uint4 hv = make_uint4(h2_bits((int16_t)(r.x & 0xffff), (int16_t)(r.x >> 16)),
+                                        h2_bits((int16_t)(r.y & 0xffff), (int16_t)(r.y >> 16)),
+                                        h2_bits((int16_t)(r.z & 0xffff), (int16_t)(r.z >> 16)),
+                                        h2_bits((int16_t)(r.w & 0xffff), (int16_t)(r.w >> 16)));
+            __builtin_memcpy(&a_bs, &hv, 16);
+        }
+
+        // ---- contraction: 16 int8 MFMAs (two planes x 8 sub-blocks), 2 fp16 MFMAs
+        const v16i zero = {};
+        v16i ah = zero, al = zero;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const v4i a = v4i{(int)act[j].x, (int)act[j].y, (int)act[j].z, (int)act[j].w};
+            ah = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bhi[j], ah, 0, 0, 0);
+            al = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, blo[j], al, 0, 0, 0);
+        }
+        const v16f zf = {};
+        v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmh, zf, 0, 0, 0);
+        mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bml, mn, 0, 0, 0);
+
+        // ---- epilogue: acc += d_a * (d * S - dmin * Mn)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 d4 = *reinterpret_cast<const float4 *>(&s_da[wave][8 * q + 4 * hh]);
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q + e;
+                const int S = (ah[r] << 3) + al[r];
+                const float t = fmaf(dcol, (float)S, mn[r]);
+                acc[r] = fmaf(dv[e], t, acc[r]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    const int64_t b0 = wave < nb ? wave : nb - 1;
+    Stage st0, st1;
+    load(b0, st0);
+    for (int64_t b = wave; b < nb; b += 2 * SK_WAVES) {
+        step(b, st0, st1);
+        if (b + SK_WAVES < nb) step(b + SK_WAVES, st1, st0);
+    }
+
+    // ---- sum the eight K-split partial tiles and store the valid outputs
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    for (int o = tid; o < 32 * 32; o += SK_THREADS) {
+        const int m = o >> 5, c = o & 31;            // output row m, column n_base + c
+        const int r = 4 * (m >> 3) + (m & 3);        // register holding row m ...
+        const int l = c + 32 * ((m >> 2) & 1);       // ... in lane l
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < SK_WAVES; ++w) s += red[w][r][l];
+        if (m < M && n_base + c < N) out[(int64_t)m * N + n_base + c] = s;
+    }
+}
+
+}  // namespace
+
+int64_t skinny_max_m() { return SK_MAX_M; }
+
+hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                              int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    const dim3 grid((unsigned)((N + 31) / 32)), block(SK_THREADS);
+    if (repacked)
+        hipLaunchKernelGGL(k_skinny_q4_K<true>, grid, block, 0, s, w, y, out, M, N, K);
+    else
+        hipLaunchKernelGGL(k_skinny_q4_K<false>, grid, block, 0, s, w, y, out, M, N, K);
+    return hipGetLastError();
+}
+
+}  // namespace qmm

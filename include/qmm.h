@@ -73,9 +73,20 @@ typedef enum { QMM_Q8_0 = 0, QMM_Q8_K = 1 } qmm_act_type;
 typedef enum { QMM_Q4_0 = 0, QMM_Q4_K = 1 } qmm_weight_type;
 typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
 
-/* Kernel family for a mul_mat call.  AUTO picks the GEMV path for small M
- * and the MFMA GEMM path otherwise (Q4_K only; Q4_0 always uses GEMV). */
-typedef enum { QMM_ALGO_AUTO = 0, QMM_ALGO_GEMV = 1, QMM_ALGO_MFMA = 2 } qmm_algo;
+/* Kernel family for a mul_mat call (Q4_K only; Q4_0 always uses GEMV):
+ *   GEMV    vector int8 dot products, one wavefront per output row (M <= 8)
+ *   SKINNY  small-batch int8 MFMA, one 32-column tile per workgroup, K split
+ *           over its wavefronts (M <= 32; weight and activation matrices
+ *           below 4 GiB)
+ *   MFMA    prefill GEMM on int8 MFMA with LDS-staged 128 x 256 tiles (any M)
+ * AUTO takes GEMV for M = 1, SKINNY for 2 <= M <= 32 when its size limit
+ * holds, and MFMA otherwise. */
+typedef enum {
+    QMM_ALGO_AUTO = 0,
+    QMM_ALGO_GEMV = 1,
+    QMM_ALGO_MFMA = 2,
+    QMM_ALGO_SKINNY = 3
+} qmm_algo;
 
 /* Bytes of an [M, K] activation matrix in format t: M*K/32*34 or M*K/256*292.
  * Returns 0 for invalid arguments. */
@@ -131,7 +142,8 @@ qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l,
                             int64_t M, int64_t N, int64_t K, void *stream);
 
 /* Same as qmm_mul_mat_q4_K with an explicit kernel family (for measuring the
- * GEMV / GEMM crossover).  QMM_ALGO_GEMV requires M <= 8. */
+ * GEMV / GEMM crossover).  QMM_ALGO_GEMV requires M <= 8; QMM_ALGO_SKINNY
+ * requires M <= 32 and both matrices below 4 GiB (else QMM_EUNSUPPORTED). */
 qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l,
                                const void *y, size_t y_bytes,
                                float *out, size_t out_bytes,

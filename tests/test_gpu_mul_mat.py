@@ -84,7 +84,8 @@ def _window_weights(N, K, rng, dmin_one=True, smax=3, qmax=15, mmax=7):
 
 @pytest.mark.parametrize("algo,M,N,K", [("gemv", 1, 70, 1024), ("gemv", 8, 33, 2048),
                                         ("mfma", 1, 130, 512), ("mfma", 40, 257, 1024),
-                                        ("mfma", 129, 64, 2048)])
+                                        ("mfma", 129, 64, 2048), ("skinny", 2, 70, 1024),
+                                        ("skinny", 32, 33, 4608)])
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_exactness_window_q4_K(algo, M, N, K, layout):
     rng = np.random.default_rng(M * 7 + N)
@@ -145,7 +146,7 @@ def test_special_scale_cases():
     y = oracle.quantize("q8_K", activations(78, M, K))
     want, terms = full_reference("q4_K", w, y, M, N, K)
     yd = to_dev(y.reshape(-1))
-    for algo, mm in (("gemv", 8), ("mfma", M)):
+    for algo, mm in (("gemv", 8), ("mfma", M), ("skinny", 32)):
         got = to_host(qmm.mul_mat_q4_K(to_dev(w.reshape(-1)), yd, mm, N, K, algo=algo))
         assert_close(got, want[:mm], terms[:mm], f"special {algo}")
 
@@ -174,6 +175,26 @@ def test_mfma_q4_K(M, N, K, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(2, 1, 256), (2, 33, 512), (3, 100, 2304), (5, 64, 4096),
+                                   (8, 257, 6144), (17, 45, 1024), (32, 96, 3840),
+                                   (1, 70, 2048)])
+def test_skinny_q4_K(M, N, K, layout):
+    """Small-batch MFMA path: ragged N, K splits of 1..3 super-blocks per
+    wavefront (odd and even counts, wavefronts without work), M up to 32."""
+    w, x, y, _ = _case("q4_K", M, N, K, 7 * M + N)
+    want, terms = full_reference("q4_K", w, y, M, N, K)
+    wd = upload_weights("q4_K", w, N, K, layout)
+    got = to_host(qmm.mul_mat_q4_K(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout, algo="skinny"))
+    assert_close(got, want, terms, f"skinny M={M} N={N} K={K} {layout}")
+
+
+def test_skinny_rejects_large_m():
+    with pytest.raises(qmm.QmmError):
+        qmm.mul_mat_q4_K(to_dev(np.zeros(64 * 144, np.uint8)), to_dev(np.zeros(33 * 292, np.uint8)),
+                         33, 64, 256, algo="skinny")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", [(1, 256, 1024), (3, 77, 4096), (8, 9, 64), (13, 40, 512)])
 def test_q4_0(M, N, K, layout):
     w, x, y, _ = _case("q4_0", M, N, K, M + N)
@@ -184,10 +205,11 @@ def test_q4_0(M, N, K, layout):
 
 
 def test_auto_dispatch_and_overwrite():
-    """AUTO picks GEMV up to M = 8 and MFMA above; `out` is overwritten."""
+    """AUTO picks GEMV for M = 1, the small-batch kernel up to M = 32 and the
+    GEMM above; `out` is overwritten."""
     import torch
     N, K = 64, 512
-    for M in (8, 9):
+    for M in (1, 8, 9, 32, 33):
         w, x, y, _ = _case("q4_K", M, N, K, 900 + M)
         want, terms = full_reference("q4_K", w, y, M, N, K)
         out = torch.full((M, N), 1e9, device="cuda")
