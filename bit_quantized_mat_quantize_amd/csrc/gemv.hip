@@ -150,64 +150,85 @@ __host__ __device__ constexpr int64_t gemv1_lds_bytes(int64_t K) {
     return K + ((K / QK_K) * 4 + 15) / 16 * 16 + (K / QK_K) * 32 + 16;
 }
 
-// Issue the loads of this lane's weight pieces c = base + lane + 64*it of row nn.
-// Pieces past the row end load the last piece again (unused): the loads stay
+// Lane l of a pass starting at piece `base` owns the kNit consecutive
+// 16-byte pieces c = base + kNit*l + it of row nn: all in one super-block
+// (kNit divides 8), so one header serves them, and pieces 2g, 2g+1 (the two
+// halves of the 32-byte group g) share their sub-block scales.  A lane past
+// the row end loads the last group again and leaves it unused; the loads stay
 // branch-free, so the compiler can wait for older loads (the activations)
 // while these are still in flight.
 template <bool REPACKED, int kNit>
 __device__ __forceinline__ void gemv1_load(const Q4KAddr<REPACKED> &A, int64_t nn, int base,
-                                           int nchunk, int lane, uint4 (&hw)[kNit],
-                                           uint4 (&pw)[kNit]) {
+                                           int nchunk, int lane, uint4 &hw, uint4 (&pw)[kNit]) {
+    const int c0 = base + kNit * lane;
+    const int c = c0 < nchunk ? c0 : nchunk - kNit;
+    const int b = c >> 3, cc = c & 7;
+    hw = ld16(A.header(nn, b));
 #pragma unroll
-    for (int it = 0; it < kNit; ++it) {
-        const int c0 = base + lane + 64 * it;
-        const int c = c0 < nchunk ? c0 : nchunk - 1;
-        hw[it] = ld16(A.header(nn, c >> 3));
-        pw[it] = ld16(A.piece(nn, c >> 3, c & 7));
-    }
+    for (int it = 0; it < kNit; ++it) pw[it] = ld16(A.piece(nn, b, cc + it));
 }
 
-// Integer dot products of the loaded pieces with the activation row in LDS:
-// piece cc = 2g+h of super-block b holds bytes 16h..16h+15 of the 32-byte
-// group g, i.e. elements 64g+16h.. (low nibbles, sub-block 2g) and
-// 64g+32+16h.. (high nibbles, sub-block 2g+1).  Per piece:
-//   acc += d_a * (d * (s_2g*P_lo + s_2g+1*P_hi) - dmin * (m_2g*Y_lo + m_2g+1*Y_hi))
-// where Y are the matching 16-element activation sums (bsums).
+// Integer dot products of the loaded pieces with the activation row in LDS.
+// Piece cc = 2g + h of super-block b holds bytes 16h..16h+15 of the 32-byte
+// group g: elements 64g+16h.. (low nibbles, sub-block 2g) and 64g+32+16h..
+// (high nibbles, sub-block 2g+1).  With P the dot products and Y the matching
+// 16-element activation sums (bsums), the lane's pieces give
+//   S  = sum_g (s_2g * P_lo,g + s_2g+1 * P_hi,g),  Mn = sum_g (m_2g * Y_lo,g + m_2g+1 * Y_hi,g)
+//   acc += d_a * (d * S - dmin * Mn)
+// S stays an exact int32 and its conversion to fp32 exact (|S| < 2^24 for up
+// to four pieces; eight pieces are converted in two halves).
 template <int kNit>
-__device__ __forceinline__ float gemv1_accumulate(const uint4 (&hw)[kNit], const uint4 (&pw)[kNit],
+__device__ __forceinline__ float gemv1_accumulate(const uint4 &hw, const uint4 (&pw)[kNit],
                                                   int base, int nchunk, int lane,
                                                   const uint8_t *s_qs, const int16_t *s_bs,
                                                   const float *s_d, float acc) {
+    constexpr int kH = kNit >= 2 ? 2 : 1;  // pieces per 32-byte group
+    constexpr int kG = kNit / kH;          // groups per lane
+    const int c = base + kNit * lane;
+    if (c < nchunk) {
+        const int b = c >> 3, cc0 = c & 7;
+        const Q4KScales sc = unpack_scales(hw.y, hw.z, hw.w);
+        const float d = f16_bits_to_f32(hw.x & 0xffff);
+        const float dmin = f16_bits_to_f32(hw.x >> 16);
+        const uint8_t *yrow = s_qs + b * QK_K;
+        float t = 0.0f;
+        int S = 0, Mn = 0;
 #pragma unroll
-    for (int it = 0; it < kNit; ++it) {
-        const int c = base + lane + 64 * it;
-        if (c < nchunk) {
-            const int b = c >> 3, cc = c & 7, g = cc >> 1, h = cc & 1;
-            const Q4KScales sc = unpack_scales(hw[it].y, hw[it].z, hw[it].w);
+        for (int gi = 0; gi < kG; ++gi) {
+            const int g = (cc0 >> 1) + gi;
             const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
             const uint32_t mw = g < 2 ? sc.m_lo : sc.m_hi;
             const int sh = (g & 1) * 16;
             const int s0 = (sw >> sh) & 0xff, s1 = (sw >> (sh + 8)) & 0xff;
             const int m0 = (mw >> sh) & 0xff, m1 = (mw >> (sh + 8)) & 0xff;
-            const float d = f16_bits_to_f32(hw[it].x & 0xffff);
-            const float dmin = f16_bits_to_f32(hw[it].x >> 16);
-            const uint4 ylo = *reinterpret_cast<const uint4 *>(s_qs + b * QK_K + 64 * g + 16 * h);
-            const uint4 yhi = *reinterpret_cast<const uint4 *>(s_qs + b * QK_K + 64 * g + 32 + 16 * h);
-            const int blo = s_bs[16 * b + 4 * g + h], bhi = s_bs[16 * b + 4 * g + 2 + h];
-            const uint4 q = pw[it];
-            int plo = dot4(q.x & 0x0f0f0f0fu, ylo.x, 0);
-            plo = dot4(q.y & 0x0f0f0f0fu, ylo.y, plo);
-            plo = dot4(q.z & 0x0f0f0f0fu, ylo.z, plo);
-            plo = dot4(q.w & 0x0f0f0f0fu, ylo.w, plo);
-            int phi = dot4((q.x >> 4) & 0x0f0f0f0fu, yhi.x, 0);
-            phi = dot4((q.y >> 4) & 0x0f0f0f0fu, yhi.y, phi);
-            phi = dot4((q.z >> 4) & 0x0f0f0f0fu, yhi.z, phi);
-            phi = dot4((q.w >> 4) & 0x0f0f0f0fu, yhi.w, phi);
-            const int S = s0 * plo + s1 * phi;
-            const int Mn = m0 * blo + m1 * bhi;
-            const float t = fmaf(d, (float)S, -dmin * (float)Mn);
-            acc = fmaf(s_d[b], t, acc);
+            int plo = 0, phi = 0, ylo_sum = 0, yhi_sum = 0;
+#pragma unroll
+            for (int hi = 0; hi < kH; ++hi) {
+                const int h = kH == 2 ? hi : (cc0 & 1);
+                const uint4 q = pw[gi * kH + hi];
+                const uint4 ylo = *reinterpret_cast<const uint4 *>(yrow + 64 * g + 16 * h);
+                const uint4 yhi = *reinterpret_cast<const uint4 *>(yrow + 64 * g + 32 + 16 * h);
+                plo = dot4(q.x & 0x0f0f0f0fu, ylo.x, plo);
+                plo = dot4(q.y & 0x0f0f0f0fu, ylo.y, plo);
+                plo = dot4(q.z & 0x0f0f0f0fu, ylo.z, plo);
+                plo = dot4(q.w & 0x0f0f0f0fu, ylo.w, plo);
+                phi = dot4((q.x >> 4) & 0x0f0f0f0fu, yhi.x, phi);
+                phi = dot4((q.y >> 4) & 0x0f0f0f0fu, yhi.y, phi);
+                phi = dot4((q.z >> 4) & 0x0f0f0f0fu, yhi.z, phi);
+                phi = dot4((q.w >> 4) & 0x0f0f0f0fu, yhi.w, phi);
+                ylo_sum += s_bs[16 * b + 4 * g + h];
+                yhi_sum += s_bs[16 * b + 4 * g + 2 + h];
+            }
+            S += s0 * plo + s1 * phi;
+            Mn += m0 * ylo_sum + m1 * yhi_sum;
+            if (kG == 4 && gi == 1) {  // first half of an eight-piece lane
+                t = fmaf(d, (float)S, -dmin * (float)Mn);
+                S = 0;
+                Mn = 0;
+            }
         }
+        t += fmaf(d, (float)S, -dmin * (float)Mn);
+        acc = fmaf(s_d[b], t, acc);
     }
     return acc;
 }
@@ -243,7 +264,7 @@ __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ 
     const uint4 yb = ld_align4<uint4>(Y + (qb >> 1) * kQ8_KBytes + 260 + 16 * (qb & 1));
     const float yd = ld_align4<float>(Y + qd * kQ8_KBytes);
     __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
-    uint4 pw[kNit], hw[kNit];
+    uint4 pw[kNit], hw;
     gemv1_load<REPACKED, kNit>(A, nn, 0, nchunk, lane, hw, pw);
 #pragma unroll
     for (int t = 0; t < kYT; ++t) {
@@ -275,7 +296,7 @@ __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ 
 // Fused M = 1 path: the fp32 activation row is quantized to Q8_K inside the
 // GEMV, straight into LDS, so one launch covers quantize + mul_mat.
 // Quantization costs vector-ALU work that every workgroup repeats, so the
-// grid holds at most one 16-wavefront workgroup per CU and each workgroup
+// grid holds one or two 16-wavefront workgroups per CU and each workgroup
 // loops over rows (wavefront w of workgroup g takes rows g*16 + w, then
 // + 16*gridDim.x, ...).  A wavefront first issues the fp32 loads of up to kXB
 // of its activation blocks (b = wave + 16i) and the loads of its first row,
@@ -334,7 +355,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
         xv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
-    uint4 pw[kNit], hw[kNit];
+    uint4 pw[kNit], hw;
     // a wavefront without rows loads a valid row and stores nothing
     gemv1_load<REPACKED, kNit>(A, row < N ? row : N - 1, 0, nchunk, lane, hw, pw);
 #pragma unroll
@@ -345,14 +366,12 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
         const bool more = row + stride < N;
         float acc = 0.0f;
         if constexpr (kNit <= 2) {  // rows of one pass; registers for a second row
-            uint4 pn[kNit], hn[kNit];
+            uint4 pn[kNit], hn;
             if (more) gemv1_load<REPACKED, kNit>(A, row + stride, 0, nchunk, lane, hn, pn);
             acc = gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, acc);
+            hw = hn;
 #pragma unroll
-            for (int it = 0; it < kNit; ++it) {
-                hw[it] = hn[it];
-                pw[it] = pn[it];
-            }
+            for (int it = 0; it < kNit; ++it) pw[it] = pn[it];
         } else {
             acc = gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, acc);
             if (more) gemv1_load<REPACKED, kNit>(A, row + stride, 0, nchunk, lane, hw, pw);
@@ -537,9 +556,13 @@ hipError_t launch_gemv1_fused_q4_K(const uint8_t *w, bool repacked, const float 
                                    float *out, int64_t N, int64_t K, hipStream_t s) {
     const int64_t lds = gemv1_lds_bytes(K);
     const int64_t nit = (K / QK_K * 8 + 63) / 64;
+    // one workgroup per CU; two (the register budget allows two 16-wavefront
+    // workgroups per CU) when each wavefront would still loop over at least
+    // two rows, so more of the weight stream is in flight
     const int64_t groups = (N + kFusedWaves - 1) / kFusedWaves;
     const int64_t cus = cu_count();
-    const dim3 grid((unsigned)(groups < cus ? groups : cus)), block(kFusedWaves * 64);
+    const int64_t cap = groups >= 4 * cus ? 2 * cus : cus;
+    const dim3 grid((unsigned)(groups < cap ? groups : cap)), block(kFusedWaves * 64);
 #define QMM_FUSED1(NIT, XB)                                                                        \
     do {                                                                                           \
         if (repacked)                                                                              \
