@@ -524,3 +524,172 @@ void orc_repack_q4_0(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out) {
         memcpy(out + dsec + 16 * i, src + 2, 16);
     }
 }
+
+/* ======================================================================== */
+/* Q6_K (210 B / 256 weights).  P1 "更低的比特:Q6_K 与 Q2_K 的取舍": ql[128]  */
+/* holds the low 4 bits of each 6-bit value, qh[64] the high 2 bits,         */
+/* scales[16] are plain int8 (one per 16-element group), d is fp16; the      */
+/* 6-bit value is a signed integer q in [-32, 31] with no min term:          */
+/*   w = d * s_j * q,  j = element / 16.                                     */
+/* Readings (the pages list the fields but not the bit placement):           */
+/*   byte order   ql @0, qh @128, scales @192, d @208 (the order listed);    */
+/*   low 4 bits   of element k sit in ql byte 32*(k/64) + (k%64)%32, low     */
+/*                nibble for (k%64) < 32, high nibble otherwise (the split-  */
+/*                half order of the Q4_K codes);                             */
+/*   high 2 bits  of element k sit in qh byte k%64, bits 2*(k/64)+1..2*(k/64);*/
+/*   stored code  u = q + 32 in [0, 63].                                     */
+/* Parity with llama.cpp's own Q6_K files is unpinned (no vectors here).     */
+/* ======================================================================== */
+static int q6_K_code(const uint8_t *blk, int k) {
+    int g = k / 64, r = k % 64;
+    uint8_t lb = blk[32 * g + (r % 32)];
+    int lo = r < 32 ? (lb & 0x0f) : (lb >> 4);
+    int hi = (blk[128 + r] >> (2 * g)) & 3;
+    return (lo | (hi << 4)) - 32;
+}
+
+void orc_q6_K_pack_codes(const int8_t q[256], uint8_t ql_qh[192]) {
+    memset(ql_qh, 0, 192);
+    for (int k = 0; k < 256; ++k) {
+        int u = q[k] + 32, g = k / 64, r = k % 64;
+        uint8_t *lb = ql_qh + 32 * g + (r % 32);
+        *lb |= (uint8_t)(r < 32 ? (u & 0x0f) : ((u & 0x0f) << 4));
+        ql_qh[128 + r] |= (uint8_t)(((u >> 4) & 3) << (2 * g));
+    }
+}
+
+/* Q6_K encoder (input generator).  Plain symmetric reading, as for Q4_0:    */
+/* per 16-element group, xm_j = signed element of largest |x| (first wins),  */
+/* sc_j = xm_j / -32 (so xm_j maps to q = -32); d = max |sc_j| / 127;        */
+/* s_j = rint(sc_j / d) clamped to [-127, 127]; with D_j = f16(d) * s_j:     */
+/* q = rint(x / D_j) clamped to [-32, 31], or 0 where D_j = 0.               */
+void orc_quantize_q6_K(const float *x, int64_t rows, int64_t K, uint8_t *out) {
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *xb = x + r * K + b * QK_K;
+            uint8_t *blk = out + (r * nb + b) * ORC_Q6_K_BYTES;
+            float sc[16], maxsc = 0.0f;
+            for (int j = 0; j < 16; ++j) {
+                float amax = 0.0f, xm = 0.0f;
+                for (int i = 0; i < 16; ++i) {
+                    float a = fabsf(xb[16 * j + i]);
+                    if (a > amax) { amax = a; xm = xb[16 * j + i]; }
+                }
+                sc[j] = xm / -32.0f;
+                if (fabsf(sc[j]) > maxsc) maxsc = fabsf(sc[j]);
+            }
+            float d = maxsc / 127.0f;
+            uint16_t dh = orc_f32_to_f16(d);
+            float df = orc_f16_to_f32(dh);
+            int8_t s[16], q[256];
+            for (int j = 0; j < 16; ++j) {
+                s[j] = (int8_t)(d > 0.0f ? clampi((int)rintf(sc[j] / d), -127, 127) : 0);
+                float Dj = df * (float)s[j];
+                for (int i = 0; i < 16; ++i) {
+                    int k = 16 * j + i;
+                    q[k] = (int8_t)(Dj != 0.0f ? clampi((int)rintf(xb[k] / Dj), -32, 31) : 0);
+                }
+            }
+            orc_q6_K_pack_codes(q, blk);
+            for (int j = 0; j < 16; ++j) blk[192 + j] = (uint8_t)s[j];
+            wr_f16(blk + 208, dh);
+        }
+}
+
+void orc_dequantize_q6_K(const uint8_t *w, int64_t rows, int64_t K, double *out) {
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = w + (r * nb + b) * ORC_Q6_K_BYTES;
+            double d = rd_f16(blk + 208);
+            for (int k = 0; k < QK_K; ++k)
+                out[r * K + b * QK_K + k] = d * (int8_t)blk[192 + k / 16] * q6_K_code(blk, k);
+        }
+}
+
+/* Integer path, the same factorization as Q4_K without the min term:        */
+/* P_j = sum_{i in j} q_i y_i over the 16-element group j (int32),           */
+/* S = sum_j s_j P_j (int32), contribution d_a * d * S (fp64).               */
+static double q6_K_row_dot(const uint8_t *wrow, const uint8_t *yrow, int64_t nb,
+                           int32_t *P_out, double *terms) {
+    double acc = 0.0, tacc = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *wb = wrow + b * ORC_Q6_K_BYTES;
+        const uint8_t *yb = yrow + b * ORC_Q8_K_BYTES;
+        double d = rd_f16(wb + 208), da = rd_f32(yb);
+        int32_t S = 0;
+        for (int j = 0; j < 16; ++j) {
+            int s = (int8_t)wb[192 + j];
+            int32_t P = 0;
+            for (int i = 0; i < 16; ++i) {
+                int k = 16 * j + i;
+                int q = q6_K_code(wb, k);
+                int yv = (int8_t)yb[4 + k];
+                P += q * yv;
+                if (terms) tacc += fabs(d * s * q * da * yv);
+            }
+            if (P_out) P_out[b * 16 + j] = P;
+            S += s * P;
+        }
+        acc += da * (d * (double)S);
+    }
+    if (terms) *terms = tacc;
+    return acc;
+}
+
+void orc_mul_mat_q6_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                           int64_t N, int64_t K, double *out, int nthreads) {
+    const int64_t nb = K / QK_K;
+    const int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            out[m * N + n] = q6_K_row_dot(w + n * nb * ORC_Q6_K_BYTES,
+                                          y + m * nb * ORC_Q8_K_BYTES, nb, NULL, NULL);
+}
+
+void orc_q6_K_group_sums(const uint8_t *w, const uint8_t *y, int64_t M,
+                         int64_t N, int64_t K, int32_t *P) {
+    const int64_t nb = K / QK_K;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            q6_K_row_dot(w + n * nb * ORC_Q6_K_BYTES, y + m * nb * ORC_Q8_K_BYTES, nb,
+                         P + (m * N + n) * (K / 16), NULL);
+}
+
+void orc_sample_q6_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                          int64_t N, int64_t K, const int64_t *ms,
+                          const int64_t *ns, int64_t count, double *out,
+                          double *terms) {
+    const int64_t nb = K / QK_K;
+    (void)M; (void)N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = q6_K_row_dot(w + ns[i] * nb * ORC_Q6_K_BYTES,
+                              y + ms[i] * nb * ORC_Q8_K_BYTES, nb, NULL, &terms[i]);
+}
+
+/* Q6_K load-time layout (this library's own byte permutation):               */
+/*   [N*nb fp16 d, zero-padded to a multiple of 256 B][N*nb scales of 16 B]   */
+/*   [N*nb ql of 128 B][N*nb qh of 64 B], block (n,b) at index n*nb+b.        */
+int64_t orc_repacked_bytes_q6_K(int64_t N, int64_t K) {
+    int64_t nblk = N * (K / QK_K);
+    return (2 * nblk + 255) / 256 * 256 + 208 * nblk;
+}
+
+void orc_repack_q6_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out) {
+    const int64_t nblk = N * (K / QK_K);
+    const int64_t dsec = (2 * nblk + 255) / 256 * 256;
+    const int64_t s0 = dsec, l0 = s0 + 16 * nblk, h0 = l0 + 128 * nblk;
+    memset(out, 0, (size_t)dsec);
+    for (int64_t i = 0; i < nblk; ++i) {
+        const uint8_t *src = canon + i * ORC_Q6_K_BYTES;
+        memcpy(out + 2 * i, src + 208, 2);
+        memcpy(out + s0 + 16 * i, src + 192, 16);
+        memcpy(out + l0 + 128 * i, src, 128);
+        memcpy(out + h0 + 64 * i, src + 128, 64);
+    }
+}

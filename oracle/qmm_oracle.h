@@ -24,6 +24,9 @@
  *         +0 fp16 d, +2 fp16 dmin, +4 scales[12] (8 six-bit s_j + 8 six-bit m_j),
  *         +16 qs[128]: byte 32g+l holds element 64g+l (low) and 64g+32+l (high)
  *         weight w = d*s_j*q - dmin*m_j, j = element / 32
+ *   Q6_K  (210 B / 256 weights) [P1 "更低的比特:Q6_K 与 Q2_K 的取舍"]
+ *         +0 ql[128] (low 4 bits), +128 qh[64] (high 2 bits), +192 int8 scales[16],
+ *         +208 fp16 d;  weight w = d * s_j * q, q in [-32, 31], j = element / 16
  *   Q8_K  (292 B / 256 values)  [P1 "更低的比特:Q6_K 与 Q2_K 的取舍"]
  *         +0 fp32 d, +4 int8 qs[256], +260 int16 bsums[16] (sum of each 16 qs)
  *
@@ -42,6 +45,7 @@ extern "C" {
 #define ORC_Q8_0_BYTES 34
 #define ORC_Q4_K_BYTES 144
 #define ORC_Q8_K_BYTES 292
+#define ORC_Q6_K_BYTES 210
 
 /* ---- IEEE binary16 <-> binary32 (definition of the format; RNE) ---- */
 uint16_t orc_f32_to_f16(float x);
@@ -104,6 +108,24 @@ int64_t orc_repacked_bytes_q4_0(int64_t N, int64_t K);
 int64_t orc_repacked_bytes_q4_K(int64_t N, int64_t K);
 void orc_repack_q4_0(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out);
 void orc_repack_q4_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out);
+
+/* ---- Q6_K (ql[128] | qh[64] | int8 scales[16] | fp16 d; w = d*s_j*q,
+ * q in [-32, 31], 16-element groups j).  Bit placement, encoder and layout
+ * are readings stated in qmm_oracle.c. ---- */
+void orc_q6_K_pack_codes(const int8_t q[256], uint8_t ql_qh[192]);
+void orc_quantize_q6_K(const float *x, int64_t rows, int64_t K, uint8_t *out);
+void orc_dequantize_q6_K(const uint8_t *w, int64_t rows, int64_t K, double *out);
+void orc_mul_mat_q6_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                           int64_t N, int64_t K, double *out, int nthreads);
+/* per-group int32 sums P[m][n][K/16] = sum_{i in group} q_i*y_i          */
+void orc_q6_K_group_sums(const uint8_t *w, const uint8_t *y, int64_t M,
+                         int64_t N, int64_t K, int32_t *P);
+void orc_sample_q6_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                          int64_t N, int64_t K, const int64_t *ms,
+                          const int64_t *ns, int64_t count, double *out,
+                          double *terms);
+int64_t orc_repacked_bytes_q6_K(int64_t N, int64_t K);
+void orc_repack_q6_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out);
 
 int orc_max_threads(void);
 
