@@ -16,13 +16,13 @@ LIB_PATH = os.path.join(PKG, "libqmm.so")
 
 # enums of include/qmm.h
 Q8_0, Q8_K = 0, 1
-Q4_0, Q4_K = 0, 1
+Q4_0, Q4_K, Q6_K = 0, 1, 2
 CANONICAL, REPACKED = 0, 1
 ALGO_AUTO, ALGO_GEMV, ALGO_MFMA, ALGO_SKINNY = 0, 1, 2, 3
 STATUS = {0: "QMM_OK", 1: "QMM_EINVAL", 2: "QMM_EALIGN", 3: "QMM_EUNSUPPORTED", 4: "QMM_EDEVICE"}
 
 _ACT = {"q8_0": Q8_0, "q8_K": Q8_K}
-_WEIGHT = {"q4_0": Q4_0, "q4_K": Q4_K}
+_WEIGHT = {"q4_0": Q4_0, "q4_K": Q4_K, "q6_K": Q6_K}
 _LAYOUT = {"canonical": CANONICAL, "repacked": REPACKED}
 _ALGO = {"auto": ALGO_AUTO, "gemv": ALGO_GEMV, "mfma": ALGO_MFMA, "skinny": ALGO_SKINNY}
 
@@ -55,6 +55,7 @@ def load() -> ctypes.CDLL:
         "qmm_mul_mat_q4_0": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_mul_mat_q4_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_mul_mat_q4_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
+        "qmm_mul_mat_q6_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_quantize_mul_mat": (I, [I, P, SZ, I, P, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_debug_block_sums": (I, [I, P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_status_string": (ctypes.c_char_p, [I]),
@@ -175,7 +176,7 @@ def quantize_mul_mat(wfmt: str, w, x, N: int, layout: str = "canonical", y=None,
     M, K = x.shape
     if x.dtype != torch.float32:
         raise ValueError("x must be float32")
-    afmt = "q8_K" if wfmt == "q4_K" else "q8_0"
+    afmt = "q8_0" if wfmt == "q4_0" else "q8_K"
     if y is None:
         y = torch.empty(max(act_bytes(afmt, M, K), 1), dtype=torch.uint8, device=x.device)
     if out is None:
@@ -189,12 +190,26 @@ def quantize_mul_mat(wfmt: str, w, x, N: int, layout: str = "canonical", y=None,
     return out, y
 
 
-def debug_block_sums(wfmt: str, w, y, M: int, N: int, K: int, layout: str = "canonical",
-                     out=None, stream=None):
-    """int32 [M, N, K/32] per-sub-block (Q4_K) or per-block (Q4_0) sums."""
+def mul_mat_q6_K(w, y, M: int, N: int, K: int, layout: str = "canonical", out=None, stream=None):
     import torch
     if out is None:
-        out = torch.empty((M, N, K // 32), dtype=torch.int32, device=y.device)
+        out = torch.empty((M, N), dtype=torch.float32, device=y.device)
+    pw, nw = _dev(w, "w")
+    py, ny = _dev(y, "y")
+    po, no = _dev(out, "out")
+    _check(load().qmm_mul_mat_q6_K(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
+                                   _stream(stream)), "qmm_mul_mat_q6_K")
+    return out
+
+
+def debug_block_sums(wfmt: str, w, y, M: int, N: int, K: int, layout: str = "canonical",
+                     out=None, stream=None):
+    """int32 [M, N, K/32] per-sub-block (Q4_K) or per-block (Q4_0) sums, or
+    [M, N, K/16] per-group sums (Q6_K)."""
+    import torch
+    if out is None:
+        out = torch.empty((M, N, K // (16 if wfmt == "q6_K" else 32)), dtype=torch.int32,
+                          device=y.device)
     pw, nw = _dev(w, "w")
     py, ny = _dev(y, "y")
     po, no = _dev(out, "P")

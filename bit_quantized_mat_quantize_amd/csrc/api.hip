@@ -29,8 +29,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int act_qk(qmm_act_type t) { return t == QMM_Q8_0 ? 32 : (t == QMM_Q8_K ? 256 : 0); }
 int act_bytes_per_block(qmm_act_type t) { return t == QMM_Q8_0 ? 34 : 292; }
-int w_qk(qmm_weight_type t) { return t == QMM_Q4_0 ? 32 : (t == QMM_Q4_K ? 256 : 0); }
-int w_bytes_per_block(qmm_weight_type t) { return t == QMM_Q4_0 ? 18 : 144; }
+int w_qk(qmm_weight_type t) {
+    return t == QMM_Q4_0 ? 32 : ((t == QMM_Q4_K || t == QMM_Q6_K) ? 256 : 0);
+}
+int w_bytes_per_block(qmm_weight_type t) { return t == QMM_Q4_0 ? 18 : (t == QMM_Q6_K ? 210 : 144); }
 
 qmm_status check_rows(const char *name, int64_t v) {
     if (v < 0) return fail(QMM_EINVAL, "%s = %lld is negative", name, (long long)v);
@@ -105,6 +107,7 @@ size_t qmm_weight_bytes(qmm_weight_type t, qmm_layout l, int64_t N, int64_t K) {
     if (!qk || N < 0 || K < 0 || K % qk) return 0;
     if (l != QMM_LAYOUT_CANONICAL && l != QMM_LAYOUT_REPACKED) return 0;
     if (t == QMM_Q4_0 && l == QMM_LAYOUT_REPACKED) return (size_t)qmm::repacked_bytes_q4_0(N, K);
+    if (t == QMM_Q6_K && l == QMM_LAYOUT_REPACKED) return (size_t)qmm::repacked_bytes_q6_K(N, K);
     return (size_t)(N * (K / qk) * w_bytes_per_block(t));
 }
 
@@ -137,8 +140,9 @@ qmm_status qmm_quantize_weights(qmm_weight_type t, const float *w, int64_t N, in
     QMM_TRY(check_size("out", out_bytes, qmm_weight_bytes(t, QMM_LAYOUT_CANONICAL, N, K)));
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t *o = static_cast<uint8_t *>(out);
-    return device_status(t == QMM_Q4_K ? qmm::launch_encode_q4_K(w, o, N, K, s)
-                                       : qmm::launch_encode_q4_0(w, o, N, K, s),
+    return device_status(t == QMM_Q4_K   ? qmm::launch_encode_q4_K(w, o, N, K, s)
+                         : t == QMM_Q6_K ? qmm::launch_encode_q6_K(w, o, N, K, s)
+                                         : qmm::launch_encode_q4_0(w, o, N, K, s),
                          "quantize_weights launch");
 }
 
@@ -161,8 +165,9 @@ qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint8_t *in = static_cast<const uint8_t *>(w_canon);
     uint8_t *o = static_cast<uint8_t *>(w_repacked);
-    return device_status(t == QMM_Q4_K ? qmm::launch_repack_q4_K(in, o, N, K, s)
-                                       : qmm::launch_repack_q4_0(in, o, N, K, s),
+    return device_status(t == QMM_Q4_K   ? qmm::launch_repack_q4_K(in, o, N, K, s)
+                         : t == QMM_Q6_K ? qmm::launch_repack_q6_K(in, o, N, K, s)
+                                         : qmm::launch_repack_q4_0(in, o, N, K, s),
                          "repack_weights launch");
 }
 
@@ -227,6 +232,20 @@ qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l, const v
                                stream);
 }
 
+qmm_status qmm_mul_mat_q6_K(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                            size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                            int64_t K, void *stream) {
+    QMM_TRY(mul_mat_common(QMM_Q6_K, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
+    if (K > qmm::q6_K_max_k())
+        return fail(QMM_EUNSUPPORTED, "Q6_K takes K <= %lld (K = %lld)", (long long)qmm::q6_K_max_k(),
+                    (long long)K);
+    if (M == 0 || N == 0) return QMM_OK;
+    return device_status(qmm::launch_gemv_q6_K(static_cast<const uint8_t *>(w), l == QMM_LAYOUT_REPACKED,
+                                               static_cast<const uint8_t *>(y), out, M, N, K,
+                                               static_cast<hipStream_t>(stream)),
+                         "mul_mat_q6_K launch");
+}
+
 qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes, qmm_layout l,
                                 const float *x, void *y, size_t y_bytes, float *out,
                                 size_t out_bytes, int64_t M, int64_t N, int64_t K, void *stream) {
@@ -256,6 +275,7 @@ qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes
                              "quantize_mul_mat fused launch");
     QMM_TRY(qmm_quantize_row_q8(at, x, M, K, y, y_bytes, stream));
     if (N == 0) return QMM_OK;
+    if (t == QMM_Q6_K) return qmm_mul_mat_q6_K(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream);
     return t == QMM_Q4_K ? qmm_mul_mat_q4_K(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream)
                          : qmm_mul_mat_q4_0(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream);
 }
@@ -266,14 +286,19 @@ qmm_status qmm_debug_block_sums(qmm_weight_type t, const void *w, size_t w_bytes
     if (!w_qk(t)) return fail(QMM_EUNSUPPORTED, "unknown weight type %d", (int)t);
     QMM_TRY(mul_mat_common(t, w, w_bytes, l, y, y_bytes, reinterpret_cast<const float *>(P),
                            p_bytes, M, N, K));
+    if (t == QMM_Q6_K && K > qmm::q6_K_max_k())
+        return fail(QMM_EUNSUPPORTED, "Q6_K takes K <= %lld (K = %lld)", (long long)qmm::q6_K_max_k(),
+                    (long long)K);
     if (M == 0 || N == 0) return QMM_OK;
-    QMM_TRY(check_size("P", p_bytes, (size_t)(M * N * (K / 32)) * sizeof(int32_t)));
+    const int64_t group = t == QMM_Q6_K ? 16 : 32;
+    QMM_TRY(check_size("P", p_bytes, (size_t)(M * N * (K / group)) * sizeof(int32_t)));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool rep = l == QMM_LAYOUT_REPACKED;
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
-    return device_status(t == QMM_Q4_K ? qmm::launch_block_sums_q4_K(wb, rep, yb, P, M, N, K, s)
-                                       : qmm::launch_block_sums_q4_0(wb, rep, yb, P, M, N, K, s),
+    return device_status(t == QMM_Q4_K   ? qmm::launch_block_sums_q4_K(wb, rep, yb, P, M, N, K, s)
+                         : t == QMM_Q6_K ? qmm::launch_group_sums_q6_K(wb, rep, yb, P, M, N, K, s)
+                                         : qmm::launch_block_sums_q4_0(wb, rep, yb, P, M, N, K, s),
                          "debug_block_sums launch");
 }
 

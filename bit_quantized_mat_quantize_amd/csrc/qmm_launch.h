@@ -14,6 +14,7 @@ hipError_t launch_encode_q4_0(const float *w, uint8_t *out, int64_t N, int64_t K
 hipError_t launch_encode_q4_K(const float *w, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
 
 int64_t repacked_bytes_q4_0(int64_t N, int64_t K);
+int64_t repacked_bytes_q6_K(int64_t N, int64_t K);
 hipError_t launch_repack_q4_0(const uint8_t *in, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_repack_q4_K(const uint8_t *in, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
 
@@ -38,6 +39,16 @@ hipError_t launch_block_sums_q4_K(const uint8_t *w, bool repacked, const uint8_t
 int64_t skinny_max_m();
 hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                               int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+// Q6_K (encoder, load-time repack, GEMV for any M with K <= q6_K_max_k(),
+// int32 group sums P[m][n][K/16] of the same decode path).
+int64_t q6_K_max_k();
+hipError_t launch_encode_q6_K(const float *w, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_repack_q6_K(const uint8_t *in, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemv_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_group_sums_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t s);
 
 // MFMA GEMM family (any M >= 1).
 hipError_t launch_gemm_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,

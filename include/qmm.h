@@ -22,6 +22,13 @@
  *                       j<4 : s_j = byte j & 63,  m_j = byte j+4 & 63
  *                       j>=4: s_j = (byte j+4 & 15) | (byte j-4 >> 6) << 4
  *                             m_j = (byte j+4 >> 4) | (byte j   >> 6) << 4
+ *   Q6_K 210 B / 256: ql[128] (low 4 bits) | qh[64] (high 2 bits) | int8 scales[16] |
+ *                     fp16 d (section "更低的比特:Q6_K 与 Q2_K 的取舍"); w = d*s_j*q,
+ *                     q in [-32, 31], j = element / 16, no min term.  Bit placement
+ *                     (this library's reading): element k = 64g + r keeps its low
+ *                     4 bits in ql byte 32g + r%32 (low nibble for r < 32, else
+ *                     high) and its high 2 bits in qh byte r, bits 2g..2g+1; the
+ *                     stored code is q + 32
  *   Q8_K 292 B / 256: fp32 d; int8 qs[256]; int16 bsums[16] (sum of qs[16g..16g+15])
  *   Rows are arrays of blocks: row r of a [R, K] matrix starts at r * (K/QK) * bytes.
  *
@@ -32,6 +39,8 @@
  *         [N*nb payloads of 128 B: qs], block (n,b) at index n*nb+b
  *   Q4_0: [N*nb fp16 d, zero-padded to a multiple of 256 B] then
  *         [N*nb payloads of 16 B: qs]
+ *   Q6_K: [N*nb fp16 d, zero-padded to a multiple of 256 B] then [N*nb scales of
+ *         16 B] then [N*nb ql of 128 B] then [N*nb qh of 64 B]
  *   (nb = blocks per row).  The payload stream is 16-byte aligned, which lets a
  *   wavefront read weights with coalesced 16-byte loads.
  *
@@ -44,7 +53,7 @@
  *     call returns a non-zero qmm_status, enqueues nothing and leaves a
  *     message for qmm_last_error().  M or N equal to 0 is a valid empty call.
  *   - K must be a positive multiple of the block length (32 for Q4_0/Q8_0,
- *     256 for Q4_K/Q8_K), else QMM_EUNSUPPORTED.  Sizes are limited to
+ *     256 for Q4_K/Q6_K/Q8_K), else QMM_EUNSUPPORTED.  Sizes are limited to
  *     M, N <= 2^24 and K <= 2^20 (QMM_EUNSUPPORTED beyond).
  *   - `*_bytes` arguments give the size of the caller's buffer; a buffer
  *     smaller than the corresponding qmm_*_bytes() value gives QMM_EINVAL.
@@ -70,7 +79,7 @@ typedef enum {
 } qmm_status;
 
 typedef enum { QMM_Q8_0 = 0, QMM_Q8_K = 1 } qmm_act_type;
-typedef enum { QMM_Q4_0 = 0, QMM_Q4_K = 1 } qmm_weight_type;
+typedef enum { QMM_Q4_0 = 0, QMM_Q4_K = 1, QMM_Q6_K = 2 } qmm_weight_type;
 typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
 
 /* Kernel family for a mul_mat call (Q4_K only; Q4_0 always uses GEMV):
@@ -93,8 +102,9 @@ typedef enum {
 size_t qmm_act_bytes(qmm_act_type t, int64_t M, int64_t K);
 
 /* Bytes of an [N, K] weight matrix in format t and layout l.  Canonical:
- * N*K/32*18 or N*K/256*144.  Repacked Q4_0 adds the padding of its scale
- * section (at most 254 B).  Returns 0 for invalid arguments. */
+ * N*K/32*18, N*K/256*144 or N*K/256*210 (Q6_K).  Repacked Q4_0 and Q6_K add the
+ * padding of their d section (at most 254 B).  Returns 0 for invalid
+ * arguments. */
 size_t qmm_weight_bytes(qmm_weight_type t, qmm_layout l, int64_t N, int64_t K);
 
 /* Quantize fp32 activations x [M, K] (row-major) to int8 blocks y [M, K/QK]
@@ -114,6 +124,9 @@ qmm_status qmm_quantize_row_q8(qmm_act_type t, const float *x, int64_t M, int64_
  *   Q4_K: per sub-block lo = min(0, min x), sc = (max x - lo)/15, mn = -lo;
  *         d = max sc/63, dmin = max mn/63; s_j = rint(sc/d), m_j = rint(mn/dmin)
  *         (clamped to 63); q = clamp(rint((x + f16(dmin)*m_j)/(f16(d)*s_j)), 0, 15)
+ *   Q6_K: per 16-element group xm = signed element of largest |x| (first
+ *         wins), sc = xm/-32; d = max |sc|/127; s_j = rint(sc/d) in [-127, 127];
+ *         q = clamp(rint(x/(f16(d)*s_j)), -32, 31), 0 where f16(d)*s_j = 0
  * out: device, out_bytes >= qmm_weight_bytes(t, CANONICAL, N, K). */
 qmm_status qmm_quantize_weights(qmm_weight_type t, const float *w, int64_t N, int64_t K,
                                 void *out, size_t out_bytes, void *stream);
@@ -141,6 +154,17 @@ qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l,
                             float *out, size_t out_bytes,
                             int64_t M, int64_t N, int64_t K, void *stream);
 
+/* out[m*N+n] = sum over super-blocks b of d_a*d*S with S = sum_j s_j*P_j,
+ * P_j = sum_{i in j} q_i*y_i over the 16-element groups j (ggml-cpu mul_mat page,
+ * "更低的比特:Q6_K 与 Q2_K 的取舍": no min term, so no bsums path; and
+ * "正确性:缩放系数可以提到求和号外面").  fp32 output, overwritten.  w: Q6_K [N,K]
+ * in layout l; y: Q8_K [M,K].  GEMV kernels for every M (the weights are read
+ * once per activation row); K <= 53760, else QMM_EUNSUPPORTED. */
+qmm_status qmm_mul_mat_q6_K(const void *w, size_t w_bytes, qmm_layout l,
+                            const void *y, size_t y_bytes,
+                            float *out, size_t out_bytes,
+                            int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Same as qmm_mul_mat_q4_K with an explicit kernel family (for measuring the
  * GEMV / GEMM crossover).  QMM_ALGO_GEMV requires M <= 8; QMM_ALGO_SKINNY
  * requires M <= 32 and both matrices below 4 GiB (else QMM_EUNSUPPORTED). */
@@ -151,7 +175,7 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l,
                                void *stream);
 
 /* Quantize-and-multiply in one call: y = quantize_row_q8(x) (Q8_0 for t = Q4_0,
- * Q8_K for t = Q4_K), then out = mul_mat(w, y).  The ggml-cpu mul_mat page
+ * Q8_K for t = Q4_K and Q6_K), then out = mul_mat(w, y).  The ggml-cpu mul_mat page
  * ("激活量化重复与融合") notes that quantizing the activations once at the
  * start of a fused node saves both the launch and the repeated conversion;
  * here, for Q4_K with M == 1 and K <= 8192, the quantization runs inside the
@@ -170,9 +194,10 @@ qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes
                                 int64_t M, int64_t N, int64_t K, void *stream);
 
 /* Verification aid: the int32 per-sub-block (Q4_K) or per-block (Q4_0) sums
- * P[m][n][K/32] = sum_{i in block} q_i*y_i  (Q4_0: (q_i-8)*y_i), computed by
- * the same decode and int8 dot-product code the GEMV kernels use.
- * P: device int32, p_bytes >= M*N*(K/32)*4. */
+ * P[m][n][K/32] = sum_{i in block} q_i*y_i  (Q4_0: (q_i-8)*y_i), or for Q6_K the
+ * per-group sums P[m][n][K/16] of its signed codes, computed by the same decode
+ * and int8 dot-product code the GEMV kernels use.
+ * P: device int32, p_bytes >= M*N*(K/32)*4 (Q6_K: M*N*(K/16)*4). */
 qmm_status qmm_debug_block_sums(qmm_weight_type t, const void *w, size_t w_bytes,
                                 qmm_layout l, const void *y, size_t y_bytes,
                                 int32_t *P, size_t p_bytes,

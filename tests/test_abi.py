@@ -50,6 +50,10 @@ def test_size_helpers(lib):
     assert lib.qmm_weight_bytes(0, 1, 5, 64) == 256 + 5 * 2 * 16
     assert lib.qmm_weight_bytes(0, 1, 256, 1024) == (2 * 256 * 32 + 255) // 256 * 256 + 16 * 256 * 32
     assert lib.qmm_weight_bytes(7, 0, 5, 64) == 0
+    # Q6_K: 210 B per 256; repacked adds the padding of its d section
+    assert lib.qmm_weight_bytes(2, 0, 5, 512) == 5 * 2 * 210
+    assert lib.qmm_weight_bytes(2, 1, 5, 512) == 256 + 5 * 2 * 208
+    assert lib.qmm_weight_bytes(2, 0, 5, 100) == 0
 
 
 def _last(lib):
@@ -137,6 +141,22 @@ def test_quantize_mul_mat_validation(lib):
     assert call(M=0, x=None, y=None, w=None, o=None) == OK
 
 
+def test_q6_K_validation(lib):
+    f = lib.qmm_mul_mat_q6_K
+    big = 10**9
+    assert f(A, big, 1, A, big, A, big, 2, 8, 384, None) == EUNSUP          # K % 256
+    assert f(A, big, 1, A, big, A, big, 2, 8, 53760 + 256, None) == EUNSUP  # LDS limit
+    assert "Q6_K takes K" in _last(lib)
+    assert f(A, 8 * 2 * 210 - 1, 0, A, big, A, big, 2, 8, 512, None) == EINVAL
+    assert f(A, 256 + 8 * 2 * 208 - 1, 1, A, big, A, big, 2, 8, 512, None) == EINVAL
+    assert f(A, big, 1, A, 2 * 2 * 292 - 1, A, big, 2, 8, 512, None) == EINVAL
+    assert f(A, big, 1, A + 2, big, A, big, 2, 8, 512, None) == EALIGN
+    assert f(None, 0, 1, None, 0, None, 0, 0, 8, 512, None) == OK
+    assert lib.qmm_quantize_weights(2, A, 4, 300, A, 10**6, None) == EUNSUP
+    assert lib.qmm_quantize_weights(2, A, 4, 256, A, 4 * 210 - 1, None) == EINVAL
+    assert lib.qmm_repack_weights(2, A, 4, 256, A + 10**6, 256 + 4 * 208 - 1, None) == EINVAL
+
+
 def test_other_validation(lib):
     assert lib.qmm_quantize_weights(1, A, 4, 100, A, 10**6, None) == EUNSUP
     assert lib.qmm_quantize_weights(0, A, 4, 64, A, 4 * 2 * 18 - 1, None) == EINVAL
@@ -146,7 +166,10 @@ def test_other_validation(lib):
     assert lib.qmm_repack_weights(1, A, 4, 256, A + 10**6, 4 * 144 - 1, None) == EINVAL
     assert lib.qmm_debug_block_sums(1, A, 10**9, 0, A, 10**9, A, 4 * 8 * 16 * 4 - 1,
                                     4, 8, 512, None) == EINVAL
-    assert lib.qmm_debug_block_sums(2, A, 10**9, 0, A, 10**9, A, 10**9, 4, 8, 512, None) == EUNSUP
+    assert lib.qmm_debug_block_sums(7, A, 10**9, 0, A, 10**9, A, 10**9, 4, 8, 512, None) == EUNSUP
+    # Q6_K group sums: K/16 int32 per (m, n)
+    assert lib.qmm_debug_block_sums(2, A, 10**9, 0, A, 10**9, A, 4 * 8 * 32 * 4 - 1,
+                                    4, 8, 512, None) == EINVAL
 
 
 def test_status_strings(lib):
