@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 MALL_BYTES = 256 << 20
 METRIC = "Q4_K GEMV weight GB/s (% HBM peak); prefill GEMM int8 TOPS (% MFMA peak)"
+PREFILL = ("c5_m512", "c5_m2048", "q6K_c5_m512", "q6K_c5_m2048")
 
 
 def parse():
@@ -87,7 +88,7 @@ class Prepared:
         self.items = []
         for key_a, ps in groups.items():
             p0 = ps[0]
-            afmt = "q8_K" if p0.wfmt == "q4_K" else "q8_0"
+            afmt = qmm.ACT_FOR[p0.wfmt]
             x = torch.from_numpy(p0.acts()).to(dev)
             y = torch.empty(qmm.act_bytes(afmt, p0.M, p0.K), dtype=torch.uint8, device=dev)
             canons = []
@@ -121,13 +122,8 @@ class Prepared:
                 qmm.quantize_row_q8(it["x"], it["afmt"], out=it["y"])
             if only in (None, "mul_mat"):
                 for m in it["mats"]:
-                    w = m["ws"][i % self.copies]
-                    if p.wfmt == "q4_K":
-                        qmm.mul_mat_q4_K(w, it["y"], p.M, m["N"], p.K, layout=self.layout,
-                                         out=m["out"])
-                    else:
-                        qmm.mul_mat_q4_0(w, it["y"], p.M, m["N"], p.K, layout=self.layout,
-                                         out=m["out"])
+                    qmm.mul_mat(p.wfmt, m["ws"][i % self.copies], it["y"], p.M, m["N"], p.K,
+                                layout=self.layout, out=m["out"])
 
     @property
     def calls_per_step(self) -> int:
@@ -195,7 +191,7 @@ def cpu_baseline(key: str, seconds: float):
     p = max(wl.projections, key=lambda q: q.N * q.K)
     M_s = min(p.M, 2)
     w = oracle.quantize(p.wfmt, p.weights())
-    afmt = "q8_K" if p.wfmt == "q4_K" else "q8_0"
+    afmt = "q8_0" if p.wfmt == "q4_0" else "q8_K"
     y = oracle.quantize(afmt, p.acts()[:M_s])
     threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
@@ -207,7 +203,7 @@ def cpu_baseline(key: str, seconds: float):
         if el >= seconds:
             break
     per = el / reps
-    wbytes = p.N * p.K * (144 / 256 if p.wfmt == "q4_K" else 18 / 32)
+    wbytes = p.N * p.K * {"q4_0": 18 / 32, "q4_K": 144 / 256, "q6_K": 210 / 256}[p.wfmt]
     if p.M <= 8:
         val, unit = wbytes / per / 1e9, "GB/s"
         sample = (f"{p.name} projection of {key} (M={M_s}, N={p.N}, K={p.K}), integer path, "
@@ -278,7 +274,7 @@ def roofline_of(res: dict, path: str) -> dict:
     ms = r["ms_per_step"] if path == "fused" else r["mul_mat_us"] * 1e-3
     achieved = res["weight_bytes"] / n / (ms / n * 1e-3) / 1e9
     kernel = "k_gemv1_fused_q4_K" if path == "fused" else "k_gemv1_q4_K"
-    traffic = profiled_traffic(kernel, res["key"]) if n == 1 else None
+    traffic = profiled_traffic(kernel, res["key"]) if n == 1 and res["key"] == "c2" else None
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
@@ -313,20 +309,21 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     if a.prefill_only:
-        res = {k: measure_prefill(k, a.layout, a.prefill_steps) for k in ("c5_m512", "c5_m2048")}
+        res = {k: measure_prefill(k, a.layout, a.prefill_steps) for k in PREFILL}
         print(json.dumps({"prefill": res}), flush=True)
         return
     head = measure_decode(a.workload, a.layout, a.steps, a.warmup)
     extra = {}
     if a.all:
-        for k in ("c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32"):
+        for k in ("c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "q6K_down"):
             if k != a.workload:
                 r = measure_decode(k, a.layout, a.steps, a.warmup)
                 print(f"bench.py: {k} done", file=sys.stderr, flush=True)
                 extra[k] = _rounded(r)
+    q6 = measure_decode("q6K_c2", a.layout, a.steps, a.warmup)
     prefill = {}
     if not a.no_prefill:
-        for k in ("c5_m512", "c5_m2048"):
+        for k in PREFILL:
             prefill[k] = measure_prefill(k, a.layout, a.prefill_steps)
             print(f"bench.py: {k} done", file=sys.stderr, flush=True)
     cpu = None
@@ -363,6 +360,11 @@ def main():
                           "quantize_row_q8_us": round(head["unfused"]["quantize_us"], 3),
                           "roofline_mul_mat": roofline_of(head, "unfused")},
         "prefill": prefill,
+        "q6_K_gemv": {"workload": f"q6K_c2: {q6['description']}",
+                      "value": round(q6["unfused"]["value"], 2), "unit": "GB/s",
+                      "ms_per_step": round(q6["unfused"]["ms_per_step"], 6),
+                      "mul_mat_us": round(q6["unfused"]["mul_mat_us"], 3),
+                      "roofline_mul_mat": roofline_of(q6, "unfused")},
     }
     if extra:
         line["other_workloads"] = extra

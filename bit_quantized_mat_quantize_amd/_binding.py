@@ -56,6 +56,7 @@ def load() -> ctypes.CDLL:
         "qmm_mul_mat_q4_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_mul_mat_q4_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_mul_mat_q6_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
+        "qmm_mul_mat_q6_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_quantize_mul_mat": (I, [I, P, SZ, I, P, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_debug_block_sums": (I, [I, P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_status_string": (ctypes.c_char_p, [I]),
@@ -176,7 +177,7 @@ def quantize_mul_mat(wfmt: str, w, x, N: int, layout: str = "canonical", y=None,
     M, K = x.shape
     if x.dtype != torch.float32:
         raise ValueError("x must be float32")
-    afmt = "q8_0" if wfmt == "q4_0" else "q8_K"
+    afmt = ACT_FOR[wfmt]
     if y is None:
         y = torch.empty(max(act_bytes(afmt, M, K), 1), dtype=torch.uint8, device=x.device)
     if out is None:
@@ -190,16 +191,27 @@ def quantize_mul_mat(wfmt: str, w, x, N: int, layout: str = "canonical", y=None,
     return out, y
 
 
-def mul_mat_q6_K(w, y, M: int, N: int, K: int, layout: str = "canonical", out=None, stream=None):
+def mul_mat_q6_K(w, y, M: int, N: int, K: int, layout: str = "canonical", algo: str = "auto",
+                 out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=y.device)
     pw, nw = _dev(w, "w")
     py, ny = _dev(y, "y")
     po, no = _dev(out, "out")
-    _check(load().qmm_mul_mat_q6_K(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
-                                   _stream(stream)), "qmm_mul_mat_q6_K")
+    _check(load().qmm_mul_mat_q6_K_ex(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
+                                      _ALGO[algo], _stream(stream)), "qmm_mul_mat_q6_K")
     return out
+
+
+ACT_FOR = {"q4_0": "q8_0", "q4_K": "q8_K", "q6_K": "q8_K"}  # activation blocks each weight format takes
+
+
+def mul_mat(wfmt: str, w, y, M: int, N: int, K: int, layout: str = "canonical", out=None,
+            stream=None):
+    """The mul_mat entry point of weight format `wfmt` (automatic dispatch by M)."""
+    fn = {"q4_0": mul_mat_q4_0, "q4_K": mul_mat_q4_K, "q6_K": mul_mat_q6_K}[wfmt]
+    return fn(w, y, M, N, K, layout=layout, out=out, stream=stream)
 
 
 def debug_block_sums(wfmt: str, w, y, M: int, N: int, K: int, layout: str = "canonical",

@@ -3,7 +3,8 @@
 // Every entry point validates its arguments on the host before touching the
 // HIP runtime, so a bad call returns an error code, enqueues nothing and needs
 // no GPU to be tested.  Valid calls dispatch to the kernel families in
-// quantize.hip, repack.hip, gemv.hip and gemm.hip.
+// quantize.hip, repack.hip, gemv.hip, skinny.hip, gemm.hip, q6k.hip and
+// q6k_gemm.hip.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -33,6 +34,13 @@ int w_qk(qmm_weight_type t) {
     return t == QMM_Q4_0 ? 32 : ((t == QMM_Q4_K || t == QMM_Q6_K) ? 256 : 0);
 }
 int w_bytes_per_block(qmm_weight_type t) { return t == QMM_Q4_0 ? 18 : (t == QMM_Q6_K ? 210 : 144); }
+
+// The MFMA kernels address the weight and the Q8_K activation matrix with
+// 32-bit buffer offsets.
+bool below_4gib(qmm_weight_type t, qmm_layout l, int64_t M, int64_t N, int64_t K) {
+    const size_t lim = size_t(1) << 32;
+    return qmm_weight_bytes(t, l, N, K) < lim && qmm_act_bytes(QMM_Q8_K, M, K) < lim;
+}
 
 qmm_status check_rows(const char *name, int64_t v) {
     if (v < 0) return fail(QMM_EINVAL, "%s = %lld is negative", name, (long long)v);
@@ -200,14 +208,15 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, cons
     if (algo == QMM_ALGO_GEMV && M > qmm::kGemvMaxM)
         return fail(QMM_EUNSUPPORTED, "GEMV path takes M <= %d (M = %lld)", qmm::kGemvMaxM,
                     (long long)M);
-    // the small-batch kernel addresses both matrices with 32-bit offsets
-    const bool skinny_ok = M <= qmm::skinny_max_m() &&
-                           qmm_weight_bytes(QMM_Q4_K, l, N, K) < (size_t(1) << 32) &&
-                           qmm_act_bytes(QMM_Q8_K, M, K) < (size_t(1) << 32);
+    // the MFMA kernels address both matrices with 32-bit offsets
+    const bool small = below_4gib(QMM_Q4_K, l, M, N, K);
+    const bool skinny_ok = M <= qmm::skinny_max_m() && small;
     if (algo == QMM_ALGO_SKINNY && !skinny_ok)
         return fail(QMM_EUNSUPPORTED,
                     "SKINNY path takes M <= %lld and matrices below 4 GiB (M = %lld)",
                     (long long)qmm::skinny_max_m(), (long long)M);
+    if (algo == QMM_ALGO_MFMA && !small)
+        return fail(QMM_EUNSUPPORTED, "MFMA path takes matrices below 4 GiB");
     if (M == 0 || N == 0) return QMM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool rep = l == QMM_LAYOUT_REPACKED;
@@ -215,10 +224,19 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, cons
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     qmm_algo a = algo;
     if (a == QMM_ALGO_AUTO)
-        a = M == 1 ? QMM_ALGO_GEMV : (skinny_ok ? QMM_ALGO_SKINNY
-                                                : (M <= qmm::kGemvMaxM ? QMM_ALGO_GEMV : QMM_ALGO_MFMA));
-    if (a == QMM_ALGO_GEMV)
-        return device_status(qmm::launch_gemv_q4_K(wb, rep, yb, out, M, N, K, s), "mul_mat_q4_K gemv launch");
+        a = M == 1 ? QMM_ALGO_GEMV
+                   : (skinny_ok ? QMM_ALGO_SKINNY
+                                : (M <= qmm::kGemvMaxM || !small ? QMM_ALGO_GEMV : QMM_ALGO_MFMA));
+    if (a == QMM_ALGO_GEMV) {
+        // groups of up to 8 activation rows per GEMV launch
+        const int64_t rowb = (K / 256) * 292;
+        for (int64_t m0 = 0; m0 < M; m0 += qmm::kGemvMaxM) {
+            const int64_t mm = M - m0 < qmm::kGemvMaxM ? M - m0 : qmm::kGemvMaxM;
+            QMM_TRY(device_status(qmm::launch_gemv_q4_K(wb, rep, yb + m0 * rowb, out + m0 * N, mm, N, K, s),
+                                  "mul_mat_q4_K gemv launch"));
+        }
+        return QMM_OK;
+    }
     if (a == QMM_ALGO_SKINNY)
         return device_status(qmm::launch_skinny_q4_K(wb, rep, yb, out, M, N, K, s),
                              "mul_mat_q4_K skinny launch");
@@ -232,18 +250,43 @@ qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l, const v
                                stream);
 }
 
+qmm_status qmm_mul_mat_q6_K_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                               size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                               int64_t K, qmm_algo algo, void *stream) {
+    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
+        return fail(QMM_EUNSUPPORTED, "Q6_K takes the GEMV or MFMA path (algo %d)", (int)algo);
+    QMM_TRY(mul_mat_common(QMM_Q6_K, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
+    const bool gemv_ok = K <= qmm::q6_K_max_k();
+    const bool mfma_ok = l == QMM_LAYOUT_REPACKED && below_4gib(QMM_Q6_K, l, M, N, K);
+    if (algo == QMM_ALGO_GEMV && !gemv_ok)
+        return fail(QMM_EUNSUPPORTED, "Q6_K GEMV takes K <= %lld (K = %lld)",
+                    (long long)qmm::q6_K_max_k(), (long long)K);
+    if (algo == QMM_ALGO_MFMA && !mfma_ok)
+        return fail(QMM_EUNSUPPORTED, "Q6_K MFMA path takes the repacked layout and matrices below 4 GiB");
+    if (algo == QMM_ALGO_AUTO && !gemv_ok && !mfma_ok)
+        return fail(QMM_EUNSUPPORTED,
+                    "Q6_K with K = %lld > %lld needs the repacked layout and matrices below 4 GiB",
+                    (long long)K, (long long)qmm::q6_K_max_k());
+    if (M == 0 || N == 0) return QMM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const uint8_t *yb = static_cast<const uint8_t *>(y);
+    qmm_algo a = algo;
+    if (a == QMM_ALGO_AUTO)
+        a = (M <= qmm::kGemvMaxM && gemv_ok) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
+    if (a == QMM_ALGO_GEMV)
+        return device_status(qmm::launch_gemv_q6_K(wb, l == QMM_LAYOUT_REPACKED, yb, out, M, N, K, s),
+                             "mul_mat_q6_K gemv launch");
+    return device_status(qmm::launch_gemm_q6_K(wb, (int64_t)qmm_weight_bytes(QMM_Q6_K, l, N, K), yb,
+                                               out, M, N, K, s),
+                         "mul_mat_q6_K gemm launch");
+}
+
 qmm_status qmm_mul_mat_q6_K(const void *w, size_t w_bytes, qmm_layout l, const void *y,
                             size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
                             int64_t K, void *stream) {
-    QMM_TRY(mul_mat_common(QMM_Q6_K, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
-    if (K > qmm::q6_K_max_k())
-        return fail(QMM_EUNSUPPORTED, "Q6_K takes K <= %lld (K = %lld)", (long long)qmm::q6_K_max_k(),
-                    (long long)K);
-    if (M == 0 || N == 0) return QMM_OK;
-    return device_status(qmm::launch_gemv_q6_K(static_cast<const uint8_t *>(w), l == QMM_LAYOUT_REPACKED,
-                                               static_cast<const uint8_t *>(y), out, M, N, K,
-                                               static_cast<hipStream_t>(stream)),
-                         "mul_mat_q6_K launch");
+    return qmm_mul_mat_q6_K_ex(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, QMM_ALGO_AUTO,
+                               stream);
 }
 
 qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes, qmm_layout l,

@@ -21,11 +21,11 @@
 // |bsums| <= 2032 is exact in fp16 and -dmin*m_j (17 significant bits) is the
 // exact sum of two fp16 values, so only the fp32 accumulation rounds.
 //
-// Workgroup: 256 threads = 4 wavefronts, one per SIMD (all 512 registers of
-// the lane are available); tile 128 (M) x 256 (N); wavefront w owns columns
-// 64w..64w+63 (two 32-column tiles) for all 128 rows (four 32-row tiles), so
-// each weight column is decoded by exactly one wavefront and each activation
-// operand read from LDS feeds four MFMAs.  K advances one
+// Workgroup: 512 threads = 8 wavefronts, two per SIMD (256 registers per
+// lane each); tile 128 (M) x 256 (N); wavefront w owns columns 32w..32w+31
+// (one 32-column tile) for all 128 rows (four 32-row tiles), so each weight
+// column is decoded by exactly one wavefront and the decoded planes feed four
+// row tiles' MFMAs.  K advances one
 // 256-element super-block per step through two LDS buffers: while step b is
 // computed from one buffer, the codes of step b+1 stream into the other with
 // direct global->LDS loads (global_load_lds_dwordx4, no registers involved);
@@ -48,17 +48,12 @@
 // slice assignment, so the sum over a sub-block is complete whatever the
 // hardware order inside the slice.  Result register r of lane l holds row
 // 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+#include "mfma_common.h"
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
 namespace qmm {
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128, BN = 256, MT = BM / 32, NWAVE = 8, NTHR = 64 * NWAVE;
 constexpr int CT = BN / 32 / NWAVE;  // column tiles per wavefront (one)
@@ -78,36 +73,6 @@ static_assert(A_INSTR % NWAVE == 0 && P_INSTR % NWAVE == 0 && H_INSTR <= NWAVE,
               "staging must split evenly over the wavefronts");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 static_assert(CT == 1 && 2 * BM <= NTHR, "one column tile per wavefront; bsums staged by 2*BM threads");
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ uint32_t h2_bits(int lo, int hi) {
-    return f32_to_f16_bits((float)lo) | (f32_to_f16_bits((float)hi) << 16);
-}
-
-// packed per-byte product of four codes (each <= 15) with a scale digit (<= 7)
-__device__ __forceinline__ int plane(uint32_t q4, uint32_t digit_pair) {
-    const us2 p = __builtin_bit_cast(us2, q4) * __builtin_bit_cast(us2, digit_pair);
-    return (int)__builtin_bit_cast(uint32_t, p);
-}
-
-// Staging goes through buffer resources: a scalar base and byte count per
-// source (the tile's first activation row, first header, first payload) and
-// 32-bit per-lane offsets, with the super-block step in the scalar offset.
-// Loads past the byte count return zero instead of faulting.  Plain global
-// pointers would need 64-bit per-lane addresses, and a generic (flat) load
-// would make the compiler wait for every outstanding global->LDS transfer.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t *base, int64_t bytes) {
-    const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, (int)(uint32_t)n,
-                                             0x00020000);  // raw dword access (gfx9 family)
-}
-// 16 bytes per lane into LDS at lds_base + 16 * lane (lds_base wavefront-uniform)
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *lds_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, voff, soff, 0, 0);
-}
 
 template <bool REPACKED>
 __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict__ W,

@@ -1,0 +1,54 @@
+// mfma_common.h -- pieces shared by the int8 MFMA kernels (gfx950): operand
+// vector types, buffer-resource loads and the per-byte digit-plane product.
+//
+// Staging goes through buffer resources: a scalar base and byte count per
+// source and 32-bit per-lane offsets, with the K step in the scalar offset.
+// Loads past the byte count return zero instead of faulting.  Plain global
+// pointers would need 64-bit per-lane addresses, and a generic (flat) load
+// would make the compiler wait for every outstanding global->LDS transfer.
+// A resource must be built where it is used: one held across a lambda is
+// treated as divergent and the loads that take it get waterfall loops.
+#pragma once
+
+#include "qmm_device.h"
+
+namespace qmm {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t *base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, (int)(uint32_t)n,
+                                             0x00020000);  // raw dword access (gfx9 family)
+}
+__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+// 16 bytes per lane into LDS at lds_base + 16 * lane (lds_base wavefront-uniform)
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, voff, soff, 0, 0);
+}
+
+// packed per-byte product of four codes (each <= 15) with a scale digit (<= 7):
+// every byte product is below 256, so no carry crosses a byte
+__device__ __forceinline__ int plane(uint32_t q4, uint32_t digit_pair) {
+    const us2 p = __builtin_bit_cast(us2, q4) * __builtin_bit_cast(us2, digit_pair);
+    return (int)__builtin_bit_cast(uint32_t, p);
+}
+// two int16 values as two fp16 (exact for |v| <= 2048)
+__device__ __forceinline__ uint32_t h2_bits(int lo, int hi) {
+    return f32_to_f16_bits((float)lo) | (f32_to_f16_bits((float)hi) << 16);
+}
+
+}  // namespace
+}  // namespace qmm

@@ -1,0 +1,260 @@
+// q6k_gemm.hip -- Q6_K weights x Q8_K activations on int8 MFMA (prefill-sized
+// M), gfx950, for the load-time (repacked) weight layout.
+//
+// Format and integer path: ggml-cpu mul_mat page, "更低的比特:Q6_K 与 Q2_K 的取舍"
+// (ql/qh 6-bit codes, int8 scale per 16-element group, fp16 d, no min) and
+// "正确性:缩放系数可以提到求和号外面" (scales outside the integer sums):
+//   per super-block b, output (m, n):  S = sum_j s_j * sum_{i in j} q_i y_i,
+//   acc += d_a * d * S.
+//
+// Tiling as in the Q4_K GEMM: 512 threads = 8 wavefronts, tile 128 (M) x 256
+// (N), wavefront w owns the 32-column tile 32w..32w+31 for all four 32-row
+// tiles, K advances one super-block per step, the int8 activation tile is
+// double-buffered in LDS (direct global->LDS loads, XOR-swizzled pieces) with
+// d_a beside it.  The weights do not go through LDS: no other wavefront reads
+// a column, so each lane loads the 112 bytes of its column it needs straight
+// into registers, one step ahead.
+//
+// MFMA K-slices: in v_mfma_i32_32x32x32_i8 lane l supplies the 16 consecutive
+// elements 16*(l/32).. of a 32-element chunk, i.e. exactly one 16-element
+// group, so the group scale is one value per lane.  The lane forms per element
+// the scaled code t = s * q in [-4064, 4096] and splits it into two int8
+// digits, t = 256 * hi + lo with lo the signed low byte (hi in [-16, 16]);
+// two MFMAs per chunk accumulate H = sum hi*y and L = sum lo*y over the
+// super-block, and S = 256 H + L exactly (|S| <= 256 * 4096 * 127 < 2^31).
+// The products are formed in packed 16-bit lanes: with the stored code
+// u = q + 32, t + 128 = s*u + (128 - 32s) is one v_pk_mad per two codes, its
+// high byte is hi and its low byte with the top bit flipped is lo, and
+// v_perm_b32 moves bytes between the 8-bit and 16-bit lane layouts.  No bsums
+// and no min term: the epilogue is acc += d_a * (d * S).
+#include "mfma_common.h"
+#include "qmm_device.h"
+#include "qmm_launch.h"
+
+namespace qmm {
+namespace {
+
+constexpr int BM = 128, BN = 256, MT = BM / 32, NWAVE = 8, NTHR = 64 * NWAVE;
+constexpr int A_OFF = 0, A_BYTES = BM * 256;
+constexpr int DA_OFF = A_OFF + A_BYTES, DA_BYTES = BM * 4;
+constexpr int BUF_BYTES = DA_OFF + DA_BYTES;
+constexpr int LDS_BYTES = 2 * BUF_BYTES;
+constexpr int A_INSTR = A_BYTES / 1024;  // 64-lane x 16-byte loads per buffer
+constexpr int A_PER_WAVE = A_INSTR / NWAVE;
+static_assert(A_INSTR % NWAVE == 0, "activation staging must split evenly over the wavefronts");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
+static_assert(BN == 32 * NWAVE && BM <= NTHR, "one column tile per wavefront; d_a staged by BM threads");
+
+// The weight side of one super-block for lane (column c, slice h): the ql
+// pieces 2g + h (both nibbles used), the qh pieces h and h + 2, the block's
+// 16 scales and its fp16 d.
+struct Q6KStage {
+    uint4 ql[4];
+    uint4 qa, qb;
+    uint4 sc;
+    uint32_t d;
+};
+
+// Four codes u (bytes in [0, 63]) with the pairs s2 = (s, s) and
+// c2 = (128 - 32s, 128 - 32s) -> the digit bytes of t = s*(u - 32) = 256*hi + lo:
+// t' = t + 128 = s*u + 128 - 32s (one packed 16-bit multiply-add per two codes;
+// |t'| < 2^15), hi = the high byte of t' (floor(t'/256), signed), lo = the low
+// byte of t' minus 128 (its top bit flipped), both in int8 range.
+__device__ __forceinline__ void t_digits(uint32_t u, s16x2 s2, s16x2 c2, uint32_t &hi, uint32_t &lo) {
+    const uint32_t e = __builtin_amdgcn_perm(u, u, 0x0c020c00u);  // u0, u2 in 16-bit lanes
+    const uint32_t o = __builtin_amdgcn_perm(u, u, 0x0c030c01u);  // u1, u3
+    const uint32_t te = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, e) * s2 + c2);
+    const uint32_t to = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, o) * s2 + c2);
+    // bytes 0-3 of the pair are the second operand, 4-7 the first
+    hi = __builtin_amdgcn_perm(to, te, 0x07030501u);
+    lo = __builtin_amdgcn_perm(to, te, 0x06020400u) ^ 0x80808080u;
+}
+
+__global__ __launch_bounds__(NTHR, 1) void k_gemm_q6_K(const uint8_t *__restrict__ W, int64_t w_bytes,
+                                                       const uint8_t *__restrict__ Y,
+                                                       float *__restrict__ out, int64_t M, int64_t N,
+                                                       int64_t K, int tiles_m, int tiles_n) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hh = lane >> 5;
+
+    // XCD-aware tile order (as in the Q4_K GEMM): each XCD gets a contiguous
+    // range of v, and v walks groups of GM row tiles with the row tile fastest.
+    constexpr int GM = 4;
+    const int nwg = tiles_m * tiles_n;
+    const int bid = blockIdx.x;
+    const int v = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+    const int group = v / (GM * tiles_n), first_m = group * GM;
+    const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;
+    const int in_group = v - group * GM * tiles_n;
+    // (the division runs on the vector ALU; readfirstlane keeps the tile uniform)
+    const int tile_m = __builtin_amdgcn_readfirstlane(first_m + in_group % gm);
+    const int tile_n = __builtin_amdgcn_readfirstlane(in_group / gm);
+    const int64_t m_base = (int64_t)tile_m * BM, n_base = (int64_t)tile_n * BN;
+    const int64_t nb = K / QK_K;
+
+    // ---- activation staging (rows past M clamped to the last valid one)
+    const int m_last = (int)(M - 1 - m_base < BM - 1 ? M - 1 - m_base : BM - 1);
+    const uint32_t a_rowstride = (uint32_t)(nb * kQ8_KBytes);
+    const int64_t a_first = m_base * nb * kQ8_KBytes;
+    const int64_t a_bytes = M * nb * kQ8_KBytes - a_first;
+    uint32_t a_goff[A_PER_WAVE];
+#pragma unroll
+    for (int t = 0; t < A_PER_WAVE; ++t) {
+        const int row = (wave * A_PER_WAVE + t) * 4 + (lane >> 4);
+        const int gp = (lane & 15) ^ (row & 15);  // global piece stored at position lane & 15
+        const int rr = row < m_last ? row : m_last;
+        a_goff[t] = (uint32_t)rr * a_rowstride + 4 + 16 * gp;
+    }
+    const uint32_t d_off = (uint32_t)((tid & (BM - 1)) < m_last ? (tid & (BM - 1)) : m_last) * a_rowstride;
+
+    // ---- this lane's weight column (columns past N clamped; never stored)
+    const int64_t NB = N * nb;
+    const int64_t dsec = (2 * NB + 255) / 256 * 256;
+    const int64_t n_lane = n_base + wave * 32 + l32 < N ? n_base + wave * 32 + l32 : N - 1;
+    const int64_t i0 = n_lane * nb;  // block index of the column's first super-block
+    const uint32_t v_d = (uint32_t)(2 * i0);
+    const uint32_t v_sc = (uint32_t)(dsec + 16 * i0);
+    const uint32_t v_ql = (uint32_t)(dsec + 16 * NB + 128 * i0 + 16 * hh);
+    const uint32_t v_qh = (uint32_t)(dsec + 144 * NB + 64 * i0 + 16 * hh);
+
+    auto issue = [&](int64_t b, uint8_t *buf) {
+        const rsrc_t ra = make_rsrc(Y + a_first, a_bytes);
+        const uint32_t sa = (uint32_t)b * kQ8_KBytes;
+#pragma unroll
+        for (int t = 0; t < A_PER_WAVE; ++t)
+            dma16(ra, a_goff[t], sa, buf + A_OFF + (wave * A_PER_WAVE + t) * 1024);
+    };
+    auto prefetch = [&](int64_t b, uint32_t &draw) {
+        const rsrc_t ra = make_rsrc(Y + a_first, a_bytes);
+        if (tid < BM) draw = __builtin_amdgcn_raw_buffer_load_b32(ra, d_off, (uint32_t)b * kQ8_KBytes, 0);
+    };
+    auto wload = [&](int64_t b, Q6KStage &x) {
+        const rsrc_t rw = make_rsrc(W, w_bytes);
+        const uint32_t bb = (uint32_t)b;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) x.ql[g] = bld16(rw, v_ql + 32 * g, 128 * bb);
+        x.qa = bld16(rw, v_qh, 64 * bb);
+        x.qb = bld16(rw, v_qh + 32, 64 * bb);
+        x.sc = bld16(rw, v_sc, 16 * bb);
+        x.d = __builtin_amdgcn_raw_buffer_load_b16(rw, v_d, 2 * bb, 0);
+    };
+
+    float acc[MT][16];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+    uint32_t draw = 0;
+    Q6KStage wx;
+    issue(0, lds);
+    prefetch(0, draw);
+    wload(0, wx);
+
+    for (int64_t b = 0; b < nb; ++b) {
+        uint8_t *buf = lds + (b & 1) * BUF_BYTES;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of step b
+        if (tid < BM) *reinterpret_cast<uint32_t *>(buf + DA_OFF + 4 * tid) = draw;
+
+        // ---------------- decode: chunk c holds group G = 2c + hh of this lane
+        const float dcol = f16_bits_to_f32(wx.d);
+        const uint32_t sw[4] = {wx.sc.x, wx.sc.y, wx.sc.z, wx.sc.w};
+        v4i bhi[8], blo[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int g = c >> 1, hi_nib = c & 1;
+            const int s = (int)(int8_t)(sw[g] >> (16 * hi_nib + 8 * hh));  // scale byte 2c + hh
+            const s16x2 s2 = {(short)s, (short)s};
+            const s16x2 c2 = {(short)(128 - 32 * s), (short)(128 - 32 * s)};
+            const uint32_t ql[4] = {wx.ql[g].x, wx.ql[g].y, wx.ql[g].z, wx.ql[g].w};
+            const uint4 qhp = hi_nib ? wx.qb : wx.qa;
+            const uint32_t qh[4] = {qhp.x, qhp.y, qhp.z, qhp.w};
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t u = ((ql[w] >> (4 * hi_nib)) & 0x0f0f0f0fu) |
+                                   (((qh[w] >> (2 * g)) & 0x03030303u) << 4);
+                t_digits(u, s2, c2, hw[w], lw[w]);
+            }
+            bhi[c] = v4i{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
+            blo[c] = v4i{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
+        }
+
+        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
+        if (b + 1 < nb) {
+            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
+            prefetch(b + 1, draw);
+            wload(b + 1, wx);
+        }
+        const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
+
+        // ---------------- the four row tiles of this column tile
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int row = i * 32 + l32;
+            const v16i zero = {};
+            v16i ah, al;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                v4i a_op[4];
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int c = 4 * half + cc;
+                    const uint4 a = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * 256 +
+                                                                     16 * ((2 * c + hh) ^ (row & 15)));
+                    a_op[cc] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+                }
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int c = 4 * half + cc;
+                    ah = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[cc], bhi[c], c ? ah : zero, 0, 0, 0);
+                    al = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[cc], blo[c], c ? al : zero, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q + e;
+                    const int S = (ah[r] << 8) + al[r];  // |S| <= 256 * 4096 * 127
+                    acc[i][r] = fmaf(dv[e], dcol * (float)S, acc[i][r]);
+                }
+            }
+        }
+    }
+
+    // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
+    const int64_t n = n_base + wave * 32 + l32;
+    if (n < N) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m_base + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (m < M) out[m * N + n] = acc[i][r];
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_q6_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    static bool attr_set = false;  // the LDS budget above 64 KiB must be opted into once
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_q6_K,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    hipLaunchKernelGGL(k_gemm_q6_K, dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), LDS_BYTES, s,
+                       w, w_bytes, y, out, M, N, K, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace qmm

@@ -50,8 +50,12 @@ hipError_t launch_gemv_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, f
 hipError_t launch_group_sums_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
                                   int64_t M, int64_t N, int64_t K, hipStream_t s);
 
-// MFMA GEMM family (any M >= 1).
+// MFMA GEMM family (any M >= 1; weight and activation matrices below 4 GiB:
+// 32-bit buffer offsets).  The Q6_K GEMM takes the repacked layout of
+// w_bytes bytes.
 hipError_t launch_gemm_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemm_q6_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
 
 constexpr int kGemvMaxM = 8;

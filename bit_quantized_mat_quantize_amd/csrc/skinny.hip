@@ -29,40 +29,15 @@
 // MFMA operand convention (v_mfma_*_32x32xK): lane l supplies row (A) or
 // column (B) l % 32 and the K-slice selected by l / 32; the result register r
 // of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+#include "mfma_common.h"
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
 namespace qmm {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
 constexpr int SK_WAVES = 8, SK_THREADS = 64 * SK_WAVES;
 constexpr int SK_MAX_M = 32;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t *base, int64_t bytes) {
-    const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, (int)(uint32_t)n,
-                                             0x00020000);  // raw dword access (gfx9 family)
-}
-__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t voff, uint32_t soff) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-// packed per-byte product of four codes (each <= 15) with a scale digit (<= 7)
-__device__ __forceinline__ int plane(uint32_t q4, uint32_t digit_pair) {
-    const us2 p = __builtin_bit_cast(us2, q4) * __builtin_bit_cast(us2, digit_pair);
-    return (int)__builtin_bit_cast(uint32_t, p);
-}
-__device__ __forceinline__ uint32_t h2_bits(int lo, int hi) {
-    return f32_to_f16_bits((float)lo) | (f32_to_f16_bits((float)hi) << 16);
-}
 
 // The weight side of one super-block in this lane's registers (loaded one
 // step ahead), plus the row's bsums and d_a.

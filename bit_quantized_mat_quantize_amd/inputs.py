@@ -65,7 +65,7 @@ def activations(seed, m: int, k: int, outlier_frac: float = 0.0,
 class Projection:
     """One weight matrix [N, K] in format `wfmt` and its activations [M, K]."""
     name: str
-    wfmt: str           # "q4_0" or "q4_K"
+    wfmt: str           # "q4_0", "q4_K" or "q6_K"
     M: int
     N: int
     K: int
@@ -92,7 +92,7 @@ class Workload:
 
     @property
     def weight_bytes(self) -> int:
-        per = {"q4_0": 18 / 32, "q4_K": 144 / 256}
+        per = {"q4_0": 18 / 32, "q4_K": 144 / 256, "q6_K": 210 / 256}
         return int(sum(p.N * p.K * per[p.wfmt] for p in self.projections))
 
     @property
@@ -108,6 +108,10 @@ def workload(key: str) -> Workload:
     c3        Q4_K FFN at M=1: gate, up (N=14336, K=4096), down (N=4096, K=14336)
     c4_m{4,8,32}   Q4_K, N=K=8192 (70B projection), M in {4, 8, 32}
     c5_m{512,2048} Q4_K prefill, N=28672, K=8192, activations with 1% outliers x20
+    q6K_c2    Q6_K x Q8_K GEMV, M=1, N=K=4096, the weights of c2 in 6-bit form
+    q6K_down  Q6_K x Q8_K GEMV, M=1, N=4096, K=14336 (the FFN down projection,
+              the matrix 4-bit model files commonly keep at 6 bits)
+    q6K_c5_m{512,2048}  Q6_K prefill on the c5 shapes (N=28672, K=8192)
     """
     if key == "c1":
         return Workload(key, "Q4_0xQ8_0 GEMV M=1 N=256 K=1024", [
@@ -130,7 +134,19 @@ def workload(key: str) -> Workload:
         assert m in (512, 2048)
         return Workload(key, f"Q4_K prefill M={m} N=28672 K=8192", [
             Projection("w", "q4_K", m, 28672, 8192, 5, [105, m], outliers=0.01)])
+    if key == "q6K_c2":
+        return Workload(key, "Q6_KxQ8_K GEMV M=1 N=4096 K=4096", [
+            Projection("w", "q6_K", 1, 4096, 4096, 2, 102)])
+    if key == "q6K_down":
+        return Workload(key, "Q6_KxQ8_K GEMV M=1 N=4096 K=14336", [
+            Projection("down", "q6_K", 1, 4096, 14336, [3, 2], [103, 1])])
+    if key.startswith("q6K_c5_m"):
+        m = int(key[8:])
+        assert m in (512, 2048)
+        return Workload(key, f"Q6_K prefill M={m} N=28672 K=8192", [
+            Projection("w", "q6_K", m, 28672, 8192, 5, [105, m], outliers=0.01)])
     raise KeyError(key)
 
 
-ALL_WORKLOADS = ["c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "c5_m512", "c5_m2048"]
+ALL_WORKLOADS = ["c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "c5_m512", "c5_m2048",
+                 "q6K_c2", "q6K_down", "q6K_c5_m512", "q6K_c5_m2048"]

@@ -82,14 +82,18 @@ typedef enum { QMM_Q8_0 = 0, QMM_Q8_K = 1 } qmm_act_type;
 typedef enum { QMM_Q4_0 = 0, QMM_Q4_K = 1, QMM_Q6_K = 2 } qmm_weight_type;
 typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
 
-/* Kernel family for a mul_mat call (Q4_K only; Q4_0 always uses GEMV):
- *   GEMV    vector int8 dot products, one wavefront per output row (M <= 8)
+/* Kernel family for a mul_mat call (Q4_K and Q6_K; Q4_0 always uses GEMV):
+ *   GEMV    vector int8 dot products, one wavefront per output row (Q4_K:
+ *           M <= 8; Q6_K: any M, K <= 53760)
  *   SKINNY  small-batch int8 MFMA, one 32-column tile per workgroup, K split
- *           over its wavefronts (M <= 32; weight and activation matrices
- *           below 4 GiB)
- *   MFMA    prefill GEMM on int8 MFMA with LDS-staged 128 x 256 tiles (any M)
- * AUTO takes GEMV for M = 1, SKINNY for 2 <= M <= 32 when its size limit
- * holds, and MFMA otherwise. */
+ *           over its wavefronts (Q4_K only; M <= 32)
+ *   MFMA    prefill GEMM on int8 MFMA, 128 x 256 output tiles (any M; Q6_K
+ *           needs the repacked layout)
+ * SKINNY and MFMA address the weight and activation matrices with 32-bit
+ * offsets, so both must be below 4 GiB.  AUTO for Q4_K takes GEMV for M = 1,
+ * SKINNY for 2 <= M <= 32, MFMA above (GEMV in groups of 8 rows where the
+ * size limit rules the MFMA kernels out); for Q6_K it takes GEMV for M <= 8
+ * and MFMA above, GEMV where MFMA is ruled out. */
 typedef enum {
     QMM_ALGO_AUTO = 0,
     QMM_ALGO_GEMV = 1,
@@ -158,16 +162,28 @@ qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l,
  * P_j = sum_{i in j} q_i*y_i over the 16-element groups j (ggml-cpu mul_mat page,
  * "更低的比特:Q6_K 与 Q2_K 的取舍": no min term, so no bsums path; and
  * "正确性:缩放系数可以提到求和号外面").  fp32 output, overwritten.  w: Q6_K [N,K]
- * in layout l; y: Q8_K [M,K].  GEMV kernels for every M (the weights are read
- * once per activation row); K <= 53760, else QMM_EUNSUPPORTED. */
+ * in layout l; y: Q8_K [M,K].  Kernel choice as QMM_ALGO_AUTO describes; a
+ * call that no Q6_K kernel takes (K > 53760 with the canonical layout or with
+ * a matrix of 4 GiB or more) gives QMM_EUNSUPPORTED. */
 qmm_status qmm_mul_mat_q6_K(const void *w, size_t w_bytes, qmm_layout l,
                             const void *y, size_t y_bytes,
                             float *out, size_t out_bytes,
                             int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Same as qmm_mul_mat_q6_K with an explicit kernel family: QMM_ALGO_GEMV
+ * (K <= 53760) or QMM_ALGO_MFMA (repacked layout, both matrices below 4 GiB);
+ * QMM_ALGO_SKINNY and a family whose limits the call exceeds give
+ * QMM_EUNSUPPORTED. */
+qmm_status qmm_mul_mat_q6_K_ex(const void *w, size_t w_bytes, qmm_layout l,
+                               const void *y, size_t y_bytes,
+                               float *out, size_t out_bytes,
+                               int64_t M, int64_t N, int64_t K, qmm_algo algo,
+                               void *stream);
+
 /* Same as qmm_mul_mat_q4_K with an explicit kernel family (for measuring the
  * GEMV / GEMM crossover).  QMM_ALGO_GEMV requires M <= 8; QMM_ALGO_SKINNY
- * requires M <= 32 and both matrices below 4 GiB (else QMM_EUNSUPPORTED). */
+ * requires M <= 32; SKINNY and MFMA require both matrices below 4 GiB (else
+ * QMM_EUNSUPPORTED). */
 qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l,
                                const void *y, size_t y_bytes,
                                float *out, size_t out_bytes,

@@ -145,8 +145,24 @@ def test_q6_K_validation(lib):
     f = lib.qmm_mul_mat_q6_K
     big = 10**9
     assert f(A, big, 1, A, big, A, big, 2, 8, 384, None) == EUNSUP          # K % 256
-    assert f(A, big, 1, A, big, A, big, 2, 8, 53760 + 256, None) == EUNSUP  # LDS limit
-    assert "Q6_K takes K" in _last(lib)
+    # K beyond the GEMV's LDS limit: only the MFMA path (repacked layout) takes it
+    assert f(A, big, 0, A, big, A, big, 2, 8, 53760 + 256, None) == EUNSUP
+    assert "needs the repacked layout" in _last(lib)
+    fx = lib.qmm_mul_mat_q6_K_ex
+    assert fx(A, big, 1, A, big, A, big, 2, 8, 53760 + 256, 1, None) == EUNSUP  # GEMV
+    assert "Q6_K GEMV takes K" in _last(lib)
+    assert fx(A, big, 0, A, big, A, big, 2, 8, 512, 2, None) == EUNSUP  # MFMA, canonical
+    assert "repacked layout" in _last(lib)
+    assert fx(A, big, 1, A, big, A, big, 2, 8, 512, 3, None) == EUNSUP  # SKINNY
+    assert fx(A, big, 1, A, big, A, big, 2, 8, 512, 9, None) == EUNSUP  # unknown
+    # 32-bit offsets: a weight matrix of 4 GiB or more rules the MFMA path out
+    kk = 1 << 20
+    n4g = (1 << 32) // (kk // 256 * 208) + 1  # repacked rows of K = 2^20 past 4 GiB
+    assert fx(A, 2**62, 1, A, 2**40, A, 2**40, 2, n4g, kk, 2, None) == EUNSUP
+    assert "below 4 GiB" in _last(lib)
+    n4g = (1 << 32) // 288 + 1  # Q4_K rows of K = 512 (288 B each) past 4 GiB, N < 2^24
+    assert lib.qmm_mul_mat_q4_K_ex(A, 2**62, 0, A, big, A, 2**40, 2, n4g, 512, 2, None) == EUNSUP
+    assert "below 4 GiB" in _last(lib)
     assert f(A, 8 * 2 * 210 - 1, 0, A, big, A, big, 2, 8, 512, None) == EINVAL
     assert f(A, 256 + 8 * 2 * 208 - 1, 1, A, big, A, big, 2, 8, 512, None) == EINVAL
     assert f(A, big, 1, A, 2 * 2 * 292 - 1, A, big, 2, 8, 512, None) == EINVAL

@@ -1,4 +1,4 @@
-"""The five measured workloads at full size, in the launch configuration the
+"""The measured workloads at full size, in the launch configuration the
 benchmark times (repacked weights, automatic GEMV/MFMA dispatch).
 
 The weights are encoded on the GPU exactly as the benchmark does it and must be
@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _run_projection(p, full: bool):
-    afmt = "q8_K" if p.wfmt == "q4_K" else "q8_0"
+    afmt = qmm.ACT_FOR[p.wfmt]
     wf = p.weights()
     w_gpu = qmm.quantize_weights(to_dev(wf), p.wfmt)
     w_orc = oracle.quantize(p.wfmt, wf)
@@ -28,11 +28,7 @@ def _run_projection(p, full: bool):
     y_orc = oracle.quantize(afmt, x)
     assert np.array_equal(to_host(y_gpu), y_orc.reshape(-1)), f"{p.name}: activation bytes differ"
     wr = qmm.repack_weights(w_gpu, p.wfmt, p.N, p.K)
-    if p.wfmt == "q4_K":
-        out = qmm.mul_mat_q4_K(wr, y_gpu, p.M, p.N, p.K, layout="repacked")
-    else:
-        out = qmm.mul_mat_q4_0(wr, y_gpu, p.M, p.N, p.K, layout="repacked")
-    got = to_host(out)
+    got = to_host(qmm.mul_mat(p.wfmt, wr, y_gpu, p.M, p.N, p.K, layout="repacked"))
     if full:
         want, terms = full_reference(p.wfmt, w_orc, y_orc, p.M, p.N, p.K)
         assert_close(got, want, terms, p.name)
@@ -46,13 +42,13 @@ def _run_projection(p, full: bool):
         assert_close(got[ms, ns], want, terms, p.name + " (sampled)")
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "q6K_c2", "q6K_down"])
 def test_decode_workloads(key):
     for p in workload(key).projections:
         _run_projection(p, full=True)
 
 
-@pytest.mark.parametrize("key", ["c5_m512", "c5_m2048"])
+@pytest.mark.parametrize("key", ["c5_m512", "c5_m2048", "q6K_c5_m512"])
 def test_prefill_workloads(key):
     for p in workload(key).projections:
         _run_projection(p, full=False)

@@ -2,12 +2,15 @@
 
 * GPU encoder and load-time repack: byte-identical to the oracle's.
 * int32 group sums P[m][n][K/16] (the GEMV decode path): bit-exact.
-* exactness window: integer activations with amax = 127 per block (d_a = 1),
-  weights with d = 1 and small scales keep every partial sum an integer below
-  2^24, so the fp32 outputs equal the integer result exactly.
+* exactness windows (GEMV and MFMA GEMM): integer activations with amax = 127
+  per block (d_a = 1), weights with d = 1 and scales/codes that keep every
+  partial sum an integer below 2^24, so the fp32 outputs equal the integer
+  result exactly -- including the extreme scales -128 and 127 with the extreme
+  codes -32 and 31, the corners of the GEMM's digit split.
 * fp32 outputs: |gpu - oracle| <= 1e-4 * sum_k |w a| for every checked (m, n).
-Shapes: one, two and four units per lane (K up to 53760, the last with a
-second pass), ragged N, several activation rows, both layouts.
+Shapes: GEMV with one, two and four units per lane (K up to 53760, the last
+with a second pass), ragged N, several activation rows, both layouts; GEMM with
+ragged row and column tiles, K past the GEMV's limit, and AUTO dispatch.
 """
 import struct
 
@@ -118,3 +121,66 @@ def test_full_size_sampled():
     ns = np.arange(0, N, 7)
     want, terms = oracle.sample("q6_K", w, y, M, N, K, np.zeros_like(ns), ns)
     assert_close(got[0, ns], want, terms, "q6_K 4096^2 sampled")
+
+
+# ---------------------------------------------------------------- MFMA GEMM
+def _window_blocks(rng, N, K, scales, codes):
+    return np.frombuffer(b"".join(_q6k_block(1.0, scales(rng), codes(rng))
+                                  for _ in range(N * K // 256)), np.uint8).reshape(N, -1)
+
+
+def test_mfma_exactness_window():
+    """Ragged tiles (M = 130, N = 300), d = 1, d_a = 1, small scales: exact."""
+    M, N, K = 130, 300, 1024
+    rng = np.random.default_rng(12)
+    w = _window_blocks(rng, N, K, lambda r: r.integers(-3, 4, 16), lambda r: r.integers(-32, 32, 256))
+    x = rng.integers(-20, 21, (M, K)).astype(np.float32)
+    x[:, ::256] = 127.0
+    y = oracle.quantize("q8_K", x)
+    want, terms = full_reference("q6_K", w, y, M, N, K)
+    assert terms.max() < 2 ** 24
+    got = to_host(qmm.mul_mat_q6_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K,
+                                   layout="repacked", algo="mfma"))
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_mfma_extreme_digits():
+    """Scales in {-128, -127, -1, 0, 1, 127} and codes in {-32, -31, 0, 31}
+    (t = s*q spans [-4064, 4096], both ends of the 256*hi + lo split), with
+    activations that are 0 or +-1 apart from one 127 per block: every sum is an
+    integer below 2^24, so the outputs are exact."""
+    M, N, K = 40, 70, 512
+    rng = np.random.default_rng(13)
+    w = _window_blocks(rng, N, K, lambda r: r.choice([-128, -127, -1, 0, 1, 127], 16),
+                       lambda r: r.choice([-32, -31, 0, 31], 256))
+    x = rng.integers(-1, 2, (M, K)).astype(np.float32)
+    x[:, ::256] = 127.0
+    y = oracle.quantize("q8_K", x)
+    want, terms = full_reference("q6_K", w, y, M, N, K)
+    assert terms.max() < 2 ** 24
+    for algo in ("mfma", "gemv"):
+        got = to_host(qmm.mul_mat_q6_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N,
+                                       K, layout="repacked", algo=algo))
+        assert np.array_equal(got.astype(np.float64), want), algo
+
+
+@pytest.mark.parametrize("M,N,K", [(9, 1, 256), (128, 256, 2048), (200, 257, 4096), (33, 40, Q6K_MAX_K + 256)])
+def test_mul_mat_q6_K_mfma(M, N, K):
+    w, y = _case(M, N, K, 11 * M + N)
+    want, terms = full_reference("q6_K", w, y, M, N, K)
+    got = to_host(qmm.mul_mat_q6_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K,
+                                   layout="repacked", algo="mfma"))
+    assert_close(got, want, terms, f"q6_K mfma M={M} N={N} K={K}")
+
+
+def test_auto_dispatch():
+    """AUTO: GEMV up to M = 8, the GEMM above (repacked), the GEMV for the
+    canonical layout at any M; every choice agrees with the oracle."""
+    N, K = 96, 2048
+    for M in (1, 8, 9, 64):
+        w, y = _case(M, N, K, 900 + M)
+        want, terms = full_reference("q6_K", w, y, M, N, K)
+        for layout in LAYOUTS:
+            got = to_host(qmm.mul_mat_q6_K(_upload(w, N, K, layout), to_dev(y.reshape(-1)), M, N, K,
+                                           layout=layout))
+            assert_close(got, want, terms, f"q6_K auto M={M} {layout}")
