@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmm_oracle.c")
 _LIB = os.path.join(_HERE, "libqmm_oracle.so")
 
-Q4_0_BYTES, Q8_0_BYTES, Q4_K_BYTES, Q8_K_BYTES, Q6_K_BYTES = 18, 34, 144, 292, 210
+Q4_0_BYTES, Q8_0_BYTES, Q4_K_BYTES, Q8_K_BYTES, Q6_K_BYTES, Q2_K_BYTES = 18, 34, 144, 292, 210, 84
 QK4_0, QK_K = 32, 256
 
 _lib = None
@@ -80,6 +80,14 @@ def _load():
         "orc_sample_q6_K_q8_K": (None, [P, P, I64, I64, I64, P, P, I64, P, P]),
         "orc_repacked_bytes_q6_K": (I64, [I64, I64]),
         "orc_repack_q6_K": (None, [P, I64, I64, P]),
+        "orc_q2_K_pack_codes": (None, [P, P]),
+        "orc_quantize_q2_K": (None, [P, I64, I64, P]),
+        "orc_dequantize_q2_K": (None, [P, I64, I64, P]),
+        "orc_mul_mat_q2_K_q8_K": (None, [P, P, I64, I64, I64, P, ctypes.c_int]),
+        "orc_q2_K_group_sums": (None, [P, P, I64, I64, I64, P]),
+        "orc_sample_q2_K_q8_K": (None, [P, P, I64, I64, I64, P, P, I64, P, P]),
+        "orc_repacked_bytes_q2_K": (I64, [I64, I64]),
+        "orc_repack_q2_K": (None, [P, I64, I64, P]),
         "orc_max_threads": (ctypes.c_int, []),
     }
     for name, (res, args) in sigs.items():
@@ -102,7 +110,7 @@ def _c(a, dtype):
 def _nblocks(fmt: str, K: int) -> tuple[int, int]:
     return {"q4_0": (K // 32, Q4_0_BYTES), "q8_0": (K // 32, Q8_0_BYTES),
             "q4_K": (K // 256, Q4_K_BYTES), "q8_K": (K // 256, Q8_K_BYTES),
-            "q6_K": (K // 256, Q6_K_BYTES)}[fmt]
+            "q6_K": (K // 256, Q6_K_BYTES), "q2_K": (K // 256, Q2_K_BYTES)}[fmt]
 
 
 def f32_to_f16(x: float) -> int:
@@ -167,19 +175,19 @@ def mul_mat(wfmt: str, w: np.ndarray, y: np.ndarray, M: int, N: int, K: int,
     y = _c(y, np.uint8)
     out = np.zeros((M, N), np.float64)
     fn = {"q4_0": "orc_mul_mat_q4_0_q8_0", "q4_K": "orc_mul_mat_q4_K_q8_K",
-          "q6_K": "orc_mul_mat_q6_K_q8_K"}[wfmt]
+          "q6_K": "orc_mul_mat_q6_K_q8_K", "q2_K": "orc_mul_mat_q2_K_q8_K"}[wfmt]
     getattr(_load(), fn)(_p(w), _p(y), M, N, K, _p(out), int(nthreads))
     return out
 
 
 def subblock_sums(wfmt: str, w: np.ndarray, y: np.ndarray, M: int, N: int, K: int):
     """int32 P[m, n, K/32] (Q4_K sub-blocks, Q4_0 blocks) or P[m, n, K/16]
-    (Q6_K 16-element groups)."""
+    (Q6_K and Q2_K 16-element groups)."""
     w = _c(w, np.uint8)
     y = _c(y, np.uint8)
-    P = np.zeros((M, N, K // (16 if wfmt == "q6_K" else 32)), np.int32)
+    P = np.zeros((M, N, K // (16 if wfmt in ("q6_K", "q2_K") else 32)), np.int32)
     fn = {"q4_0": "orc_q4_0_block_sums", "q4_K": "orc_q4_K_subblock_sums",
-          "q6_K": "orc_q6_K_group_sums"}[wfmt]
+          "q6_K": "orc_q6_K_group_sums", "q2_K": "orc_q2_K_group_sums"}[wfmt]
     getattr(_load(), fn)(_p(w), _p(y), M, N, K, _p(P))
     return P
 
@@ -195,7 +203,7 @@ def sample(wfmt: str, w: np.ndarray, y: np.ndarray, M: int, N: int, K: int,
     out = np.zeros(ms.shape, np.float64)
     terms = np.zeros(ms.shape, np.float64)
     fn = {"q4_0": "orc_sample_q4_0_q8_0", "q4_K": "orc_sample_q4_K_q8_K",
-          "q6_K": "orc_sample_q6_K_q8_K"}[wfmt]
+          "q6_K": "orc_sample_q6_K_q8_K", "q2_K": "orc_sample_q2_K_q8_K"}[wfmt]
     getattr(_load(), fn)(_p(w), _p(y), M, N, K, _p(ms), _p(ns), ms.size, _p(out), _p(terms))
     return out, terms
 
@@ -217,6 +225,15 @@ def q6_K_pack_codes(q) -> np.ndarray:
     assert q.size == 256
     out = np.zeros(192, np.uint8)
     _load().orc_q6_K_pack_codes(_p(q), _p(out))
+    return out
+
+
+def q2_K_pack_codes(q) -> np.ndarray:
+    """qs[64] bytes of 256 2-bit codes (the documented placement)."""
+    q = _c(q, np.uint8)
+    assert q.size == 256
+    out = np.zeros(64, np.uint8)
+    _load().orc_q2_K_pack_codes(_p(q), _p(out))
     return out
 
 

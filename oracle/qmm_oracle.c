@@ -693,3 +693,178 @@ void orc_repack_q6_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out) {
         memcpy(out + h0 + 64 * i, src + 128, 64);
     }
 }
+
+/* ======================================================================== */
+/* Q2_K.  P1 "更低的比特:Q6_K 与 Q2_K 的取舍": 256 2-bit values in 64 bytes,  */
+/* 16 sub-blocks (16 elements each) with a 4-bit scale and a 4-bit min,     */
+/* fp16 d and dmin: 84 B / 256 = 2.625 bpw, asymmetric like Q4_K:           */
+/*   w = d * s_j * q - dmin * m_j,  q in [0, 3],  j = element / 16.         */
+/* Readings (the page gives the fields and sizes, not the placement):      */
+/*   byte order   scales[16] @0, qs[64] @16, d @80, dmin @82;               */
+/*   scale byte j s_j in the low nibble, m_j in the high nibble (the order */
+/*                the Q4_K decode rule uses for its packed 4-bit pairs);    */
+/*   codes        element k = 128h + 32s + l sits in qs byte 32h + l,       */
+/*                bits 2s..2s+1 (BitBLAS page, "位级打包": field i of a word */
+/*                is (u >> b*i) & (2^b - 1), here with b = 2 on bytes, over */
+/*                split halves of 128 elements as the Q4_K codes use).      */
+/* Parity with llama.cpp's own Q2_K files is unpinned (no vectors here).    */
+/* ======================================================================== */
+static int q2_K_code(const uint8_t *blk, int k) {
+    int h = k / 128, sh = (k % 128) / 32, l = k % 32;
+    return (blk[16 + 32 * h + l] >> (2 * sh)) & 3;
+}
+
+void orc_q2_K_pack_codes(const uint8_t q[256], uint8_t qs[64]) {
+    memset(qs, 0, 64);
+    for (int k = 0; k < 256; ++k) {
+        int h = k / 128, sh = (k % 128) / 32, l = k % 32;
+        qs[32 * h + l] |= (uint8_t)((q[k] & 3) << (2 * sh));
+    }
+}
+
+/* Q2_K encoder (input generator), the Q4_K reading with 2-bit codes and     */
+/* 4-bit scales: per 16-element group lo = min(0, min x), hi = max x,        */
+/* sc = (hi - lo)/3, mn = -lo; d = max sc/15, dmin = max mn/15;              */
+/* s_j = rint(sc/d), m_j = rint(mn/dmin), both clamped to [0, 15]; with      */
+/* D_j = f16(d)*s_j and M_j = f16(dmin)*m_j: q = rint((x + M_j)/D_j)         */
+/* clamped to [0, 3], or 0 where D_j = 0.                                    */
+void orc_quantize_q2_K(const float *x, int64_t rows, int64_t K, uint8_t *out) {
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *xb = x + r * K + b * QK_K;
+            uint8_t *blk = out + (r * nb + b) * ORC_Q2_K_BYTES;
+            float sc[16], mn[16], maxsc = 0.0f, maxmn = 0.0f;
+            for (int j = 0; j < 16; ++j) {
+                const float *xs = xb + 16 * j;
+                float lo = xs[0], hi = xs[0];
+                for (int i = 1; i < 16; ++i) {
+                    if (xs[i] < lo) lo = xs[i];
+                    if (xs[i] > hi) hi = xs[i];
+                }
+                if (!(lo < 0.0f)) lo = 0.0f;
+                sc[j] = (hi - lo) / 3.0f;
+                mn[j] = 0.0f - lo;
+                if (sc[j] > maxsc) maxsc = sc[j];
+                if (mn[j] > maxmn) maxmn = mn[j];
+            }
+            float d = maxsc / 15.0f, dmin = maxmn / 15.0f;
+            uint8_t s[16], m[16], q[QK_K];
+            for (int j = 0; j < 16; ++j) {
+                s[j] = (uint8_t)(d > 0.0f ? clampi((int)rintf(sc[j] / d), 0, 15) : 0);
+                m[j] = (uint8_t)(dmin > 0.0f ? clampi((int)rintf(mn[j] / dmin), 0, 15) : 0);
+            }
+            uint16_t dh = orc_f32_to_f16(d), dmh = orc_f32_to_f16(dmin);
+            float df = orc_f16_to_f32(dh), dmf = orc_f16_to_f32(dmh);
+            for (int j = 0; j < 16; ++j) {
+                float Dj = df * (float)s[j], Mj = dmf * (float)m[j];
+                for (int i = 0; i < 16; ++i) {
+                    int k = 16 * j + i;
+                    q[k] = (uint8_t)(Dj > 0.0f ? clampi((int)rintf((xb[k] + Mj) / Dj), 0, 3) : 0);
+                }
+                blk[j] = (uint8_t)(s[j] | (m[j] << 4));
+            }
+            orc_q2_K_pack_codes(q, blk + 16);
+            wr_f16(blk + 80, dh);
+            wr_f16(blk + 82, dmh);
+        }
+}
+
+void orc_dequantize_q2_K(const uint8_t *w, int64_t rows, int64_t K, double *out) {
+    const int64_t nb = K / QK_K;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = w + (r * nb + b) * ORC_Q2_K_BYTES;
+            double d = rd_f16(blk + 80), dmin = rd_f16(blk + 82);
+            for (int k = 0; k < QK_K; ++k) {
+                int sj = blk[k / 16] & 15, mj = blk[k / 16] >> 4;
+                out[r * K + b * QK_K + k] = d * sj * q2_K_code(blk, k) - dmin * mj;
+            }
+        }
+}
+
+/* Integer path, the Q4_K factorization over 16-element groups (one Q8_K    */
+/* bsum per group): P_j = sum_{i in j} q_i y_i, S = sum_j s_j P_j,           */
+/* Mn = sum_j m_j bsums[j], contribution d_a * (d*S - dmin*Mn).              */
+static double q2_K_row_dot(const uint8_t *wrow, const uint8_t *yrow, int64_t nb,
+                           int32_t *P_out, double *terms) {
+    double acc = 0.0, tacc = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *wb = wrow + b * ORC_Q2_K_BYTES;
+        const uint8_t *yb = yrow + b * ORC_Q8_K_BYTES;
+        double d = rd_f16(wb + 80), dmin = rd_f16(wb + 82), da = rd_f32(yb);
+        int32_t S = 0, Mn = 0;
+        for (int j = 0; j < 16; ++j) {
+            int sj = wb[j] & 15, mj = wb[j] >> 4;
+            int32_t P = 0;
+            for (int i = 0; i < 16; ++i) {
+                int k = 16 * j + i;
+                int q = q2_K_code(wb, k);
+                int yv = (int8_t)yb[4 + k];
+                P += q * yv;
+                if (terms) tacc += fabs((d * sj * q - dmin * mj) * da * yv);
+            }
+            if (P_out) P_out[b * 16 + j] = P;
+            S += sj * P;
+            Mn += mj * (int32_t)rd_i16(yb + 260 + 2 * j);
+        }
+        acc += da * (d * (double)S - dmin * (double)Mn);
+    }
+    if (terms) *terms = tacc;
+    return acc;
+}
+
+void orc_mul_mat_q2_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                           int64_t N, int64_t K, double *out, int nthreads) {
+    const int64_t nb = K / QK_K;
+    const int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            out[m * N + n] = q2_K_row_dot(w + n * nb * ORC_Q2_K_BYTES,
+                                          y + m * nb * ORC_Q8_K_BYTES, nb, NULL, NULL);
+}
+
+void orc_q2_K_group_sums(const uint8_t *w, const uint8_t *y, int64_t M,
+                         int64_t N, int64_t K, int32_t *P) {
+    const int64_t nb = K / QK_K;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            q2_K_row_dot(w + n * nb * ORC_Q2_K_BYTES, y + m * nb * ORC_Q8_K_BYTES, nb,
+                         P + (m * N + n) * (K / 16), NULL);
+}
+
+void orc_sample_q2_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                          int64_t N, int64_t K, const int64_t *ms,
+                          const int64_t *ns, int64_t count, double *out,
+                          double *terms) {
+    const int64_t nb = K / QK_K;
+    (void)M; (void)N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = q2_K_row_dot(w + ns[i] * nb * ORC_Q2_K_BYTES,
+                              y + ms[i] * nb * ORC_Q8_K_BYTES, nb, NULL, &terms[i]);
+}
+
+/* Q2_K load-time layout (this library's own byte permutation):              */
+/*   [N*nb (d, dmin) pairs of 4 B, zero-padded to a multiple of 256 B]       */
+/*   [N*nb scales of 16 B][N*nb qs of 64 B], block (n,b) at index n*nb+b.    */
+int64_t orc_repacked_bytes_q2_K(int64_t N, int64_t K) {
+    int64_t nblk = N * (K / QK_K);
+    return (4 * nblk + 255) / 256 * 256 + 80 * nblk;
+}
+
+void orc_repack_q2_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out) {
+    const int64_t nblk = N * (K / QK_K);
+    const int64_t dsec = (4 * nblk + 255) / 256 * 256;
+    const int64_t s0 = dsec, q0 = s0 + 16 * nblk;
+    memset(out, 0, (size_t)dsec);
+    for (int64_t i = 0; i < nblk; ++i) {
+        const uint8_t *src = canon + i * ORC_Q2_K_BYTES;
+        memcpy(out + 4 * i, src + 80, 4);
+        memcpy(out + s0 + 16 * i, src, 16);
+        memcpy(out + q0 + 64 * i, src + 16, 64);
+    }
+}

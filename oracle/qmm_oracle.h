@@ -27,6 +27,10 @@
  *   Q6_K  (210 B / 256 weights) [P1 "更低的比特:Q6_K 与 Q2_K 的取舍"]
  *         +0 ql[128] (low 4 bits), +128 qh[64] (high 2 bits), +192 int8 scales[16],
  *         +208 fp16 d;  weight w = d * s_j * q, q in [-32, 31], j = element / 16
+ *   Q2_K  ( 84 B / 256 weights) [P1 "更低的比特:Q6_K 与 Q2_K 的取舍"]
+ *         +0 scales[16] (s_j low nibble, m_j high), +16 qs[64] (2-bit codes),
+ *         +80 fp16 d, +82 fp16 dmin;  weight w = d*s_j*q - dmin*m_j, q in [0, 3],
+ *         j = element / 16
  *   Q8_K  (292 B / 256 values)  [P1 "更低的比特:Q6_K 与 Q2_K 的取舍"]
  *         +0 fp32 d, +4 int8 qs[256], +260 int16 bsums[16] (sum of each 16 qs)
  *
@@ -46,6 +50,7 @@ extern "C" {
 #define ORC_Q4_K_BYTES 144
 #define ORC_Q8_K_BYTES 292
 #define ORC_Q6_K_BYTES 210
+#define ORC_Q2_K_BYTES 84
 
 /* ---- IEEE binary16 <-> binary32 (definition of the format; RNE) ---- */
 uint16_t orc_f32_to_f16(float x);
@@ -126,6 +131,24 @@ void orc_sample_q6_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
                           double *terms);
 int64_t orc_repacked_bytes_q6_K(int64_t N, int64_t K);
 void orc_repack_q6_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out);
+
+/* ---- Q2_K (scales[16] (s_j low nibble, m_j high) | qs[64] | fp16 d | fp16 dmin;
+ * w = d*s_j*q - dmin*m_j, q in [0, 3], 16-element groups j).  Byte order,
+ * code placement, encoder and layout are readings stated in qmm_oracle.c. ---- */
+void orc_q2_K_pack_codes(const uint8_t q[256], uint8_t qs[64]);
+void orc_quantize_q2_K(const float *x, int64_t rows, int64_t K, uint8_t *out);
+void orc_dequantize_q2_K(const uint8_t *w, int64_t rows, int64_t K, double *out);
+void orc_mul_mat_q2_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                           int64_t N, int64_t K, double *out, int nthreads);
+/* per-group int32 sums P[m][n][K/16] = sum_{i in group} q_i*y_i          */
+void orc_q2_K_group_sums(const uint8_t *w, const uint8_t *y, int64_t M,
+                         int64_t N, int64_t K, int32_t *P);
+void orc_sample_q2_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
+                          int64_t N, int64_t K, const int64_t *ms,
+                          const int64_t *ns, int64_t count, double *out,
+                          double *terms);
+int64_t orc_repacked_bytes_q2_K(int64_t N, int64_t K);
+void orc_repack_q2_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out);
 
 int orc_max_threads(void);
 

@@ -46,7 +46,8 @@ def test_fp16_matches_numpy_rne(orc):
 # -------------------------------------------------------------- block sizes
 def test_block_sizes(orc):
     g = _gold("block_sizes.json")
-    for fmt, K in (("q4_0", 64), ("q8_0", 64), ("q4_K", 512), ("q8_K", 512), ("q6_K", 512)):
+    for fmt, K in (("q4_0", 64), ("q8_0", 64), ("q4_K", 512), ("q8_K", 512), ("q6_K", 512),
+                   ("q2_K", 512)):
         x = np.zeros((3, K), np.float32)
         b = orc.quantize(fmt, x)
         per = g[fmt]
