@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 MALL_BYTES = 256 << 20
 METRIC = "Q4_K GEMV weight GB/s (% HBM peak); prefill GEMM int8 TOPS (% MFMA peak)"
-PREFILL = ("c5_m512", "c5_m2048", "q6K_c5_m512", "q6K_c5_m2048")
+PREFILL = ("c5_m512", "c5_m2048", "q6K_c5_m512", "q6K_c5_m2048", "q2K_c5_m512", "q2K_c5_m2048")
 
 
 def parse():
@@ -203,7 +203,7 @@ def cpu_baseline(key: str, seconds: float):
         if el >= seconds:
             break
     per = el / reps
-    wbytes = p.N * p.K * {"q4_0": 18 / 32, "q4_K": 144 / 256, "q6_K": 210 / 256}[p.wfmt]
+    wbytes = p.N * p.K * {"q4_0": 18 / 32, "q4_K": 144 / 256, "q6_K": 210 / 256, "q2_K": 84 / 256}[p.wfmt]
     if p.M <= 8:
         val, unit = wbytes / per / 1e9, "GB/s"
         sample = (f"{p.name} projection of {key} (M={M_s}, N={p.N}, K={p.K}), integer path, "
@@ -315,7 +315,7 @@ def main():
     head = measure_decode(a.workload, a.layout, a.steps, a.warmup)
     extra = {}
     if a.all:
-        for k in ("c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "q6K_down"):
+        for k in ("c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "q6K_down", "q2K_c2"):
             if k != a.workload:
                 r = measure_decode(k, a.layout, a.steps, a.warmup)
                 print(f"bench.py: {k} done", file=sys.stderr, flush=True)

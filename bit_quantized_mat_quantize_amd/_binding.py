@@ -16,13 +16,13 @@ LIB_PATH = os.path.join(PKG, "libqmm.so")
 
 # enums of include/qmm.h
 Q8_0, Q8_K = 0, 1
-Q4_0, Q4_K, Q6_K = 0, 1, 2
+Q4_0, Q4_K, Q6_K, Q2_K = 0, 1, 2, 3
 CANONICAL, REPACKED = 0, 1
 ALGO_AUTO, ALGO_GEMV, ALGO_MFMA, ALGO_SKINNY = 0, 1, 2, 3
 STATUS = {0: "QMM_OK", 1: "QMM_EINVAL", 2: "QMM_EALIGN", 3: "QMM_EUNSUPPORTED", 4: "QMM_EDEVICE"}
 
 _ACT = {"q8_0": Q8_0, "q8_K": Q8_K}
-_WEIGHT = {"q4_0": Q4_0, "q4_K": Q4_K, "q6_K": Q6_K}
+_WEIGHT = {"q4_0": Q4_0, "q4_K": Q4_K, "q6_K": Q6_K, "q2_K": Q2_K}
 _LAYOUT = {"canonical": CANONICAL, "repacked": REPACKED}
 _ALGO = {"auto": ALGO_AUTO, "gemv": ALGO_GEMV, "mfma": ALGO_MFMA, "skinny": ALGO_SKINNY}
 
@@ -57,6 +57,8 @@ def load() -> ctypes.CDLL:
         "qmm_mul_mat_q4_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_mul_mat_q6_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_mul_mat_q6_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
+        "qmm_mul_mat_q2_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
+        "qmm_mul_mat_q2_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_quantize_mul_mat": (I, [I, P, SZ, I, P, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_debug_block_sums": (I, [I, P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_status_string": (ctypes.c_char_p, [I]),
@@ -204,23 +206,36 @@ def mul_mat_q6_K(w, y, M: int, N: int, K: int, layout: str = "canonical", algo: 
     return out
 
 
-ACT_FOR = {"q4_0": "q8_0", "q4_K": "q8_K", "q6_K": "q8_K"}  # activation blocks each weight format takes
+def mul_mat_q2_K(w, y, M: int, N: int, K: int, layout: str = "canonical", algo: str = "auto",
+                 out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=y.device)
+    pw, nw = _dev(w, "w")
+    py, ny = _dev(y, "y")
+    po, no = _dev(out, "out")
+    _check(load().qmm_mul_mat_q2_K_ex(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
+                                      _ALGO[algo], _stream(stream)), "qmm_mul_mat_q2_K")
+    return out
+
+
+ACT_FOR = {"q4_0": "q8_0", "q4_K": "q8_K", "q6_K": "q8_K", "q2_K": "q8_K"}  # activation blocks each weight format takes
 
 
 def mul_mat(wfmt: str, w, y, M: int, N: int, K: int, layout: str = "canonical", out=None,
             stream=None):
     """The mul_mat entry point of weight format `wfmt` (automatic dispatch by M)."""
-    fn = {"q4_0": mul_mat_q4_0, "q4_K": mul_mat_q4_K, "q6_K": mul_mat_q6_K}[wfmt]
+    fn = {"q4_0": mul_mat_q4_0, "q4_K": mul_mat_q4_K, "q6_K": mul_mat_q6_K, "q2_K": mul_mat_q2_K}[wfmt]
     return fn(w, y, M, N, K, layout=layout, out=out, stream=stream)
 
 
 def debug_block_sums(wfmt: str, w, y, M: int, N: int, K: int, layout: str = "canonical",
                      out=None, stream=None):
     """int32 [M, N, K/32] per-sub-block (Q4_K) or per-block (Q4_0) sums, or
-    [M, N, K/16] per-group sums (Q6_K)."""
+    [M, N, K/16] per-group sums (Q6_K, Q2_K)."""
     import torch
     if out is None:
-        out = torch.empty((M, N, K // (16 if wfmt == "q6_K" else 32)), dtype=torch.int32,
+        out = torch.empty((M, N, K // (16 if wfmt in ("q6_K", "q2_K") else 32)), dtype=torch.int32,
                           device=y.device)
     pw, nw = _dev(w, "w")
     py, ny = _dev(y, "y")

@@ -3,8 +3,8 @@
 // Every entry point validates its arguments on the host before touching the
 // HIP runtime, so a bad call returns an error code, enqueues nothing and needs
 // no GPU to be tested.  Valid calls dispatch to the kernel families in
-// quantize.hip, repack.hip, gemv.hip, skinny.hip, gemm.hip, q6k.hip and
-// q6k_gemm.hip.
+// quantize.hip, repack.hip, gemv.hip, skinny.hip, gemm.hip, q6k.hip,
+// q6k_gemm.hip, q2k.hip and q2k_gemm.hip.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -31,9 +31,11 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int act_qk(qmm_act_type t) { return t == QMM_Q8_0 ? 32 : (t == QMM_Q8_K ? 256 : 0); }
 int act_bytes_per_block(qmm_act_type t) { return t == QMM_Q8_0 ? 34 : 292; }
 int w_qk(qmm_weight_type t) {
-    return t == QMM_Q4_0 ? 32 : ((t == QMM_Q4_K || t == QMM_Q6_K) ? 256 : 0);
+    return t == QMM_Q4_0 ? 32 : ((t == QMM_Q4_K || t == QMM_Q6_K || t == QMM_Q2_K) ? 256 : 0);
 }
-int w_bytes_per_block(qmm_weight_type t) { return t == QMM_Q4_0 ? 18 : (t == QMM_Q6_K ? 210 : 144); }
+int w_bytes_per_block(qmm_weight_type t) {
+    return t == QMM_Q4_0 ? 18 : (t == QMM_Q6_K ? 210 : (t == QMM_Q2_K ? 84 : 144));
+}
 
 // The MFMA kernels address the weight and the Q8_K activation matrix with
 // 32-bit buffer offsets.
@@ -116,6 +118,7 @@ size_t qmm_weight_bytes(qmm_weight_type t, qmm_layout l, int64_t N, int64_t K) {
     if (l != QMM_LAYOUT_CANONICAL && l != QMM_LAYOUT_REPACKED) return 0;
     if (t == QMM_Q4_0 && l == QMM_LAYOUT_REPACKED) return (size_t)qmm::repacked_bytes_q4_0(N, K);
     if (t == QMM_Q6_K && l == QMM_LAYOUT_REPACKED) return (size_t)qmm::repacked_bytes_q6_K(N, K);
+    if (t == QMM_Q2_K && l == QMM_LAYOUT_REPACKED) return (size_t)qmm::repacked_bytes_q2_K(N, K);
     return (size_t)(N * (K / qk) * w_bytes_per_block(t));
 }
 
@@ -150,6 +153,7 @@ qmm_status qmm_quantize_weights(qmm_weight_type t, const float *w, int64_t N, in
     uint8_t *o = static_cast<uint8_t *>(out);
     return device_status(t == QMM_Q4_K   ? qmm::launch_encode_q4_K(w, o, N, K, s)
                          : t == QMM_Q6_K ? qmm::launch_encode_q6_K(w, o, N, K, s)
+                         : t == QMM_Q2_K ? qmm::launch_encode_q2_K(w, o, N, K, s)
                                          : qmm::launch_encode_q4_0(w, o, N, K, s),
                          "quantize_weights launch");
 }
@@ -175,6 +179,7 @@ qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N,
     uint8_t *o = static_cast<uint8_t *>(w_repacked);
     return device_status(t == QMM_Q4_K   ? qmm::launch_repack_q4_K(in, o, N, K, s)
                          : t == QMM_Q6_K ? qmm::launch_repack_q6_K(in, o, N, K, s)
+                         : t == QMM_Q2_K ? qmm::launch_repack_q2_K(in, o, N, K, s)
                                          : qmm::launch_repack_q4_0(in, o, N, K, s),
                          "repack_weights launch");
 }
@@ -250,23 +255,40 @@ qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l, const v
                                stream);
 }
 
-qmm_status qmm_mul_mat_q6_K_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,
-                               size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
-                               int64_t K, qmm_algo algo, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Q6_K and Q2_K (16-element groups): a GEMV for any M while the activation
+// row fits LDS, and an MFMA GEMM for the repacked layout; AUTO takes the GEMV
+// up to M = 8.
+struct GroupedKernels {
+    const char *name;
+    int64_t gemv_max_k;
+    hipError_t (*gemv)(const uint8_t *, bool, const uint8_t *, float *, int64_t, int64_t, int64_t,
+                       hipStream_t);
+    hipError_t (*gemm)(const uint8_t *, int64_t, const uint8_t *, float *, int64_t, int64_t, int64_t,
+                       hipStream_t);
+};
+
+qmm_status mul_mat_grouped(qmm_weight_type t, const GroupedKernels &k, const void *w, size_t w_bytes,
+                           qmm_layout l, const void *y, size_t y_bytes, float *out, size_t out_bytes,
+                           int64_t M, int64_t N, int64_t K, qmm_algo algo, void *stream) {
     if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
-        return fail(QMM_EUNSUPPORTED, "Q6_K takes the GEMV or MFMA path (algo %d)", (int)algo);
-    QMM_TRY(mul_mat_common(QMM_Q6_K, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
-    const bool gemv_ok = K <= qmm::q6_K_max_k();
-    const bool mfma_ok = l == QMM_LAYOUT_REPACKED && below_4gib(QMM_Q6_K, l, M, N, K);
+        return fail(QMM_EUNSUPPORTED, "%s takes the GEMV or MFMA path (algo %d)", k.name, (int)algo);
+    QMM_TRY(mul_mat_common(t, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
+    const bool gemv_ok = K <= k.gemv_max_k;
+    const bool mfma_ok = l == QMM_LAYOUT_REPACKED && below_4gib(t, l, M, N, K);
     if (algo == QMM_ALGO_GEMV && !gemv_ok)
-        return fail(QMM_EUNSUPPORTED, "Q6_K GEMV takes K <= %lld (K = %lld)",
-                    (long long)qmm::q6_K_max_k(), (long long)K);
+        return fail(QMM_EUNSUPPORTED, "%s GEMV takes K <= %lld (K = %lld)", k.name,
+                    (long long)k.gemv_max_k, (long long)K);
     if (algo == QMM_ALGO_MFMA && !mfma_ok)
-        return fail(QMM_EUNSUPPORTED, "Q6_K MFMA path takes the repacked layout and matrices below 4 GiB");
+        return fail(QMM_EUNSUPPORTED, "%s MFMA path takes the repacked layout and matrices below 4 GiB",
+                    k.name);
     if (algo == QMM_ALGO_AUTO && !gemv_ok && !mfma_ok)
         return fail(QMM_EUNSUPPORTED,
-                    "Q6_K with K = %lld > %lld needs the repacked layout and matrices below 4 GiB",
-                    (long long)K, (long long)qmm::q6_K_max_k());
+                    "%s with K = %lld > %lld needs the repacked layout and matrices below 4 GiB", k.name,
+                    (long long)K, (long long)k.gemv_max_k);
     if (M == 0 || N == 0) return QMM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint8_t *wb = static_cast<const uint8_t *>(w);
@@ -275,17 +297,47 @@ qmm_status qmm_mul_mat_q6_K_ex(const void *w, size_t w_bytes, qmm_layout l, cons
     if (a == QMM_ALGO_AUTO)
         a = (M <= qmm::kGemvMaxM && gemv_ok) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
     if (a == QMM_ALGO_GEMV)
-        return device_status(qmm::launch_gemv_q6_K(wb, l == QMM_LAYOUT_REPACKED, yb, out, M, N, K, s),
-                             "mul_mat_q6_K gemv launch");
-    return device_status(qmm::launch_gemm_q6_K(wb, (int64_t)qmm_weight_bytes(QMM_Q6_K, l, N, K), yb,
-                                               out, M, N, K, s),
-                         "mul_mat_q6_K gemm launch");
+        return device_status(k.gemv(wb, l == QMM_LAYOUT_REPACKED, yb, out, M, N, K, s), "mul_mat gemv launch");
+    return device_status(k.gemm(wb, (int64_t)qmm_weight_bytes(t, l, N, K), yb, out, M, N, K, s),
+                         "mul_mat gemm launch");
+}
+
+GroupedKernels q6_K_kernels() {
+    return GroupedKernels{"Q6_K", qmm::q6_K_max_k(), qmm::launch_gemv_q6_K, qmm::launch_gemm_q6_K};
+}
+GroupedKernels q2_K_kernels() {
+    return GroupedKernels{"Q2_K", qmm::q2_K_max_k(), qmm::launch_gemv_q2_K, qmm::launch_gemm_q2_K};
+}
+
+}  // namespace
+
+extern "C" {
+
+qmm_status qmm_mul_mat_q6_K_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                               size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                               int64_t K, qmm_algo algo, void *stream) {
+    return mul_mat_grouped(QMM_Q6_K, q6_K_kernels(), w, w_bytes, l, y, y_bytes, out, out_bytes, M, N,
+                           K, algo, stream);
 }
 
 qmm_status qmm_mul_mat_q6_K(const void *w, size_t w_bytes, qmm_layout l, const void *y,
                             size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
                             int64_t K, void *stream) {
     return qmm_mul_mat_q6_K_ex(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, QMM_ALGO_AUTO,
+                               stream);
+}
+
+qmm_status qmm_mul_mat_q2_K_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                               size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                               int64_t K, qmm_algo algo, void *stream) {
+    return mul_mat_grouped(QMM_Q2_K, q2_K_kernels(), w, w_bytes, l, y, y_bytes, out, out_bytes, M, N,
+                           K, algo, stream);
+}
+
+qmm_status qmm_mul_mat_q2_K(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                            size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                            int64_t K, void *stream) {
+    return qmm_mul_mat_q2_K_ex(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, QMM_ALGO_AUTO,
                                stream);
 }
 
@@ -319,6 +371,7 @@ qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes
     QMM_TRY(qmm_quantize_row_q8(at, x, M, K, y, y_bytes, stream));
     if (N == 0) return QMM_OK;
     if (t == QMM_Q6_K) return qmm_mul_mat_q6_K(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream);
+    if (t == QMM_Q2_K) return qmm_mul_mat_q2_K(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream);
     return t == QMM_Q4_K ? qmm_mul_mat_q4_K(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream)
                          : qmm_mul_mat_q4_0(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream);
 }
@@ -329,11 +382,11 @@ qmm_status qmm_debug_block_sums(qmm_weight_type t, const void *w, size_t w_bytes
     if (!w_qk(t)) return fail(QMM_EUNSUPPORTED, "unknown weight type %d", (int)t);
     QMM_TRY(mul_mat_common(t, w, w_bytes, l, y, y_bytes, reinterpret_cast<const float *>(P),
                            p_bytes, M, N, K));
-    if (t == QMM_Q6_K && K > qmm::q6_K_max_k())
-        return fail(QMM_EUNSUPPORTED, "Q6_K takes K <= %lld (K = %lld)", (long long)qmm::q6_K_max_k(),
-                    (long long)K);
+    if ((t == QMM_Q6_K || t == QMM_Q2_K) && K > qmm::q8k_group_max_k())
+        return fail(QMM_EUNSUPPORTED, "group sums take K <= %lld (K = %lld)",
+                    (long long)qmm::q8k_group_max_k(), (long long)K);
     if (M == 0 || N == 0) return QMM_OK;
-    const int64_t group = t == QMM_Q6_K ? 16 : 32;
+    const int64_t group = (t == QMM_Q6_K || t == QMM_Q2_K) ? 16 : 32;
     QMM_TRY(check_size("P", p_bytes, (size_t)(M * N * (K / group)) * sizeof(int32_t)));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool rep = l == QMM_LAYOUT_REPACKED;
@@ -341,6 +394,7 @@ qmm_status qmm_debug_block_sums(qmm_weight_type t, const void *w, size_t w_bytes
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     return device_status(t == QMM_Q4_K   ? qmm::launch_block_sums_q4_K(wb, rep, yb, P, M, N, K, s)
                          : t == QMM_Q6_K ? qmm::launch_group_sums_q6_K(wb, rep, yb, P, M, N, K, s)
+                         : t == QMM_Q2_K ? qmm::launch_group_sums_q2_K(wb, rep, yb, P, M, N, K, s)
                                          : qmm::launch_block_sums_q4_0(wb, rep, yb, P, M, N, K, s),
                          "debug_block_sums launch");
 }

@@ -1,0 +1,267 @@
+// q2k_gemm.hip -- Q2_K weights x Q8_K activations on int8 MFMA (prefill-sized
+// M), gfx950, for the load-time (repacked) weight layout.
+//
+// Format and integer path: ggml-cpu mul_mat page, "更低的比特:Q6_K 与 Q2_K 的取舍"
+// (2-bit codes, 4-bit scale and min per 16-element group, fp16 d and dmin),
+// "正确性:缩放系数可以提到求和号外面" and "min 项与最终归约":
+//   per super-block b, output (m, n):
+//     S  = sum_j s_j * sum_{i in j} q_i y_i,   Mn = sum_j m_j * bsums_j,
+//     acc += d_a * (d * S - dmin * Mn).
+//
+// Tiling as in the Q6_K GEMM: 512 threads = 8 wavefronts, tile 128 (M) x 256
+// (N), wavefront w owns the 32-column tile 32w..32w+31 for all four 32-row
+// tiles, K advances one super-block per step; the int8 activation tile, its
+// bsums (as fp16) and d_a are double-buffered in LDS (direct global->LDS
+// loads for the codes), and each lane loads the 52 bytes of its column it
+// needs straight into registers, one step ahead.
+//
+// In v_mfma_i32_32x32x32_i8 lane l supplies the 16 consecutive elements
+// 16*(l/32).. of a 32-element chunk -- one Q2_K group -- so the group scale is
+// one value per lane, and s_j * q <= 15 * 3 = 45 fits an int8 operand: the
+// scale is folded into the weight bytes with one packed 16-bit multiply per
+// four codes (no byte product reaches 256, so no carry crosses a byte), and
+// one MFMA per chunk accumulates S exactly.  The min term is a 16-long
+// contraction per (m, n) on one fp16 MFMA (v_mfma_f32_32x32x16_f16, K = 16 =
+// the groups of a super-block): m_j and bsums_j (|.| <= 2032) are exact in
+// fp16 and |Mn| < 2^24, so Mn is exact.
+#include "mfma_common.h"
+#include "qmm_device.h"
+#include "qmm_launch.h"
+
+namespace qmm {
+namespace {
+
+constexpr int BM = 128, BN = 256, MT = BM / 32, NWAVE = 8, NTHR = 64 * NWAVE;
+constexpr int A_OFF = 0, A_BYTES = BM * 256;
+constexpr int BS_OFF = A_OFF + A_BYTES, BS_STRIDE = 48, BS_BYTES = BM * BS_STRIDE;
+constexpr int DA_OFF = BS_OFF + BS_BYTES, DA_BYTES = BM * 4;
+constexpr int BUF_BYTES = DA_OFF + DA_BYTES;
+constexpr int LDS_BYTES = 2 * BUF_BYTES;
+constexpr int A_INSTR = A_BYTES / 1024;  // 64-lane x 16-byte loads per buffer
+constexpr int A_PER_WAVE = A_INSTR / NWAVE;
+static_assert(A_INSTR % NWAVE == 0, "activation staging must split evenly over the wavefronts");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
+static_assert(BN == 32 * NWAVE && 2 * BM <= NTHR, "one column tile per wavefront; bsums staged by 2*BM threads");
+
+// The weight side of one super-block for lane (column c, slice h): the qs
+// pieces h and h + 2 (four 2-bit fields each), the 16 scale/min bytes and
+// fp16 d | fp16 dmin << 16.
+struct Q2KStage {
+    uint4 qa, qb;
+    uint4 sc;
+    uint32_t dm;
+};
+
+__global__ __launch_bounds__(NTHR, 1) void k_gemm_q2_K(const uint8_t *__restrict__ W, int64_t w_bytes,
+                                                       const uint8_t *__restrict__ Y,
+                                                       float *__restrict__ out, int64_t M, int64_t N,
+                                                       int64_t K, int tiles_m, int tiles_n) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hh = lane >> 5;
+
+    // XCD-aware tile order (as in the Q4_K GEMM): each XCD gets a contiguous
+    // range of v, and v walks groups of GM row tiles with the row tile fastest.
+    constexpr int GM = 4;
+    const int nwg = tiles_m * tiles_n;
+    const int bid = blockIdx.x;
+    const int v = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+    const int group = v / (GM * tiles_n), first_m = group * GM;
+    const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;
+    const int in_group = v - group * GM * tiles_n;
+    // (the division runs on the vector ALU; readfirstlane keeps the tile uniform)
+    const int tile_m = __builtin_amdgcn_readfirstlane(first_m + in_group % gm);
+    const int tile_n = __builtin_amdgcn_readfirstlane(in_group / gm);
+    const int64_t m_base = (int64_t)tile_m * BM, n_base = (int64_t)tile_n * BN;
+    const int64_t nb = K / QK_K;
+
+    // ---- activation staging (rows past M clamped to the last valid one)
+    const int m_last = (int)(M - 1 - m_base < BM - 1 ? M - 1 - m_base : BM - 1);
+    const uint32_t a_rowstride = (uint32_t)(nb * kQ8_KBytes);
+    const int64_t a_first = m_base * nb * kQ8_KBytes;
+    const int64_t a_bytes = M * nb * kQ8_KBytes - a_first;
+    uint32_t a_goff[A_PER_WAVE];
+#pragma unroll
+    for (int t = 0; t < A_PER_WAVE; ++t) {
+        const int row = (wave * A_PER_WAVE + t) * 4 + (lane >> 4);
+        const int gp = (lane & 15) ^ (row & 15);  // global piece stored at position lane & 15
+        const int rr = row < m_last ? row : m_last;
+        a_goff[t] = (uint32_t)rr * a_rowstride + 4 + 16 * gp;
+    }
+    // bsums: row tid>>1, 16-byte half tid&1 (threads < 256); d_a: row tid (threads < 128)
+    const int s_row = (tid >> 1) & (BM - 1);
+    const uint32_t s_off = (uint32_t)(s_row < m_last ? s_row : m_last) * a_rowstride + 260 + 16 * (tid & 1);
+    const uint32_t d_off = (uint32_t)((tid & (BM - 1)) < m_last ? (tid & (BM - 1)) : m_last) * a_rowstride;
+
+    // ---- this lane's weight column (columns past N clamped; never stored)
+    const int64_t NB = N * nb;
+    const int64_t dsec = (4 * NB + 255) / 256 * 256;
+    const int64_t n_lane = n_base + wave * 32 + l32 < N ? n_base + wave * 32 + l32 : N - 1;
+    const int64_t i0 = n_lane * nb;  // block index of the column's first super-block
+    const uint32_t v_dm = (uint32_t)(4 * i0);
+    const uint32_t v_sc = (uint32_t)(dsec + 16 * i0);
+    const uint32_t v_qs = (uint32_t)(dsec + 16 * NB + 64 * i0 + 16 * hh);
+
+    auto issue = [&](int64_t b, uint8_t *buf) {
+        const rsrc_t ra = make_rsrc(Y + a_first, a_bytes);
+        const uint32_t sa = (uint32_t)b * kQ8_KBytes;
+#pragma unroll
+        for (int t = 0; t < A_PER_WAVE; ++t)
+            dma16(ra, a_goff[t], sa, buf + A_OFF + (wave * A_PER_WAVE + t) * 1024);
+    };
+    auto prefetch = [&](int64_t b, uint4 &raw, uint32_t &draw) {
+        const rsrc_t ra = make_rsrc(Y + a_first, a_bytes);
+        const uint32_t sa = (uint32_t)b * kQ8_KBytes;
+        if (tid < 2 * BM) {
+            const u32x4 vv = __builtin_amdgcn_raw_buffer_load_b128(ra, s_off, sa, 0);
+            raw = make_uint4(vv.x, vv.y, vv.z, vv.w);
+        }
+        if (tid < BM) draw = __builtin_amdgcn_raw_buffer_load_b32(ra, d_off, sa, 0);
+    };
+    auto commit = [&](const uint4 &raw, uint32_t draw, uint8_t *buf) {
+        if (tid < 2 * BM) {
+            const uint4 hv = make_uint4(h2_bits((int16_t)(raw.x & 0xffff), (int16_t)(raw.x >> 16)),
+                                        h2_bits((int16_t)(raw.y & 0xffff), (int16_t)(raw.y >> 16)),
+                                        h2_bits((int16_t)(raw.z & 0xffff), (int16_t)(raw.z >> 16)),
+                                        h2_bits((int16_t)(raw.w & 0xffff), (int16_t)(raw.w >> 16)));
+            *reinterpret_cast<uint4 *>(buf + BS_OFF + s_row * BS_STRIDE + 16 * (tid & 1)) = hv;
+        }
+        if (tid < BM) *reinterpret_cast<uint32_t *>(buf + DA_OFF + 4 * tid) = draw;
+    };
+    auto wload = [&](int64_t b, Q2KStage &x) {
+        const rsrc_t rw = make_rsrc(W, w_bytes);
+        const uint32_t bb = (uint32_t)b;
+        x.qa = bld16(rw, v_qs, 64 * bb);
+        x.qb = bld16(rw, v_qs + 32, 64 * bb);
+        x.sc = bld16(rw, v_sc, 16 * bb);
+        x.dm = __builtin_amdgcn_raw_buffer_load_b32(rw, v_dm, 4 * bb, 0);
+    };
+
+    float acc[MT][16];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    uint32_t draw = 0;
+    Q2KStage wx;
+    issue(0, lds);
+    prefetch(0, raw, draw);
+    wload(0, wx);
+
+    for (int64_t b = 0; b < nb; ++b) {
+        uint8_t *buf = lds + (b & 1) * BUF_BYTES;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of step b
+        commit(raw, draw, buf);
+
+        // ---------------- decode: chunk c holds group G = 2c + hh of this lane,
+        // elements 128(c/4) + 32(c%4) + 16hh + i: qs piece (c/4)*2 + hh, field c%4
+        const float dcol = f16_bits_to_f32(wx.dm & 0xffff);
+        const float dmneg = -f16_bits_to_f32(wx.dm >> 16);
+        const uint32_t sw[4] = {wx.sc.x, wx.sc.y, wx.sc.z, wx.sc.w};
+        v4i bq[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint4 pc = c < 4 ? wx.qa : wx.qb;
+            const int sh = 2 * (c & 3);
+            // scale byte 2c + hh: dword c/2, byte 2(c%2) + hh; s_j is its low nibble
+            const uint32_t sj = (sw[c >> 1] >> (16 * (c & 1) + 8 * hh)) & 15;
+            const uint32_t s2 = sj * 0x00010001u;
+            bq[c] = v4i{plane((pc.x >> sh) & 0x03030303u, s2), plane((pc.y >> sh) & 0x03030303u, s2),
+                        plane((pc.z >> sh) & 0x03030303u, s2), plane((pc.w >> sh) & 0x03030303u, s2)};
+        }
+        // mins of groups 8hh..8hh+7 as fp16 (the B operand of the Mn contraction)
+        v8h bmn;
+        {
+            const uint32_t m_lo = hh ? sw[2] : sw[0], m_hi = hh ? sw[3] : sw[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bmn[e] = (_Float16)(float)((m_lo >> (8 * e + 4)) & 15);
+                bmn[4 + e] = (_Float16)(float)((m_hi >> (8 * e + 4)) & 15);
+            }
+        }
+
+        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
+        if (b + 1 < nb) {
+            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
+            prefetch(b + 1, raw, draw);
+            wload(b + 1, wx);
+        }
+        const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
+
+        // ---------------- the four row tiles of this column tile
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int row = i * 32 + l32;
+            const v16i zero = {};
+            v16i as;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                v4i a_op[4];
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int c = 4 * half + cc;
+                    const uint4 a = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * 256 +
+                                                                     16 * ((2 * c + hh) ^ (row & 15)));
+                    a_op[cc] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+                }
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int c = 4 * half + cc;
+                    as = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[cc], bq[c], c ? as : zero, 0, 0, 0);
+                }
+            }
+            v8h a_bs;
+            {
+                const uint4 au = *reinterpret_cast<const uint4 *>(buf + BS_OFF + row * BS_STRIDE + 16 * hh);
+                __builtin_memcpy(&a_bs, &au, 16);
+            }
+            const v16f zf = {};
+            const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmn, zf, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q + e;
+                    const float t = fmaf(dcol, (float)as[r], dmneg * mn[r]);
+                    acc[i][r] = fmaf(dv[e], t, acc[i][r]);
+                }
+            }
+        }
+    }
+
+    // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
+    const int64_t n = n_base + wave * 32 + l32;
+    if (n < N) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m_base + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (m < M) out[m * N + n] = acc[i][r];
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    static bool attr_set = false;  // the LDS budget above 64 KiB must be opted into once
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_q2_K,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    hipLaunchKernelGGL(k_gemm_q2_K, dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), LDS_BYTES, s,
+                       w, w_bytes, y, out, M, N, K, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace qmm

@@ -21,6 +21,7 @@
 //   [fp16 d of every block, zero-padded to a multiple of 256 B]
 //   [scales, 16 B each][ql, 128 B each][qh, 64 B each]
 // so every 16-byte piece a lane loads is aligned.
+#include "q8k_row.h"
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(256) void k_repack_q6_K(const uint8_t *__restrict__
 // pieces 2g + h (g = 0..3, both nibbles) and the qh pieces h and h + 2 --
 // 96 bytes that no other unit reads -- i.e. the 16-element groups 4g + h
 // (low nibbles) and 4g + 2 + h (high nibbles).  One wavefront per output row,
-// lane l takes units l, l + 64, ...; the activation row is staged in LDS as
-// qs[K] | d[nb] (padded to 16 B) | bsums[nb][16] | 16-byte trash slot.
+// lane l takes units l, l + 64, ...; the activation row is staged in LDS
+// (q8k_row.h).
 // ---------------------------------------------------------------------------
 template <bool REPACKED>
 struct Q6KAddr {
@@ -218,33 +219,6 @@ __device__ __forceinline__ void q6k_group_sums(const Q6KUnit &x, int u, const ui
     }
 }
 
-__host__ __device__ constexpr int64_t q6k_lds_bytes(int64_t K) {
-    return K + ((K / QK_K) * 4 + 15) / 16 * 16 + (K / QK_K) * 32 + 16;
-}
-
-// Stage activation row m into LDS (branch-free loads; spare threads store to
-// the trash slot), then barrier.
-__device__ __forceinline__ void q6k_stage_row(const uint8_t *__restrict__ Yrow, int64_t K,
-                                              uint8_t *ys) {
-    const int64_t nb = K / QK_K;
-    const int nq = (int)(K / 16), nbs = (int)(nb * 2);
-    uint8_t *s_qs = ys;
-    uint8_t *s_d = ys + K;
-    uint8_t *s_bs = ys + K + (nb * 4 + 15) / 16 * 16;
-    uint8_t *trash = s_bs + nb * 32;
-    const int tid = threadIdx.x;
-    for (int pc = tid; pc < nq; pc += 256)
-        *reinterpret_cast<uint4 *>(s_qs + 16 * pc) =
-            ld_align4<uint4>(Yrow + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
-    for (int q = tid; q < nbs; q += 256)
-        *reinterpret_cast<uint4 *>(s_bs + 16 * q) =
-            ld_align4<uint4>(Yrow + (q >> 1) * kQ8_KBytes + 260 + 16 * (q & 1));
-    for (int q = tid; q < nb; q += 256)
-        *reinterpret_cast<float *>(s_d + 4 * q) = ld_align4<float>(Yrow + q * kQ8_KBytes);
-    (void)trash;
-    __syncthreads();
-}
-
 constexpr int kQ6Waves = 4;
 
 // MODE 0: out[m*N + n] (fp32).  MODE 1: P[m][n][K/16] (int32 group sums).
@@ -268,10 +242,10 @@ __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W
         const int u = lane + 64 * it;
         q6k_load<REPACKED>(A, nn, nb, u < nunits ? u : nunits - 1, x[it]);
     }
-    q6k_stage_row(Y + m * nb * kQ8_KBytes, K, ys);
-    const uint8_t *s_qs = ys;
-    const float *s_d = reinterpret_cast<const float *>(ys + K);
-    const int16_t *s_bs = reinterpret_cast<const int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
+    const Q8KRowLds row = stage_q8k_row<256>(Y + m * nb * kQ8_KBytes, K, ys);
+    const uint8_t *s_qs = row.qs;
+    const float *s_d = row.d;
+    const int16_t *s_bs = row.bsums;
 
     float acc = 0.0f;
     for (int base = 0; base < nunits; base += 64 * kNit) {
@@ -322,7 +296,7 @@ hipError_t dispatch_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, void
     const int64_t nunits = 2 * (K / QK_K);
     const int64_t nit = (nunits + 63) / 64;
     const dim3 grid((unsigned)((N + kQ6Waves - 1) / kQ6Waves), (unsigned)M);  // M <= 65535
-    const unsigned lds = (unsigned)q6k_lds_bytes(K);
+    const unsigned lds = (unsigned)q8k_row_lds_bytes(K);
 #define QMM_Q6(NIT)                                                                                \
     do {                                                                                           \
         if (repacked)                                                                              \
@@ -344,12 +318,7 @@ int64_t repacked_bytes_q6_K(int64_t N, int64_t K) {
     return (2 * nblk + 255) / 256 * 256 + 208 * nblk;
 }
 
-int64_t q6_K_max_k() {
-    // the activation row must fit the 64 KiB of LDS a workgroup gets by default
-    int64_t k = 0;
-    while (q6k_lds_bytes(k + QK_K) <= 60 * 1024) k += QK_K;
-    return k;
-}
+int64_t q6_K_max_k() { return q8k_row_max_k(); }  // the staged activation row fits LDS
 
 hipError_t launch_encode_q6_K(const float *w, uint8_t *out, int64_t N, int64_t K, hipStream_t s) {
     const int64_t nb = K / QK_K, total = N * nb;

@@ -1,0 +1,52 @@
+// q8k_row.h -- one Q8_K activation row staged in LDS for the GEMVs whose
+// weights use 16-element groups (Q6_K, Q2_K): one Q8_K bsum per group.
+//
+// LDS layout: qs[K] | d[nb] (padded to 16 B) | bsums[nb][16] | 16-byte trash
+// slot.  The row must fit the 64 KiB a workgroup gets by default.
+#pragma once
+
+#include "qmm_device.h"
+
+namespace qmm {
+
+__host__ __device__ constexpr int64_t q8k_row_lds_bytes(int64_t K) {
+    return K + ((K / QK_K) * 4 + 15) / 16 * 16 + (K / QK_K) * 32 + 16;
+}
+
+// Largest K (a multiple of 256) whose staged row fits 60 KiB.
+inline int64_t q8k_row_max_k() {
+    int64_t k = 0;
+    while (q8k_row_lds_bytes(k + QK_K) <= 60 * 1024) k += QK_K;
+    return k;
+}
+
+struct Q8KRowLds {
+    const uint8_t *qs;
+    const float *d;
+    const int16_t *bsums;
+};
+
+// Stage activation row Yrow into ys with `nthreads` threads (branch-free
+// loads, 16 bytes per thread and trip), then barrier.
+template <int kThreads>
+__device__ __forceinline__ Q8KRowLds stage_q8k_row(const uint8_t *__restrict__ Yrow, int64_t K,
+                                                   uint8_t *ys) {
+    const int64_t nb = K / QK_K;
+    const int nq = (int)(K / 16), nbs = (int)(nb * 2);
+    uint8_t *s_qs = ys;
+    uint8_t *s_d = ys + K;
+    uint8_t *s_bs = ys + K + (nb * 4 + 15) / 16 * 16;
+    const int tid = threadIdx.x;
+    for (int pc = tid; pc < nq; pc += kThreads)
+        *reinterpret_cast<uint4 *>(s_qs + 16 * pc) =
+            ld_align4<uint4>(Yrow + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
+    for (int q = tid; q < nbs; q += kThreads)
+        *reinterpret_cast<uint4 *>(s_bs + 16 * q) =
+            ld_align4<uint4>(Yrow + (q >> 1) * kQ8_KBytes + 260 + 16 * (q & 1));
+    for (int q = tid; q < nb; q += kThreads)
+        *reinterpret_cast<float *>(s_d + 4 * q) = ld_align4<float>(Yrow + q * kQ8_KBytes);
+    __syncthreads();
+    return Q8KRowLds{s_qs, reinterpret_cast<const float *>(s_d), reinterpret_cast<const int16_t *>(s_bs)};
+}
+
+}  // namespace qmm

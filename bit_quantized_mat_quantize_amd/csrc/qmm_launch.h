@@ -50,12 +50,27 @@ hipError_t launch_gemv_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, f
 hipError_t launch_group_sums_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
                                   int64_t M, int64_t N, int64_t K, hipStream_t s);
 
+// Q2_K (encoder, load-time repack, GEMV for any M with K <= q2_K_max_k(),
+// int32 group sums P[m][n][K/16] of the same decode path).
+int64_t repacked_bytes_q2_K(int64_t N, int64_t K);
+int64_t q2_K_max_k();
+hipError_t launch_encode_q2_K(const float *w, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_repack_q2_K(const uint8_t *in, uint8_t *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemv_q2_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_group_sums_q2_K(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t s);
+// both group-sum paths stage one activation row in LDS
+inline int64_t q8k_group_max_k() { return q6_K_max_k() < q2_K_max_k() ? q6_K_max_k() : q2_K_max_k(); }
+
 // MFMA GEMM family (any M >= 1; weight and activation matrices below 4 GiB:
-// 32-bit buffer offsets).  The Q6_K GEMM takes the repacked layout of
-// w_bytes bytes.
+// 32-bit buffer offsets).  The Q6_K and Q2_K GEMMs take the repacked layout
+// of w_bytes bytes.
 hipError_t launch_gemm_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_q6_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemm_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
 
 constexpr int kGemvMaxM = 8;

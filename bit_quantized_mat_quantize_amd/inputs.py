@@ -65,7 +65,7 @@ def activations(seed, m: int, k: int, outlier_frac: float = 0.0,
 class Projection:
     """One weight matrix [N, K] in format `wfmt` and its activations [M, K]."""
     name: str
-    wfmt: str           # "q4_0", "q4_K" or "q6_K"
+    wfmt: str           # "q4_0", "q4_K", "q6_K" or "q2_K"
     M: int
     N: int
     K: int
@@ -92,7 +92,7 @@ class Workload:
 
     @property
     def weight_bytes(self) -> int:
-        per = {"q4_0": 18 / 32, "q4_K": 144 / 256, "q6_K": 210 / 256}
+        per = {"q4_0": 18 / 32, "q4_K": 144 / 256, "q6_K": 210 / 256, "q2_K": 84 / 256}
         return int(sum(p.N * p.K * per[p.wfmt] for p in self.projections))
 
     @property
@@ -112,6 +112,8 @@ def workload(key: str) -> Workload:
     q6K_down  Q6_K x Q8_K GEMV, M=1, N=4096, K=14336 (the FFN down projection,
               the matrix 4-bit model files commonly keep at 6 bits)
     q6K_c5_m{512,2048}  Q6_K prefill on the c5 shapes (N=28672, K=8192)
+    q2K_c2    Q2_K x Q8_K GEMV, M=1, N=K=4096, the weights of c2 in 2-bit form
+    q2K_c5_m{512,2048}  Q2_K prefill on the c5 shapes
     """
     if key == "c1":
         return Workload(key, "Q4_0xQ8_0 GEMV M=1 N=256 K=1024", [
@@ -145,8 +147,17 @@ def workload(key: str) -> Workload:
         assert m in (512, 2048)
         return Workload(key, f"Q6_K prefill M={m} N=28672 K=8192", [
             Projection("w", "q6_K", m, 28672, 8192, 5, [105, m], outliers=0.01)])
+    if key == "q2K_c2":
+        return Workload(key, "Q2_KxQ8_K GEMV M=1 N=4096 K=4096", [
+            Projection("w", "q2_K", 1, 4096, 4096, 2, 102)])
+    if key.startswith("q2K_c5_m"):
+        m = int(key[8:])
+        assert m in (512, 2048)
+        return Workload(key, f"Q2_K prefill M={m} N=28672 K=8192", [
+            Projection("w", "q2_K", m, 28672, 8192, 5, [105, m], outliers=0.01)])
     raise KeyError(key)
 
 
 ALL_WORKLOADS = ["c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "c5_m512", "c5_m2048",
-                 "q6K_c2", "q6K_down", "q6K_c5_m512", "q6K_c5_m2048"]
+                 "q6K_c2", "q6K_down", "q6K_c5_m512", "q6K_c5_m2048",
+                 "q2K_c2", "q2K_c5_m512", "q2K_c5_m2048"]

@@ -1,6 +1,6 @@
 /*
- * qmm.h -- C ABI of libqmm: quantized mul_mat (Q4_0 / Q4_K weights times
- * Q8_0 / Q8_K activations) on AMD Instinct MI355X (gfx950).
+ * qmm.h -- C ABI of libqmm: quantized mul_mat (Q4_0 / Q4_K / Q6_K / Q2_K weights
+ * times Q8_0 / Q8_K activations) on AMD Instinct MI355X (gfx950).
  *
  * Operation (BitBLAS page, "从数学表达式到真实存储:混合精度 GEMM 的计算对象";
  * ggml-cpu mul_mat page, "mul_mat:一次矩阵乘被切成什么样"):
@@ -29,6 +29,12 @@
  *                     4 bits in ql byte 32g + r%32 (low nibble for r < 32, else
  *                     high) and its high 2 bits in qh byte r, bits 2g..2g+1; the
  *                     stored code is q + 32
+ *   Q2_K  84 B / 256: scales[16] | qs[64] | fp16 d | fp16 dmin (same section: 2-bit
+ *                     codes, a 4-bit scale and a 4-bit min per 16-element group);
+ *                     w = d*s_j*q - dmin*m_j, q in [0, 3], j = element / 16.
+ *                     Placement (this library's reading): scale byte j = s_j (low
+ *                     nibble) | m_j << 4; element k = 128h + 32s + l sits in qs
+ *                     byte 32h + l, bits 2s..2s+1
  *   Q8_K 292 B / 256: fp32 d; int8 qs[256]; int16 bsums[16] (sum of qs[16g..16g+15])
  *   Rows are arrays of blocks: row r of a [R, K] matrix starts at r * (K/QK) * bytes.
  *
@@ -41,6 +47,8 @@
  *         [N*nb payloads of 16 B: qs]
  *   Q6_K: [N*nb fp16 d, zero-padded to a multiple of 256 B] then [N*nb scales of
  *         16 B] then [N*nb ql of 128 B] then [N*nb qh of 64 B]
+ *   Q2_K: [N*nb (d, dmin) pairs of 4 B, zero-padded to a multiple of 256 B] then
+ *         [N*nb scales of 16 B] then [N*nb qs of 64 B]
  *   (nb = blocks per row).  The payload stream is 16-byte aligned, which lets a
  *   wavefront read weights with coalesced 16-byte loads.
  *
@@ -79,21 +87,21 @@ typedef enum {
 } qmm_status;
 
 typedef enum { QMM_Q8_0 = 0, QMM_Q8_K = 1 } qmm_act_type;
-typedef enum { QMM_Q4_0 = 0, QMM_Q4_K = 1, QMM_Q6_K = 2 } qmm_weight_type;
+typedef enum { QMM_Q4_0 = 0, QMM_Q4_K = 1, QMM_Q6_K = 2, QMM_Q2_K = 3 } qmm_weight_type;
 typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
 
-/* Kernel family for a mul_mat call (Q4_K and Q6_K; Q4_0 always uses GEMV):
+/* Kernel family for a mul_mat call (Q4_K, Q6_K, Q2_K; Q4_0 always uses GEMV):
  *   GEMV    vector int8 dot products, one wavefront per output row (Q4_K:
- *           M <= 8; Q6_K: any M, K <= 53760)
+ *           M <= 8; Q6_K and Q2_K: any M, K <= 53760)
  *   SKINNY  small-batch int8 MFMA, one 32-column tile per workgroup, K split
  *           over its wavefronts (Q4_K only; M <= 32)
  *   MFMA    prefill GEMM on int8 MFMA, 128 x 256 output tiles (any M; Q6_K
- *           needs the repacked layout)
+ *           and Q2_K need the repacked layout)
  * SKINNY and MFMA address the weight and activation matrices with 32-bit
  * offsets, so both must be below 4 GiB.  AUTO for Q4_K takes GEMV for M = 1,
  * SKINNY for 2 <= M <= 32, MFMA above (GEMV in groups of 8 rows where the
- * size limit rules the MFMA kernels out); for Q6_K it takes GEMV for M <= 8
- * and MFMA above, GEMV where MFMA is ruled out. */
+ * size limit rules the MFMA kernels out); for Q6_K and Q2_K it takes GEMV for
+ * M <= 8 and MFMA above, GEMV where MFMA is ruled out. */
 typedef enum {
     QMM_ALGO_AUTO = 0,
     QMM_ALGO_GEMV = 1,
@@ -106,8 +114,8 @@ typedef enum {
 size_t qmm_act_bytes(qmm_act_type t, int64_t M, int64_t K);
 
 /* Bytes of an [N, K] weight matrix in format t and layout l.  Canonical:
- * N*K/32*18, N*K/256*144 or N*K/256*210 (Q6_K).  Repacked Q4_0 and Q6_K add the
- * padding of their d section (at most 254 B).  Returns 0 for invalid
+ * N*K/32*18, N*K/256*144, N*K/256*210 (Q6_K) or N*K/256*84 (Q2_K).  Repacked
+ * Q4_0, Q6_K and Q2_K add the padding of their d section (at most 252 B).  Returns 0 for invalid
  * arguments. */
 size_t qmm_weight_bytes(qmm_weight_type t, qmm_layout l, int64_t N, int64_t K);
 
@@ -131,6 +139,9 @@ qmm_status qmm_quantize_row_q8(qmm_act_type t, const float *x, int64_t M, int64_
  *   Q6_K: per 16-element group xm = signed element of largest |x| (first
  *         wins), sc = xm/-32; d = max |sc|/127; s_j = rint(sc/d) in [-127, 127];
  *         q = clamp(rint(x/(f16(d)*s_j)), -32, 31), 0 where f16(d)*s_j = 0
+ *   Q2_K: the Q4_K rule per 16-element group with 2-bit codes and 4-bit
+ *         scales: sc = (max x - lo)/3, d = max sc/15, dmin = max mn/15,
+ *         s_j, m_j clamped to 15, q clamped to [0, 3]
  * out: device, out_bytes >= qmm_weight_bytes(t, CANONICAL, N, K). */
 qmm_status qmm_quantize_weights(qmm_weight_type t, const float *w, int64_t N, int64_t K,
                                 void *out, size_t out_bytes, void *stream);
@@ -190,8 +201,27 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l,
                                int64_t M, int64_t N, int64_t K, qmm_algo algo,
                                void *stream);
 
+/* out[m*N+n] = sum over super-blocks b of d_a*(d*S - dmin*Mn) with
+ * S = sum_j s_j*P_j, P_j = sum_{i in j} q_i*y_i and Mn = sum_j m_j*bsums[j] over
+ * the 16-element groups j (ggml-cpu mul_mat page, "更低的比特:Q6_K 与 Q2_K 的取舍",
+ * "正确性:缩放系数可以提到求和号外面", "min 项与最终归约").  fp32 output,
+ * overwritten.  w: Q2_K [N,K] in layout l; y: Q8_K [M,K].  Kernel choice and
+ * limits as for qmm_mul_mat_q6_K. */
+qmm_status qmm_mul_mat_q2_K(const void *w, size_t w_bytes, qmm_layout l,
+                            const void *y, size_t y_bytes,
+                            float *out, size_t out_bytes,
+                            int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Same as qmm_mul_mat_q2_K with an explicit kernel family, with the rules of
+ * qmm_mul_mat_q6_K_ex. */
+qmm_status qmm_mul_mat_q2_K_ex(const void *w, size_t w_bytes, qmm_layout l,
+                               const void *y, size_t y_bytes,
+                               float *out, size_t out_bytes,
+                               int64_t M, int64_t N, int64_t K, qmm_algo algo,
+                               void *stream);
+
 /* Quantize-and-multiply in one call: y = quantize_row_q8(x) (Q8_0 for t = Q4_0,
- * Q8_K for t = Q4_K and Q6_K), then out = mul_mat(w, y).  The ggml-cpu mul_mat page
+ * Q8_K for t = Q4_K, Q6_K and Q2_K), then out = mul_mat(w, y).  The ggml-cpu mul_mat page
  * ("激活量化重复与融合") notes that quantizing the activations once at the
  * start of a fused node saves both the launch and the repeated conversion;
  * here, for Q4_K with M == 1 and K <= 8192, the quantization runs inside the
@@ -210,10 +240,11 @@ qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes
                                 int64_t M, int64_t N, int64_t K, void *stream);
 
 /* Verification aid: the int32 per-sub-block (Q4_K) or per-block (Q4_0) sums
- * P[m][n][K/32] = sum_{i in block} q_i*y_i  (Q4_0: (q_i-8)*y_i), or for Q6_K the
- * per-group sums P[m][n][K/16] of its signed codes, computed by the same decode
- * and int8 dot-product code the GEMV kernels use.
- * P: device int32, p_bytes >= M*N*(K/32)*4 (Q6_K: M*N*(K/16)*4). */
+ * P[m][n][K/32] = sum_{i in block} q_i*y_i  (Q4_0: (q_i-8)*y_i), or for Q6_K
+ * and Q2_K the per-group sums P[m][n][K/16] of their codes (Q6_K: signed),
+ * computed by the same decode and int8 dot-product code the GEMV kernels use.
+ * P: device int32, p_bytes >= M*N*(K/32)*4 (Q6_K, Q2_K: M*N*(K/16)*4 and
+ * K <= 53760). */
 qmm_status qmm_debug_block_sums(qmm_weight_type t, const void *w, size_t w_bytes,
                                 qmm_layout l, const void *y, size_t y_bytes,
                                 int32_t *P, size_t p_bytes,

@@ -54,6 +54,11 @@ def test_size_helpers(lib):
     assert lib.qmm_weight_bytes(2, 0, 5, 512) == 5 * 2 * 210
     assert lib.qmm_weight_bytes(2, 1, 5, 512) == 256 + 5 * 2 * 208
     assert lib.qmm_weight_bytes(2, 0, 5, 100) == 0
+    # Q2_K: 84 B per 256; repacked pads its (d, dmin) section to 256 B
+    assert lib.qmm_weight_bytes(3, 0, 5, 512) == 5 * 2 * 84
+    assert lib.qmm_weight_bytes(3, 1, 5, 512) == 256 + 5 * 2 * 80
+    assert lib.qmm_weight_bytes(3, 1, 64, 512) == 64 * 2 * 4 + 64 * 2 * 80
+    assert lib.qmm_weight_bytes(3, 0, 5, 128) == 0
 
 
 def _last(lib):
@@ -173,10 +178,32 @@ def test_q6_K_validation(lib):
     assert lib.qmm_repack_weights(2, A, 4, 256, A + 10**6, 256 + 4 * 208 - 1, None) == EINVAL
 
 
+def test_q2_K_validation(lib):
+    f = lib.qmm_mul_mat_q2_K
+    fx = lib.qmm_mul_mat_q2_K_ex
+    big = 10**9
+    assert f(A, big, 1, A, big, A, big, 2, 8, 384, None) == EUNSUP          # K % 256
+    assert f(A, big, 0, A, big, A, big, 2, 8, 53760 + 256, None) == EUNSUP
+    assert "Q2_K with K" in _last(lib)
+    assert fx(A, big, 1, A, big, A, big, 2, 8, 53760 + 256, 1, None) == EUNSUP  # GEMV
+    assert fx(A, big, 0, A, big, A, big, 2, 8, 512, 2, None) == EUNSUP        # MFMA, canonical
+    assert fx(A, big, 1, A, big, A, big, 2, 8, 512, 3, None) == EUNSUP        # SKINNY
+    assert f(A, 8 * 2 * 84 - 1, 0, A, big, A, big, 2, 8, 512, None) == EINVAL
+    assert f(A, 256 + 8 * 2 * 80 - 1, 1, A, big, A, big, 2, 8, 512, None) == EINVAL
+    assert f(A, big, 1, A, 2 * 2 * 292 - 1, A, big, 2, 8, 512, None) == EINVAL
+    assert f(A, big, 1, A, big, A + 4, big, 2, 8, 512, None) == EALIGN
+    assert f(None, 0, 1, None, 0, None, 0, 2, 0, 512, None) == OK
+    assert lib.qmm_quantize_weights(3, A, 4, 300, A, 10**6, None) == EUNSUP
+    assert lib.qmm_quantize_weights(3, A, 4, 256, A, 4 * 84 - 1, None) == EINVAL
+    assert lib.qmm_repack_weights(3, A, 4, 256, A + 10**6, 256 + 4 * 80 - 1, None) == EINVAL
+    assert lib.qmm_debug_block_sums(3, A, 10**9, 0, A, 10**9, A, 4 * 8 * 32 * 4 - 1,
+                                    4, 8, 512, None) == EINVAL
+
+
 def test_other_validation(lib):
     assert lib.qmm_quantize_weights(1, A, 4, 100, A, 10**6, None) == EUNSUP
     assert lib.qmm_quantize_weights(0, A, 4, 64, A, 4 * 2 * 18 - 1, None) == EINVAL
-    assert lib.qmm_quantize_weights(3, A, 4, 64, A, 10**6, None) == EUNSUP
+    assert lib.qmm_quantize_weights(7, A, 4, 256, A, 10**6, None) == EUNSUP   # unknown type
     assert lib.qmm_repack_weights(1, A, 4, 256, A + 4 * 144 - 16, 10**6, None) == EINVAL  # overlap
     assert "overlap" in _last(lib)
     assert lib.qmm_repack_weights(1, A, 4, 256, A + 10**6, 4 * 144 - 1, None) == EINVAL

@@ -42,13 +42,14 @@ def _run_projection(p, full: bool):
         assert_close(got[ms, ns], want, terms, p.name + " (sampled)")
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "q6K_c2", "q6K_down"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "q6K_c2", "q6K_down",
+                                 "q2K_c2"])
 def test_decode_workloads(key):
     for p in workload(key).projections:
         _run_projection(p, full=True)
 
 
-@pytest.mark.parametrize("key", ["c5_m512", "c5_m2048", "q6K_c5_m512"])
+@pytest.mark.parametrize("key", ["c5_m512", "c5_m2048", "q6K_c5_m512", "q2K_c5_m512"])
 def test_prefill_workloads(key):
     for p in workload(key).projections:
         _run_projection(p, full=False)
