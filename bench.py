@@ -35,7 +35,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 MALL_BYTES = 256 << 20
 METRIC = "Q4_K GEMV weight GB/s (% HBM peak); prefill GEMM int8 TOPS (% MFMA peak)"
-PREFILL = ("c5_m512", "c5_m2048", "q6K_c5_m512", "q6K_c5_m2048", "q2K_c5_m512", "q2K_c5_m2048")
+PREFILL = ("c5_m512", "c5_m2048", "q6K_c5_m512", "q6K_c5_m2048", "q2K_c5_m512", "q2K_c5_m2048",
+           "q40_c5_m512", "q40_c5_m2048")
 
 
 def parse():

@@ -58,6 +58,7 @@ def load() -> ctypes.CDLL:
         "qmm_mul_mat_q6_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_mul_mat_q6_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_mul_mat_q2_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
+        "qmm_mul_mat_q4_0_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_mul_mat_q2_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_quantize_mul_mat": (I, [I, P, SZ, I, P, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_debug_block_sums": (I, [I, P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
@@ -144,15 +145,16 @@ def repack_weights(w, fmt: str, N: int, K: int, out=None, stream=None):
     return out
 
 
-def mul_mat_q4_0(w, y, M: int, N: int, K: int, layout: str = "canonical", out=None, stream=None):
+def mul_mat_q4_0(w, y, M: int, N: int, K: int, layout: str = "canonical", algo: str = "auto",
+                 out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=y.device)
     pw, nw = _dev(w, "w")
     py, ny = _dev(y, "y")
     po, no = _dev(out, "out")
-    _check(load().qmm_mul_mat_q4_0(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
-                                   _stream(stream)), "qmm_mul_mat_q4_0")
+    _check(load().qmm_mul_mat_q4_0_ex(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
+                                      _ALGO[algo], _stream(stream)), "qmm_mul_mat_q4_0")
     return out
 
 

@@ -4,7 +4,7 @@
 // HIP runtime, so a bad call returns an error code, enqueues nothing and needs
 // no GPU to be tested.  Valid calls dispatch to the kernel families in
 // quantize.hip, repack.hip, gemv.hip, skinny.hip, gemm.hip, q6k.hip,
-// q6k_gemm.hip, q2k.hip and q2k_gemm.hip.
+// q6k_gemm.hip, q2k.hip, q2k_gemm.hip and q40_gemm.hip.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -37,11 +37,12 @@ int w_bytes_per_block(qmm_weight_type t) {
     return t == QMM_Q4_0 ? 18 : (t == QMM_Q6_K ? 210 : (t == QMM_Q2_K ? 84 : 144));
 }
 
-// The MFMA kernels address the weight and the Q8_K activation matrix with
-// 32-bit buffer offsets.
+// The MFMA kernels address the weight and the activation matrix with 32-bit
+// buffer offsets.
 bool below_4gib(qmm_weight_type t, qmm_layout l, int64_t M, int64_t N, int64_t K) {
     const size_t lim = size_t(1) << 32;
-    return qmm_weight_bytes(t, l, N, K) < lim && qmm_act_bytes(QMM_Q8_K, M, K) < lim;
+    const qmm_act_type at = t == QMM_Q4_0 ? QMM_Q8_0 : QMM_Q8_K;
+    return qmm_weight_bytes(t, l, N, K) < lim && qmm_act_bytes(at, M, K) < lim;
 }
 
 qmm_status check_rows(const char *name, int64_t v) {
@@ -184,23 +185,43 @@ qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N,
                          "repack_weights launch");
 }
 
-qmm_status qmm_mul_mat_q4_0(const void *w, size_t w_bytes, qmm_layout l, const void *y,
-                            size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
-                            int64_t K, void *stream) {
+qmm_status qmm_mul_mat_q4_0_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                               size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                               int64_t K, qmm_algo algo, void *stream) {
+    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
+        return fail(QMM_EUNSUPPORTED, "Q4_0 takes the GEMV or MFMA path (algo %d)", (int)algo);
     QMM_TRY(mul_mat_common(QMM_Q4_0, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
+    // the MFMA kernel steps K by 256 and takes the repacked layout
+    const bool mfma_ok = l == QMM_LAYOUT_REPACKED && K % 256 == 0 && below_4gib(QMM_Q4_0, l, M, N, K);
+    if (algo == QMM_ALGO_MFMA && !mfma_ok)
+        return fail(QMM_EUNSUPPORTED,
+                    "Q4_0 MFMA path takes the repacked layout, K a multiple of 256 and matrices below 4 GiB");
     if (M == 0 || N == 0) return QMM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool rep = l == QMM_LAYOUT_REPACKED;
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
+    qmm_algo a = algo;
+    if (a == QMM_ALGO_AUTO) a = M <= qmm::kGemvMaxM || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
+    if (a == QMM_ALGO_MFMA)
+        return device_status(qmm::launch_gemm_q4_0(wb, (int64_t)qmm_weight_bytes(QMM_Q4_0, l, N, K), yb,
+                                                   out, M, N, K, s),
+                             "mul_mat_q4_0 gemm launch");
     // groups of up to 8 activation rows per GEMV launch
+    const bool rep = l == QMM_LAYOUT_REPACKED;
     for (int64_t m0 = 0; m0 < M; m0 += qmm::kGemvMaxM) {
         const int64_t mm = M - m0 < qmm::kGemvMaxM ? M - m0 : qmm::kGemvMaxM;
         QMM_TRY(device_status(qmm::launch_gemv_q4_0(wb, rep, yb + m0 * (K / 32) * 34, out + m0 * N,
                                                     mm, N, K, s),
-                              "mul_mat_q4_0 launch"));
+                              "mul_mat_q4_0 gemv launch"));
     }
     return QMM_OK;
+}
+
+qmm_status qmm_mul_mat_q4_0(const void *w, size_t w_bytes, qmm_layout l, const void *y,
+                            size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
+                            int64_t K, void *stream) {
+    return qmm_mul_mat_q4_0_ex(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, QMM_ALGO_AUTO,
+                               stream);
 }
 
 qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,

@@ -72,6 +72,9 @@ hipError_t launch_gemm_q6_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
+// Q4_0 x Q8_0, repacked layout, K a multiple of 256.
+hipError_t launch_gemm_q4_0(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
 
 constexpr int kGemvMaxM = 8;
 

@@ -114,6 +114,8 @@ def workload(key: str) -> Workload:
     q6K_c5_m{512,2048}  Q6_K prefill on the c5 shapes (N=28672, K=8192)
     q2K_c2    Q2_K x Q8_K GEMV, M=1, N=K=4096, the weights of c2 in 2-bit form
     q2K_c5_m{512,2048}  Q2_K prefill on the c5 shapes
+    q40_c5_m{512,2048}  Q4_0 x Q8_0 prefill on the c5 shapes, weights N(0, 0.02)
+                        as in c1
     """
     if key == "c1":
         return Workload(key, "Q4_0xQ8_0 GEMV M=1 N=256 K=1024", [
@@ -155,9 +157,14 @@ def workload(key: str) -> Workload:
         assert m in (512, 2048)
         return Workload(key, f"Q2_K prefill M={m} N=28672 K=8192", [
             Projection("w", "q2_K", m, 28672, 8192, 5, [105, m], outliers=0.01)])
+    if key.startswith("q40_c5_m"):
+        m = int(key[8:])
+        assert m in (512, 2048)
+        return Workload(key, f"Q4_0xQ8_0 prefill M={m} N=28672 K=8192", [
+            Projection("w", "q4_0", m, 28672, 8192, 5, [105, m], w_kind="normal", outliers=0.01)])
     raise KeyError(key)
 
 
 ALL_WORKLOADS = ["c1", "c2", "c3", "c4_m4", "c4_m8", "c4_m32", "c5_m512", "c5_m2048",
                  "q6K_c2", "q6K_down", "q6K_c5_m512", "q6K_c5_m2048",
-                 "q2K_c2", "q2K_c5_m512", "q2K_c5_m2048"]
+                 "q2K_c2", "q2K_c5_m512", "q2K_c5_m2048", "q40_c5_m512", "q40_c5_m2048"]

@@ -90,18 +90,18 @@ typedef enum { QMM_Q8_0 = 0, QMM_Q8_K = 1 } qmm_act_type;
 typedef enum { QMM_Q4_0 = 0, QMM_Q4_K = 1, QMM_Q6_K = 2, QMM_Q2_K = 3 } qmm_weight_type;
 typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
 
-/* Kernel family for a mul_mat call (Q4_K, Q6_K, Q2_K; Q4_0 always uses GEMV):
- *   GEMV    vector int8 dot products, one wavefront per output row (Q4_K:
- *           M <= 8; Q6_K and Q2_K: any M, K <= 53760)
+/* Kernel family for a mul_mat call:
+ *   GEMV    vector int8 dot products, one wavefront per output row (Q4_0 and
+ *           Q4_K: M <= 8 per launch; Q6_K and Q2_K: any M, K <= 53760)
  *   SKINNY  small-batch int8 MFMA, one 32-column tile per workgroup, K split
  *           over its wavefronts (Q4_K only; M <= 32)
- *   MFMA    prefill GEMM on int8 MFMA, 128 x 256 output tiles (any M; Q6_K
- *           and Q2_K need the repacked layout)
+ *   MFMA    prefill GEMM on int8 MFMA, 128 x 256 output tiles (any M; Q6_K,
+ *           Q2_K and Q4_0 need the repacked layout, Q4_0 also K % 256 == 0)
  * SKINNY and MFMA address the weight and activation matrices with 32-bit
  * offsets, so both must be below 4 GiB.  AUTO for Q4_K takes GEMV for M = 1,
  * SKINNY for 2 <= M <= 32, MFMA above (GEMV in groups of 8 rows where the
- * size limit rules the MFMA kernels out); for Q6_K and Q2_K it takes GEMV for
- * M <= 8 and MFMA above, GEMV where MFMA is ruled out. */
+ * size limit rules the MFMA kernels out); for Q6_K, Q2_K and Q4_0 it takes
+ * GEMV for M <= 8 and MFMA above, GEMV where MFMA is ruled out. */
 typedef enum {
     QMM_ALGO_AUTO = 0,
     QMM_ALGO_GEMV = 1,
@@ -154,11 +154,21 @@ qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N,
 
 /* out[m*N+n] = sum over blocks b of d_w*d_a*sum_i (q_i-8)*y_i  (fp32 output,
  * overwritten).  w: Q4_0 [N,K] in layout l; y: Q8_0 [M,K] from
- * qmm_quantize_row_q8. */
+ * qmm_quantize_row_q8.  Kernel choice as QMM_ALGO_AUTO describes. */
 qmm_status qmm_mul_mat_q4_0(const void *w, size_t w_bytes, qmm_layout l,
                             const void *y, size_t y_bytes,
                             float *out, size_t out_bytes,
                             int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Same as qmm_mul_mat_q4_0 with an explicit kernel family: QMM_ALGO_GEMV (any
+ * M, launched in groups of 8 rows) or QMM_ALGO_MFMA (repacked layout, K a
+ * multiple of 256, both matrices below 4 GiB); QMM_ALGO_SKINNY and a family
+ * whose limits the call exceeds give QMM_EUNSUPPORTED. */
+qmm_status qmm_mul_mat_q4_0_ex(const void *w, size_t w_bytes, qmm_layout l,
+                               const void *y, size_t y_bytes,
+                               float *out, size_t out_bytes,
+                               int64_t M, int64_t N, int64_t K, qmm_algo algo,
+                               void *stream);
 
 /* out[m*N+n] = sum over super-blocks b of d_a*(d*S - dmin*Mn) with
  * S = sum_j s_j*P_j, P_j = sum_{i in j} q_i*y_i, Mn = sum_j m_j*(bsums[2j]+bsums[2j+1])

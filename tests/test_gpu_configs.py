@@ -49,7 +49,7 @@ def test_decode_workloads(key):
         _run_projection(p, full=True)
 
 
-@pytest.mark.parametrize("key", ["c5_m512", "c5_m2048", "q6K_c5_m512", "q2K_c5_m512"])
+@pytest.mark.parametrize("key", ["c5_m512", "c5_m2048", "q6K_c5_m512", "q2K_c5_m512", "q40_c5_m512"])
 def test_prefill_workloads(key):
     for p in workload(key).projections:
         _run_projection(p, full=False)
