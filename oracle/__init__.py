@@ -88,6 +88,7 @@ def _load():
         "orc_sample_q2_K_q8_K": (None, [P, P, I64, I64, I64, P, P, I64, P, P]),
         "orc_repacked_bytes_q2_K": (I64, [I64, I64]),
         "orc_repack_q2_K": (None, [P, I64, I64, P]),
+        "orc_mul_mat_id": (ctypes.c_int, [ctypes.c_int, P, I64, I64, I64, P, P, I64, I64, ctypes.c_int, P, P]),
         "orc_max_threads": (ctypes.c_int, []),
     }
     for name, (res, args) in sigs.items():
@@ -226,6 +227,27 @@ def q6_K_pack_codes(q) -> np.ndarray:
     out = np.zeros(192, np.uint8)
     _load().orc_q6_K_pack_codes(_p(q), _p(out))
     return out
+
+
+_WFMT = {"q4_0": 0, "q4_K": 1, "q6_K": 2, "q2_K": 3}
+
+
+def mul_mat_id(wfmt: str, w: np.ndarray, E: int, N: int, K: int, y: np.ndarray,
+               ids: np.ndarray, y_per_slot: bool = False):
+    """Expert-routed integer path: w is the canonical stack [E*N, ...], ids
+    [T, U] int32; returns (out [T, U, N], sum|terms| [T, U, N]).  Raises
+    ValueError for an id outside [0, E)."""
+    w = _c(w, np.uint8)
+    y = _c(y, np.uint8)
+    ids = _c(ids, np.int32)
+    T, U = ids.shape
+    out = np.zeros((T, U, N), np.float64)
+    terms = np.zeros((T, U, N), np.float64)
+    rc = _load().orc_mul_mat_id(_WFMT[wfmt], _p(w), E, N, K, _p(y), _p(ids), T, U,
+                                int(bool(y_per_slot)), _p(out), _p(terms))
+    if rc != 0:
+        raise ValueError("mul_mat_id: expert id out of range")
+    return out, terms
 
 
 def q2_K_pack_codes(q) -> np.ndarray:

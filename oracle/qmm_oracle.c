@@ -868,3 +868,42 @@ void orc_repack_q2_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out) {
         memcpy(out + q0 + 64 * i, src + 16, 64);
     }
 }
+
+/* ======================================================================== */
+/* mul_mat_id.  P1 closing list of follow-ups ("mul_mat_id(MoE 专家路由下的  */
+/* 矩阵乘)"): mul_mat with one more level, the grouping by expert id.        */
+/* Reading: a stack of E weight matrices [E][N][K] (expert e's rows start at */
+/* e*N rows), a token-by-slot table ids[T][U] of expert ids, and activation  */
+/* rows either one per token (y_per_slot = 0: row t serves every slot of     */
+/* token t) or one per (token, slot) (y_per_slot = 1: row t*U + u);          */
+/*   out[(t*U + u)*N + n] = mul_mat(W[ids[t][u]], y_row)[n].                 */
+/* Each (t, u) is the plain integer path of its format; an id outside        */
+/* [0, E) makes the call fail (returns -1, out untouched).                   */
+/* wfmt: 0 Q4_0, 1 Q4_K, 2 Q6_K, 3 Q2_K (the activation format follows).     */
+/* ======================================================================== */
+int orc_mul_mat_id(int wfmt, const uint8_t *w, int64_t E, int64_t N, int64_t K,
+                   const uint8_t *y, const int32_t *ids, int64_t T, int64_t U,
+                   int y_per_slot, double *out, double *terms) {
+    int64_t nb, wblk, yblk;
+    double (*dot)(const uint8_t *, const uint8_t *, int64_t, int32_t *, double *);
+    switch (wfmt) {
+        case 0: nb = K / QK4_0; wblk = ORC_Q4_0_BYTES; yblk = ORC_Q8_0_BYTES; dot = q4_0_row_dot; break;
+        case 1: nb = K / QK_K; wblk = ORC_Q4_K_BYTES; yblk = ORC_Q8_K_BYTES; dot = q4_K_row_dot; break;
+        case 2: nb = K / QK_K; wblk = ORC_Q6_K_BYTES; yblk = ORC_Q8_K_BYTES; dot = q6_K_row_dot; break;
+        case 3: nb = K / QK_K; wblk = ORC_Q2_K_BYTES; yblk = ORC_Q8_K_BYTES; dot = q2_K_row_dot; break;
+        default: return -1;
+    }
+    for (int64_t p = 0; p < T * U; ++p)
+        if (ids[p] < 0 || ids[p] >= E) return -1;
+    const int64_t wrow = nb * wblk, yrow = nb * yblk;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t p = 0; p < T * U; ++p)
+        for (int64_t n = 0; n < N; ++n) {
+            const int64_t e = ids[p];
+            const int64_t r = y_per_slot ? p : p / U;
+            double tm = 0.0;
+            out[p * N + n] = dot(w + (e * N + n) * wrow, y + r * yrow, nb, NULL, terms ? &tm : NULL);
+            if (terms) terms[p * N + n] = tm;
+        }
+    return 0;
+}

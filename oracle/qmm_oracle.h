@@ -150,6 +150,15 @@ void orc_sample_q2_K_q8_K(const uint8_t *w, const uint8_t *y, int64_t M,
 int64_t orc_repacked_bytes_q2_K(int64_t N, int64_t K);
 void orc_repack_q2_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out);
 
+/* ---- mul_mat_id: out[(t*U+u)*N + n] = mul_mat(W[ids[t*U+u]], y_row)[n] with
+ * W a stack [E][N][K] of canonical matrices in format wfmt (0 Q4_0, 1 Q4_K,
+ * 2 Q6_K, 3 Q2_K) and y_row = row t (y_per_slot = 0) or t*U+u (1).  Returns
+ * -1 for an id outside [0, E) or an unknown format, 0 otherwise.  terms may
+ * be NULL. ---- */
+int orc_mul_mat_id(int wfmt, const uint8_t *w, int64_t E, int64_t N, int64_t K,
+                   const uint8_t *y, const int32_t *ids, int64_t T, int64_t U,
+                   int y_per_slot, double *out, double *terms);
+
 int orc_max_threads(void);
 
 #ifdef __cplusplus
