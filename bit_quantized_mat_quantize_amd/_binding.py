@@ -59,6 +59,8 @@ def load() -> ctypes.CDLL:
         "qmm_mul_mat_q6_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_mul_mat_q2_K": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_mul_mat_q4_0_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
+        "qmm_mul_mat_id_workspace_bytes": (SZ, [I64, I64, I64]),
+        "qmm_mul_mat_id_q4_K": (I, [P, SZ, I64, I, P, SZ, I, P, I64, I64, P, SZ, I64, I64, P, SZ, I, P]),
         "qmm_mul_mat_q2_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_quantize_mul_mat": (I, [I, P, SZ, I, P, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_debug_block_sums": (I, [I, P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
@@ -218,6 +220,35 @@ def mul_mat_q2_K(w, y, M: int, N: int, K: int, layout: str = "canonical", algo: 
     po, no = _dev(out, "out")
     _check(load().qmm_mul_mat_q2_K_ex(pw, nw, _LAYOUT[layout], py, ny, po, no, M, N, K,
                                       _ALGO[algo], _stream(stream)), "qmm_mul_mat_q2_K")
+    return out
+
+
+def mul_mat_id_workspace_bytes(T: int, U: int, E: int) -> int:
+    return int(load().qmm_mul_mat_id_workspace_bytes(T, U, E))
+
+
+def mul_mat_id_q4_K(w, E: int, y, ids, N: int, K: int, layout: str = "canonical",
+                    y_per_slot: bool = False, algo: str = "auto", out=None, workspace=None,
+                    stream=None):
+    """out [T, U, N] fp32: slot u of token t multiplies expert ids[t, u]'s Q4_K
+    matrix (w = E matrices back to back) with activation row t (or t*U + u)."""
+    import torch
+    T, U = ids.shape
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    if out is None:
+        out = torch.empty((T, U, N), dtype=torch.float32, device=ids.device)
+    if workspace is None:
+        workspace = torch.empty(max(mul_mat_id_workspace_bytes(T, U, E), 16), dtype=torch.uint8,
+                                device=ids.device)
+    pw, nw = _dev(w, "w")
+    py, ny = _dev(y, "y")
+    pi, _ = _dev(ids, "ids")
+    po, no = _dev(out, "out")
+    pws, nws = _dev(workspace, "workspace")
+    _check(load().qmm_mul_mat_id_q4_K(pw, nw, E, _LAYOUT[layout], py, ny, int(bool(y_per_slot)), pi, T, U,
+                                      po, no, N, K, pws, nws, _ALGO[algo], _stream(stream)),
+           "qmm_mul_mat_id_q4_K")
     return out
 
 

@@ -4,7 +4,7 @@
 // HIP runtime, so a bad call returns an error code, enqueues nothing and needs
 // no GPU to be tested.  Valid calls dispatch to the kernel families in
 // quantize.hip, repack.hip, gemv.hip, skinny.hip, gemm.hip, q6k.hip,
-// q6k_gemm.hip, q2k.hip, q2k_gemm.hip and q40_gemm.hip.
+// q6k_gemm.hip, q2k.hip, q2k_gemm.hip, q40_gemm.hip and moe.hip.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -360,6 +360,64 @@ qmm_status qmm_mul_mat_q2_K(const void *w, size_t w_bytes, qmm_layout l, const v
                             int64_t K, void *stream) {
     return qmm_mul_mat_q2_K_ex(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, QMM_ALGO_AUTO,
                                stream);
+}
+
+size_t qmm_mul_mat_id_workspace_bytes(int64_t T, int64_t U, int64_t E) {
+    if (T < 0 || U < 1 || E < 1 || E > qmm::kMoeMaxExperts || T * U > (int64_t(1) << 31) - 1) return 0;
+    return (size_t)qmm::moe_group_layout(T * U, E, qmm::gemm_tile_rows()).words * 4;
+}
+
+qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_layout l, const void *y,
+                               size_t y_bytes, int y_per_slot, const int32_t *ids, int64_t T,
+                               int64_t U, float *out, size_t out_bytes, int64_t N, int64_t K,
+                               void *workspace, size_t ws_bytes, qmm_algo algo, void *stream) {
+    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
+        return fail(QMM_EUNSUPPORTED, "mul_mat_id takes the GEMV or MFMA path (algo %d)", (int)algo);
+    if (l != QMM_LAYOUT_CANONICAL && l != QMM_LAYOUT_REPACKED)
+        return fail(QMM_EUNSUPPORTED, "unknown layout %d", (int)l);
+    if (E < 1 || E > qmm::kMoeMaxExperts)
+        return fail(QMM_EUNSUPPORTED, "E = %lld experts; 1 <= E <= %d", (long long)E, qmm::kMoeMaxExperts);
+    if (U < 1 || U > E) return fail(QMM_EINVAL, "U = %lld slots per token; 1 <= U <= E", (long long)U);
+    if (y_per_slot != 0 && y_per_slot != 1) return fail(QMM_EINVAL, "y_per_slot must be 0 or 1");
+    QMM_TRY(check_rows("T", T));
+    QMM_TRY(check_rows("N", N));
+    QMM_TRY(check_k(K, 256));
+    const int64_t P = T * U;
+    if (P > (int64_t(1) << 31) - 1) return fail(QMM_EUNSUPPORTED, "T*U = %lld pairs exceeds 2^31 - 1", (long long)P);
+    if (P == 0 || N == 0) return QMM_OK;
+    const int64_t y_rows = y_per_slot ? P : T;
+    const size_t w_one = qmm_weight_bytes(QMM_Q4_K, l, N, K);
+    QMM_TRY(check_ptr("w", w));
+    QMM_TRY(check_ptr("y", y));
+    QMM_TRY(check_ptr("ids", ids));
+    QMM_TRY(check_ptr("out", out));
+    QMM_TRY(check_size("w", w_bytes, w_one * (size_t)E));
+    QMM_TRY(check_size("y", y_bytes, qmm_act_bytes(QMM_Q8_K, y_rows, K)));
+    QMM_TRY(check_size("out", out_bytes, (size_t)(P * N) * sizeof(float)));
+    const bool gemv_ok = K <= qmm::gemv1_max_k();
+    // the grouped GEMM addresses one expert matrix and the activations with 32-bit offsets
+    const bool mfma_ok = w_one < (size_t(1) << 32) && qmm_act_bytes(QMM_Q8_K, y_rows, K) < (size_t(1) << 32);
+    if (algo == QMM_ALGO_GEMV && !gemv_ok)
+        return fail(QMM_EUNSUPPORTED, "mul_mat_id GEMV takes K <= %lld", (long long)qmm::gemv1_max_k());
+    if (algo != QMM_ALGO_GEMV && !mfma_ok && !(algo == QMM_ALGO_AUTO && gemv_ok))
+        return fail(QMM_EUNSUPPORTED, "mul_mat_id MFMA path takes matrices below 4 GiB");
+    qmm_algo a = algo;
+    if (a == QMM_ALGO_AUTO) a = (P <= 64 && gemv_ok) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const uint8_t *yb = static_cast<const uint8_t *>(y);
+    const bool rep = l == QMM_LAYOUT_REPACKED;
+    if (a == QMM_ALGO_GEMV)
+        return device_status(qmm::launch_gemv_id_q4_K(wb, rep, (int64_t)w_one, yb, y_per_slot, ids, P, U, E,
+                                                      out, N, K, s),
+                             "mul_mat_id gemv launch");
+    QMM_TRY(check_ptr("workspace", workspace));
+    QMM_TRY(check_size("workspace", ws_bytes, qmm_mul_mat_id_workspace_bytes(T, U, E)));
+    int32_t *ws = static_cast<int32_t *>(workspace);
+    QMM_TRY(device_status(qmm::launch_moe_group_ids(ids, P, E, ws, out, N, s), "mul_mat_id grouping launch"));
+    return device_status(qmm::launch_gemm_id_q4_K(wb, rep, (int64_t)w_one, yb, y_rows, y_per_slot, U, ws, E,
+                                                  P, out, N, K, s),
+                         "mul_mat_id gemm launch");
 }
 
 qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes, qmm_layout l,

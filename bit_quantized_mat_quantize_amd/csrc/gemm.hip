@@ -74,11 +74,22 @@ static_assert(A_INSTR % NWAVE == 0 && P_INSTR % NWAVE == 0 && H_INSTR <= NWAVE,
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 static_assert(CT == 1 && 2 * BM <= NTHR, "one column tile per wavefront; bsums staged by 2*BM threads");
 
-template <bool REPACKED>
+// mul_mat_id (GROUPED = true): the expert-grouped tile table that
+// k_moe_group_ids builds.  Tile g covers the sorted slots tile_r0[g] .. of
+// expert tile_e[g] (at most BM of them, up to start[e+1]); sorted[slot] is a
+// (token, slot) pair p, whose activation row is p (y_per_slot) or p / U and
+// whose output row is p.  M is then the number of activation rows.
+struct Grouping {
+    const int32_t *start, *tile_e, *tile_r0, *ntiles, *sorted;
+    int64_t U, w_stride;
+    int y_per_slot;
+};
+
+template <bool REPACKED, bool GROUPED>
 __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict__ W,
                                                        const uint8_t *__restrict__ Y,
                                                        float *__restrict__ out, int64_t M, int64_t N,
-                                                       int64_t K, int tiles_m, int tiles_n) {
+                                                       int64_t K, int tiles_m, int tiles_n, Grouping grp) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -92,29 +103,52 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
     constexpr int GM = 4;
     const int nwg = tiles_m * tiles_n;
     const int bid = blockIdx.x;
-    const int v = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
-    const int group = v / (GM * tiles_n), first_m = group * GM;
-    const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;
-    const int in_group = v - group * GM * tiles_n;
-    const int tile_m = first_m + in_group % gm, tile_n = in_group / gm;
+    int tile_m, tile_n, m_last_g = 0, r0 = 0;
+    if constexpr (GROUPED) {
+        const int g = bid / tiles_n;
+        tile_n = bid - g * tiles_n;
+        tile_m = 0;
+        if (g >= *grp.ntiles) return;  // beyond the tiles this routing produced (uniform)
+        const int e = grp.tile_e[g];
+        r0 = grp.tile_r0[g];
+        const int rows = grp.start[e + 1] - r0;
+        m_last_g = (rows < BM ? rows : BM) - 1;
+        W += (int64_t)e * grp.w_stride;
+    } else {
+        const int v = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+        const int group = v / (GM * tiles_n), first_m = group * GM;
+        const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;
+        const int in_group = v - group * GM * tiles_n;
+        tile_m = first_m + in_group % gm;
+        tile_n = in_group / gm;
+    }
     const int64_t m_base = (int64_t)tile_m * BM, n_base = (int64_t)tile_n * BN;
     const int64_t nb = K / QK_K;
 
     // ---- staging sources.  Rows past M and columns past N are clamped to the
     // last valid one (their results are never stored), so every load is in
     // bounds and none is predicated.
-    const int m_last = (int)(M - 1 - m_base < BM - 1 ? M - 1 - m_base : BM - 1);
+    const int m_last = GROUPED ? m_last_g : (int)(M - 1 - m_base < BM - 1 ? M - 1 - m_base : BM - 1);
     const int n_last = (int)(N - 1 - n_base < BN - 1 ? N - 1 - n_base : BN - 1);
     const uint32_t a_rowstride = (uint32_t)(nb * kQ8_KBytes);
     const int64_t a_first = m_base * nb * kQ8_KBytes;
     const int64_t a_bytes = M * nb * kQ8_KBytes - a_first;
+    // byte offset (from Y + a_first) of tile row rr <= m_last
+    auto arow = [&](int rr) -> uint32_t {
+        if constexpr (GROUPED) {
+            const int p = grp.sorted[r0 + rr];
+            return (uint32_t)(grp.y_per_slot ? (int64_t)p : (int64_t)p / grp.U) * a_rowstride;
+        } else {
+            return (uint32_t)rr * a_rowstride;
+        }
+    };
     uint32_t a_goff[A_PER_WAVE];
 #pragma unroll
     for (int t = 0; t < A_PER_WAVE; ++t) {
         const int row = (wave * A_PER_WAVE + t) * 4 + (lane >> 4);
         const int gp = (lane & 15) ^ (row & 15);  // global piece stored at position lane & 15
         const int rr = row < m_last ? row : m_last;
-        a_goff[t] = (uint32_t)rr * a_rowstride + 4 + 16 * gp;
+        a_goff[t] = arow(rr) + 4 + 16 * gp;
     }
     const uint32_t hdr_step = REPACKED ? 16 : kQ4_KBytes, pay_step = REPACKED ? 128 : kQ4_KBytes;
     const int64_t w_bytes = N * nb * kQ4_KBytes;
@@ -137,8 +171,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
     }
     // bsums: row tid>>1, 16-byte half tid&1 (threads < 256); d_a: row tid (threads < 128)
     const int s_row = (tid >> 1) & (BM - 1);
-    const uint32_t s_off = (uint32_t)(s_row < m_last ? s_row : m_last) * a_rowstride + 260 + 16 * (tid & 1);
-    const uint32_t d_off = (uint32_t)((tid & (BM - 1)) < m_last ? (tid & (BM - 1)) : m_last) * a_rowstride;
+    const uint32_t s_off = arow(s_row < m_last ? s_row : m_last) + 260 + 16 * (tid & 1);
+    const uint32_t d_off = arow((tid & (BM - 1)) < m_last ? (tid & (BM - 1)) : m_last);
 
     auto issue = [&](int64_t b, uint8_t *buf) {
         const rsrc_t ra = make_rsrc(Y + a_first, a_bytes);
@@ -298,34 +332,55 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
             for (int i = 0; i < MT; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t m = m_base + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (m < M) out[m * N + n] = acc[i][c][r];
+                    if constexpr (GROUPED) {
+                        const int lm = i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        if (lm <= m_last) out[(int64_t)grp.sorted[r0 + lm] * N + n] = acc[i][c][r];
+                    } else {
+                        const int64_t m = m_base + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        if (m < M) out[m * N + n] = acc[i][c][r];
+                    }
                 }
         }
     }
 }
 
-template <bool REPACKED>
+// tiles_m is the row-tile count (GROUPED: the most tiles any routing can
+// produce; surplus workgroups exit at once)
+template <bool REPACKED, bool GROUPED>
 hipError_t launch(const uint8_t *w, const uint8_t *y, float *out, int64_t M, int64_t N, int64_t K,
-                  hipStream_t s) {
+                  int tiles_m, const Grouping &g, hipStream_t s) {
     static bool attr_set = false;  // the LDS budget above 64 KiB must be opted into once
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_q4_K<REPACKED>,
+        const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_q4_K<REPACKED, GROUPED>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    hipLaunchKernelGGL(k_gemm_q4_K<REPACKED>, dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR),
-                       LDS_BYTES, s, w, y, out, M, N, K, tiles_m, tiles_n);
+    const int tiles_n = (int)((N + BN - 1) / BN);
+    hipLaunchKernelGGL((k_gemm_q4_K<REPACKED, GROUPED>), dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR),
+                       LDS_BYTES, s, w, y, out, M, N, K, tiles_m, tiles_n, g);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int gemm_tile_rows() { return BM; }
+
 hipError_t launch_gemm_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s) {
-    return repacked ? launch<true>(w, y, out, M, N, K, s) : launch<false>(w, y, out, M, N, K, s);
+    const int tiles_m = (int)((M + BM - 1) / BM);
+    return repacked ? launch<true, false>(w, y, out, M, N, K, tiles_m, Grouping{}, s)
+                    : launch<false, false>(w, y, out, M, N, K, tiles_m, Grouping{}, s);
+}
+
+hipError_t launch_gemm_id_q4_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
+                               int64_t y_rows, int y_per_slot, int64_t U, const int32_t *group_ws,
+                               int64_t E, int64_t P, float *out, int64_t N, int64_t K, hipStream_t s) {
+    const MoeGroupLayout L = moe_group_layout(P, E, BM);
+    const Grouping g{group_ws + L.start, group_ws + L.tile_e, group_ws + L.tile_r0, group_ws + L.ntiles,
+                     group_ws + L.sorted, U, w_stride, y_per_slot};
+    return repacked ? launch<true, true>(w, y, out, y_rows, N, K, (int)L.max_tiles, g, s)
+                    : launch<false, true>(w, y, out, y_rows, N, K, (int)L.max_tiles, g, s);
 }
 
 }  // namespace qmm

@@ -233,10 +233,32 @@ __device__ __forceinline__ float gemv1_accumulate(const uint4 &hw, const uint4 (
     return acc;
 }
 
-template <bool REPACKED, int kNit>
+// ID = true (mul_mat_id): blockIdx.y is a (token, slot) pair p0 + y; its
+// expert id selects the weight matrix, its token (or the pair itself) the
+// activation row, and the pair the output row.  An id outside [0, E) reads
+// expert 0 (every load stays in bounds) and stores NaN.
+struct IdRoute {
+    const int32_t *ids;
+    int64_t p0, U, E;
+    int64_t w_stride;    // bytes per expert matrix
+    int64_t y_rowbytes;  // bytes per activation row
+    int y_per_slot;
+};
+
+template <bool REPACKED, int kNit, bool ID>
 __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ W,
                                                     const uint8_t *__restrict__ Y,
-                                                    float *__restrict__ out, int64_t N, int64_t K) {
+                                                    float *__restrict__ out, int64_t N, int64_t K,
+                                                    IdRoute route) {
+    bool valid = true;
+    if constexpr (ID) {
+        const int64_t p = route.p0 + blockIdx.y;
+        const int e = route.ids[p];
+        valid = e >= 0 && e < route.E;
+        W += (valid ? (int64_t)e : 0) * route.w_stride;
+        Y += (route.y_per_slot ? p : p / route.U) * route.y_rowbytes;
+        out += p * N;
+    }
     // 16-byte activation pieces per thread loaded up front (K <= 4096 * kYT)
     constexpr int kYT = kNit >= 8 ? 4 : (kNit + 1) / 2;
     extern __shared__ __attribute__((aligned(16))) uint8_t ys[];
@@ -289,7 +311,7 @@ __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ 
         acc = gemv1_accumulate<kNit>(hw, pw, base, nchunk, lane, s_qs, s_bs, s_d, acc);
     }
     acc = wave_sum(acc);
-    if (lane == 0 && n < N) out[n] = acc;
+    if (lane == 0 && n < N) out[n] = valid ? acc : __builtin_nanf("");
 }
 
 // ---------------------------------------------------------------------------
@@ -518,9 +540,11 @@ hipError_t launch_gemv_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, f
 #define QMM_GEMV1(NIT)                                                                                     \
     do {                                                                                                   \
         if (repacked)                                                                                      \
-            hipLaunchKernelGGL((k_gemv1_q4_K<true, NIT>), grid, dim3(256), (unsigned)lds, s, w, y, out, N, K);  \
+            hipLaunchKernelGGL((k_gemv1_q4_K<true, NIT, false>), grid, dim3(256), (unsigned)lds, s, w, y, out,   \
+                               N, K, IdRoute{});                                                           \
         else                                                                                               \
-            hipLaunchKernelGGL((k_gemv1_q4_K<false, NIT>), grid, dim3(256), (unsigned)lds, s, w, y, out, N, K); \
+            hipLaunchKernelGGL((k_gemv1_q4_K<false, NIT, false>), grid, dim3(256), (unsigned)lds, s, w, y, out,  \
+                               N, K, IdRoute{});                                                           \
     } while (0)
         if (nit <= 1) QMM_GEMV1(1);
         else if (nit <= 2) QMM_GEMV1(2);
@@ -530,6 +554,41 @@ hipError_t launch_gemv_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, f
         return hipGetLastError();
     }
     return dispatch_q4_K<0>(w, repacked, y, out, M, N, K, s);
+}
+
+int64_t gemv1_max_k() {
+    int64_t k = 0;
+    while (gemv1_lds_bytes(k + QK_K) <= 60 * 1024) k += QK_K;
+    return k;
+}
+
+hipError_t launch_gemv_id_q4_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
+                               int y_per_slot, const int32_t *ids, int64_t P, int64_t U, int64_t E,
+                               float *out, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t lds = gemv1_lds_bytes(K);
+    const int64_t nit = (K / QK_K * 8 + 63) / 64;
+    for (int64_t p0 = 0; p0 < P; p0 += 65535) {
+        const int64_t pp = P - p0 < 65535 ? P - p0 : 65535;
+        const dim3 grid((unsigned)((N + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)pp);
+        const IdRoute r{ids, p0, U, E, w_stride, (K / QK_K) * kQ8_KBytes, y_per_slot};
+#define QMM_GEMV_ID(NIT)                                                                                   \
+    do {                                                                                                   \
+        if (repacked)                                                                                      \
+            hipLaunchKernelGGL((k_gemv1_q4_K<true, NIT, true>), grid, dim3(256), (unsigned)lds, s, w, y, out,    \
+                               N, K, r);                                                                   \
+        else                                                                                               \
+            hipLaunchKernelGGL((k_gemv1_q4_K<false, NIT, true>), grid, dim3(256), (unsigned)lds, s, w, y, out,   \
+                               N, K, r);                                                                   \
+    } while (0)
+        if (nit <= 1) QMM_GEMV_ID(1);
+        else if (nit <= 2) QMM_GEMV_ID(2);
+        else if (nit <= 4) QMM_GEMV_ID(4);
+        else QMM_GEMV_ID(8);
+#undef QMM_GEMV_ID
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 int64_t gemv1_fused_max_k() {

@@ -78,4 +78,41 @@ hipError_t launch_gemm_q4_0(const uint8_t *w, int64_t w_bytes, const uint8_t *y,
 
 constexpr int kGemvMaxM = 8;
 
+// ---- mul_mat_id (Q4_K).  The expert grouping lives in a caller workspace of
+// int32 words: start[E+1] (first sorted slot of each expert), tile_e and
+// tile_r0 [max_tiles] (expert and first sorted slot of each GEMM row tile),
+// ntiles[1], sorted[P] (pair index per sorted slot), each section aligned to
+// 16 bytes.  Each expert adds at most one partial tile, so max_tiles =
+// ceil(P / bm) + E.
+struct MoeGroupLayout {
+    int64_t start, tile_e, tile_r0, ntiles, sorted, max_tiles, words;
+};
+inline MoeGroupLayout moe_group_layout(int64_t P, int64_t E, int64_t bm) {
+    auto up4 = [](int64_t v) { return (v + 3) / 4 * 4; };
+    MoeGroupLayout L;
+    L.max_tiles = (P + bm - 1) / bm + E;
+    L.start = 0;
+    L.tile_e = L.start + up4(E + 1);
+    L.tile_r0 = L.tile_e + up4(L.max_tiles);
+    L.ntiles = L.tile_r0 + up4(L.max_tiles);
+    L.sorted = L.ntiles + 4;
+    L.words = L.sorted + up4(P);
+    return L;
+}
+constexpr int kMoeMaxExperts = 4096;
+int gemm_tile_rows();  // BM of the Q4_K GEMM
+int64_t gemv1_max_k();
+// Build the grouping for pairs p < P with expert ids[p] (ids outside [0, E)
+// are left out, and their output rows are filled with NaN).
+hipError_t launch_moe_group_ids(const int32_t *ids, int64_t P, int64_t E, int32_t *ws, float *out,
+                                int64_t N, hipStream_t s);
+// M = 1 GEMV per (token, slot) pair; w_stride = bytes per expert matrix.
+hipError_t launch_gemv_id_q4_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
+                               int y_per_slot, const int32_t *ids, int64_t P, int64_t U, int64_t E,
+                               float *out, int64_t N, int64_t K, hipStream_t s);
+// The Q4_K GEMM over the grouped tiles (after launch_moe_group_ids on ws).
+hipError_t launch_gemm_id_q4_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
+                               int64_t y_rows, int y_per_slot, int64_t U, const int32_t *group_ws,
+                               int64_t E, int64_t P, float *out, int64_t N, int64_t K, hipStream_t s);
+
 }  // namespace qmm

@@ -230,6 +230,35 @@ qmm_status qmm_mul_mat_q2_K_ex(const void *w, size_t w_bytes, qmm_layout l,
                                int64_t M, int64_t N, int64_t K, qmm_algo algo,
                                void *stream);
 
+/* Bytes of the workspace qmm_mul_mat_id_q4_K needs for its MFMA path (T
+ * tokens, U slots per token, E experts): int32 tables of the expert grouping.
+ * Returns 0 for invalid arguments (U < 1, E outside [1, 4096], T*U >= 2^31). */
+size_t qmm_mul_mat_id_workspace_bytes(int64_t T, int64_t U, int64_t E);
+
+/* mul_mat_id (ggml-cpu mul_mat page, closing list of follow-ups: mul_mat with
+ * one more level, the grouping by expert id).  For every token t < T and slot
+ * u < U, with e = ids[t*U + u]:
+ *     out[(t*U + u)*N + n] = mul_mat_q4_K(W_e, y_row)[n]
+ * where W_e is expert e's Q4_K [N,K] matrix -- w holds the E matrices one
+ * after another, each qmm_weight_bytes(QMM_Q4_K, l, N, K) bytes in layout l --
+ * and y_row is Q8_K activation row t (y_per_slot = 0: every slot of a token
+ * reads its row) or row t*U + u (y_per_slot = 1).  ids: device int32 [T*U].
+ * Kernels: QMM_ALGO_GEMV runs one M = 1 GEMV per (token, slot) (K <= 53760);
+ * QMM_ALGO_MFMA sorts the pairs by expert on the device into `workspace`
+ * (device, at least qmm_mul_mat_id_workspace_bytes(T, U, E) bytes, contents
+ * overwritten; not needed by the GEMV path, may be NULL there) and runs the
+ * Q4_K GEMM over each expert's rows (one expert matrix and the activations
+ * below 4 GiB); AUTO takes the GEMV for T*U <= 64, the GEMM above.  An id
+ * outside [0, E) cannot be checked on the host: that pair's output row is
+ * filled with NaN and nothing is read out of bounds.  Requires 1 <= E <= 4096,
+ * 1 <= U <= E. */
+qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_layout l,
+                               const void *y, size_t y_bytes, int y_per_slot,
+                               const int32_t *ids, int64_t T, int64_t U,
+                               float *out, size_t out_bytes, int64_t N, int64_t K,
+                               void *workspace, size_t ws_bytes, qmm_algo algo,
+                               void *stream);
+
 /* Quantize-and-multiply in one call: y = quantize_row_q8(x) (Q8_0 for t = Q4_0,
  * Q8_K for t = Q4_K, Q6_K and Q2_K), then out = mul_mat(w, y).  The ggml-cpu mul_mat page
  * ("激活量化重复与融合") notes that quantizing the activations once at the

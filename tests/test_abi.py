@@ -200,6 +200,43 @@ def test_q2_K_validation(lib):
                                     4, 8, 512, None) == EINVAL
 
 
+def test_mul_mat_id_validation(lib):
+    f = lib.qmm_mul_mat_id_q4_K
+    big = 10**9
+    wsb = lib.qmm_mul_mat_id_workspace_bytes
+    # int32 words: start[E+1], tile_e/tile_r0[ceil(P/128)+E], ntiles, sorted[P], 16-byte sections
+    up4 = lambda v: (v + 3) // 4 * 4
+    for T, U, E in ((3, 2, 8), (300, 8, 64), (1, 1, 1)):
+        mt = (T * U + 127) // 128 + E
+        assert wsb(T, U, E) == 4 * (up4(E + 1) + 2 * up4(mt) + 4 + up4(T * U))
+    assert wsb(3, 0, 8) == 0 and wsb(3, 2, 0) == 0 and wsb(3, 2, 4097) == 0
+
+    def call(**kw):
+        a = dict(w=A, wb=big, E=4, l=1, y=A, yb=big, yps=0, ids=A, T=3, U=2, o=A, ob=big, N=8, K=512,
+                 ws=A, wsb=big, algo=0)
+        a.update(kw)
+        return f(a["w"], a["wb"], a["E"], a["l"], a["y"], a["yb"], a["yps"], a["ids"], a["T"], a["U"],
+                 a["o"], a["ob"], a["N"], a["K"], a["ws"], a["wsb"], a["algo"], None)
+
+    assert call(E=0) == EUNSUP and call(E=4097) == EUNSUP
+    assert call(U=0) == EINVAL and call(U=5) == EINVAL
+    assert call(yps=2) == EINVAL
+    assert call(K=384) == EUNSUP
+    assert call(l=2) == EUNSUP
+    assert call(algo=3) == EUNSUP
+    assert call(T=0, w=None, y=None, ids=None, o=None, ws=None) == OK
+    assert call(ids=None) == EINVAL and "ids" in _last(lib)
+    assert call(ids=A + 4) == EALIGN
+    assert call(wb=4 * 8 * 2 * 144 - 1) == EINVAL          # four expert matrices
+    assert call(yb=3 * 2 * 292 - 1) == EINVAL               # one row per token
+    assert call(yps=1, yb=6 * 2 * 292 - 1) == EINVAL        # one row per (token, slot)
+    assert call(ob=3 * 2 * 8 * 4 - 1) == EINVAL
+    assert call(algo=1, K=53760 + 256) == EUNSUP            # GEMV row limit
+    # the MFMA path needs its workspace
+    assert call(algo=2, ws=None) == EINVAL
+    assert call(algo=2, wsb=wsb(3, 2, 4) - 1) == EINVAL
+
+
 def test_other_validation(lib):
     assert lib.qmm_quantize_weights(1, A, 4, 100, A, 10**6, None) == EUNSUP
     assert lib.qmm_quantize_weights(0, A, 4, 64, A, 4 * 2 * 18 - 1, None) == EINVAL

@@ -1,0 +1,150 @@
+"""mul_mat_id (Q4_K experts x Q8_K activations) against the oracle.
+
+* decode (per-pair M = 1 GEMV) and prefill (expert grouping on the device +
+  the Q4_K GEMM over each expert's rows): fp32 outputs within
+  1e-4 * sum_k |w a| of the oracle's mul_mat_id for every checked (t, u, n);
+  uneven routing (an expert with no pair, one with more than a GEMM row tile),
+  ragged N, activations per token and per (token, slot), both layouts.
+* exactness window through the grouped GEMM: weights with d = dmin = 1 and
+  small scales, integer activations with amax = 127 per block: outputs equal
+  the integer result exactly.
+* AUTO equals both forced paths; out-of-range ids give NaN rows for exactly
+  those pairs on both paths, and every other row is still right.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import bit_quantized_mat_quantize_amd as qmm
+from bit_quantized_mat_quantize_amd.inputs import activations, weights_t4_skewed
+from gpu_helpers import assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _stack(E, N, K, seed):
+    return np.concatenate([oracle.quantize("q4_K", weights_t4_skewed([seed, e], N, K)) for e in range(E)])
+
+
+def _upload(w, E, N, K, layout):
+    wd = to_dev(w.reshape(-1))
+    if layout == "canonical":
+        return wd
+    per = w.size // E
+    return qmm_cat([qmm.repack_weights(wd[e * per:(e + 1) * per], "q4_K", N, K) for e in range(E)])
+
+
+def qmm_cat(parts):
+    import torch
+    return torch.cat(parts)
+
+
+def _routing(rng, T, U, E, skew=True):
+    """ids [T, U] without repeats inside a token; with skew, expert 0 gets no
+    pair and expert 1 takes every token's first slot."""
+    ids = np.zeros((T, U), np.int32)
+    for t in range(T):
+        pool = np.arange(2 if skew else 0, E)
+        rest = rng.choice(pool, U - 1 if skew else U, replace=False)
+        ids[t] = np.concatenate([[1], rest]) if skew else rest
+    return ids
+
+
+def _check(w, E, N, K, y, ids, y_per_slot, got, what):
+    want, terms = oracle.mul_mat_id("q4_K", w, E, N, K, y, ids, y_per_slot)
+    assert_close(got, want, terms, what)
+
+
+@pytest.mark.parametrize("layout", ["canonical", "repacked"])
+@pytest.mark.parametrize("T,U,E,N,K,y_per_slot", [(1, 2, 8, 96, 1024, False), (3, 4, 8, 70, 4096, True),
+                                                  (8, 8, 16, 33, 2048, False)])
+def test_gemv_id(T, U, E, N, K, y_per_slot, layout):
+    rng = np.random.default_rng(T * 100 + U)
+    w = _stack(E, N, K, 800 + T)
+    y = oracle.quantize("q8_K", activations([801, T], T * U if y_per_slot else T, K))
+    ids = _routing(rng, T, U, E)
+    got = to_host(qmm.mul_mat_id_q4_K(_upload(w, E, N, K, layout), E, to_dev(y.reshape(-1)),
+                                      to_dev(ids), N, K, layout=layout, y_per_slot=y_per_slot,
+                                      algo="gemv"))
+    _check(w, E, N, K, y, ids, y_per_slot, got, f"gemv_id T={T} U={U} {layout}")
+
+
+@pytest.mark.parametrize("layout", ["canonical", "repacked"])
+@pytest.mark.parametrize("y_per_slot", [False, True])
+def test_grouped_gemm(layout, y_per_slot):
+    T, U, E, N, K = 300, 3, 6, 300, 1024      # expert 1: 300 rows (3 tiles), expert 0: none
+    rng = np.random.default_rng(41)
+    w = _stack(E, N, K, 810)
+    y = oracle.quantize("q8_K", activations([811, int(y_per_slot)], T * U if y_per_slot else T, K,
+                                            outlier_frac=0.01))
+    ids = _routing(rng, T, U, E)
+    got = to_host(qmm.mul_mat_id_q4_K(_upload(w, E, N, K, layout), E, to_dev(y.reshape(-1)),
+                                      to_dev(ids), N, K, layout=layout, y_per_slot=y_per_slot,
+                                      algo="mfma"))
+    _check(w, E, N, K, y, ids, y_per_slot, got, f"grouped T={T} {layout} per_slot={y_per_slot}")
+
+
+def test_grouped_exactness_window():
+    T, U, E, N, K = 130, 2, 4, 100, 512
+    rng = np.random.default_rng(42)
+    import struct
+    blocks = bytearray()
+    for _ in range(E * N * K // 256):
+        s = rng.integers(0, 4, 8)
+        m = rng.integers(0, 8, 8)
+        q = rng.integers(0, 16, 256)
+        qs = bytes(int(q[64 * g + l] | (q[64 * g + 32 + l] << 4)) for g in range(4) for l in range(32))
+        blocks += struct.pack("<ee", 1.0, 1.0) + oracle.pack_scales(s, m).tobytes() + qs
+    w = np.frombuffer(bytes(blocks), np.uint8).reshape(E * N, -1)
+    x = rng.integers(-20, 21, (T, K)).astype(np.float32)
+    x[:, ::256] = 127.0
+    y = oracle.quantize("q8_K", x)
+    ids = _routing(rng, T, U, E, skew=False)
+    want, terms = oracle.mul_mat_id("q4_K", w, E, N, K, y, ids)
+    assert terms.max() < 2 ** 24
+    got = to_host(qmm.mul_mat_id_q4_K(_upload(w, E, N, K, "repacked"), E, to_dev(y.reshape(-1)),
+                                      to_dev(ids), N, K, layout="repacked", algo="mfma"))
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_auto_matches_forced_paths_and_bad_ids():
+    E, N, K = 8, 64, 1024
+    w = _stack(E, N, K, 820)
+    wd = _upload(w, E, N, K, "repacked")
+    rng = np.random.default_rng(43)
+    for T, U in ((4, 2), (100, 2)):          # AUTO: GEMV (8 pairs), GEMM (200 pairs)
+        y = oracle.quantize("q8_K", activations([821, T], T, K))
+        ids = _routing(rng, T, U, E, skew=False)
+        outs = [to_host(qmm.mul_mat_id_q4_K(wd, E, to_dev(y.reshape(-1)), to_dev(ids), N, K,
+                                            layout="repacked", algo=a)) for a in ("auto", "gemv", "mfma")]
+        _check(w, E, N, K, y, ids, False, outs[0], f"auto T={T}")
+        _check(w, E, N, K, y, ids, False, outs[1], f"gemv T={T}")
+        _check(w, E, N, K, y, ids, False, outs[2], f"mfma T={T}")
+        bad = ids.copy()
+        bad[0, 1], bad[-1, 0] = -1, E
+        good = np.ones((T, U), bool)
+        good[0, 1] = good[-1, 0] = False
+        safe = np.where(good, bad, 0).astype(np.int32)
+        want, terms = oracle.mul_mat_id("q4_K", w, E, N, K, y, safe)
+        for a in ("gemv", "mfma"):
+            got = to_host(qmm.mul_mat_id_q4_K(wd, E, to_dev(y.reshape(-1)), to_dev(bad), N, K,
+                                              layout="repacked", algo=a))
+            assert np.isnan(got[~good]).all(), a
+            assert_close(got[good], want[good], terms[good], f"{a} with bad ids")
+
+
+def test_mixture_of_experts_shape_sampled():
+    """Eight experts of 4096 x 4096, two slots per token, 512 tokens (1024
+    pairs through the grouped GEMM); 16 tokens checked against the oracle."""
+    T, U, E, N, K = 512, 2, 8, 4096, 4096
+    w = _stack(E, N, K, 830)
+    x = activations([831, 0], T, K, outlier_frac=0.01)
+    y = oracle.quantize("q8_K", x)
+    rng = np.random.default_rng(44)
+    ids = _routing(rng, T, U, E, skew=False)
+    got = to_host(qmm.mul_mat_id_q4_K(_upload(w, E, N, K, "repacked"), E, to_dev(y.reshape(-1)),
+                                      to_dev(ids), N, K, layout="repacked"))
+    sub = np.sort(rng.choice(T, 16, replace=False))
+    rows = y.reshape(T, -1)[sub]
+    want, terms = oracle.mul_mat_id("q4_K", w, E, N, K, rows, ids[sub])
+    assert_close(got[sub], want, terms, "moe 8x4096x4096 sampled")
