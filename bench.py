@@ -170,6 +170,75 @@ def time_graph(prep: Prepared, steps: int, only=None, reps: int = 1):
     return best
 
 
+MOE = dict(E=8, U=2, N=14336, K=4096)   # eight experts of an FFN gate/up projection, two per token
+
+
+class MoePrepared:
+    """mul_mat_id on Q4_K experts: E matrices [N, K] repacked back to back,
+    seeded top-U routing, a step = quantize_row_q8 + mul_mat_id."""
+
+    def __init__(self, T: int, copies: int):
+        import numpy as np
+        import torch
+        import bit_quantized_mat_quantize_amd as qmm
+        from bit_quantized_mat_quantize_amd.inputs import activations, weights_t4_skewed
+        E, U, N, K = MOE["E"], MOE["U"], MOE["N"], MOE["K"]
+        dev = torch.device("cuda:0")
+        mats = []
+        for e in range(E):
+            wf = torch.from_numpy(weights_t4_skewed([6, e], N, K)).to(dev)
+            mats.append(qmm.repack_weights(qmm.quantize_weights(wf, "q4_K"), "q4_K", N, K))
+            del wf
+        w0 = torch.cat(mats)
+        del mats
+        self.ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        self.copies = copies
+        rng = np.random.default_rng(106)
+        ids = np.stack([rng.choice(E, U, replace=False) for _ in range(T)]).astype(np.int32)
+        self.ids = torch.from_numpy(ids).to(dev)
+        self.x = torch.from_numpy(activations([106, T], T, K)).to(dev)
+        self.y = torch.empty(qmm.act_bytes("q8_K", T, K), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((T, U, N), dtype=torch.float32, device=dev)
+        self.wsb = torch.empty(max(qmm.mul_mat_id_workspace_bytes(T, U, E), 16), dtype=torch.uint8,
+                               device=dev)
+        self.T, self.E, self.U, self.N, self.K = T, E, U, N, K
+        self.experts_used = int(len(np.unique(ids)))
+        self.expert_bytes = qmm.weight_bytes("q4_K", "repacked", N, K)
+        torch.cuda.synchronize()
+
+    def step(self, i: int, only: str | None = None):
+        import bit_quantized_mat_quantize_amd as qmm
+        if only in (None, "quantize"):
+            qmm.quantize_row_q8(self.x, "q8_K", out=self.y)
+        if only in (None, "mul_mat"):
+            qmm.mul_mat_id_q4_K(self.ws[i % self.copies], self.E, self.y, self.ids, self.N, self.K,
+                                layout="repacked", out=self.out, workspace=self.wsb)
+
+
+def measure_moe(steps: int):
+    """Decode (one token) and prefill (512 tokens) through mul_mat_id."""
+    import torch
+    res = {"experts": MOE["E"], "slots_per_token": MOE["U"], "N": MOE["N"], "K": MOE["K"]}
+    for name, T, copies, st in (("decode_T1", 1, 2, steps), ("prefill_T512", 512, 1, max(5, steps // 10))):
+        prep = MoePrepared(T, copies)
+        ms = time_graph(prep, st, reps=3)
+        ms_mm = time_graph(prep, st, only="mul_mat", reps=3)
+        r = dict(tokens=T, ms_per_step=round(ms, 6), mul_mat_id_us=round(ms_mm * 1e3, 3),
+                 experts_used=prep.experts_used)
+        if T == 1:
+            wb = prep.experts_used * prep.expert_bytes
+            r.update(weight_bytes=wb, weight_GBps=round(wb / (ms_mm * 1e-3) / 1e9, 1),
+                     frac_hbm_peak=round(wb / (ms_mm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        else:
+            ops = 2 * T * MOE["U"] * MOE["N"] * MOE["K"]
+            r.update(tops=round(ops / (ms_mm * 1e-3) / 1e12, 1),
+                     frac_int8_peak=round(ops / (ms_mm * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4))
+        res[name] = r
+        del prep
+        torch.cuda.empty_cache()
+    return res
+
+
 def calibrate_copy():
     """Plain device copies of a known size (read 256 MiB, write 256 MiB)."""
     import torch
@@ -322,6 +391,8 @@ def main():
                 print(f"bench.py: {k} done", file=sys.stderr, flush=True)
                 extra[k] = _rounded(r)
     q6 = measure_decode("q6K_c2", a.layout, a.steps, a.warmup)
+    moe = measure_moe(a.steps)
+    print("bench.py: mul_mat_id done", file=sys.stderr, flush=True)
     prefill = {}
     if not a.no_prefill:
         for k in PREFILL:
@@ -366,6 +437,7 @@ def main():
                       "ms_per_step": round(q6["unfused"]["ms_per_step"], 6),
                       "mul_mat_us": round(q6["unfused"]["mul_mat_us"], 3),
                       "roofline_mul_mat": roofline_of(q6, "unfused")},
+        "mul_mat_id_q4_K": moe,
     }
     if extra:
         line["other_workloads"] = extra
