@@ -25,23 +25,22 @@
 // lane each); tile 128 (M) x 256 (N); wavefront w owns columns 32w..32w+31
 // (one 32-column tile) for all 128 rows (four 32-row tiles), so each weight
 // column is decoded by exactly one wavefront and the decoded planes feed four
-// row tiles' MFMAs.  K advances one
-// 256-element super-block per step through two LDS buffers: while step b is
-// computed from one buffer, the codes of step b+1 stream into the other with
-// direct global->LDS loads (global_load_lds_dwordx4, no registers involved);
-// bsums and d_a of step b+1 travel through registers (they are converted to
-// fp16 on the way).  One barrier per step.  Per buffer:
+// row tiles' MFMAs.  K advances one 256-element super-block per step.  The
+// int8 activation codes of step b+1 stream into the other of two LDS buffers
+// with direct global->LDS loads (buffer_load ... lds, no registers involved)
+// while step b is computed; bsums and d_a of step b+1 travel through
+// registers (converted to fp16 on the way).  The weights do not go through
+// LDS: no other wavefront reads a column, so each lane loads the 80 bytes of
+// its column it needs (the 16-byte header and the payload pieces of its
+// K-slice) straight into registers, one step ahead.  One barrier per step.
+// Per buffer:
 //   A   int8 codes   [128][256]  16-byte piece p of row r at position p ^ (r & 15)
-//   HDR Q4_K headers [256][16]   d, dmin, scales[12] per column
-//   PAY Q4_K payload [256][128]  16-byte piece p of column c at position p ^ ((c >> 1) & 7)
 //   BS  bsums, fp16  [128][24]   stride 48 B
 //   DA  d_a          [128]
-// (the XOR placements make the 16-byte reads down 16 consecutive rows or
-// columns hit distinct banks).  Each wavefront decodes the eight sub-block
-// planes of its two column tiles into registers once per step, then walks the
-// eight (row tile, column tile) pairs software-pipelined: the MFMAs of pair
-// p+1 are issued before the fp32 epilogue of pair p, so the vector ALU work
-// runs in the matrix core's shadow.
+// (the XOR placement makes the 16-byte reads down 16 consecutive rows hit
+// distinct banks).  Each wavefront decodes the eight sub-block planes of its
+// column tile into registers once per step, before the barrier, then walks
+// its four row tiles.
 //
 // MFMA operand convention (v_mfma_*_32x32xK): lane l supplies row (A) or
 // column (B) l % 32 and the K-slice selected by l / 32; A and B use the same
@@ -58,19 +57,13 @@ namespace {
 constexpr int BM = 128, BN = 256, MT = BM / 32, NWAVE = 8, NTHR = 64 * NWAVE;
 constexpr int CT = BN / 32 / NWAVE;  // column tiles per wavefront (one)
 constexpr int A_OFF = 0, A_BYTES = BM * 256;
-constexpr int H_OFF = A_OFF + A_BYTES, H_BYTES = BN * 16;
-constexpr int P_OFF = H_OFF + H_BYTES, P_BYTES = BN * 128;
-constexpr int BS_OFF = P_OFF + P_BYTES, BS_STRIDE = 48, BS_BYTES = BM * BS_STRIDE;
+constexpr int BS_OFF = A_OFF + A_BYTES, BS_STRIDE = 48, BS_BYTES = BM * BS_STRIDE;
 constexpr int DA_OFF = BS_OFF + BS_BYTES, DA_BYTES = BM * 4;
 constexpr int BUF_BYTES = DA_OFF + DA_BYTES;
 constexpr int LDS_BYTES = 2 * BUF_BYTES;
 constexpr int A_INSTR = A_BYTES / 1024;  // 64-lane x 16-byte loads per buffer
-constexpr int H_INSTR = H_BYTES / 1024;
-constexpr int P_INSTR = P_BYTES / 1024;
 constexpr int A_PER_WAVE = A_INSTR / NWAVE;
-constexpr int P_PER_WAVE = P_INSTR / NWAVE;
-static_assert(A_INSTR % NWAVE == 0 && P_INSTR % NWAVE == 0 && H_INSTR <= NWAVE,
-              "staging must split evenly over the wavefronts");
+static_assert(A_INSTR % NWAVE == 0, "staging must split evenly over the wavefronts");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 static_assert(CT == 1 && 2 * BM <= NTHR, "one column tile per wavefront; bsums staged by 2*BM threads");
 
@@ -119,8 +112,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
         const int group = v / (GM * tiles_n), first_m = group * GM;
         const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;
         const int in_group = v - group * GM * tiles_n;
-        tile_m = first_m + in_group % gm;
-        tile_n = in_group / gm;
+        // (the division runs on the vector ALU; readfirstlane keeps the tile uniform)
+        tile_m = __builtin_amdgcn_readfirstlane(first_m + in_group % gm);
+        tile_n = __builtin_amdgcn_readfirstlane(in_group / gm);
     }
     const int64_t m_base = (int64_t)tile_m * BM, n_base = (int64_t)tile_n * BN;
     const int64_t nb = K / QK_K;
@@ -150,25 +144,13 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
         const int rr = row < m_last ? row : m_last;
         a_goff[t] = arow(rr) + 4 + 16 * gp;
     }
+    // this lane's weight column (clamped), straight into registers
     const uint32_t hdr_step = REPACKED ? 16 : kQ4_KBytes, pay_step = REPACKED ? 128 : kQ4_KBytes;
     const int64_t w_bytes = N * nb * kQ4_KBytes;
-    const int64_t h_first = (int64_t)hdr_step * (n_base * nb);
-    const int64_t p_first = REPACKED ? 16 * N * nb + 128 * (n_base * nb) : kQ4_KBytes * (n_base * nb) + 16;
-    // (the resources are built where they are used: a resource held across the
-    // lambdas below would be treated as divergent and waterfall-looped)
-    // headers: wavefront w < H_INSTR loads columns 64w + lane
-    const int h_col = wave * 64 + lane;
-    const uint32_t h_goff = (uint32_t)(h_col < n_last ? h_col : n_last) * (uint32_t)nb * hdr_step;
-    // payload: load t of wavefront w covers columns 8*(w*P_PER_WAVE + t) + lane/8,
-    // position lane & 7 holds piece (lane & 7) ^ ((col >> 1) & 7)
-    uint32_t p_goff[P_PER_WAVE];
-#pragma unroll
-    for (int t = 0; t < P_PER_WAVE; ++t) {
-        const int c = (wave * P_PER_WAVE + t) * 8 + (lane >> 3);
-        const int piece = (lane & 7) ^ ((c >> 1) & 7);
-        const int cc = c < n_last ? c : n_last;
-        p_goff[t] = (uint32_t)cc * (uint32_t)nb * pay_step + 16 * piece;
-    }
+    const int64_t n_lane = n_base + wave * 32 + l32 < N ? n_base + wave * 32 + l32 : N - 1;
+    const int64_t i0 = n_lane * nb;
+    const uint32_t v_hdr = (uint32_t)(hdr_step * i0);
+    const uint32_t v_pay = (uint32_t)(REPACKED ? 16 * N * nb + 128 * i0 + 16 * hh : kQ4_KBytes * i0 + 16 + 16 * hh);
     // bsums: row tid>>1, 16-byte half tid&1 (threads < 256); d_a: row tid (threads < 128)
     const int s_row = (tid >> 1) & (BM - 1);
     const uint32_t s_off = arow(s_row < m_last ? s_row : m_last) + 260 + 16 * (tid & 1);
@@ -176,17 +158,20 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
 
     auto issue = [&](int64_t b, uint8_t *buf) {
         const rsrc_t ra = make_rsrc(Y + a_first, a_bytes);
-        const rsrc_t rp = make_rsrc(W + p_first, w_bytes - p_first);
-        const rsrc_t rh = make_rsrc(W + h_first, w_bytes - h_first);
         const uint32_t sa = (uint32_t)b * kQ8_KBytes;
 #pragma unroll
         for (int t = 0; t < A_PER_WAVE; ++t)
             dma16(ra, a_goff[t], sa, buf + A_OFF + (wave * A_PER_WAVE + t) * 1024);
-        const uint32_t sp = (uint32_t)b * pay_step;
+    };
+    struct WStage {
+        uint4 hdr, pay[4];
+    };
+    auto wload = [&](int64_t b, WStage &x) {
+        const rsrc_t rw = make_rsrc(W, w_bytes);
+        const uint32_t bb = (uint32_t)b;
+        x.hdr = bld16(rw, v_hdr, hdr_step * bb);
 #pragma unroll
-        for (int t = 0; t < P_PER_WAVE; ++t)
-            dma16(rp, p_goff[t], sp, buf + P_OFF + (wave * P_PER_WAVE + t) * 1024);
-        if (wave < H_INSTR) dma16(rh, h_goff, (uint32_t)b * hdr_step, buf + H_OFF + wave * 1024);
+        for (int g = 0; g < 4; ++g) x.pay[g] = bld16(rw, v_pay + 32 * g, pay_step * bb);
     };
     auto prefetch = [&](int64_t b, uint4 &raw, uint32_t &draw) {
         const rsrc_t ra = make_rsrc(Y + a_first, a_bytes);
@@ -218,22 +203,17 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
 
     uint4 raw = make_uint4(0, 0, 0, 0);
     uint32_t draw = 0;
+    WStage wx;
     issue(0, lds);
     prefetch(0, raw, draw);
+    wload(0, wx);
 
     for (int64_t b = 0; b < nb; ++b) {
         uint8_t *buf = lds + (b & 1) * BUF_BYTES;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of step b
         commit(raw, draw, buf);
-        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
-        if (b + 1 < nb) {
-            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
-            prefetch(b + 1, raw, draw);
-        }
-
         // ---------------- this lane's column: header and the 8 sub-block planes
-        const int col = wave * 32 + l32;
-        const uint4 hdr = *reinterpret_cast<const uint4 *>(buf + H_OFF + 16 * col);
+        const uint4 hdr = wx.hdr;
         const float dcol = f16_bits_to_f32(hdr.x & 0xffff);
         const float dmcol = f16_bits_to_f32(hdr.x >> 16);
         const Q4KScales sc = unpack_scales(hdr.y, hdr.z, hdr.w);
@@ -241,8 +221,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int piece = 2 * g + hh;  // this lane's K-slice of sub-blocks 2g, 2g+1
-            const uint4 pw = *reinterpret_cast<const uint4 *>(buf + P_OFF + 128 * col +
-                                                              16 * (piece ^ ((col >> 1) & 7)));
+            const uint4 pw = wx.pay[g];
+            (void)piece;
             const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {  // t = 0: low nibbles (sub-block 2g), 1: high (2g+1)
@@ -275,6 +255,13 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
             __builtin_memcpy(&bmh, bh, 16);
             __builtin_memcpy(&bml, bl, 16);
         }
+        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
+        if (b + 1 < nb) {
+            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
+            prefetch(b + 1, raw, draw);
+            wload(b + 1, wx);
+        }
+
         const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
 
         // ---------------- the four row tiles of this column tile
