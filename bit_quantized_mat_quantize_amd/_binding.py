@@ -61,6 +61,7 @@ def load() -> ctypes.CDLL:
         "qmm_mul_mat_q4_0_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_mul_mat_id_workspace_bytes": (SZ, [I64, I64, I64]),
         "qmm_mul_mat_id_q4_K": (I, [P, SZ, I64, I, P, SZ, I, P, I64, I64, P, SZ, I64, I64, P, SZ, I, P]),
+        "qmm_mul_mat_id": (I, [I, P, SZ, I64, I, P, SZ, I, P, I64, I64, P, SZ, I64, I64, P, SZ, I, P]),
         "qmm_mul_mat_q2_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_quantize_mul_mat": (I, [I, P, SZ, I, P, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_debug_block_sums": (I, [I, P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
@@ -227,11 +228,11 @@ def mul_mat_id_workspace_bytes(T: int, U: int, E: int) -> int:
     return int(load().qmm_mul_mat_id_workspace_bytes(T, U, E))
 
 
-def mul_mat_id_q4_K(w, E: int, y, ids, N: int, K: int, layout: str = "canonical",
-                    y_per_slot: bool = False, algo: str = "auto", out=None, workspace=None,
-                    stream=None):
-    """out [T, U, N] fp32: slot u of token t multiplies expert ids[t, u]'s Q4_K
-    matrix (w = E matrices back to back) with activation row t (or t*U + u)."""
+def mul_mat_id(wfmt: str, w, E: int, y, ids, N: int, K: int, layout: str = "canonical",
+               y_per_slot: bool = False, algo: str = "auto", out=None, workspace=None, stream=None):
+    """out [T, U, N] fp32: slot u of token t multiplies expert ids[t, u]'s matrix
+    in format `wfmt` (w = E matrices back to back) with activation row t (or
+    t*U + u)."""
     import torch
     T, U = ids.shape
     if ids.dtype != torch.int32:
@@ -246,10 +247,17 @@ def mul_mat_id_q4_K(w, E: int, y, ids, N: int, K: int, layout: str = "canonical"
     pi, _ = _dev(ids, "ids")
     po, no = _dev(out, "out")
     pws, nws = _dev(workspace, "workspace")
-    _check(load().qmm_mul_mat_id_q4_K(pw, nw, E, _LAYOUT[layout], py, ny, int(bool(y_per_slot)), pi, T, U,
-                                      po, no, N, K, pws, nws, _ALGO[algo], _stream(stream)),
-           "qmm_mul_mat_id_q4_K")
+    _check(load().qmm_mul_mat_id(_WEIGHT[wfmt], pw, nw, E, _LAYOUT[layout], py, ny, int(bool(y_per_slot)), pi,
+                                 T, U, po, no, N, K, pws, nws, _ALGO[algo], _stream(stream)),
+           "qmm_mul_mat_id")
     return out
+
+
+def mul_mat_id_q4_K(w, E: int, y, ids, N: int, K: int, layout: str = "canonical",
+                    y_per_slot: bool = False, algo: str = "auto", out=None, workspace=None,
+                    stream=None):
+    return mul_mat_id("q4_K", w, E, y, ids, N, K, layout=layout, y_per_slot=y_per_slot, algo=algo,
+                      out=out, workspace=workspace, stream=stream)
 
 
 ACT_FOR = {"q4_0": "q8_0", "q4_K": "q8_K", "q6_K": "q8_K", "q2_K": "q8_K"}  # activation blocks each weight format takes

@@ -362,15 +362,66 @@ qmm_status qmm_mul_mat_q2_K(const void *w, size_t w_bytes, qmm_layout l, const v
                                stream);
 }
 
+
+}  // extern "C"
+
+namespace {
+
+// The kernels each weight format uses for mul_mat_id.
+struct IdKernels {
+    int64_t gemv_max_k;
+    bool gemm_canonical;  // the GEMM also reads the canonical layout
+    int64_t gemm_k_mult;  // the GEMM's K step
+    hipError_t (*gemv)(const uint8_t *, bool, int64_t, const uint8_t *, int, const int32_t *, int64_t, int64_t,
+                       int64_t, float *, int64_t, int64_t, hipStream_t);
+    hipError_t (*gemm)(const uint8_t *, bool, int64_t, const uint8_t *, int64_t, int, int64_t, const int32_t *,
+                       int64_t, int64_t, float *, int64_t, int64_t, hipStream_t);
+};
+
+template <hipError_t (*G)(const uint8_t *, int64_t, const uint8_t *, int64_t, int, int64_t, const int32_t *,
+                          int64_t, int64_t, float *, int64_t, int64_t, hipStream_t)>
+hipError_t gemm_id_repacked(const uint8_t *w, bool, int64_t w_stride, const uint8_t *y, int64_t y_rows,
+                            int y_per_slot, int64_t U, const int32_t *ws, int64_t E, int64_t P, float *out,
+                            int64_t N, int64_t K, hipStream_t s) {
+    return G(w, w_stride, y, y_rows, y_per_slot, U, ws, E, P, out, N, K, s);
+}
+
+bool id_kernels(qmm_weight_type t, IdKernels &k) {
+    switch (t) {
+        case QMM_Q4_K:
+            k = IdKernels{qmm::gemv1_max_k(), true, 256, qmm::launch_gemv_id_q4_K, qmm::launch_gemm_id_q4_K};
+            return true;
+        case QMM_Q6_K:
+            k = IdKernels{qmm::q6_K_max_k(), false, 256, qmm::launch_gemv_id_q6_K,
+                          gemm_id_repacked<qmm::launch_gemm_id_q6_K>};
+            return true;
+        case QMM_Q2_K:
+            k = IdKernels{qmm::q2_K_max_k(), false, 256, qmm::launch_gemv_id_q2_K,
+                          gemm_id_repacked<qmm::launch_gemm_id_q2_K>};
+            return true;
+        case QMM_Q4_0:  // the GEMV reads whole Q8_0 rows from global memory: no K limit of its own
+            k = IdKernels{int64_t(1) << 20, false, 256, qmm::launch_gemv_id_q4_0,
+                          gemm_id_repacked<qmm::launch_gemm_id_q4_0>};
+            return true;
+    }
+    return false;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t qmm_mul_mat_id_workspace_bytes(int64_t T, int64_t U, int64_t E) {
     if (T < 0 || U < 1 || E < 1 || E > qmm::kMoeMaxExperts || T * U > (int64_t(1) << 31) - 1) return 0;
     return (size_t)qmm::moe_group_layout(T * U, E, qmm::gemm_tile_rows()).words * 4;
 }
 
-qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_layout l, const void *y,
-                               size_t y_bytes, int y_per_slot, const int32_t *ids, int64_t T,
-                               int64_t U, float *out, size_t out_bytes, int64_t N, int64_t K,
-                               void *workspace, size_t ws_bytes, qmm_algo algo, void *stream) {
+qmm_status qmm_mul_mat_id(qmm_weight_type t, const void *w, size_t w_bytes, int64_t E, qmm_layout l,
+                          const void *y, size_t y_bytes, int y_per_slot, const int32_t *ids, int64_t T,
+                          int64_t U, float *out, size_t out_bytes, int64_t N, int64_t K, void *workspace,
+                          size_t ws_bytes, qmm_algo algo, void *stream) {
+    IdKernels kk;
+    if (!id_kernels(t, kk)) return fail(QMM_EUNSUPPORTED, "unknown weight type %d", (int)t);
     if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
         return fail(QMM_EUNSUPPORTED, "mul_mat_id takes the GEMV or MFMA path (algo %d)", (int)algo);
     if (l != QMM_LAYOUT_CANONICAL && l != QMM_LAYOUT_REPACKED)
@@ -381,26 +432,32 @@ qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_lay
     if (y_per_slot != 0 && y_per_slot != 1) return fail(QMM_EINVAL, "y_per_slot must be 0 or 1");
     QMM_TRY(check_rows("T", T));
     QMM_TRY(check_rows("N", N));
-    QMM_TRY(check_k(K, 256));
+    QMM_TRY(check_k(K, w_qk(t)));
     const int64_t P = T * U;
     if (P > (int64_t(1) << 31) - 1) return fail(QMM_EUNSUPPORTED, "T*U = %lld pairs exceeds 2^31 - 1", (long long)P);
     if (P == 0 || N == 0) return QMM_OK;
+    const qmm_act_type at = t == QMM_Q4_0 ? QMM_Q8_0 : QMM_Q8_K;
     const int64_t y_rows = y_per_slot ? P : T;
-    const size_t w_one = qmm_weight_bytes(QMM_Q4_K, l, N, K);
+    const size_t w_one = qmm_weight_bytes(t, l, N, K);
     QMM_TRY(check_ptr("w", w));
     QMM_TRY(check_ptr("y", y));
     QMM_TRY(check_ptr("ids", ids));
     QMM_TRY(check_ptr("out", out));
     QMM_TRY(check_size("w", w_bytes, w_one * (size_t)E));
-    QMM_TRY(check_size("y", y_bytes, qmm_act_bytes(QMM_Q8_K, y_rows, K)));
+    QMM_TRY(check_size("y", y_bytes, qmm_act_bytes(at, y_rows, K)));
     QMM_TRY(check_size("out", out_bytes, (size_t)(P * N) * sizeof(float)));
-    const bool gemv_ok = K <= qmm::gemv1_max_k();
-    // the grouped GEMM addresses one expert matrix and the activations with 32-bit offsets
-    const bool mfma_ok = w_one < (size_t(1) << 32) && qmm_act_bytes(QMM_Q8_K, y_rows, K) < (size_t(1) << 32);
+    const bool gemv_ok = K <= kk.gemv_max_k;
+    // the grouped GEMMs address one expert matrix and the activations with 32-bit offsets
+    const bool mfma_ok = (kk.gemm_canonical || l == QMM_LAYOUT_REPACKED) && K % kk.gemm_k_mult == 0 &&
+                         w_one < (size_t(1) << 32) && qmm_act_bytes(at, y_rows, K) < (size_t(1) << 32);
     if (algo == QMM_ALGO_GEMV && !gemv_ok)
-        return fail(QMM_EUNSUPPORTED, "mul_mat_id GEMV takes K <= %lld", (long long)qmm::gemv1_max_k());
-    if (algo != QMM_ALGO_GEMV && !mfma_ok && !(algo == QMM_ALGO_AUTO && gemv_ok))
-        return fail(QMM_EUNSUPPORTED, "mul_mat_id MFMA path takes matrices below 4 GiB");
+        return fail(QMM_EUNSUPPORTED, "mul_mat_id GEMV takes K <= %lld", (long long)kk.gemv_max_k);
+    if (algo == QMM_ALGO_MFMA && !mfma_ok)
+        return fail(QMM_EUNSUPPORTED,
+                    "mul_mat_id MFMA path: this format needs the repacked layout, K a multiple of %lld and "
+                    "matrices below 4 GiB", (long long)kk.gemm_k_mult);
+    if (algo == QMM_ALGO_AUTO && !gemv_ok && !mfma_ok)
+        return fail(QMM_EUNSUPPORTED, "no mul_mat_id kernel takes this call (K = %lld)", (long long)K);
     qmm_algo a = algo;
     if (a == QMM_ALGO_AUTO) a = (P <= 64 && gemv_ok) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -408,16 +465,22 @@ qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_lay
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     const bool rep = l == QMM_LAYOUT_REPACKED;
     if (a == QMM_ALGO_GEMV)
-        return device_status(qmm::launch_gemv_id_q4_K(wb, rep, (int64_t)w_one, yb, y_per_slot, ids, P, U, E,
-                                                      out, N, K, s),
+        return device_status(kk.gemv(wb, rep, (int64_t)w_one, yb, y_per_slot, ids, P, U, E, out, N, K, s),
                              "mul_mat_id gemv launch");
     QMM_TRY(check_ptr("workspace", workspace));
     QMM_TRY(check_size("workspace", ws_bytes, qmm_mul_mat_id_workspace_bytes(T, U, E)));
     int32_t *ws = static_cast<int32_t *>(workspace);
     QMM_TRY(device_status(qmm::launch_moe_group_ids(ids, P, E, ws, out, N, s), "mul_mat_id grouping launch"));
-    return device_status(qmm::launch_gemm_id_q4_K(wb, rep, (int64_t)w_one, yb, y_rows, y_per_slot, U, ws, E,
-                                                  P, out, N, K, s),
+    return device_status(kk.gemm(wb, rep, (int64_t)w_one, yb, y_rows, y_per_slot, U, ws, E, P, out, N, K, s),
                          "mul_mat_id gemm launch");
+}
+
+qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_layout l, const void *y,
+                               size_t y_bytes, int y_per_slot, const int32_t *ids, int64_t T,
+                               int64_t U, float *out, size_t out_bytes, int64_t N, int64_t K,
+                               void *workspace, size_t ws_bytes, qmm_algo algo, void *stream) {
+    return qmm_mul_mat_id(QMM_Q4_K, w, w_bytes, E, l, y, y_bytes, y_per_slot, ids, T, U, out, out_bytes, N, K,
+                          workspace, ws_bytes, algo, stream);
 }
 
 qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes, qmm_layout l,

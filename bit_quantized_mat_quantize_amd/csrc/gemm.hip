@@ -67,17 +67,6 @@ static_assert(A_INSTR % NWAVE == 0, "staging must split evenly over the wavefron
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 static_assert(CT == 1 && 2 * BM <= NTHR, "one column tile per wavefront; bsums staged by 2*BM threads");
 
-// mul_mat_id (GROUPED = true): the expert-grouped tile table that
-// k_moe_group_ids builds.  Tile g covers the sorted slots tile_r0[g] .. of
-// expert tile_e[g] (at most BM of them, up to start[e+1]); sorted[slot] is a
-// (token, slot) pair p, whose activation row is p (y_per_slot) or p / U and
-// whose output row is p.  M is then the number of activation rows.
-struct Grouping {
-    const int32_t *start, *tile_e, *tile_r0, *ntiles, *sorted;
-    int64_t U, w_stride;
-    int y_per_slot;
-};
-
 template <bool REPACKED, bool GROUPED>
 __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict__ W,
                                                        const uint8_t *__restrict__ Y,
@@ -98,14 +87,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
     const int bid = blockIdx.x;
     int tile_m, tile_n, m_last_g = 0, r0 = 0;
     if constexpr (GROUPED) {
-        const int g = bid / tiles_n;
-        tile_n = bid - g * tiles_n;
+        int e;
         tile_m = 0;
-        if (g >= *grp.ntiles) return;  // beyond the tiles this routing produced (uniform)
-        const int e = grp.tile_e[g];
-        r0 = grp.tile_r0[g];
-        const int rows = grp.start[e + 1] - r0;
-        m_last_g = (rows < BM ? rows : BM) - 1;
+        if (!grouped_tile(grp, bid, tiles_n, BM, tile_n, r0, m_last_g, e)) return;  // uniform
         W += (int64_t)e * grp.w_stride;
     } else {
         const int v = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
@@ -130,8 +114,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
     // byte offset (from Y + a_first) of tile row rr <= m_last
     auto arow = [&](int rr) -> uint32_t {
         if constexpr (GROUPED) {
-            const int p = grp.sorted[r0 + rr];
-            return (uint32_t)(grp.y_per_slot ? (int64_t)p : (int64_t)p / grp.U) * a_rowstride;
+            return (uint32_t)grouped_row(grp, r0, rr) * a_rowstride;
         } else {
             return (uint32_t)rr * a_rowstride;
         }

@@ -233,18 +233,7 @@ __device__ __forceinline__ float gemv1_accumulate(const uint4 &hw, const uint4 (
     return acc;
 }
 
-// ID = true (mul_mat_id): blockIdx.y is a (token, slot) pair p0 + y; its
-// expert id selects the weight matrix, its token (or the pair itself) the
-// activation row, and the pair the output row.  An id outside [0, E) reads
-// expert 0 (every load stays in bounds) and stores NaN.
-struct IdRoute {
-    const int32_t *ids;
-    int64_t p0, U, E;
-    int64_t w_stride;    // bytes per expert matrix
-    int64_t y_rowbytes;  // bytes per activation row
-    int y_per_slot;
-};
-
+// ID = true: mul_mat_id, one (token, slot) pair per blockIdx.y (id_route).
 template <bool REPACKED, int kNit, bool ID>
 __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ W,
                                                     const uint8_t *__restrict__ Y,
@@ -252,12 +241,11 @@ __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ 
                                                     IdRoute route) {
     bool valid = true;
     if constexpr (ID) {
-        const int64_t p = route.p0 + blockIdx.y;
-        const int e = route.ids[p];
-        valid = e >= 0 && e < route.E;
-        W += (valid ? (int64_t)e : 0) * route.w_stride;
-        Y += (route.y_per_slot ? p : p / route.U) * route.y_rowbytes;
-        out += p * N;
+        const IdPair ip = id_route(route);
+        valid = ip.valid;
+        W += ip.w_off;
+        Y += ip.y_off;
+        out += ip.out_row * N;
     }
     // 16-byte activation pieces per thread loaded up front (K <= 4096 * kYT)
     constexpr int kYT = kNit >= 8 ? 4 : (kNit + 1) / 2;
@@ -414,11 +402,20 @@ __device__ __forceinline__ uint32_t ld_u32_a2(const uint8_t *p) {
     return (uint32_t)q[0] | ((uint32_t)q[1] << 16);
 }
 
-template <int M, bool REPACKED, int MODE>
+// ID = true (M = 1, MODE 0): mul_mat_id, one (token, slot) pair per blockIdx.y.
+template <int M, bool REPACKED, int MODE, bool ID = false>
 __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ W,
                                                    const uint8_t *__restrict__ Y,
                                                    void *__restrict__ dst, int64_t N, int64_t K,
-                                                   int64_t dsec) {
+                                                   int64_t dsec, IdRoute route = {}) {
+    bool valid = true;
+    if constexpr (ID) {
+        const IdPair ip = id_route(route);
+        valid = ip.valid;
+        W += ip.w_off;
+        Y += ip.y_off;
+        dst = reinterpret_cast<float *>(dst) + ip.out_row * N;
+    }
     const int64_t nb = K / QK4_0;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -466,7 +463,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ W
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const float v = wave_sum(acc[m]);
-            if (lane == 0) out[(int64_t)m * N + n] = v;
+            if (lane == 0) out[(int64_t)m * N + n] = valid ? v : __builtin_nanf("");
         }
     }
 }
@@ -654,6 +651,26 @@ hipError_t launch_block_sums_q4_K(const uint8_t *w, bool repacked, const uint8_t
 hipError_t launch_gemv_q4_0(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s) {
     return dispatch_q4_0<0>(w, repacked, y, out, M, N, K, s);
+}
+
+hipError_t launch_gemv_id_q4_0(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
+                               int y_per_slot, const int32_t *ids, int64_t P, int64_t U, int64_t E,
+                               float *out, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t dsec = repacked ? (2 * N * (K / QK4_0) + 255) / 256 * 256 : 0;
+    for (int64_t p0 = 0; p0 < P; p0 += 65535) {
+        const int64_t pp = P - p0 < 65535 ? P - p0 : 65535;
+        const dim3 grid((unsigned)((N + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)pp);
+        const IdRoute r{ids, p0, U, E, w_stride, (K / QK4_0) * kQ8_0Bytes, y_per_slot};
+        if (repacked)
+            hipLaunchKernelGGL((k_gemv_q4_0<1, true, 0, true>), grid, dim3(256), 0, s, w, y, (void *)out, N, K,
+                               dsec, r);
+        else
+            hipLaunchKernelGGL((k_gemv_q4_0<1, false, 0, true>), grid, dim3(256), 0, s, w, y, (void *)out, N, K,
+                               dsec, r);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_block_sums_q4_0(const uint8_t *w, bool repacked, const uint8_t *y, int32_t *P,

@@ -50,5 +50,34 @@ __device__ __forceinline__ uint32_t h2_bits(int lo, int hi) {
     return f32_to_f16_bits((float)lo) | (f32_to_f16_bits((float)hi) << 16);
 }
 
+// mul_mat_id (GROUPED GEMMs): the expert-grouped tile table that
+// k_moe_group_ids builds.  Tile g covers the sorted slots tile_r0[g] .. of
+// expert tile_e[g] (at most 128 of them, up to start[e+1]); sorted[slot] is a
+// (token, slot) pair p, whose activation row is p (y_per_slot) or p / U and
+// whose output row is p.  The GEMM's M is then the number of activation rows.
+struct Grouping {
+    const int32_t *start, *tile_e, *tile_r0, *ntiles, *sorted;
+    int64_t U, w_stride;
+    int y_per_slot;
+};
+// Tile of workgroup bid (tiles_n column tiles per row tile): false when the
+// routing produced fewer tiles (the whole workgroup then exits).
+__device__ __forceinline__ bool grouped_tile(const Grouping &g, int bid, int tiles_n, int bm, int &tile_n,
+                                             int &r0, int &m_last, int &e) {
+    const int t = bid / tiles_n;
+    tile_n = bid - t * tiles_n;
+    if (t >= *g.ntiles) return false;
+    e = g.tile_e[t];
+    r0 = g.tile_r0[t];
+    const int rows = g.start[e + 1] - r0;
+    m_last = (rows < bm ? rows : bm) - 1;
+    return true;
+}
+// activation row of tile row rr (0 <= rr <= m_last)
+__device__ __forceinline__ int64_t grouped_row(const Grouping &g, int r0, int rr) {
+    const int p = g.sorted[r0 + rr];
+    return g.y_per_slot ? (int64_t)p : (int64_t)p / g.U;
+}
+
 }  // namespace
 }  // namespace qmm

@@ -182,13 +182,24 @@ __device__ __forceinline__ void q2k_group_sums(const Q2KUnit &x, int u, const ui
 constexpr int kQ2Waves = 4;
 
 // MODE 0: out[m*N + n] (fp32).  MODE 1: P[m][n][K/16] (int32 group sums).
-template <bool REPACKED, int kNit, int MODE>
+// ID = true (MODE 0): mul_mat_id, one (token, slot) pair per blockIdx.y.
+template <bool REPACKED, int kNit, int MODE, bool ID = false>
 __global__ __launch_bounds__(256) void k_gemv_q2_K(const uint8_t *__restrict__ W,
                                                    const uint8_t *__restrict__ Y,
-                                                   void *__restrict__ dst, int64_t N, int64_t K) {
+                                                   void *__restrict__ dst, int64_t N, int64_t K,
+                                                   IdRoute route = {}) {
     extern __shared__ __attribute__((aligned(16))) uint8_t ys[];
     const int64_t nb = K / QK_K;
-    const int64_t m = blockIdx.y;
+    int64_t m = blockIdx.y, m_out = blockIdx.y;  // activation row, output row
+    bool valid = true;
+    if constexpr (ID) {
+        const IdPair ip = id_route(route);
+        valid = ip.valid;
+        W += ip.w_off;
+        Y += ip.y_off;
+        m_out = ip.out_row;
+        m = 0;
+    }
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t n = (int64_t)blockIdx.x * kQ2Waves + wave;
     const int64_t nn = n < N ? n : N - 1;  // a tail wavefront loads a valid row, stores nothing
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(256) void k_gemv_q2_K(const uint8_t *__restrict__ W
     }
     if (MODE == 0) {
         acc = wave_sum(acc);
-        if (lane == 0 && n < N) reinterpret_cast<float *>(dst)[m * N + n] = acc;
+        if (lane == 0 && n < N) reinterpret_cast<float *>(dst)[m_out * N + n] = valid ? acc : __builtin_nanf("");
     }
 }
 
@@ -301,6 +312,32 @@ hipError_t launch_gemv_q2_K(const uint8_t *w, bool repacked, const uint8_t *y, f
     for (int64_t m0 = 0; m0 < M; m0 += 65535) {
         const int64_t mm = M - m0 < 65535 ? M - m0 : 65535;
         const hipError_t e = dispatch_q2_K<0>(w, repacked, y + m0 * rowb, out + m0 * N, mm, N, K, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_gemv_id_q2_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
+                               int y_per_slot, const int32_t *ids, int64_t P, int64_t U, int64_t E,
+                               float *out, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t nit = (4 * (K / QK_K) + 63) / 64;
+    const unsigned lds = (unsigned)q8k_row_lds_bytes(K);
+    for (int64_t p0 = 0; p0 < P; p0 += 65535) {
+        const int64_t pp = P - p0 < 65535 ? P - p0 : 65535;
+        const dim3 grid((unsigned)((N + kQ2Waves - 1) / kQ2Waves), (unsigned)pp);
+        const IdRoute r{ids, p0, U, E, w_stride, (K / QK_K) * kQ8_KBytes, y_per_slot};
+#define QMM_ID(NIT)                                                                                   \
+    do {                                                                                              \
+        if (repacked)                                                                                 \
+            hipLaunchKernelGGL((k_gemv_q2_K<true, NIT, 0, true>), grid, dim3(256), lds, s, w, y, (void *)out, N, K, r);  \
+        else                                                                                          \
+            hipLaunchKernelGGL((k_gemv_q2_K<false, NIT, 0, true>), grid, dim3(256), lds, s, w, y, (void *)out, N, K, r); \
+    } while (0)
+        if (nit <= 1) QMM_ID(1);
+        else if (nit <= 2) QMM_ID(2);
+        else QMM_ID(4);
+#undef QMM_ID
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -52,10 +52,11 @@ struct Q2KStage {
     uint32_t dm;
 };
 
+template <bool GROUPED>
 __global__ __launch_bounds__(NTHR, 1) void k_gemm_q2_K(const uint8_t *__restrict__ W, int64_t w_bytes,
                                                        const uint8_t *__restrict__ Y,
                                                        float *__restrict__ out, int64_t M, int64_t N,
-                                                       int64_t K, int tiles_m, int tiles_n) {
+                                                       int64_t K, int tiles_m, int tiles_n, Grouping grp) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -66,33 +67,46 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q2_K(const uint8_t *__restrict
     constexpr int GM = 4;
     const int nwg = tiles_m * tiles_n;
     const int bid = blockIdx.x;
-    const int v = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
-    const int group = v / (GM * tiles_n), first_m = group * GM;
-    const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;
-    const int in_group = v - group * GM * tiles_n;
-    // (the division runs on the vector ALU; readfirstlane keeps the tile uniform)
-    const int tile_m = __builtin_amdgcn_readfirstlane(first_m + in_group % gm);
-    const int tile_n = __builtin_amdgcn_readfirstlane(in_group / gm);
+    int tile_m, tile_n, m_last_g = 0, r0 = 0;
+    if constexpr (GROUPED) {  // mul_mat_id: tile from the expert grouping
+        int e;
+        tile_m = 0;
+        if (!grouped_tile(grp, bid, tiles_n, BM, tile_n, r0, m_last_g, e)) return;  // uniform
+        W += (int64_t)e * grp.w_stride;
+    } else {
+        const int v = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+        const int group = v / (GM * tiles_n), first_m = group * GM;
+        const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;
+        const int in_group = v - group * GM * tiles_n;
+        // (the division runs on the vector ALU; readfirstlane keeps the tile uniform)
+        tile_m = __builtin_amdgcn_readfirstlane(first_m + in_group % gm);
+        tile_n = __builtin_amdgcn_readfirstlane(in_group / gm);
+    }
     const int64_t m_base = (int64_t)tile_m * BM, n_base = (int64_t)tile_n * BN;
     const int64_t nb = K / QK_K;
 
     // ---- activation staging (rows past M clamped to the last valid one)
-    const int m_last = (int)(M - 1 - m_base < BM - 1 ? M - 1 - m_base : BM - 1);
+    const int m_last = GROUPED ? m_last_g : (int)(M - 1 - m_base < BM - 1 ? M - 1 - m_base : BM - 1);
     const uint32_t a_rowstride = (uint32_t)(nb * kQ8_KBytes);
     const int64_t a_first = m_base * nb * kQ8_KBytes;
     const int64_t a_bytes = M * nb * kQ8_KBytes - a_first;
+    // byte offset (from Y + a_first) of tile row rr <= m_last
+    auto arow = [&](int rr) -> uint32_t {
+        if constexpr (GROUPED) return (uint32_t)grouped_row(grp, r0, rr) * a_rowstride;
+        else return (uint32_t)rr * a_rowstride;
+    };
     uint32_t a_goff[A_PER_WAVE];
 #pragma unroll
     for (int t = 0; t < A_PER_WAVE; ++t) {
         const int row = (wave * A_PER_WAVE + t) * 4 + (lane >> 4);
         const int gp = (lane & 15) ^ (row & 15);  // global piece stored at position lane & 15
         const int rr = row < m_last ? row : m_last;
-        a_goff[t] = (uint32_t)rr * a_rowstride + 4 + 16 * gp;
+        a_goff[t] = arow(rr) + 4 + 16 * gp;
     }
     // bsums: row tid>>1, 16-byte half tid&1 (threads < 256); d_a: row tid (threads < 128)
     const int s_row = (tid >> 1) & (BM - 1);
-    const uint32_t s_off = (uint32_t)(s_row < m_last ? s_row : m_last) * a_rowstride + 260 + 16 * (tid & 1);
-    const uint32_t d_off = (uint32_t)((tid & (BM - 1)) < m_last ? (tid & (BM - 1)) : m_last) * a_rowstride;
+    const uint32_t s_off = arow(s_row < m_last ? s_row : m_last) + 260 + 16 * (tid & 1);
+    const uint32_t d_off = arow((tid & (BM - 1)) < m_last ? (tid & (BM - 1)) : m_last);
 
     // ---- this lane's weight column (columns past N clamped; never stored)
     const int64_t NB = N * nb;
@@ -241,27 +255,50 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q2_K(const uint8_t *__restrict
         for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = m_base + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (m < M) out[m * N + n] = acc[i][r];
+                if constexpr (GROUPED) {
+                    const int lm = i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (lm <= m_last) out[(int64_t)grp.sorted[r0 + lm] * N + n] = acc[i][r];
+                } else {
+                    const int64_t m = m_base + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (m < M) out[m * N + n] = acc[i][r];
+                }
             }
     }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
-                            int64_t M, int64_t N, int64_t K, hipStream_t s) {
+namespace {
+template <bool GROUPED>
+hipError_t launch_t(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M, int64_t N,
+                    int64_t K, int tiles_m, const Grouping &g, hipStream_t s) {
     static bool attr_set = false;  // the LDS budget above 64 KiB must be opted into once
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_q2_K,
+        const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_q2_K<GROUPED>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    hipLaunchKernelGGL(k_gemm_q2_K, dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), LDS_BYTES, s,
-                       w, w_bytes, y, out, M, N, K, tiles_m, tiles_n);
+    const int tiles_n = (int)((N + BN - 1) / BN);
+    hipLaunchKernelGGL((k_gemm_q2_K<GROUPED>), dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), LDS_BYTES, s,
+                       w, w_bytes, y, out, M, N, K, tiles_m, tiles_n, g);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    return launch_t<false>(w, w_bytes, y, out, M, N, K, (int)((M + BM - 1) / BM), Grouping{}, s);
+}
+
+// mul_mat_id: w_bytes and w_stride are the bytes of one expert matrix
+hipError_t launch_gemm_id_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, int64_t y_rows,
+                               int y_per_slot, int64_t U, const int32_t *group_ws, int64_t E, int64_t P,
+                               float *out, int64_t N, int64_t K, hipStream_t s) {
+    const MoeGroupLayout L = moe_group_layout(P, E, BM);
+    const Grouping g{group_ws + L.start, group_ws + L.tile_e, group_ws + L.tile_r0, group_ws + L.ntiles,
+                     group_ws + L.sorted, U, w_bytes, y_per_slot};
+    return launch_t<true>(w, w_bytes, y, out, y_rows, N, K, (int)L.max_tiles, g, s);
 }
 
 }  // namespace qmm

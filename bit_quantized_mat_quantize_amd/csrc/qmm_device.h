@@ -137,4 +137,27 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xff) << 24);
 }
 
+// ---- mul_mat_id routing for the per-pair GEMVs: blockIdx.y is the (token,
+// slot) pair p0 + y; its expert id selects the weight matrix, its token (or the
+// pair itself) the activation row, and the pair the output row.  An id outside
+// [0, E) selects expert 0 (every load stays in bounds) and reports invalid;
+// the caller then stores NaN.
+struct IdRoute {
+    const int32_t *ids;
+    int64_t p0, U, E;
+    int64_t w_stride;    // bytes per expert matrix
+    int64_t y_rowbytes;  // bytes per activation row
+    int y_per_slot;
+};
+struct IdPair {
+    int64_t w_off, y_off, out_row;  // byte offsets into W and Y, output row
+    bool valid;
+};
+__device__ __forceinline__ IdPair id_route(const IdRoute &r) {
+    const int64_t p = r.p0 + blockIdx.y;
+    const int e = r.ids[p];
+    const bool valid = e >= 0 && e < r.E;
+    return IdPair{(valid ? (int64_t)e : 0) * r.w_stride, (r.y_per_slot ? p : p / r.U) * r.y_rowbytes, p, valid};
+}
+
 }  // namespace qmm

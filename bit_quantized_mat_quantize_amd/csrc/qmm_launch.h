@@ -110,7 +110,26 @@ hipError_t launch_moe_group_ids(const int32_t *ids, int64_t P, int64_t E, int32_
 hipError_t launch_gemv_id_q4_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
                                int y_per_slot, const int32_t *ids, int64_t P, int64_t U, int64_t E,
                                float *out, int64_t N, int64_t K, hipStream_t s);
-// The Q4_K GEMM over the grouped tiles (after launch_moe_group_ids on ws).
+hipError_t launch_gemv_id_q6_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
+                               int y_per_slot, const int32_t *ids, int64_t P, int64_t U, int64_t E,
+                               float *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemv_id_q2_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
+                               int y_per_slot, const int32_t *ids, int64_t P, int64_t U, int64_t E,
+                               float *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemv_id_q4_0(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
+                               int y_per_slot, const int32_t *ids, int64_t P, int64_t U, int64_t E,
+                               float *out, int64_t N, int64_t K, hipStream_t s);
+// The GEMMs over the grouped tiles (after launch_moe_group_ids on ws); the
+// Q6_K, Q2_K and Q4_0 ones take the repacked layout, w_bytes = one expert.
+hipError_t launch_gemm_id_q6_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, int64_t y_rows,
+                               int y_per_slot, int64_t U, const int32_t *group_ws, int64_t E, int64_t P,
+                               float *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemm_id_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, int64_t y_rows,
+                               int y_per_slot, int64_t U, const int32_t *group_ws, int64_t E, int64_t P,
+                               float *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemm_id_q4_0(const uint8_t *w, int64_t w_bytes, const uint8_t *y, int64_t y_rows,
+                               int y_per_slot, int64_t U, const int32_t *group_ws, int64_t E, int64_t P,
+                               float *out, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_id_q4_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
                                int64_t y_rows, int y_per_slot, int64_t U, const int32_t *group_ws,
                                int64_t E, int64_t P, float *out, int64_t N, int64_t K, hipStream_t s);

@@ -251,13 +251,27 @@ size_t qmm_mul_mat_id_workspace_bytes(int64_t T, int64_t U, int64_t E);
  * below 4 GiB); AUTO takes the GEMV for T*U <= 64, the GEMM above.  An id
  * outside [0, E) cannot be checked on the host: that pair's output row is
  * filled with NaN and nothing is read out of bounds.  Requires 1 <= E <= 4096,
- * 1 <= U <= E. */
+ * 1 <= U <= E.  Equal to qmm_mul_mat_id(QMM_Q4_K, ...). */
 qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_layout l,
                                const void *y, size_t y_bytes, int y_per_slot,
                                const int32_t *ids, int64_t T, int64_t U,
                                float *out, size_t out_bytes, int64_t N, int64_t K,
                                void *workspace, size_t ws_bytes, qmm_algo algo,
                                void *stream);
+
+/* mul_mat_id for any weight format t: the same contract as
+ * qmm_mul_mat_id_q4_K with W_e in format t (Q8_0 activations for Q4_0, Q8_K
+ * otherwise).  Kernels: QMM_ALGO_GEMV -- one GEMV per (token, slot) (K <=
+ * 53760 for Q4_K, Q6_K and Q2_K); QMM_ALGO_MFMA -- the expert grouping into
+ * `workspace`, then the format's MFMA GEMM over each expert's rows (Q6_K, Q2_K
+ * and Q4_0 need the repacked layout, and K % 256 == 0); AUTO takes the GEMV
+ * for T*U <= 64 and the GEMM above, whichever the call allows otherwise. */
+qmm_status qmm_mul_mat_id(qmm_weight_type t, const void *w, size_t w_bytes, int64_t E, qmm_layout l,
+                          const void *y, size_t y_bytes, int y_per_slot,
+                          const int32_t *ids, int64_t T, int64_t U,
+                          float *out, size_t out_bytes, int64_t N, int64_t K,
+                          void *workspace, size_t ws_bytes, qmm_algo algo,
+                          void *stream);
 
 /* Quantize-and-multiply in one call: y = quantize_row_q8(x) (Q8_0 for t = Q4_0,
  * Q8_K for t = Q4_K, Q6_K and Q2_K), then out = mul_mat(w, y).  The ggml-cpu mul_mat page

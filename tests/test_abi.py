@@ -237,6 +237,37 @@ def test_mul_mat_id_validation(lib):
     assert call(algo=2, wsb=wsb(3, 2, 4) - 1) == EINVAL
 
 
+
+def test_mul_mat_id_generic_validation(lib):
+    f = lib.qmm_mul_mat_id
+    big = 10**9
+    wsb = lib.qmm_mul_mat_id_workspace_bytes
+
+    def call(t, **kw):
+        a = dict(w=A, wb=big, E=4, l=1, y=A, yb=big, yps=0, ids=A, T=3, U=2, o=A, ob=big, N=8, K=512,
+                 ws=A, wsb=big, algo=0)
+        a.update(kw)
+        return f(t, a["w"], a["wb"], a["E"], a["l"], a["y"], a["yb"], a["yps"], a["ids"], a["T"], a["U"],
+                 a["o"], a["ob"], a["N"], a["K"], a["ws"], a["wsb"], a["algo"], None)
+
+    assert call(7) == EUNSUP and "weight type" in _last(lib)
+    # Q4_0 rows of 32-weight blocks against Q8_0 activations (34 bytes per 32)
+    assert call(0, K=96, algo=1, wb=4 * 8 * 3 * 18 - 1) == EINVAL
+    assert call(0, K=96, algo=1, yb=3 * 3 * 34 - 1) == EINVAL
+    assert call(0, K=100) == EUNSUP                          # K not a multiple of 32
+    assert call(0, K=96, algo=2) == EUNSUP                   # MFMA path steps K by 256
+    assert call(0, K=512, algo=2, l=0) == EUNSUP             # ... and reads the repacked layout
+    # Q6_K and Q2_K: canonical matrices only through the GEMV
+    for t, per in ((2, 210), (3, 84)):
+        assert call(t, algo=2, l=0) == EUNSUP
+        assert call(t, algo=1, wb=4 * 8 * 2 * per - 1, l=0) == EINVAL
+        assert call(t, algo=1, K=53760 + 256) == EUNSUP      # one Q8_K row staged in LDS
+        assert call(t, algo=2, wsb=wsb(3, 2, 4) - 1) == EINVAL
+        assert call(t, T=0, w=None, y=None, ids=None, o=None, ws=None) == OK
+    # the Q4_K entry point is the generic one with its type fixed
+    assert call(1, algo=1, K=53760 + 256) == EUNSUP
+
+
 def test_other_validation(lib):
     assert lib.qmm_quantize_weights(1, A, 4, 100, A, 10**6, None) == EUNSUP
     assert lib.qmm_quantize_weights(0, A, 4, 64, A, 4 * 2 * 18 - 1, None) == EINVAL

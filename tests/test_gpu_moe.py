@@ -148,3 +148,56 @@ def test_mixture_of_experts_shape_sampled():
     rows = y.reshape(T, -1)[sub]
     want, terms = oracle.mul_mat_id("q4_K", w, E, N, K, rows, ids[sub])
     assert_close(got[sub], want, terms, "moe 8x4096x4096 sampled")
+
+
+# ------------------------------------------------ the other weight formats
+OTHER = ["q4_0", "q6_K", "q2_K"]
+ACT = {"q4_0": "q8_0", "q6_K": "q8_K", "q2_K": "q8_K"}
+
+
+def _stack_fmt(fmt, E, N, K, seed):
+    return np.concatenate([oracle.quantize(fmt, weights_t4_skewed([seed, e], N, K)) for e in range(E)])
+
+
+def _upload_fmt(fmt, w, E, N, K, layout):
+    wd = to_dev(w.reshape(-1))
+    if layout == "canonical":
+        return wd
+    per = w.size // E
+    return qmm_cat([qmm.repack_weights(wd[e * per:(e + 1) * per], fmt, N, K) for e in range(E)])
+
+
+@pytest.mark.parametrize("fmt", OTHER)
+@pytest.mark.parametrize("algo,T,layouts", [("gemv", 5, ("canonical", "repacked")), ("mfma", 200, ("repacked",))])
+@pytest.mark.parametrize("y_per_slot", [False, True])
+def test_mul_mat_id_formats(fmt, algo, T, layouts, y_per_slot):
+    U, E, N, K = 2, 5, 130, 1024
+    rng = np.random.default_rng(50 + T)
+    w = _stack_fmt(fmt, E, N, K, 840)
+    y = oracle.quantize(ACT[fmt], activations([841, T], T * U if y_per_slot else T, K, outlier_frac=0.01))
+    ids = _routing(rng, T, U, E)
+    want, terms = oracle.mul_mat_id(fmt, w, E, N, K, y, ids, y_per_slot)
+    for layout in layouts:
+        got = to_host(qmm.mul_mat_id(fmt, _upload_fmt(fmt, w, E, N, K, layout), E, to_dev(y.reshape(-1)),
+                                     to_dev(ids), N, K, layout=layout, y_per_slot=y_per_slot, algo=algo))
+        assert_close(got, want, terms, f"{fmt} {algo} {layout} per_slot={y_per_slot}")
+
+
+@pytest.mark.parametrize("fmt", OTHER)
+def test_mul_mat_id_formats_bad_ids(fmt):
+    T, U, E, N, K = 100, 2, 4, 40, 512
+    rng = np.random.default_rng(51)
+    w = _stack_fmt(fmt, E, N, K, 842)
+    y = oracle.quantize(ACT[fmt], activations([843, 0], T, K))
+    ids = _routing(rng, T, U, E, skew=False)
+    bad = ids.copy()
+    bad[3, 0], bad[50, 1] = E + 2, -5
+    good = np.ones((T, U), bool)
+    good[3, 0] = good[50, 1] = False
+    want, terms = oracle.mul_mat_id(fmt, w, E, N, K, y, np.where(good, bad, 0).astype(np.int32))
+    wd = _upload_fmt(fmt, w, E, N, K, "repacked")
+    for algo in ("gemv", "mfma"):
+        got = to_host(qmm.mul_mat_id(fmt, wd, E, to_dev(y.reshape(-1)), to_dev(bad), N, K, layout="repacked",
+                                     algo=algo))
+        assert np.isnan(got[~good]).all(), algo
+        assert_close(got[good], want[good], terms[good], f"{fmt} {algo} with bad ids")
