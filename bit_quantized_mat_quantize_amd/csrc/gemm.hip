@@ -38,9 +38,14 @@
 //   BS  bsums, fp16  [128][24]   stride 48 B
 //   DA  d_a          [128]
 // (the XOR placement makes the 16-byte reads down 16 consecutive rows hit
-// distinct banks).  Each wavefront decodes the eight sub-block planes of its
-// column tile into registers once per step, before the barrier, then walks
-// its four row tiles.
+// distinct banks).  Each wavefront walks its four row tiles once per step.
+// The eight sub-block planes of its column tile are built inside row tile 0,
+// plane j just before the first MFMAs that read it, so the decode of j + 1
+// issues while the MFMAs of j run; the next step's weights are loaded once
+// the planes are built.  The tail of row tile i (S = 8*ACC_hi + ACC_lo,
+// t = d*S on the vector ALU, the min term added by two fp16 MFMAs that take
+// t as their accumulator input, acc += d_a*t) is placed after the MFMAs of
+// row tile i + 1 for the same reason.
 //
 // MFMA operand convention (v_mfma_*_32x32xK): lane l supplies row (A) or
 // column (B) l % 32 and the K-slice selected by l / 32; A and B use the same
@@ -195,34 +200,34 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
         uint8_t *buf = lds + (b & 1) * BUF_BYTES;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of step b
         commit(raw, draw, buf);
-        // ---------------- this lane's column: header and the 8 sub-block planes
+        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
+        if (b + 1 < nb) {
+            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
+            prefetch(b + 1, raw, draw);
+        }
+        // ---------------- this lane's column: header; the 8 sub-block planes are
+        // built inside row tile 0, each just before its first MFMAs, so the
+        // decode of sub-block j + 1 overlaps the MFMAs of sub-block j
         const uint4 hdr = wx.hdr;
         const float dcol = f16_bits_to_f32(hdr.x & 0xffff);
         const float dmcol = f16_bits_to_f32(hdr.x >> 16);
         const Q4KScales sc = unpack_scales(hdr.y, hdr.z, hdr.w);
         v4i bhi[8], blo[8];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int piece = 2 * g + hh;  // this lane's K-slice of sub-blocks 2g, 2g+1
-            const uint4 pw = wx.pay[g];
-            (void)piece;
-            const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {  // t = 0: low nibbles (sub-block 2g), 1: high (2g+1)
-                const int j = 2 * g + t;
-                const int shift = t * 4;
-                const uint32_t q0 = (pw.x >> shift) & 0x0f0f0f0fu, q1 = (pw.y >> shift) & 0x0f0f0f0fu;
-                const uint32_t q2 = (pw.z >> shift) & 0x0f0f0f0fu, q3 = (pw.w >> shift) & 0x0f0f0f0fu;
-                const uint32_t sj = (sw >> (8 * (j & 3))) & 0xff;
-                const uint32_t hi2 = (sj >> 3) * 0x00010001u, lo2 = (sj & 7) * 0x00010001u;
-                bhi[j] = v4i{plane(q0, hi2), plane(q1, hi2), plane(q2, hi2), plane(q3, hi2)};
-                blo[j] = v4i{plane(q0, lo2), plane(q1, lo2), plane(q2, lo2), plane(q3, lo2)};
-            }
-        }
+        auto build = [&](int j) {
+            const uint4 pw = wx.pay[j >> 1];
+            const uint32_t sw = j < 4 ? sc.s_lo : sc.s_hi;
+            const int shift = (j & 1) * 4;  // low nibbles: sub-block 2g, high: 2g + 1
+            const uint32_t q0 = (pw.x >> shift) & 0x0f0f0f0fu, q1 = (pw.y >> shift) & 0x0f0f0f0fu;
+            const uint32_t q2 = (pw.z >> shift) & 0x0f0f0f0fu, q3 = (pw.w >> shift) & 0x0f0f0f0fu;
+            const uint32_t sj = (sw >> (8 * (j & 3))) & 0xff;
+            const uint32_t hi2 = (sj >> 3) * 0x00010001u, lo2 = (sj & 7) * 0x00010001u;
+            bhi[j] = v4i{plane(q0, hi2), plane(q1, hi2), plane(q2, hi2), plane(q3, hi2)};
+            blo[j] = v4i{plane(q0, lo2), plane(q1, lo2), plane(q2, lo2), plane(q3, lo2)};
+        };
         // min-term operand: -dmin*m_j has at most 17 significant bits, so it is
         // the exact sum of two fp16 values (hi = fp16(-dmin*m), lo = remainder);
-        // two fp16 MFMAs against the exact fp16 bsums give -dmin*Mn with fp32
-        // rounding only.
+        // two fp16 MFMAs against the exact fp16 bsums add -dmin*Mn to d*S in
+        // fp32 (the MFMA's accumulator input carries d*S).
         v8h bmh, bml;
         {
             const uint32_t mw = hh == 0 ? sc.m_lo : sc.m_hi;  // m_{4hh .. 4hh+3}
@@ -238,16 +243,27 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
             __builtin_memcpy(&bmh, bh, 16);
             __builtin_memcpy(&bml, bl, 16);
         }
-        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
-        if (b + 1 < nb) {
-            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
-            prefetch(b + 1, raw, draw);
-            wload(b + 1, wx);
-        }
-
         const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
 
-        // ---------------- the four row tiles of this column tile
+        // ---------------- the four row tiles of this column tile.  The tail of
+        // row tile i - 1 (conversion, min term, accumulation) is placed after the
+        // MFMAs of row tile i, so its vector work can issue while they run.
+        v16i s_prev;
+        v8h bs_prev;
+        auto tail = [&](int i, const v16i &S, const v8h &a_bs) {
+            v16f t;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[r] = dcol * (float)S[r];
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmh, t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bml, t, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][0][4 * q + e] = fmaf(dv[e], t[4 * q + e], acc[i][0][4 * q + e]);
+            }
+        };
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int row = i * 32 + l32;
@@ -266,31 +282,21 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int j = 4 * half + jj;
+                    if (i == 0) build(j);
                     ah = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[jj], bhi[j], j ? ah : zero, 0, 0, 0);
                     al = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[jj], blo[j], j ? al : zero, 0, 0, 0);
                 }
             }
-            v8h a_bs;
+            if (i == 0 && b + 1 < nb) wload(b + 1, wx);  // the planes no longer need wx
+            if (i > 0) tail(i - 1, s_prev, bs_prev);
             {
                 const uint4 au = *reinterpret_cast<const uint4 *>(buf + BS_OFF + row * BS_STRIDE + 16 * hh);
-                __builtin_memcpy(&a_bs, &au, 16);
+                __builtin_memcpy(&bs_prev, &au, 16);
             }
-            const v16f zf = {};
-            v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmh, zf, 0, 0, 0);
-            mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bml, mn, 0, 0, 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
-                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * q + e;
-                    const int S = (ah[r] << 3) + al[r];
-                    const float t = fmaf(dcol, (float)S, mn[r]);
-                    acc[i][0][r] = fmaf(dv[e], t, acc[i][0][r]);
-                }
-            }
+            for (int r = 0; r < 16; ++r) s_prev[r] = (ah[r] << 3) + al[r];
         }
+        tail(MT - 1, s_prev, bs_prev);
     }
 
     // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
