@@ -14,6 +14,10 @@
 // bsums (as fp16) and d_a are double-buffered in LDS (direct global->LDS
 // loads for the codes), and each lane loads the 52 bytes of its column it
 // needs straight into registers, one step ahead.
+// Step order as in the Q4_K GEMM: the weight operands of chunk c are built
+// inside row tile 0 just before its first MFMAs (the next step's weights load
+// once they are built), and the tail of row tile i sits after the MFMAs of
+// row tile i + 1, so vector and matrix work of one wavefront overlap.
 //
 // In v_mfma_i32_32x32x32_i8 lane l supplies the 16 consecutive elements
 // 16*(l/32).. of a 32-element chunk -- one Q2_K group -- so the group scale is
@@ -170,14 +174,22 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q2_K(const uint8_t *__restrict
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of step b
         commit(raw, draw, buf);
 
+        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
+        if (b + 1 < nb) {
+            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
+            prefetch(b + 1, raw, draw);
+        }
+        const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
+
         // ---------------- decode: chunk c holds group G = 2c + hh of this lane,
-        // elements 128(c/4) + 32(c%4) + 16hh + i: qs piece (c/4)*2 + hh, field c%4
+        // elements 128(c/4) + 32(c%4) + 16hh + i: qs piece (c/4)*2 + hh, field c%4.
+        // The planes are built inside row tile 0, chunk c just before its MFMA,
+        // so the decode of c + 1 issues while the MFMA of c runs.
         const float dcol = f16_bits_to_f32(wx.dm & 0xffff);
         const float dmneg = -f16_bits_to_f32(wx.dm >> 16);
         const uint32_t sw[4] = {wx.sc.x, wx.sc.y, wx.sc.z, wx.sc.w};
         v4i bq[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        auto build = [&](int c) {
             const uint4 pc = c < 4 ? wx.qa : wx.qb;
             const int sh = 2 * (c & 3);
             // scale byte 2c + hh: dword c/2, byte 2(c%2) + hh; s_j is its low nibble
@@ -185,7 +197,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q2_K(const uint8_t *__restrict
             const uint32_t s2 = sj * 0x00010001u;
             bq[c] = v4i{plane((pc.x >> sh) & 0x03030303u, s2), plane((pc.y >> sh) & 0x03030303u, s2),
                         plane((pc.z >> sh) & 0x03030303u, s2), plane((pc.w >> sh) & 0x03030303u, s2)};
-        }
+        };
         // mins of groups 8hh..8hh+7 as fp16 (the B operand of the Mn contraction)
         v8h bmn;
         {
@@ -197,15 +209,30 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q2_K(const uint8_t *__restrict
             }
         }
 
-        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
-        if (b + 1 < nb) {
-            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
-            prefetch(b + 1, raw, draw);
-            wload(b + 1, wx);
-        }
-        const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
-
-        // ---------------- the four row tiles of this column tile
+        // ---------------- the four row tiles of this column tile.  The tail of
+        // row tile i - 1 (min term, conversion, accumulation) is placed after the
+        // MFMAs of row tile i, so its vector work can issue while they run.
+        v16i s_prev;
+        auto tail = [&](int i, const v16i &S) {
+            v8h a_bs;
+            {
+                const uint4 au = *reinterpret_cast<const uint4 *>(buf + BS_OFF + (i * 32 + l32) * BS_STRIDE + 16 * hh);
+                __builtin_memcpy(&a_bs, &au, 16);
+            }
+            const v16f zf = {};
+            const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmn, zf, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q + e;
+                    const float t = fmaf(dcol, (float)S[r], dmneg * mn[r]);
+                    acc[i][r] = fmaf(dv[e], t, acc[i][r]);
+                }
+            }
+        };
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int row = i * 32 + l32;
@@ -224,28 +251,15 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q2_K(const uint8_t *__restrict
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
                     const int c = 4 * half + cc;
+                    if (i == 0) build(c);
                     as = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[cc], bq[c], c ? as : zero, 0, 0, 0);
                 }
             }
-            v8h a_bs;
-            {
-                const uint4 au = *reinterpret_cast<const uint4 *>(buf + BS_OFF + row * BS_STRIDE + 16 * hh);
-                __builtin_memcpy(&a_bs, &au, 16);
-            }
-            const v16f zf = {};
-            const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmn, zf, 0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
-                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * q + e;
-                    const float t = fmaf(dcol, (float)as[r], dmneg * mn[r]);
-                    acc[i][r] = fmaf(dv[e], t, acc[i][r]);
-                }
-            }
+            if (i == 0 && b + 1 < nb) wload(b + 1, wx);  // the planes no longer need wx
+            if (i > 0) tail(i - 1, s_prev);
+            s_prev = as;
         }
+        tail(MT - 1, s_prev);
     }
 
     // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32

@@ -14,6 +14,10 @@
 // d_a beside it.  The weights do not go through LDS: no other wavefront reads
 // a column, so each lane loads the 112 bytes of its column it needs straight
 // into registers, one step ahead.
+// Step order as in the Q4_K GEMM: the weight operands of chunk c are built
+// inside row tile 0 just before its first MFMAs (the next step's weights load
+// once they are built), and the tail of row tile i sits after the MFMAs of
+// row tile i + 1, so vector and matrix work of one wavefront overlap.
 //
 // MFMA K-slices: in v_mfma_i32_32x32x32_i8 lane l supplies the 16 consecutive
 // elements 16*(l/32).. of a 32-element chunk, i.e. exactly one 16-element
@@ -172,12 +176,20 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q6_K(const uint8_t *__restrict
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of step b
         if (tid < BM) *reinterpret_cast<uint32_t *>(buf + DA_OFF + 4 * tid) = draw;
 
-        // ---------------- decode: chunk c holds group G = 2c + hh of this lane
+        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
+        if (b + 1 < nb) {
+            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
+            prefetch(b + 1, draw);
+        }
+        const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
+
+        // ---------------- decode: chunk c holds group G = 2c + hh of this lane.
+        // The planes are built inside row tile 0, chunk c just before its first
+        // MFMAs, so the decode of c + 1 issues while the MFMAs of c run.
         const float dcol = f16_bits_to_f32(wx.d);
-        const uint32_t sw[4] = {wx.sc.x, wx.sc.y, wx.sc.z, wx.sc.w};
         v4i bhi[8], blo[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        auto build = [&](int c) {
+            const uint32_t sw[4] = {wx.sc.x, wx.sc.y, wx.sc.z, wx.sc.w};
             const int g = c >> 1, hi_nib = c & 1;
             const int s = (int)(int8_t)(sw[g] >> (16 * hi_nib + 8 * hh));  // scale byte 2c + hh
             const s16x2 s2 = {(short)s, (short)s};
@@ -194,17 +206,24 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q6_K(const uint8_t *__restrict
             }
             bhi[c] = v4i{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
             blo[c] = v4i{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
-        }
+        };
 
-        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
-        if (b + 1 < nb) {
-            issue(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
-            prefetch(b + 1, draw);
-            wload(b + 1, wx);
-        }
-        const float *da = reinterpret_cast<const float *>(buf + DA_OFF);
-
-        // ---------------- the four row tiles of this column tile
+        // ---------------- the four row tiles of this column tile.  The tail of
+        // row tile i - 1 (conversion and accumulation) is placed after the MFMAs
+        // of row tile i, so its vector work can issue while they run.
+        v16i s_prev;
+        auto tail = [&](int i, const v16i &S) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q + e;
+                    acc[i][r] = fmaf(dv[e], dcol * (float)S[r], acc[i][r]);
+                }
+            }
+        };
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int row = i * 32 + l32;
@@ -223,22 +242,17 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q6_K(const uint8_t *__restrict
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
                     const int c = 4 * half + cc;
+                    if (i == 0) build(c);
                     ah = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[cc], bhi[c], c ? ah : zero, 0, 0, 0);
                     al = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op[cc], blo[c], c ? al : zero, 0, 0, 0);
                 }
             }
+            if (i == 0 && b + 1 < nb) wload(b + 1, wx);  // the planes no longer need wx
+            if (i > 0) tail(i - 1, s_prev);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 d4 = *reinterpret_cast<const float4 *>(da + i * 32 + 8 * q + 4 * hh);
-                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * q + e;
-                    const int S = (ah[r] << 8) + al[r];  // |S| <= 256 * 4096 * 127
-                    acc[i][r] = fmaf(dv[e], dcol * (float)S, acc[i][r]);
-                }
-            }
+            for (int r = 0; r < 16; ++r) s_prev[r] = (ah[r] << 8) + al[r];  // |S| <= 256 * 4096 * 127
         }
+        tail(MT - 1, s_prev);
     }
 
     // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
