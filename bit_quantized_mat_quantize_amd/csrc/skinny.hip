@@ -22,9 +22,13 @@
 // wavefront w takes the super-blocks b = w, w + 8, ... (a split of K), and the
 // eight partial tiles are summed through LDS at the end.  Each wavefront
 // streams its columns' weights straight from memory into registers (no LDS
-// staging: every byte is used by exactly one wavefront) and reads the
-// activation operands from L2, where all workgroups share them.  The weight
-// loads of super-block b + 8 are issued before b is computed.
+// staging: every byte is used by exactly one wavefront).  The activation rows
+// of its super-block (read from L2, where all workgroups share them) go into
+// the wavefront's own LDS stage by direct global->LDS loads, 16 lanes per
+// contiguous 256-byte row: loaded straight into MFMA operand registers, every
+// lane would read a different row and one load would touch 64 cache lines.
+// Only the rows M needs are staged (8, 16 or 32).  The weights and activation
+// rows of super-block b + 8 are requested before b is computed.
 //
 // MFMA operand convention (v_mfma_*_32x32xK): lane l supplies row (A) or
 // column (B) l % 32 and the K-slice selected by l / 32; the result register r
@@ -38,14 +42,20 @@ namespace {
 
 constexpr int SK_WAVES = 8, SK_THREADS = 64 * SK_WAVES;
 constexpr int SK_MAX_M = 32;
+// Per-wavefront LDS stage: the activation rows of one super-block.
+//   A   int8 codes [32][256]   16-byte piece p of row r at position p ^ (r & 15)
+//   BS  bsums      [32][2][16 B]
+//   DA  d_a        [64] (rows l % 32)
+constexpr int ST_A = 0, ST_BS = 32 * 256, ST_DA = ST_BS + 32 * 32, ST_BYTES = ST_DA + 64 * 4;
+constexpr int SK_LDS = SK_WAVES * 2 * ST_BYTES;
+constexpr int RED_BYTES = SK_WAVES * 16 * 64 * 4;
+static_assert(SK_LDS <= 160 * 1024 && RED_BYTES <= SK_LDS, "LDS budget of a gfx950 CU");
 
 // The weight side of one super-block in this lane's registers (loaded one
-// step ahead), plus the row's bsums and d_a.
+// step ahead).
 struct Stage {
     uint4 hdr;      // Q4_K header of column l%32
     uint4 pay[4];   // payload pieces 2g + l/32, g = 0..3
-    uint4 bs;       // bsums 8*(l/32)..+7 of row l%32
-    uint32_t da;    // d_a of row l%32
 };
 
 template <bool REPACKED>
@@ -53,8 +63,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
                                                              const uint8_t *__restrict__ Y,
                                                              float *__restrict__ out, int64_t M,
                                                              int64_t N, int64_t K) {
-    __shared__ __attribute__((aligned(16))) float red[SK_WAVES][16][64];  // partial tiles
-    __shared__ __attribute__((aligned(16))) float s_da[SK_WAVES][32];      // d_a of the step
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wavefront-uniform, and known to be: the super-block index derived from it
@@ -64,74 +73,82 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
     const int64_t nb = K / QK_K;
     const int64_t n_base = (int64_t)blockIdx.x * 32;
     const int64_t col = n_base + l32 < N ? n_base + l32 : N - 1;  // clamped: loads stay in bounds
-    const int64_t row = l32 < M ? l32 : M - 1;
+    uint8_t *const my = lds + wave * 2 * ST_BYTES;                // this wavefront's two stages
 
     // weights: this lane's column; offsets relative to the matrix start
     // (buffer resources are built where they are used: one held across the
-    // lambda below would be treated as divergent and waterfall-looped)
+    // lambdas below would be treated as divergent and waterfall-looped)
     const int64_t w_bytes = N * nb * kQ4_KBytes, y_bytes = M * nb * kQ8_KBytes;
     const uint32_t hdr_step = REPACKED ? 16 : kQ4_KBytes, pay_step = REPACKED ? 128 : kQ4_KBytes;
     const uint32_t h_off = (uint32_t)(col * nb) * hdr_step;
     const uint32_t p_off = REPACKED ? (uint32_t)(16 * N * nb + 128 * col * nb) + 16 * hh
                                     : (uint32_t)(kQ4_KBytes * col * nb) + 16 + 16 * hh;
-    // activations: row l%32 (clamped to M - 1)
-    const uint32_t y_off = (uint32_t)(row * nb * kQ8_KBytes);
+    // activations: rows past M - 1 are clamped to it (loaded, never stored)
+    const uint32_t row_stride = (uint32_t)(nb * kQ8_KBytes);
+    auto row_off = [&](int r) -> uint32_t { return (uint32_t)(r < M ? r : M - 1) * row_stride; };
+    // codes: instruction t moves rows 4t .. 4t+3, 16 lanes per 256-byte row
+    const int c_row = lane >> 4, c_pos = lane & 15;
+    const uint32_t bs_off = row_off(lane >> 1) + 260 + 16 * (lane & 1);
+    const uint32_t da_off = row_off(l32);
+    // rows staged: the power of two >= M among 8, 16, 32; MFMA row l32 reads
+    // staged row l32 & (R - 1) (rows >= M are computed and never stored)
+    const int R = M <= 8 ? 8 : (M <= 16 ? 16 : 32);
+    const int arow = l32 & (R - 1);
 
-    auto load = [&](int64_t b, Stage &st) {
-        const rsrc_t rw = make_rsrc(W, w_bytes), ry = make_rsrc(Y, y_bytes);
+    auto wload = [&](int64_t b, Stage &st) {
+        const rsrc_t rw = make_rsrc(W, w_bytes);
         st.hdr = bld16(rw, h_off, (uint32_t)b * hdr_step);
 #pragma unroll
         for (int g = 0; g < 4; ++g) st.pay[g] = bld16(rw, p_off + 32 * g, (uint32_t)b * pay_step);
+    };
+    // activation rows of super-block b into stage buffer st (direct global->LDS)
+    auto aload = [&](int64_t b, uint8_t *st) {
+        const rsrc_t ry = make_rsrc(Y, y_bytes);
         const uint32_t sy = (uint32_t)b * kQ8_KBytes;
-        st.bs = bld16(ry, y_off + 260 + 16 * hh, sy);
-        st.da = __builtin_amdgcn_raw_buffer_load_b32(ry, y_off, sy, 0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (4 * t >= R) break;  // wavefront-uniform
+            const int r = 4 * t + c_row;
+            dma16(ry, row_off(r) + 4 + 16 * (uint32_t)(c_pos ^ (r & 15)), sy, st + ST_A + 1024 * t);
+        }
+        dma16(ry, bs_off, sy, st + ST_BS);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void *)(st + ST_DA), 4, da_off, sy, 0, 0);
     };
 
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-    // Loads are never predicated (a branch around a load makes the compiler
-    // wait for every outstanding load before the next use): a wavefront without
+    // Register loads are never predicated (a branch around a load makes the
+    // compiler wait for every outstanding load before the next use): a wavefront without
     // super-blocks loads block nb - 1 and skips the loop; the step after its
     // last one loads that block again (from L2) and leaves it unused.
-    // One step: this step's activation operands first, then the next step's
-    // weights into the other stage (waiting for the activations leaves that
-    // prefetch in flight), then decode, contraction and epilogue.  Two stages
-    // alternate (the loop is unrolled by two) so no register copy forces a
-    // wait for the prefetch.
-    auto step = [&](int64_t b, const Stage &cur, Stage &nxt) {
-        uint4 act[8];
-        const rsrc_t ry = make_rsrc(Y, y_bytes);
-        const uint32_t sy = (uint32_t)b * kQ8_KBytes;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) act[j] = bld16(ry, y_off + 4 + 32 * j + 16 * hh, sy);
-        load(b + SK_WAVES < nb ? b + SK_WAVES : b, nxt);
+    // One step: wait for this step's data, start the next step's (activations
+    // into the other LDS stage, weights into the other register stage), then
+    // decode, contraction and epilogue.  Two register stages alternate (the
+    // loop is unrolled by two) so no register copy forces a wait.
+    auto step = [&](int64_t b, int si, const Stage &cur, Stage &nxt) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this step's weights and LDS rows
+        const int64_t bn = b + SK_WAVES < nb ? b + SK_WAVES : b;
+        aload(bn, my + (si ^ 1) * ST_BYTES);
+        wload(bn, nxt);
+        const uint8_t *st = my + si * ST_BYTES;
 
-        // d_a of the 32 rows, shared through this wavefront's LDS slot
-        if (hh == 0) s_da[wave][l32] = __uint_as_float(cur.da);
-
-        // ---- decode: 8 sub-block digit planes of this lane's K-slice
         const float dcol = f16_bits_to_f32(cur.hdr.x & 0xffff);
         const float dmcol = f16_bits_to_f32(cur.hdr.x >> 16);
         const Q4KScales sc = unpack_scales(cur.hdr.y, cur.hdr.z, cur.hdr.w);
-        v4i bhi[8], blo[8];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const uint4 pw = cur.pay[g];
-            const uint32_t sw = g < 2 ? sc.s_lo : sc.s_hi;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {  // t = 0: low nibbles (sub-block 2g), 1: high (2g+1)
-                const int j = 2 * g + t;
-                const int shift = t * 4;
-                const uint32_t q0 = (pw.x >> shift) & 0x0f0f0f0fu, q1 = (pw.y >> shift) & 0x0f0f0f0fu;
-                const uint32_t q2 = (pw.z >> shift) & 0x0f0f0f0fu, q3 = (pw.w >> shift) & 0x0f0f0f0fu;
-                const uint32_t sj = (sw >> (8 * (j & 3))) & 0xff;
-                const uint32_t hi2 = (sj >> 3) * 0x00010001u, lo2 = (sj & 7) * 0x00010001u;
-                bhi[j] = v4i{plane(q0, hi2), plane(q1, hi2), plane(q2, hi2), plane(q3, hi2)};
-                blo[j] = v4i{plane(q0, lo2), plane(q1, lo2), plane(q2, lo2), plane(q3, lo2)};
-            }
-        }
+        // plane j is built just before the two MFMAs that read it
+        auto build = [&](int j, v4i &bh, v4i &bl) {
+            const uint4 pw = cur.pay[j >> 1];
+            const uint32_t sw = j < 4 ? sc.s_lo : sc.s_hi;
+            const int shift = (j & 1) * 4;  // low nibbles: sub-block 2g, high: 2g + 1
+            const uint32_t q0 = (pw.x >> shift) & 0x0f0f0f0fu, q1 = (pw.y >> shift) & 0x0f0f0f0fu;
+            const uint32_t q2 = (pw.z >> shift) & 0x0f0f0f0fu, q3 = (pw.w >> shift) & 0x0f0f0f0fu;
+            const uint32_t sj = (sw >> (8 * (j & 3))) & 0xff;
+            const uint32_t hi2 = (sj >> 3) * 0x00010001u, lo2 = (sj & 7) * 0x00010001u;
+            bh = v4i{plane(q0, hi2), plane(q1, hi2), plane(q2, hi2), plane(q3, hi2)};
+            bl = v4i{plane(q0, lo2), plane(q1, lo2), plane(q2, lo2), plane(q3, lo2)};
+        };
         // min-term operands: -dmin*m_j = hi + lo exactly in fp16; bsums exact in fp16
         v8h bmh, bml, a_bs;
         {
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
             }
             __builtin_memcpy(&bmh, bh, 16);
             __builtin_memcpy(&bml, bl, 16);
-            const uint4 r = cur.bs;
+            const uint4 r = *reinterpret_cast<const uint4 *>(st + ST_BS + 16 * (2 * arow + hh));
             const uint4 hv = make_uint4(h2_bits((int16_t)(r.x & 0xffff), (int16_t)(r.x >> 16)),
                                         h2_bits((int16_t)(r.y & 0xffff), (int16_t)(r.y >> 16)),
                                         h2_bits((int16_t)(r.z & 0xffff), (int16_t)(r.z >> 16)),
@@ -160,19 +177,23 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
         v16i ah = zero, al = zero;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const v4i a = v4i{(int)act[j].x, (int)act[j].y, (int)act[j].z, (int)act[j].w};
-            ah = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bhi[j], ah, 0, 0, 0);
-            al = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, blo[j], al, 0, 0, 0);
+            const uint4 av = *reinterpret_cast<const uint4 *>(st + ST_A + arow * 256 +
+                                                              16 * ((2 * j + hh) ^ (arow & 15)));
+            const v4i a = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+            v4i bh, bl;
+            build(j, bh, bl);
+            ah = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bh, ah, 0, 0, 0);
+            al = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bl, al, 0, 0, 0);
         }
         const v16f zf = {};
         v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmh, zf, 0, 0, 0);
         mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bml, mn, 0, 0, 0);
 
         // ---- epilogue: acc += d_a * (d * S - dmin * Mn)
-        __builtin_amdgcn_wave_barrier();
+        const float *da = reinterpret_cast<const float *>(st + ST_DA);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float4 d4 = *reinterpret_cast<const float4 *>(&s_da[wave][8 * q + 4 * hh]);
+            const float4 d4 = *reinterpret_cast<const float4 *>(da + 8 * q + 4 * hh);
             const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -182,20 +203,24 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
                 acc[r] = fmaf(dv[e], t, acc[r]);
             }
         }
-        __builtin_amdgcn_wave_barrier();
     };
 
     const int64_t b0 = wave < nb ? wave : nb - 1;
     Stage st0, st1;
-    load(b0, st0);
+    aload(b0, my);
+    wload(b0, st0);
     for (int64_t b = wave; b < nb; b += 2 * SK_WAVES) {
-        step(b, st0, st1);
-        if (b + SK_WAVES < nb) step(b + SK_WAVES, st1, st0);
+        step(b, 0, st0, st1);
+        if (b + SK_WAVES < nb) step(b + SK_WAVES, 1, st1, st0);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no transfer into LDS outlives the loop
 
-    // ---- sum the eight K-split partial tiles and store the valid outputs
+    // ---- sum the eight K-split partial tiles (in the staging LDS, now free)
+    // and store the valid outputs
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(lds);  // [SK_WAVES][16][64]
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
+    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
     __syncthreads();
     for (int o = tid; o < 32 * 32; o += SK_THREADS) {
         const int m = o >> 5, c = o & 31;            // output row m, column n_base + c
@@ -203,7 +228,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
         const int l = c + 32 * ((m >> 2) & 1);       // ... in lane l
         float s = 0.0f;
 #pragma unroll
-        for (int w = 0; w < SK_WAVES; ++w) s += red[w][r][l];
+        for (int w = 0; w < SK_WAVES; ++w) s += red[(w * 16 + r) * 64 + l];
         if (m < M && n_base + c < N) out[(int64_t)m * N + n_base + c] = s;
     }
 }
@@ -214,11 +239,19 @@ int64_t skinny_max_m() { return SK_MAX_M; }
 
 hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                               int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    static bool attr_set[2] = {false, false};  // the LDS budget above 64 KiB must be opted into once
+    if (!attr_set[repacked]) {
+        const hipError_t e = hipFuncSetAttribute(
+            repacked ? (const void *)k_skinny_q4_K<true> : (const void *)k_skinny_q4_K<false>,
+            hipFuncAttributeMaxDynamicSharedMemorySize, SK_LDS);
+        if (e != hipSuccess) return e;
+        attr_set[repacked] = true;
+    }
     const dim3 grid((unsigned)((N + 31) / 32)), block(SK_THREADS);
     if (repacked)
-        hipLaunchKernelGGL(k_skinny_q4_K<true>, grid, block, 0, s, w, y, out, M, N, K);
+        hipLaunchKernelGGL(k_skinny_q4_K<true>, grid, block, SK_LDS, s, w, y, out, M, N, K);
     else
-        hipLaunchKernelGGL(k_skinny_q4_K<false>, grid, block, 0, s, w, y, out, M, N, K);
+        hipLaunchKernelGGL(k_skinny_q4_K<false>, grid, block, SK_LDS, s, w, y, out, M, N, K);
     return hipGetLastError();
 }
 

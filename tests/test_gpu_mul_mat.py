@@ -176,11 +176,12 @@ def test_mfma_q4_K(M, N, K, layout):
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", [(2, 1, 256), (2, 33, 512), (3, 100, 2304), (5, 64, 4096),
-                                   (8, 257, 6144), (17, 45, 1024), (32, 96, 3840),
-                                   (1, 70, 2048)])
+                                   (8, 257, 6144), (9, 40, 1536), (16, 64, 2560), (17, 45, 1024),
+                                   (32, 96, 3840), (1, 70, 2048)])
 def test_skinny_q4_K(M, N, K, layout):
     """Small-batch MFMA path: ragged N, K splits of 1..3 super-blocks per
-    wavefront (odd and even counts, wavefronts without work), M up to 32."""
+    wavefront (odd and even counts, wavefronts without work), M up to 32
+    (8, 16 and 32 staged activation rows)."""
     w, x, y, _ = _case("q4_K", M, N, K, 7 * M + N)
     want, terms = full_reference("q4_K", w, y, M, N, K)
     wd = upload_weights("q4_K", w, N, K, layout)
