@@ -150,22 +150,35 @@ __host__ __device__ constexpr int64_t gemv1_lds_bytes(int64_t K) {
     return K + ((K / QK_K) * 4 + 15) / 16 * 16 + (K / QK_K) * 32 + 16;
 }
 
-// Lane l of a pass starting at piece `base` owns the kNit consecutive
-// 16-byte pieces c = base + kNit*l + it of row nn: all in one super-block
-// (kNit divides 8), so one header serves them, and pieces 2g, 2g+1 (the two
-// halves of the 32-byte group g) share their sub-block scales.  A lane past
+// A pass moves kNit 16-byte pieces per lane, in kNit / kP sub-passes of kP =
+// min(kNit, 2) consecutive pieces: in sub-pass s, lane l owns the pieces
+// c = base + 64*kP*s + kP*l + i (i < kP) of row nn.  The kP pieces of a
+// sub-pass lie in one super-block, so one header serves them, and pieces 2g,
+// 2g+1 (the two halves of the 32-byte group g) share their sub-block scales.
+// The wavefront's pieces of one sub-pass are contiguous (64 * kP * 16 bytes),
+// so each load touches few cache lines whatever the row length.  A lane past
 // the row end loads the last group again and leaves it unused; the loads stay
 // branch-free, so the compiler can wait for older loads (the activations)
 // while these are still in flight.
+template <int kNit>
+constexpr int gemv1_kp() { return kNit >= 2 ? 2 : 1; }
+template <int kNit>
+constexpr int gemv1_subs() { return kNit / gemv1_kp<kNit>(); }
+
 template <bool REPACKED, int kNit>
 __device__ __forceinline__ void gemv1_load(const Q4KAddr<REPACKED> &A, int64_t nn, int base,
-                                           int nchunk, int lane, uint4 &hw, uint4 (&pw)[kNit]) {
-    const int c0 = base + kNit * lane;
-    const int c = c0 < nchunk ? c0 : nchunk - kNit;
-    const int b = c >> 3, cc = c & 7;
-    hw = ld16(A.header(nn, b));
+                                           int nchunk, int lane, uint4 (&hw)[gemv1_subs<kNit>()],
+                                           uint4 (&pw)[kNit]) {
+    constexpr int kP = gemv1_kp<kNit>();
 #pragma unroll
-    for (int it = 0; it < kNit; ++it) pw[it] = ld16(A.piece(nn, b, cc + it));
+    for (int sp = 0; sp < gemv1_subs<kNit>(); ++sp) {
+        const int c0 = base + 64 * kP * sp + kP * lane;
+        const int c = c0 < nchunk ? c0 : nchunk - kP;
+        const int b = c >> 3, cc = c & 7;
+        hw[sp] = ld16(A.header(nn, b));
+#pragma unroll
+        for (int i = 0; i < kP; ++i) pw[kP * sp + i] = ld16(A.piece(nn, b, cc + i));
+    }
 }
 
 // Integer dot products of the loaded pieces with the activation row in LDS.
@@ -175,13 +188,12 @@ __device__ __forceinline__ void gemv1_load(const Q4KAddr<REPACKED> &A, int64_t n
 // 16-element activation sums (bsums), the lane's pieces give
 //   S  = sum_g (s_2g * P_lo,g + s_2g+1 * P_hi,g),  Mn = sum_g (m_2g * Y_lo,g + m_2g+1 * Y_hi,g)
 //   acc += d_a * (d * S - dmin * Mn)
-// S stays an exact int32 and its conversion to fp32 exact (|S| < 2^24 for up
-// to four pieces; eight pieces are converted in two halves).
+// for the kNit (at most 2) pieces of one sub-pass.  S stays an exact int32 and
+// its conversion to fp32 exact (|S| < 2^24).
 template <int kNit>
-__device__ __forceinline__ float gemv1_accumulate(const uint4 &hw, const uint4 (&pw)[kNit],
-                                                  int base, int nchunk, int lane,
-                                                  const uint8_t *s_qs, const int16_t *s_bs,
-                                                  const float *s_d, float acc) {
+__device__ __forceinline__ float gemv1_acc_sub(const uint4 &hw, const uint4 *pw, int base, int nchunk,
+                                               int lane, const uint8_t *s_qs, const int16_t *s_bs,
+                                               const float *s_d, float acc) {
     constexpr int kH = kNit >= 2 ? 2 : 1;  // pieces per 32-byte group
     constexpr int kG = kNit / kH;          // groups per lane
     const int c = base + kNit * lane;
@@ -233,6 +245,18 @@ __device__ __forceinline__ float gemv1_accumulate(const uint4 &hw, const uint4 (
     return acc;
 }
 
+template <int kNit>
+__device__ __forceinline__ float gemv1_accumulate(const uint4 (&hw)[gemv1_subs<kNit>()],
+                                                  const uint4 (&pw)[kNit], int base, int nchunk,
+                                                  int lane, const uint8_t *s_qs, const int16_t *s_bs,
+                                                  const float *s_d, float acc) {
+    constexpr int kP = gemv1_kp<kNit>();
+#pragma unroll
+    for (int sp = 0; sp < gemv1_subs<kNit>(); ++sp)
+        acc = gemv1_acc_sub<kP>(hw[sp], pw + kP * sp, base + 64 * kP * sp, nchunk, lane, s_qs, s_bs, s_d, acc);
+    return acc;
+}
+
 // ID = true: mul_mat_id, one (token, slot) pair per blockIdx.y (id_route).
 template <bool REPACKED, int kNit, bool ID>
 __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ W,
@@ -274,7 +298,7 @@ __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ 
     const uint4 yb = ld_align4<uint4>(Y + (qb >> 1) * kQ8_KBytes + 260 + 16 * (qb & 1));
     const float yd = ld_align4<float>(Y + qd * kQ8_KBytes);
     __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
-    uint4 pw[kNit], hw;
+    uint4 pw[kNit], hw[gemv1_subs<kNit>()];
     gemv1_load<REPACKED, kNit>(A, nn, 0, nchunk, lane, hw, pw);
 #pragma unroll
     for (int t = 0; t < kYT; ++t) {
@@ -365,7 +389,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
         xv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
-    uint4 pw[kNit], hw;
+    uint4 pw[kNit], hw[gemv1_subs<kNit>()];
     // a wavefront without rows loads a valid row and stores nothing
     gemv1_load<REPACKED, kNit>(A, row < N ? row : N - 1, 0, nchunk, lane, hw, pw);
 #pragma unroll
@@ -376,10 +400,11 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
         const bool more = row + stride < N;
         float acc = 0.0f;
         if constexpr (kNit <= 2) {  // rows of one pass; registers for a second row
-            uint4 pn[kNit], hn;
+            uint4 pn[kNit], hn[gemv1_subs<kNit>()];
             if (more) gemv1_load<REPACKED, kNit>(A, row + stride, 0, nchunk, lane, hn, pn);
             acc = gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, acc);
-            hw = hn;
+#pragma unroll
+            for (int sp = 0; sp < gemv1_subs<kNit>(); ++sp) hw[sp] = hn[sp];
 #pragma unroll
             for (int it = 0; it < kNit; ++it) pw[it] = pn[it];
         } else {
