@@ -23,12 +23,14 @@
 // eight partial tiles are summed through LDS at the end.  Each wavefront
 // streams its columns' weights straight from memory into registers (no LDS
 // staging: every byte is used by exactly one wavefront).  The activation rows
-// of its super-block (read from L2, where all workgroups share them) go into
-// the wavefront's own LDS stage by direct global->LDS loads, 16 lanes per
-// contiguous 256-byte row: loaded straight into MFMA operand registers, every
-// lane would read a different row and one load would touch 64 cache lines.
-// Only the rows M needs are staged (8, 16 or 32).  The weights and activation
-// rows of super-block b + 8 are requested before b is computed.
+// come from L2, where all workgroups share them.  Up to 8 rows, each lane
+// loads its row's operands straight into MFMA operand registers at the start
+// of the step (the loads touch few distinct rows).  With more rows every lane
+// would read a different row and one load would touch up to 64 cache lines,
+// so the rows of the wavefront's super-block go into its own LDS stage by
+// direct global->LDS loads instead, 16 lanes per contiguous 256-byte row (only
+// the rows M needs: 16 or 32).  The weights (and the staged rows) of
+// super-block b + 8 are requested before b is computed.
 //
 // MFMA operand convention (v_mfma_*_32x32xK): lane l supplies row (A) or
 // column (B) l % 32 and the K-slice selected by l / 32; the result register r
@@ -51,14 +53,21 @@ constexpr int SK_LDS = SK_WAVES * 2 * ST_BYTES;
 constexpr int RED_BYTES = SK_WAVES * 16 * 64 * 4;
 static_assert(SK_LDS <= 160 * 1024 && RED_BYTES <= SK_LDS, "LDS budget of a gfx950 CU");
 
-// The weight side of one super-block in this lane's registers (loaded one
-// step ahead).
+// One super-block in this lane's registers (loaded one step ahead): the
+// weight side, and with activation registers also the row's bsums and d_a.
 struct Stage {
     uint4 hdr;      // Q4_K header of column l%32
     uint4 pay[4];   // payload pieces 2g + l/32, g = 0..3
+    uint4 bs;       // bsums 8*(l/32)..+7 of row l%32 (activation registers)
+    uint32_t da;    // d_a of row l%32 (activation registers)
 };
+// LDS of the activation-register variant: the partial tiles, then d_a per wavefront
+constexpr int SK_LDS_REG = RED_BYTES + SK_WAVES * 32 * 4;
 
-template <bool REPACKED>
+// LDS_ACT: activation rows staged in LDS (M > 8); otherwise each lane loads its
+// row's operands into registers at the start of the step (few distinct rows,
+// so few cache lines per load).
+template <bool REPACKED, bool LDS_ACT>
 __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__restrict__ W,
                                                              const uint8_t *__restrict__ Y,
                                                              float *__restrict__ out, int64_t M,
@@ -101,6 +110,15 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
 #pragma unroll
         for (int g = 0; g < 4; ++g) st.pay[g] = bld16(rw, p_off + 32 * g, (uint32_t)b * pay_step);
     };
+    // activation-register variant: the row's bsums and d_a with the weights
+    const uint32_t y_off = row_off(l32);
+    auto sload = [&](int64_t b, Stage &st) {
+        const rsrc_t ry = make_rsrc(Y, y_bytes);
+        const uint32_t sy = (uint32_t)b * kQ8_KBytes;
+        st.bs = bld16(ry, y_off + 260 + 16 * hh, sy);
+        st.da = __builtin_amdgcn_raw_buffer_load_b32(ry, y_off, sy, 0);
+    };
+    float *const s_da = reinterpret_cast<float *>(lds + RED_BYTES) + 32 * wave;
     // activation rows of super-block b into stage buffer st (direct global->LDS)
     auto aload = [&](int64_t b, uint8_t *st) {
         const rsrc_t ry = make_rsrc(Y, y_bytes);
@@ -128,11 +146,24 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
     // decode, contraction and epilogue.  Two register stages alternate (the
     // loop is unrolled by two) so no register copy forces a wait.
     auto step = [&](int64_t b, int si, const Stage &cur, Stage &nxt) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this step's weights and LDS rows
         const int64_t bn = b + SK_WAVES < nb ? b + SK_WAVES : b;
-        aload(bn, my + (si ^ 1) * ST_BYTES);
-        wload(bn, nxt);
         const uint8_t *st = my + si * ST_BYTES;
+        uint4 act[8];
+        if constexpr (LDS_ACT) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this step's weights and LDS rows
+            aload(bn, my + (si ^ 1) * ST_BYTES);
+            wload(bn, nxt);
+        } else {
+            // this step's activation operands first, then the next step's loads
+            // (waiting for the activations leaves that prefetch in flight)
+            const rsrc_t ry = make_rsrc(Y, y_bytes);
+            const uint32_t sy = (uint32_t)b * kQ8_KBytes;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) act[j] = bld16(ry, y_off + 4 + 32 * j + 16 * hh, sy);
+            wload(bn, nxt);
+            sload(bn, nxt);
+            if (hh == 0) s_da[l32] = __uint_as_float(cur.da);
+        }
 
         const float dcol = f16_bits_to_f32(cur.hdr.x & 0xffff);
         const float dmcol = f16_bits_to_f32(cur.hdr.x >> 16);
@@ -164,7 +195,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
             }
             __builtin_memcpy(&bmh, bh, 16);
             __builtin_memcpy(&bml, bl, 16);
-            const uint4 r = *reinterpret_cast<const uint4 *>(st + ST_BS + 16 * (2 * arow + hh));
+            const uint4 r = LDS_ACT ? *reinterpret_cast<const uint4 *>(st + ST_BS + 16 * (2 * arow + hh)) : cur.bs;
             const uint4 hv = make_uint4(h2_bits((int16_t)(r.x & 0xffff), (int16_t)(r.x >> 16)),
                                         h2_bits((int16_t)(r.y & 0xffff), (int16_t)(r.y >> 16)),
                                         h2_bits((int16_t)(r.z & 0xffff), (int16_t)(r.z >> 16)),
@@ -177,8 +208,9 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
         v16i ah = zero, al = zero;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint4 av = *reinterpret_cast<const uint4 *>(st + ST_A + arow * 256 +
-                                                              16 * ((2 * j + hh) ^ (arow & 15)));
+            const uint4 av = LDS_ACT ? *reinterpret_cast<const uint4 *>(st + ST_A + arow * 256 +
+                                                                        16 * ((2 * j + hh) ^ (arow & 15)))
+                                     : act[j];
             const v4i a = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
             v4i bh, bl;
             build(j, bh, bl);
@@ -190,7 +222,8 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
         mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bml, mn, 0, 0, 0);
 
         // ---- epilogue: acc += d_a * (d * S - dmin * Mn)
-        const float *da = reinterpret_cast<const float *>(st + ST_DA);
+        const float *da = LDS_ACT ? reinterpret_cast<const float *>(st + ST_DA) : s_da;
+        if constexpr (!LDS_ACT) __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float4 d4 = *reinterpret_cast<const float4 *>(da + 8 * q + 4 * hh);
@@ -203,11 +236,13 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
                 acc[r] = fmaf(dv[e], t, acc[r]);
             }
         }
+        if constexpr (!LDS_ACT) __builtin_amdgcn_wave_barrier();  // s_da is rewritten next step
     };
 
     const int64_t b0 = wave < nb ? wave : nb - 1;
     Stage st0, st1;
-    aload(b0, my);
+    if constexpr (LDS_ACT) aload(b0, my);
+    else sload(b0, st0);
     wload(b0, st0);
     for (int64_t b = wave; b < nb; b += 2 * SK_WAVES) {
         step(b, 0, st0, st1);
@@ -242,16 +277,23 @@ hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y,
     static bool attr_set[2] = {false, false};  // the LDS budget above 64 KiB must be opted into once
     if (!attr_set[repacked]) {
         const hipError_t e = hipFuncSetAttribute(
-            repacked ? (const void *)k_skinny_q4_K<true> : (const void *)k_skinny_q4_K<false>,
+            repacked ? (const void *)k_skinny_q4_K<true, true> : (const void *)k_skinny_q4_K<false, true>,
             hipFuncAttributeMaxDynamicSharedMemorySize, SK_LDS);
         if (e != hipSuccess) return e;
         attr_set[repacked] = true;
     }
     const dim3 grid((unsigned)((N + 31) / 32)), block(SK_THREADS);
-    if (repacked)
-        hipLaunchKernelGGL(k_skinny_q4_K<true>, grid, block, SK_LDS, s, w, y, out, M, N, K);
-    else
-        hipLaunchKernelGGL(k_skinny_q4_K<false>, grid, block, SK_LDS, s, w, y, out, M, N, K);
+    // up to 8 rows the per-lane operand loads touch few cache lines and beat
+    // the LDS staging; more rows are staged
+    const bool lds_act = M > 8;
+    const unsigned lds = lds_act ? SK_LDS : SK_LDS_REG;
+#define QMM_SKINNY(RP, LA) hipLaunchKernelGGL((k_skinny_q4_K<RP, LA>), grid, block, lds, s, w, y, out, M, N, K)
+    if (repacked) {
+        if (lds_act) QMM_SKINNY(true, true); else QMM_SKINNY(true, false);
+    } else {
+        if (lds_act) QMM_SKINNY(false, true); else QMM_SKINNY(false, false);
+    }
+#undef QMM_SKINNY
     return hipGetLastError();
 }
 
