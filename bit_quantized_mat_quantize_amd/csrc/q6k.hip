@@ -21,6 +21,8 @@
 //   [fp16 d of every block, zero-padded to a multiple of 256 B]
 //   [scales, 16 B each][ql, 128 B each][qh, 64 B each]
 // so every 16-byte piece a lane loads is aligned.
+#include <type_traits>
+
 #include "q8k_row.h"
 #include "qmm_device.h"
 #include "qmm_launch.h"
@@ -133,11 +135,18 @@ __global__ __launch_bounds__(256) void k_repack_q6_K(const uint8_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// GEMV.  The unit of work is half a super-block: unit u = 2b + h owns the ql
-// pieces 2g + h (g = 0..3, both nibbles) and the qh pieces h and h + 2 --
-// 96 bytes that no other unit reads -- i.e. the 16-element groups 4g + h
-// (low nibbles) and 4g + 2 + h (high nibbles).  One wavefront per output row,
-// lane l takes units l, l + 64, ...; the activation row is staged in LDS
+// GEMV, rows of at most four units per lane (K <= 8192).  The unit of work is
+// one 16-byte ql piece: unit u = 8b + p (p = 2g + h)
+// holds the low nibbles of group 4g + h and the high nibbles of group
+// 4g + 2 + h of super-block b; their 2-bit high parts sit in bits 2g..2g+1 of
+// the qh pieces h and h + 2, their scales in bytes h and 2 + h of scale dword
+// g.  One wavefront per output row, lane l takes units l, l + 64, ...: the
+// wavefront's ql loads cover a contiguous 1 KB (eight blocks) and its qh loads
+// 512 bytes (each qh piece is read by the four lanes of its half of the block),
+// so every load touches few cache lines.  Longer rows use half a super-block
+// per unit (Q6KHalf below): per element it needs fewer loads and less
+// scale work, which outweighs its less contiguous loads once a lane holds
+// more than four piece units.  The activation row is staged in LDS
 // (q8k_row.h).
 // ---------------------------------------------------------------------------
 template <bool REPACKED>
@@ -173,6 +182,63 @@ __device__ __forceinline__ uint4 ld16a(const uint8_t *p) {
 }
 
 struct Q6KUnit {
+    uint4 ql;      // ql piece p
+    uint4 qa, qb;  // qh pieces h and h + 2
+    uint32_t sc;   // scale dword g (scales of groups 4g .. 4g + 3)
+    uint32_t d;    // fp16 d bits
+};
+
+// 4 bytes at an address that is 4-byte aligned (repacked) or only 2-byte
+// aligned (canonical blocks)
+template <bool ALIGNED>
+__device__ __forceinline__ uint32_t ld4a(const uint8_t *p) {
+    if constexpr (ALIGNED) {
+        return *reinterpret_cast<const uint32_t *>(p);
+    } else {
+        return ld_u16(p) | (ld_u16(p + 2) << 16);
+    }
+}
+
+template <bool REPACKED>
+__device__ __forceinline__ void q6k_load(const Q6KAddr<REPACKED> &A, int64_t n, int64_t nb, int u,
+                                         Q6KUnit &x) {
+    const int64_t i = n * nb + (u >> 3);
+    const int p = u & 7, g = p >> 1, h = p & 1;
+    x.ql = ld16a<REPACKED>(A.ql(i) + 16 * p);
+    x.qa = ld16a<REPACKED>(A.qh(i) + 16 * h);
+    x.qb = ld16a<REPACKED>(A.qh(i) + 32 + 16 * h);
+    x.sc = ld4a<REPACKED>(A.sc(i) + 4 * g);
+    x.d = ld_u16(A.d(i));
+}
+
+// The two group sums of a unit: group 4g + h -> P[0], group 4g + 2 + h -> P[1].
+__device__ __forceinline__ void q6k_group_sums(const Q6KUnit &x, int u, const uint8_t *s_qs,
+                                               const int16_t *s_bs, int P[2]) {
+    const int b = u >> 3, p = u & 7, g = p >> 1, h = p & 1;
+    const uint8_t *yrow = s_qs + b * QK_K;
+    const uint32_t qa[4] = {x.qa.x, x.qa.y, x.qa.z, x.qa.w};
+    const uint32_t qb[4] = {x.qb.x, x.qb.y, x.qb.z, x.qb.w};
+    const uint32_t ql[4] = {x.ql.x, x.ql.y, x.ql.z, x.ql.w};
+    const uint4 ylo = *reinterpret_cast<const uint4 *>(yrow + 64 * g + 16 * h);
+    const uint4 yhi = *reinterpret_cast<const uint4 *>(yrow + 64 * g + 32 + 16 * h);
+    const uint32_t yl[4] = {ylo.x, ylo.y, ylo.z, ylo.w};
+    const uint32_t yh[4] = {yhi.x, yhi.y, yhi.z, yhi.w};
+    int plo = 0, phi = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t ulo = (ql[w] & 0x0f0f0f0fu) | (((qa[w] >> (2 * g)) & 0x03030303u) << 4);
+        const uint32_t uhi = ((ql[w] >> 4) & 0x0f0f0f0fu) | (((qb[w] >> (2 * g)) & 0x03030303u) << 4);
+        plo = dot4(ulo, yl[w], plo);
+        phi = dot4(uhi, yh[w], phi);
+    }
+    P[0] = plo - 32 * s_bs[16 * b + 4 * g + h];
+    P[1] = phi - 32 * s_bs[16 * b + 4 * g + 2 + h];
+}
+
+// Half a super-block: unit u = 2b + h owns the ql pieces 2g + h (g = 0..3,
+// both nibbles) and the qh pieces h and h + 2 -- 96 bytes no other unit reads
+// -- i.e. the 16-element groups 4g + h (low nibbles) and 4g + 2 + h (high).
+struct Q6KHalf {
     uint4 ql[4];   // ql pieces 2g + h
     uint4 qa, qb;  // qh pieces h and h + 2
     uint4 sc;      // the block's 16 scales
@@ -180,8 +246,8 @@ struct Q6KUnit {
 };
 
 template <bool REPACKED>
-__device__ __forceinline__ void q6k_load(const Q6KAddr<REPACKED> &A, int64_t n, int64_t nb, int u,
-                                         Q6KUnit &x) {
+__device__ __forceinline__ void q6k_load_half(const Q6KAddr<REPACKED> &A, int64_t n, int64_t nb, int u,
+                                         Q6KHalf &x) {
     const int64_t i = n * nb + (u >> 1);
     const int h = u & 1;
 #pragma unroll
@@ -193,7 +259,7 @@ __device__ __forceinline__ void q6k_load(const Q6KAddr<REPACKED> &A, int64_t n, 
 }
 
 // The eight group sums P of a unit (groups 4g + h -> P[2g], 4g + 2 + h -> P[2g+1]).
-__device__ __forceinline__ void q6k_group_sums(const Q6KUnit &x, int u, const uint8_t *s_qs,
+__device__ __forceinline__ void q6k_group_sums_half(const Q6KHalf &x, int u, const uint8_t *s_qs,
                                                const int16_t *s_bs, int P[8]) {
     const int b = u >> 1, h = u & 1;
     const uint8_t *yrow = s_qs + b * QK_K;
@@ -223,7 +289,7 @@ constexpr int kQ6Waves = 4;
 
 // MODE 0: out[m*N + n] (fp32).  MODE 1: P[m][n][K/16] (int32 group sums).
 // ID = true (MODE 0): mul_mat_id, one (token, slot) pair per blockIdx.y.
-template <bool REPACKED, int kNit, int MODE, bool ID = false>
+template <bool REPACKED, int kNit, int MODE, bool ID = false, bool PIECE = true>
 __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W,
                                                    const uint8_t *__restrict__ Y,
                                                    void *__restrict__ dst, int64_t N, int64_t K,
@@ -243,15 +309,20 @@ __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t n = (int64_t)blockIdx.x * kQ6Waves + wave;
     const int64_t nn = n < N ? n : N - 1;  // a tail wavefront loads a valid row, stores nothing
-    const int nunits = (int)(2 * nb);
+    const int nunits = (int)((PIECE ? 8 : 2) * nb);
     const Q6KAddr<REPACKED> A{W, N * nb, REPACKED ? (2 * N * nb + 255) / 256 * 256 : 0};
+    using Unit = std::conditional_t<PIECE, Q6KUnit, Q6KHalf>;
+    auto load = [&](int u, Unit &x) {
+        if constexpr (PIECE) q6k_load<REPACKED>(A, nn, nb, u, x);
+        else q6k_load_half<REPACKED>(A, nn, nb, u, x);
+    };
 
     // this row's first units: issue the weight loads, then stage the activations
-    Q6KUnit x[kNit];
+    Unit x[kNit];
 #pragma unroll
     for (int it = 0; it < kNit; ++it) {
         const int u = lane + 64 * it;
-        q6k_load<REPACKED>(A, nn, nb, u < nunits ? u : nunits - 1, x[it]);
+        load(u < nunits ? u : nunits - 1, x[it]);
     }
     const Q8KRowLds row = stage_q8k_row<256>(Y + m * nb * kQ8_KBytes, K, ys);
     const uint8_t *s_qs = row.qs;
@@ -264,15 +335,16 @@ __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W
 #pragma unroll
             for (int it = 0; it < kNit; ++it) {
                 const int u = base + lane + 64 * it;
-                q6k_load<REPACKED>(A, nn, nb, u < nunits ? u : nunits - 1, x[it]);
+                load(u < nunits ? u : nunits - 1, x[it]);
             }
         }
 #pragma unroll
         for (int it = 0; it < kNit; ++it) {
             const int u = base + lane + 64 * it;
-            if (u < nunits) {
+            if (u >= nunits) continue;
+            if constexpr (!PIECE) {
                 int P[8];
-                q6k_group_sums(x[it], u, s_qs, s_bs, P);
+                q6k_group_sums_half(x[it], u, s_qs, s_bs, P);
                 const int b = u >> 1, h = u & 1;
                 if (MODE == 0) {
                     const uint32_t sw[4] = {x[it].sc.x, x[it].sc.y, x[it].sc.z, x[it].sc.w};
@@ -292,6 +364,20 @@ __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W
                         Pout[4 * g + 2 + h] = P[2 * g + 1];
                     }
                 }
+            } else {
+                int P[2];
+                q6k_group_sums(x[it], u, s_qs, s_bs, P);
+                const int b = u >> 3, p = u & 7, g = p >> 1, h = p & 1;
+                if (MODE == 0) {
+                    const int s_lo = (int)(int8_t)(x[it].sc >> (8 * h));
+                    const int s_hi = (int)(int8_t)(x[it].sc >> (8 * (2 + h)));
+                    const int S = s_lo * P[0] + s_hi * P[1];
+                    acc = fmaf(s_d[b], f16_bits_to_f32(x[it].d) * (float)S, acc);
+                } else if (n < N) {
+                    int32_t *Pout = reinterpret_cast<int32_t *>(dst) + (m * N + n) * (K / 16) + 16 * b;
+                    Pout[4 * g + h] = P[0];
+                    Pout[4 * g + 2 + h] = P[1];
+                }
             }
         }
     }
@@ -304,20 +390,24 @@ __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W
 template <int MODE>
 hipError_t dispatch_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, void *dst, int64_t M,
                          int64_t N, int64_t K, hipStream_t s) {
-    const int64_t nunits = 2 * (K / QK_K);
-    const int64_t nit = (nunits + 63) / 64;
+    const int64_t nit = (8 * (K / QK_K) + 63) / 64;       // piece units per lane
+    const int64_t nit_half = (2 * (K / QK_K) + 63) / 64;  // half-block units per lane
     const dim3 grid((unsigned)((N + kQ6Waves - 1) / kQ6Waves), (unsigned)M);  // M <= 65535
     const unsigned lds = (unsigned)q8k_row_lds_bytes(K);
-#define QMM_Q6(NIT)                                                                                \
-    do {                                                                                           \
-        if (repacked)                                                                              \
-            hipLaunchKernelGGL((k_gemv_q6_K<true, NIT, MODE>), grid, dim3(256), lds, s, w, y, dst, N, K); \
-        else                                                                                       \
-            hipLaunchKernelGGL((k_gemv_q6_K<false, NIT, MODE>), grid, dim3(256), lds, s, w, y, dst, N, K); \
+#define QMM_Q6(NIT, PC)                                                                                    \
+    do {                                                                                                   \
+        if (repacked)                                                                                      \
+            hipLaunchKernelGGL((k_gemv_q6_K<true, NIT, MODE, false, PC>), grid, dim3(256), lds, s, w, y, dst, N, K, \
+                               IdRoute{});                                                                 \
+        else                                                                                               \
+            hipLaunchKernelGGL((k_gemv_q6_K<false, NIT, MODE, false, PC>), grid, dim3(256), lds, s, w, y, dst, N, \
+                               K, IdRoute{});                                                              \
     } while (0)
-    if (nit <= 1) QMM_Q6(1);
-    else if (nit <= 2) QMM_Q6(2);
-    else QMM_Q6(4);
+    if (nit <= 1) QMM_Q6(1, true);
+    else if (nit <= 2) QMM_Q6(2, true);
+    else if (nit <= 4) QMM_Q6(4, true);
+    else if (nit_half <= 2) QMM_Q6(2, false);
+    else QMM_Q6(4, false);
 #undef QMM_Q6
     return hipGetLastError();
 }
@@ -362,22 +452,26 @@ hipError_t launch_gemv_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, f
 hipError_t launch_gemv_id_q6_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,
                                int y_per_slot, const int32_t *ids, int64_t P, int64_t U, int64_t E,
                                float *out, int64_t N, int64_t K, hipStream_t s) {
-    const int64_t nit = (2 * (K / QK_K) + 63) / 64;
+    const int64_t nit = (8 * (K / QK_K) + 63) / 64, nit_half = (2 * (K / QK_K) + 63) / 64;
     const unsigned lds = (unsigned)q8k_row_lds_bytes(K);
     for (int64_t p0 = 0; p0 < P; p0 += 65535) {
         const int64_t pp = P - p0 < 65535 ? P - p0 : 65535;
         const dim3 grid((unsigned)((N + kQ6Waves - 1) / kQ6Waves), (unsigned)pp);
         const IdRoute r{ids, p0, U, E, w_stride, (K / QK_K) * kQ8_KBytes, y_per_slot};
-#define QMM_ID(NIT)                                                                                   \
-    do {                                                                                              \
-        if (repacked)                                                                                 \
-            hipLaunchKernelGGL((k_gemv_q6_K<true, NIT, 0, true>), grid, dim3(256), lds, s, w, y, (void *)out, N, K, r);  \
-        else                                                                                          \
-            hipLaunchKernelGGL((k_gemv_q6_K<false, NIT, 0, true>), grid, dim3(256), lds, s, w, y, (void *)out, N, K, r); \
+#define QMM_ID(NIT, PC)                                                                                 \
+    do {                                                                                                \
+        if (repacked)                                                                                   \
+            hipLaunchKernelGGL((k_gemv_q6_K<true, NIT, 0, true, PC>), grid, dim3(256), lds, s, w, y, (void *)out, N, \
+                               K, r);                                                                   \
+        else                                                                                            \
+            hipLaunchKernelGGL((k_gemv_q6_K<false, NIT, 0, true, PC>), grid, dim3(256), lds, s, w, y, (void *)out, \
+                               N, K, r);                                                                \
     } while (0)
-        if (nit <= 1) QMM_ID(1);
-        else if (nit <= 2) QMM_ID(2);
-        else QMM_ID(4);
+        if (nit <= 1) QMM_ID(1, true);
+        else if (nit <= 2) QMM_ID(2, true);
+        else if (nit <= 4) QMM_ID(4, true);
+        else if (nit_half <= 2) QMM_ID(2, false);
+        else QMM_ID(4, false);
 #undef QMM_ID
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -8,7 +8,8 @@
   result exactly -- including the extreme scales -128 and 127 with the extreme
   codes -32 and 31, the corners of the GEMM's digit split.
 * fp32 outputs: |gpu - oracle| <= 1e-4 * sum_k |w a| for every checked (m, n).
-Shapes: GEMV with one, two and four units per lane (K up to 53760, the last
+Shapes: GEMV with one, two and four 16-byte piece units per lane (K <= 8192)
+and two or four half-block units per lane (longer rows, K up to 53760, the last
 with a second pass), ragged N, several activation rows, both layouts; GEMM with
 ragged row and column tiles, K past the GEMV's limit, and AUTO dispatch.
 """
@@ -59,7 +60,8 @@ def test_repack_bytes(N, K):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("M,N,K", [(1, 5, 256), (2, 37, 4096), (3, 9, 14336), (1, 3, 33024)])
+@pytest.mark.parametrize("M,N,K", [(1, 5, 256), (2, 37, 4096), (1, 6, 6144), (3, 9, 14336),
+                                   (1, 3, 33024)])
 def test_group_sums_bit_exact(M, N, K, layout):
     w, y = _case(M, N, K, M * 100 + N)
     want = oracle.subblock_sums("q6_K", w, y, M, N, K)
@@ -97,8 +99,8 @@ def test_exactness_window(layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 131, 3072), (4, 66, 4096), (2, 17, 14336),
-                                   (1, 5, Q6K_MAX_K)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 131, 3072), (4, 66, 4096), (1, 9, 6144),
+                                   (2, 12, 8192), (2, 17, 14336), (1, 5, Q6K_MAX_K)])
 def test_mul_mat_q6_K(M, N, K, layout):
     w, y = _case(M, N, K, 7 * M + N)
     want, terms = full_reference("q6_K", w, y, M, N, K)
