@@ -273,17 +273,52 @@ def cpu_baseline(key: str, seconds: float):
         if el >= seconds:
             break
     per = el / reps
+    # the same sample on one thread (half the time budget)
+    t0 = time.perf_counter()
+    reps1 = 0
+    while True:
+        oracle.mul_mat(p.wfmt, w, y, M_s, p.N, p.K, nthreads=1)
+        reps1 += 1
+        el1 = time.perf_counter() - t0
+        if el1 >= seconds / 2:
+            break
+    per1 = el1 / reps1
     wbytes = p.N * p.K * {"q4_0": 18 / 32, "q4_K": 144 / 256, "q6_K": 210 / 256, "q2_K": 84 / 256}[p.wfmt]
     if p.M <= 8:
-        val, unit = wbytes / per / 1e9, "GB/s"
+        val, val1, unit = wbytes / per / 1e9, wbytes / per1 / 1e9, "GB/s"
         sample = (f"{p.name} projection of {key} (M={M_s}, N={p.N}, K={p.K}), integer path, "
                   f"{reps} repetitions in {el:.1f} s")
     else:
-        val, unit = 2 * M_s * p.N * p.K / per / 1e12, "TOPS"
+        ops = 2 * M_s * p.N * p.K
+        val, val1, unit = ops / per / 1e12, ops / per1 / 1e12, "TOPS"
         sample = (f"{M_s} of the {p.M} activation rows of {key} (N={p.N}, K={p.K}), "
                   f"integer path, {reps} repetitions in {el:.1f} s")
     return {"value": round(val, 4), "unit": unit, "cores": min(threads, oracle.max_threads()),
-            "kind": "oracle", "sample": sample}
+            "kind": "oracle", "sample": sample, "value_1_thread": round(val1, 4),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def system_info() -> dict:
+    """GPU name and the HIP / ROCm versions of this run."""
+    import torch
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            rocm = fh.read().strip()
+    except OSError:
+        pass
+    return {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "rocm": rocm}
 
 
 def measure_decode(key: str, layout: str, steps: int, warmup: int):
@@ -304,6 +339,9 @@ def measure_decode(key: str, layout: str, steps: int, warmup: int):
         if not fused:
             res[tag]["mul_mat_us"] = time_graph(prep, steps, only="mul_mat", reps=3) * 1e3
             res[tag]["quantize_us"] = time_graph(prep, steps, only="quantize", reps=3) * 1e3
+            ops = sum(2 * q.M * q.N * q.K for q in prep.wl.projections)
+            if max(q.M for q in prep.wl.projections) > 1:  # small batch: also int8 TOPS
+                res[tag]["mul_mat_tops"] = ops / (res[tag]["mul_mat_us"] * 1e-6) / 1e12
         res.update(description=prep.wl.description, weight_bytes=wbytes, copies=prep.copies)
         del prep
         torch.cuda.empty_cache()
@@ -438,6 +476,7 @@ def main():
                       "mul_mat_us": round(q6["unfused"]["mul_mat_us"], 3),
                       "roofline_mul_mat": roofline_of(q6, "unfused")},
         "mul_mat_id_q4_K": moe,
+        "system": system_info(),
     }
     if extra:
         line["other_workloads"] = extra
