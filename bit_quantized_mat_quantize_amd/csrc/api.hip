@@ -400,7 +400,7 @@ bool id_kernels(qmm_weight_type t, IdKernels &k) {
                           gemm_id_repacked<qmm::launch_gemm_id_q2_K>};
             return true;
         case QMM_Q4_0:  // the GEMV reads whole Q8_0 rows from global memory: no K limit of its own
-            k = IdKernels{int64_t(1) << 20, false, 256, qmm::launch_gemv_id_q4_0,
+            k = IdKernels{kMaxK, false, 256, qmm::launch_gemv_id_q4_0,
                           gemm_id_repacked<qmm::launch_gemm_id_q4_0>};
             return true;
     }

@@ -230,8 +230,9 @@ qmm_status qmm_mul_mat_q2_K_ex(const void *w, size_t w_bytes, qmm_layout l,
                                int64_t M, int64_t N, int64_t K, qmm_algo algo,
                                void *stream);
 
-/* Bytes of the workspace qmm_mul_mat_id_q4_K needs for its MFMA path (T
- * tokens, U slots per token, E experts): int32 tables of the expert grouping.
+/* Bytes of the workspace qmm_mul_mat_id (and qmm_mul_mat_id_q4_K) needs for
+ * its MFMA path (T tokens, U slots per token, E experts, any weight format):
+ * int32 tables of the expert grouping.
  * Returns 0 for invalid arguments (U < 1, E outside [1, 4096], T*U >= 2^31). */
 size_t qmm_mul_mat_id_workspace_bytes(int64_t T, int64_t U, int64_t E);
 
@@ -262,7 +263,7 @@ qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_lay
 /* mul_mat_id for any weight format t: the same contract as
  * qmm_mul_mat_id_q4_K with W_e in format t (Q8_0 activations for Q4_0, Q8_K
  * otherwise).  Kernels: QMM_ALGO_GEMV -- one GEMV per (token, slot) (K <=
- * 53760 for Q4_K, Q6_K and Q2_K); QMM_ALGO_MFMA -- the expert grouping into
+ * 53760 for Q4_K, Q6_K and Q2_K, K <= 2^20 for Q4_0); QMM_ALGO_MFMA -- the expert grouping into
  * `workspace`, then the format's MFMA GEMM over each expert's rows (Q6_K, Q2_K
  * and Q4_0 need the repacked layout, and K % 256 == 0); AUTO takes the GEMV
  * for T*U <= 64 and the GEMM above, whichever the call allows otherwise. */
