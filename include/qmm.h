@@ -249,7 +249,7 @@ size_t qmm_mul_mat_id_workspace_bytes(int64_t T, int64_t U, int64_t E);
  * (device, at least qmm_mul_mat_id_workspace_bytes(T, U, E) bytes, contents
  * overwritten; not needed by the GEMV path, may be NULL there) and runs the
  * Q4_K GEMM over each expert's rows (one expert matrix and the activations
- * below 4 GiB); AUTO takes the GEMV for T*U <= 64, the GEMM above.  An id
+ * below 4 GiB); AUTO takes the GEMV for T*U <= 4*E, the GEMM above.  An id
  * outside [0, E) cannot be checked on the host: that pair's output row is
  * filled with NaN and nothing is read out of bounds.  Requires 1 <= E <= 4096,
  * 1 <= U <= E.  Equal to qmm_mul_mat_id(QMM_Q4_K, ...). */
@@ -266,7 +266,7 @@ qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_lay
  * 53760 for Q4_K, Q6_K and Q2_K, K <= 2^20 for Q4_0); QMM_ALGO_MFMA -- the expert grouping into
  * `workspace`, then the format's MFMA GEMM over each expert's rows (Q6_K, Q2_K
  * and Q4_0 need the repacked layout, and K % 256 == 0); AUTO takes the GEMV
- * for T*U <= 64 and the GEMM above, whichever the call allows otherwise. */
+ * for T*U <= 4*E and the GEMM above, whichever the call allows otherwise. */
 qmm_status qmm_mul_mat_id(qmm_weight_type t, const void *w, size_t w_bytes, int64_t E, qmm_layout l,
                           const void *y, size_t y_bytes, int y_per_slot,
                           const int32_t *ids, int64_t T, int64_t U,

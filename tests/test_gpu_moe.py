@@ -112,7 +112,7 @@ def test_auto_matches_forced_paths_and_bad_ids():
     w = _stack(E, N, K, 820)
     wd = _upload(w, E, N, K, "repacked")
     rng = np.random.default_rng(43)
-    for T, U in ((4, 2), (100, 2)):          # AUTO: GEMV (8 pairs), GEMM (200 pairs)
+    for T, U in ((4, 2), (16, 2), (17, 2), (100, 2)):  # AUTO: GEMV (8, 32 pairs), GEMM (34, 200)
         y = oracle.quantize("q8_K", activations([821, T], T, K))
         ids = _routing(rng, T, U, E, skew=False)
         outs = [to_host(qmm.mul_mat_id_q4_K(wd, E, to_dev(y.reshape(-1)), to_dev(ids), N, K,
@@ -120,6 +120,8 @@ def test_auto_matches_forced_paths_and_bad_ids():
         _check(w, E, N, K, y, ids, False, outs[0], f"auto T={T}")
         _check(w, E, N, K, y, ids, False, outs[1], f"gemv T={T}")
         _check(w, E, N, K, y, ids, False, outs[2], f"mfma T={T}")
+        # AUTO takes the per-pair GEMV up to 4*E pairs and the grouped GEMM above
+        assert np.array_equal(outs[0].view(np.uint32), outs[1 if T * U <= 4 * E else 2].view(np.uint32))
         bad = ids.copy()
         bad[0, 1], bad[-1, 0] = -1, E
         good = np.ones((T, U), bool)
