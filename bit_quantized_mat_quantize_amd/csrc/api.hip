@@ -185,6 +185,19 @@ qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N,
                          "repack_weights launch");
 }
 
+// AUTO between a GEMV and the MFMA GEMM.  The GEMV costs a pass over the
+// weights per activation row (or group of rows); with a single row tile the
+// GEMM runs N/256 workgroups, and as long as that is below the CU count its
+// time is one workgroup's K loop whatever N is.  The GEMV therefore wins while
+// M*N stays below a per-format constant (measured at N = K = 8192 on the
+// weight stream: Q6_K up to M ~ 16, Q2_K ~ 26, Q4_0 ~ 30), which grows with the
+// GEMM's waves of workgroups once N passes 256 column tiles.  M = 1 always
+// takes the GEMV.
+bool prefer_gemv(int64_t M, int64_t N, int64_t mn_limit) {
+    return M == 1 || M * N <= mn_limit * ((N + 65535) / 65536);
+}
+constexpr int64_t kGemvMN_Q4_0 = 30 * 8192, kGemvMN_Q6_K = 16 * 8192, kGemvMN_Q2_K = 26 * 8192;
+
 qmm_status qmm_mul_mat_q4_0_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,
                                size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
                                int64_t K, qmm_algo algo, void *stream) {
@@ -201,7 +214,7 @@ qmm_status qmm_mul_mat_q4_0_ex(const void *w, size_t w_bytes, qmm_layout l, cons
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     qmm_algo a = algo;
-    if (a == QMM_ALGO_AUTO) a = M <= qmm::kGemvMaxM || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
+    if (a == QMM_ALGO_AUTO) a = prefer_gemv(M, N, kGemvMN_Q4_0) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
     if (a == QMM_ALGO_MFMA)
         return device_status(qmm::launch_gemm_q4_0(wb, (int64_t)qmm_weight_bytes(QMM_Q4_0, l, N, K), yb,
                                                    out, M, N, K, s),
@@ -249,10 +262,16 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, cons
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     qmm_algo a = algo;
-    if (a == QMM_ALGO_AUTO)
+    // AUTO: the small-batch kernel (one workgroup per 32 columns and 32 rows,
+    // K split over its wavefronts) beats the GEMM up to 32 rows, and further
+    // while ceil(M/32)*N stays below 9*8192 (measured at K = 8192: up to
+    // M ~ 300 for N = 8192, M ~ 80 for N = 28672); K cancels, both scale with it.
+    if (a == QMM_ALGO_AUTO) {
+        const bool skinny_pref = M <= 32 || ((M + 31) / 32) * N <= 9 * 8192;
         a = M == 1 ? QMM_ALGO_GEMV
-                   : (skinny_ok ? QMM_ALGO_SKINNY
-                                : (M <= qmm::kGemvMaxM || !small ? QMM_ALGO_GEMV : QMM_ALGO_MFMA));
+                   : (skinny_ok && skinny_pref ? QMM_ALGO_SKINNY
+                                               : (M <= qmm::kGemvMaxM || !small ? QMM_ALGO_GEMV : QMM_ALGO_MFMA));
+    }
     if (a == QMM_ALGO_GEMV) {
         // groups of up to 8 activation rows per GEMV launch
         const int64_t rowb = (K / 256) * 292;
@@ -281,11 +300,11 @@ qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l, const v
 namespace {
 
 // Q6_K and Q2_K (16-element groups): a GEMV for any M while the activation
-// row fits LDS, and an MFMA GEMM for the repacked layout; AUTO takes the GEMV
-// up to M = 8.
+// row fits LDS, and an MFMA GEMM for the repacked layout; AUTO as in
+// prefer_gemv.
 struct GroupedKernels {
     const char *name;
-    int64_t gemv_max_k;
+    int64_t gemv_max_k, gemv_mn;
     hipError_t (*gemv)(const uint8_t *, bool, const uint8_t *, float *, int64_t, int64_t, int64_t,
                        hipStream_t);
     hipError_t (*gemm)(const uint8_t *, int64_t, const uint8_t *, float *, int64_t, int64_t, int64_t,
@@ -316,7 +335,7 @@ qmm_status mul_mat_grouped(qmm_weight_type t, const GroupedKernels &k, const voi
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     qmm_algo a = algo;
     if (a == QMM_ALGO_AUTO)
-        a = (M <= qmm::kGemvMaxM && gemv_ok) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
+        a = (prefer_gemv(M, N, k.gemv_mn) && gemv_ok) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
     if (a == QMM_ALGO_GEMV)
         return device_status(k.gemv(wb, l == QMM_LAYOUT_REPACKED, yb, out, M, N, K, s), "mul_mat gemv launch");
     return device_status(k.gemm(wb, (int64_t)qmm_weight_bytes(t, l, N, K), yb, out, M, N, K, s),
@@ -324,10 +343,10 @@ qmm_status mul_mat_grouped(qmm_weight_type t, const GroupedKernels &k, const voi
 }
 
 GroupedKernels q6_K_kernels() {
-    return GroupedKernels{"Q6_K", qmm::q6_K_max_k(), qmm::launch_gemv_q6_K, qmm::launch_gemm_q6_K};
+    return GroupedKernels{"Q6_K", qmm::q6_K_max_k(), kGemvMN_Q6_K, qmm::launch_gemv_q6_K, qmm::launch_gemm_q6_K};
 }
 GroupedKernels q2_K_kernels() {
-    return GroupedKernels{"Q2_K", qmm::q2_K_max_k(), qmm::launch_gemv_q2_K, qmm::launch_gemm_q2_K};
+    return GroupedKernels{"Q2_K", qmm::q2_K_max_k(), kGemvMN_Q2_K, qmm::launch_gemv_q2_K, qmm::launch_gemm_q2_K};
 }
 
 }  // namespace

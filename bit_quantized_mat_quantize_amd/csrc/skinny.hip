@@ -1,12 +1,17 @@
-// skinny.hip -- quantized mul_mat for small batches (2 <= M <= 32) on int8 MFMA, gfx950.
+// skinny.hip -- quantized mul_mat for small batches on int8 MFMA, gfx950.
 //
 // A batch of a few activation rows still reads every weight once, so the
 // operation stays bound by the weight stream (BitBLAS page, "调度与自动调优":
 // small-M shapes sit on the memory side of the roofline), but the per-row
 // vector dot products of the GEMV grow with M.  Here the contraction runs on
-// the matrix cores instead: the (at most 32) activation rows are one MFMA row
-// tile, so every weight column is decoded once per super-block and then costs
-// a handful of v_mfma_i32_32x32x32_i8 no matter how many rows there are.
+// the matrix cores instead: a workgroup's (at most 32) activation rows are one
+// MFMA row tile, so every weight column is decoded once per super-block and
+// then costs a handful of v_mfma_i32_32x32x32_i8 no matter how many rows
+// there are.  Larger batches take one 32-row chunk per grid row (blockIdx.y);
+// the chunks of a column tile read the same weights, the later ones mostly
+// from L2 or the MALL.  A single-row-tile GEMM would run only N/256
+// workgroups, so up to a few hundred rows (fewer for large N) this kernel is
+// the faster one.
 //
 // Arithmetic (ggml-cpu mul_mat page, "正确性:缩放系数可以提到求和号外面" and
 // "min 项与最终归约"), per super-block b and output (m, n):
@@ -43,7 +48,8 @@ namespace qmm {
 namespace {
 
 constexpr int SK_WAVES = 8, SK_THREADS = 64 * SK_WAVES;
-constexpr int SK_MAX_M = 32;
+constexpr int SK_ROWS = 32;                   // activation rows per workgroup (one MFMA row tile)
+constexpr int64_t SK_MAX_M = 65535ll * SK_ROWS;  // row chunks go to grid.y
 // Per-wavefront LDS stage: the activation rows of one super-block.
 //   A   int8 codes [32][256]   16-byte piece p of row r at position p ^ (r & 15)
 //   BS  bsums      [32][2][16 B]
@@ -73,6 +79,12 @@ __global__ __launch_bounds__(SK_THREADS, 1) void k_skinny_q4_K(const uint8_t *__
                                                              float *__restrict__ out, int64_t M,
                                                              int64_t N, int64_t K) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    // this workgroup's chunk of at most 32 activation rows (grid.y)
+    const int64_t m0 = (int64_t)blockIdx.y * SK_ROWS;
+    Y += m0 * (K / QK_K) * kQ8_KBytes;
+    out += m0 * N;
+    M = M - m0 < SK_ROWS ? M - m0 : SK_ROWS;
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wavefront-uniform, and known to be: the super-block index derived from it
@@ -282,7 +294,7 @@ hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y,
         if (e != hipSuccess) return e;
         attr_set[repacked] = true;
     }
-    const dim3 grid((unsigned)((N + 31) / 32)), block(SK_THREADS);
+    const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + SK_ROWS - 1) / SK_ROWS)), block(SK_THREADS);
     // up to 8 rows the per-lane operand loads touch few cache lines and beat
     // the LDS staging; more rows are staged
     const bool lds_act = M > 8;

@@ -93,15 +93,17 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
 /* Kernel family for a mul_mat call:
  *   GEMV    vector int8 dot products, one wavefront per output row (Q4_0 and
  *           Q4_K: M <= 8 per launch; Q6_K and Q2_K: any M, K <= 53760)
- *   SKINNY  small-batch int8 MFMA, one 32-column tile per workgroup, K split
- *           over its wavefronts (Q4_K only; M <= 32)
+ *   SKINNY  small-batch int8 MFMA, one 32-column x 32-row tile per workgroup,
+ *           K split over its wavefronts (Q4_K only; M <= 65535*32)
  *   MFMA    prefill GEMM on int8 MFMA, 128 x 256 output tiles (any M; Q6_K,
  *           Q2_K and Q4_0 need the repacked layout, Q4_0 also K % 256 == 0)
  * SKINNY and MFMA address the weight and activation matrices with 32-bit
- * offsets, so both must be below 4 GiB.  AUTO for Q4_K takes GEMV for M = 1,
- * SKINNY for 2 <= M <= 32, MFMA above (GEMV in groups of 8 rows where the
- * size limit rules the MFMA kernels out); for Q6_K, Q2_K and Q4_0 it takes
- * GEMV for M <= 8 and MFMA above, GEMV where MFMA is ruled out. */
+ * offsets, so both must be below 4 GiB.  AUTO follows measured crossovers:
+ * for Q4_K it takes GEMV for M = 1, SKINNY for 2 <= M <= 32 and while
+ * ceil(M/32)*N <= 9*8192, MFMA above (GEMV in groups of 8 rows where the size
+ * limit rules the MFMA kernels out); for Q6_K, Q2_K and Q4_0 it takes GEMV for
+ * M = 1 and while M*N <= c*ceil(N/65536) with c = 16*8192 (Q6_K), 26*8192
+ * (Q2_K), 30*8192 (Q4_0), MFMA above, GEMV where MFMA is ruled out. */
 typedef enum {
     QMM_ALGO_AUTO = 0,
     QMM_ALGO_GEMV = 1,
@@ -203,7 +205,7 @@ qmm_status qmm_mul_mat_q6_K_ex(const void *w, size_t w_bytes, qmm_layout l,
 
 /* Same as qmm_mul_mat_q4_K with an explicit kernel family (for measuring the
  * GEMV / GEMM crossover).  QMM_ALGO_GEMV requires M <= 8; QMM_ALGO_SKINNY
- * requires M <= 32; SKINNY and MFMA require both matrices below 4 GiB (else
+ * requires M <= 65535*32; SKINNY and MFMA require both matrices below 4 GiB (else
  * QMM_EUNSUPPORTED). */
 qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l,
                                const void *y, size_t y_bytes,

@@ -98,6 +98,10 @@ def test_mul_mat_validation(lib):
     assert call(K=384) == EUNSUP
     assert call(l=2) == EUNSUP
     assert call(algo=9) == EUNSUP
+    # SKINNY: 32-row chunks on grid.y, at most 65535 of them
+    mmax = 65535 * 32
+    assert call(M=mmax + 1, yb=2**40, ob=2**40, algo=3) == EUNSUP
+    assert call(M=mmax, N=0, yb=2**40, ob=2**40, algo=3) == OK     # valid, nothing to do
     assert call(M=-1) == EINVAL
     assert call(N=-3) == EINVAL
     assert call(w=None) == EINVAL

@@ -177,11 +177,13 @@ def test_mfma_q4_K(M, N, K, layout):
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", [(2, 1, 256), (2, 33, 512), (3, 100, 2304), (5, 64, 4096),
                                    (8, 257, 6144), (9, 40, 1536), (16, 64, 2560), (17, 45, 1024),
-                                   (32, 96, 3840), (1, 70, 2048)])
+                                   (32, 96, 3840), (1, 70, 2048), (40, 50, 1024), (65, 33, 512),
+                                   (97, 70, 2304)])
 def test_skinny_q4_K(M, N, K, layout):
     """Small-batch MFMA path: ragged N, K splits of 1..3 super-blocks per
-    wavefront (odd and even counts, wavefronts without work), M up to 32
-    (8, 16 and 32 staged activation rows)."""
+    wavefront (odd and even counts, wavefronts without work), 8, 16 and 32
+    staged activation rows, and several 32-row chunks (grid.y) with a ragged
+    last chunk."""
     w, x, y, _ = _case("q4_K", M, N, K, 7 * M + N)
     want, terms = full_reference("q4_K", w, y, M, N, K)
     wd = upload_weights("q4_K", w, N, K, layout)
@@ -189,10 +191,10 @@ def test_skinny_q4_K(M, N, K, layout):
     assert_close(got, want, terms, f"skinny M={M} N={N} K={K} {layout}")
 
 
-def test_skinny_rejects_large_m():
-    with pytest.raises(qmm.QmmError):
+def test_skinny_rejects_unsupported():
+    with pytest.raises(qmm.QmmError):   # K not a multiple of 256
         qmm.mul_mat_q4_K(to_dev(np.zeros(64 * 144, np.uint8)), to_dev(np.zeros(33 * 292, np.uint8)),
-                         33, 64, 256, algo="skinny")
+                         33, 64, 200, algo="skinny")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -206,16 +208,22 @@ def test_q4_0(M, N, K, layout):
 
 
 def test_auto_dispatch_and_overwrite():
-    """AUTO picks GEMV for M = 1, the small-batch kernel up to M = 32 and the
-    GEMM above; `out` is overwritten."""
+    """AUTO picks the GEMV for M = 1, the small-batch kernel up to M = 32 and
+    while ceil(M/32)*N <= 9*8192, the GEMM above, and is bit-identical to that
+    path; `out` is overwritten."""
     import torch
-    N, K = 64, 512
-    for M in (1, 8, 9, 32, 33):
+    K = 512
+    for M, N in ((1, 64), (8, 64), (9, 64), (32, 64), (33, 64), (100, 64), (33, 40000)):
         w, x, y, _ = _case("q4_K", M, N, K, 900 + M)
         want, terms = full_reference("q4_K", w, y, M, N, K)
+        wd, yd = to_dev(w.reshape(-1)), to_dev(y.reshape(-1))
         out = torch.full((M, N), 1e9, device="cuda")
-        qmm.mul_mat_q4_K(to_dev(w.reshape(-1)), to_dev(y.reshape(-1)), M, N, K, out=out)
-        assert_close(to_host(out), want, terms, f"auto M={M}")
+        qmm.mul_mat_q4_K(wd, yd, M, N, K, out=out)
+        assert_close(to_host(out), want, terms, f"auto M={M} N={N}")
+        algo = ("gemv" if M == 1 else
+                "skinny" if M <= 32 or (M + 31) // 32 * N <= 9 * 8192 else "mfma")
+        ref = to_host(qmm.mul_mat_q4_K(wd, yd, M, N, K, algo=algo))
+        assert np.array_equal(to_host(out).view(np.uint32), ref.view(np.uint32)), (M, N, algo)
 
 
 def test_end_to_end_quantize_then_mul_mat():

@@ -139,10 +139,11 @@ def test_mul_mat_q2_K_mfma(M, N, K):
 
 
 def test_auto_dispatch_and_fused():
-    """AUTO picks GEMV up to M = 8 and the GEMM above (repacked), the GEMV for
-    the canonical layout; quantize_mul_mat equals quantize + mul_mat."""
-    N, K = 96, 2048
-    for M in (1, 8, 9, 64):
+    """AUTO picks the GEMV for M = 1 and while M*N <= 26*8192 (per 65536
+    columns), the GEMM above (repacked), the GEMV for the canonical layout, and
+    is bit-identical to that path; quantize_mul_mat equals quantize + mul_mat."""
+    K = 2048
+    for M, N in ((1, 96), (8, 96), (64, 96), (64, 3400)):
         w, _ = _case(M, N, K, 900 + M)
         x = activations([703, M], M, K)
         y = oracle.quantize("q8_K", x)
@@ -150,7 +151,11 @@ def test_auto_dispatch_and_fused():
         for layout in LAYOUTS:
             wd = _upload(w, N, K, layout)
             got = to_host(qmm.mul_mat_q2_K(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout))
-            assert_close(got, want, terms, f"q2_K auto M={M} {layout}")
+            assert_close(got, want, terms, f"q2_K auto M={M} N={N} {layout}")
+            gemv = layout == "canonical" or M == 1 or M * N <= 26 * 8192 * ((N + 65535) // 65536)
+            ref = to_host(qmm.mul_mat_q2_K(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout,
+                                           algo="gemv" if gemv else "mfma"))
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (M, N, layout)
             fused, yq = qmm.quantize_mul_mat("q2_K", wd, to_dev(x), N, layout=layout)
             assert np.array_equal(to_host(yq).reshape(-1), y.reshape(-1))
             assert np.array_equal(to_host(fused).view(np.uint32), got.view(np.uint32))

@@ -64,9 +64,10 @@ def test_mfma_q4_0(M, N, K):
 
 
 def test_auto_dispatch():
-    """Every AUTO choice (GEMV for M <= 8, for the canonical layout and for
-    K % 256 != 0; the GEMM otherwise) agrees with the oracle."""
-    for M, N, K in [(8, 70, 1024), (40, 70, 1024), (40, 70, 288)]:
+    """Every AUTO choice (the GEMV for M = 1 and while M*N <= 30*8192 per 65536
+    columns, for the canonical layout and for K % 256 != 0; the GEMM
+    otherwise) is bit-identical to that path and agrees with the oracle."""
+    for M, N, K in [(8, 70, 1024), (40, 70, 1024), (40, 70, 288), (40, 6200, 1024)]:
         w = oracle.quantize("q4_0", weights_normal([432, M + K], N, K))
         y = oracle.quantize("q8_0", activations([433, M + K], M, K))
         want, terms = full_reference("q4_0", w, y, M, N, K)
@@ -74,6 +75,14 @@ def test_auto_dispatch():
             wd = upload_weights("q4_0", w, N, K, layout)
             got = to_host(qmm.mul_mat_q4_0(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout))
             assert_close(got, want, terms, f"q4_0 auto M={M} K={K} {layout}")
+            gemv = (layout == "canonical" or K % 256 != 0 or M == 1
+                    or M * N <= 30 * 8192 * ((N + 65535) // 65536))
+            ref = to_host(qmm.mul_mat_q4_0(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout,
+                                           algo="gemv" if gemv else "mfma"))
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (M, N, K, layout)
+    M, N, K = 40, 70, 288                                      # K % 256 != 0: no MFMA path
+    w = oracle.quantize("q4_0", weights_normal([432, M + K], N, K))
+    y = oracle.quantize("q8_0", activations([433, M + K], M, K))
     with pytest.raises(qmm.QmmError):
         qmm.mul_mat_q4_0(upload_weights("q4_0", w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K,
-                         layout="repacked", algo="mfma")       # K = 288
+                         layout="repacked", algo="mfma")

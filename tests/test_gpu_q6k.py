@@ -176,13 +176,17 @@ def test_mul_mat_q6_K_mfma(M, N, K):
 
 
 def test_auto_dispatch():
-    """AUTO: GEMV up to M = 8, the GEMM above (repacked), the GEMV for the
-    canonical layout at any M; every choice agrees with the oracle."""
-    N, K = 96, 2048
-    for M in (1, 8, 9, 64):
+    """AUTO: the GEMV for M = 1 and while M*N <= 16*8192 (per 65536 columns),
+    the GEMM above (repacked), the GEMV for the canonical layout at any M;
+    AUTO is bit-identical to that path and agrees with the oracle."""
+    K = 2048
+    for M, N in ((1, 96), (8, 96), (64, 96), (64, 2100)):
         w, y = _case(M, N, K, 900 + M)
         want, terms = full_reference("q6_K", w, y, M, N, K)
         for layout in LAYOUTS:
-            got = to_host(qmm.mul_mat_q6_K(_upload(w, N, K, layout), to_dev(y.reshape(-1)), M, N, K,
-                                           layout=layout))
-            assert_close(got, want, terms, f"q6_K auto M={M} {layout}")
+            wd, yd = _upload(w, N, K, layout), to_dev(y.reshape(-1))
+            got = to_host(qmm.mul_mat_q6_K(wd, yd, M, N, K, layout=layout))
+            assert_close(got, want, terms, f"q6_K auto M={M} N={N} {layout}")
+            gemv = layout == "canonical" or M == 1 or M * N <= 16 * 8192 * ((N + 65535) // 65536)
+            ref = to_host(qmm.mul_mat_q6_K(wd, yd, M, N, K, layout=layout, algo="gemv" if gemv else "mfma"))
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (M, N, layout)
