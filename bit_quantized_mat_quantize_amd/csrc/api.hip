@@ -190,31 +190,53 @@ qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N,
 // GEMM runs N/256 workgroups, and as long as that is below the CU count its
 // time is one workgroup's K loop whatever N is.  The GEMV therefore wins while
 // M*N stays below a per-format constant (measured at N = K = 8192 on the
-// weight stream: Q6_K up to M ~ 16, Q2_K ~ 26, Q4_0 ~ 30), which grows with the
-// GEMM's waves of workgroups once N passes 256 column tiles.  M = 1 always
-// takes the GEMV.
+// weight stream: Q6_K up to M ~ 16, Q2_K ~ 26), which grows with the GEMM's
+// waves of workgroups once N passes 256 column tiles.  M = 1 always takes the
+// GEMV.
 bool prefer_gemv(int64_t M, int64_t N, int64_t mn_limit) {
     return M == 1 || M * N <= mn_limit * ((N + 65535) / 65536);
 }
-constexpr int64_t kGemvMN_Q4_0 = 30 * 8192, kGemvMN_Q6_K = 16 * 8192, kGemvMN_Q2_K = 26 * 8192;
+constexpr int64_t kGemvMN_Q6_K = 16 * 8192, kGemvMN_Q2_K = 26 * 8192;
+// Q4_0 small-batch kernel vs GEMM: its time grows with the number of 32-row
+// chunks times N/32 workgroups, the GEMM's stays one K loop while its row
+// tiles fit the CUs; measured on N = 4096..28672, K = 4096..14336 it wins
+// while ceil(M/32)*N stays at or below this.
+constexpr int64_t kSkinnyMN_Q4_0 = 16 * 8192;
 
 qmm_status qmm_mul_mat_q4_0_ex(const void *w, size_t w_bytes, qmm_layout l, const void *y,
                                size_t y_bytes, float *out, size_t out_bytes, int64_t M, int64_t N,
                                int64_t K, qmm_algo algo, void *stream) {
-    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
-        return fail(QMM_EUNSUPPORTED, "Q4_0 takes the GEMV or MFMA path (algo %d)", (int)algo);
+    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA && algo != QMM_ALGO_SKINNY)
+        return fail(QMM_EUNSUPPORTED, "unknown algo %d", (int)algo);
     QMM_TRY(mul_mat_common(QMM_Q4_0, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
-    // the MFMA kernel steps K by 256 and takes the repacked layout
+    // the MFMA kernels step K by 256 and take the repacked layout
     const bool mfma_ok = l == QMM_LAYOUT_REPACKED && K % 256 == 0 && below_4gib(QMM_Q4_0, l, M, N, K);
+    const bool skinny_ok = mfma_ok && M <= qmm::skinny_q4_0_max_m();
     if (algo == QMM_ALGO_MFMA && !mfma_ok)
         return fail(QMM_EUNSUPPORTED,
                     "Q4_0 MFMA path takes the repacked layout, K a multiple of 256 and matrices below 4 GiB");
+    if (algo == QMM_ALGO_SKINNY && !skinny_ok)
+        return fail(QMM_EUNSUPPORTED,
+                    "Q4_0 SKINNY path takes the repacked layout, K a multiple of 256, M <= %lld and matrices "
+                    "below 4 GiB", (long long)qmm::skinny_q4_0_max_m());
     if (M == 0 || N == 0) return QMM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     qmm_algo a = algo;
-    if (a == QMM_ALGO_AUTO) a = prefer_gemv(M, N, kGemvMN_Q4_0) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
+    if (a == QMM_ALGO_AUTO) {
+        // GEMV for M = 1, and for M = 2 below 8192 columns, where the
+        // small-batch kernel's N/32 workgroups leave CUs idle and the GEMV's
+        // second pass over the weights is cheaper; GEMV too where the MFMA
+        // kernels are ruled out
+        if (!mfma_ok || M == 1 || (M == 2 && N < 8192)) a = QMM_ALGO_GEMV;
+        else if (skinny_ok && ((M + 31) / 32) * N <= kSkinnyMN_Q4_0) a = QMM_ALGO_SKINNY;
+        else a = QMM_ALGO_MFMA;
+    }
+    if (a == QMM_ALGO_SKINNY)
+        return device_status(qmm::launch_skinny_q4_0(wb, (int64_t)qmm_weight_bytes(QMM_Q4_0, l, N, K), yb, out,
+                                                     M, N, K, s),
+                             "mul_mat_q4_0 small-batch launch");
     if (a == QMM_ALGO_MFMA)
         return device_status(qmm::launch_gemm_q4_0(wb, (int64_t)qmm_weight_bytes(QMM_Q4_0, l, N, K), yb,
                                                    out, M, N, K, s),

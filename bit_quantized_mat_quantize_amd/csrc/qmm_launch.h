@@ -39,6 +39,11 @@ hipError_t launch_block_sums_q4_K(const uint8_t *w, bool repacked, const uint8_t
 int64_t skinny_max_m();
 hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                               int64_t M, int64_t N, int64_t K, hipStream_t s);
+// Q4_0 small batch: repacked layout, K % 256 == 0, M <= skinny_q4_0_max_m(),
+// matrices below 4 GiB; w_bytes is the repacked matrix size.
+int64_t skinny_q4_0_max_m();
+hipError_t launch_skinny_q4_0(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M,
+                              int64_t N, int64_t K, hipStream_t s);
 
 // Q6_K (encoder, load-time repack, GEMV for any M with K <= q6_K_max_k(),
 // int32 group sums P[m][n][K/16] of the same decode path).

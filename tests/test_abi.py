@@ -119,6 +119,13 @@ def test_mul_mat_validation(lib):
     # repacked Q4_0 needs the padded size
     need = lib.qmm_weight_bytes(0, 1, 3, 64)
     assert g(A, need - 1, 1, A, big, A, big, 1, 3, 64, None) == EINVAL
+    gx = lib.qmm_mul_mat_q4_0_ex
+    # SKINNY: repacked layout, K % 256 == 0, M <= 65535*32; unknown families refused
+    assert gx(A, big, 0, A, big, A, big, 4, 8, 512, 3, None) == EUNSUP and "SKINNY" in _last(lib)
+    assert gx(A, big, 1, A, big, A, big, 4, 8, 288, 3, None) == EUNSUP
+    assert gx(A, 2**40, 1, A, 2**40, A, 2**40, mmax + 1, 8, 512, 3, None) == EUNSUP
+    assert gx(A, 2**40, 1, A, 2**40, A, 2**40, mmax, 0, 512, 3, None) == OK
+    assert gx(A, big, 1, A, big, A, big, 4, 8, 512, 7, None) == EUNSUP and "unknown algo" in _last(lib)
 
 
 def test_quantize_mul_mat_validation(lib):

@@ -1,14 +1,15 @@
-"""Q4_0 x Q8_0 on the int8 MFMA GEMM (repacked layout, K % 256 == 0) against
-the oracle.
+"""Q4_0 x Q8_0 on the int8 MFMA kernels (repacked layout, K % 256 == 0): the
+prefill GEMM and the small-batch kernel, against the oracle.
 
 * exactness window: Q4_0 blocks with d = 1 and integer activations with
   amax = 127 per 32-block (d_a = 1) keep every partial sum an integer below
   2^24, so the fp32 outputs equal the integer result exactly -- including the
   code extremes 0 and 15 (q - 8 = -8 and 7) against y = +-127.
 * fp32 outputs: |gpu - oracle| <= 1e-4 * sum_k |w a| for every checked (m, n),
-  on ragged row and column tiles, one K step and many.
-* AUTO dispatch: GEMV up to M = 8, for the canonical layout and for K not a
-  multiple of 256; the GEMM otherwise.
+  on ragged row and column tiles, one K step and many; for the small-batch
+  kernel also step counts that leave some of its eight K-split wavefronts with
+  no step or one step more than the others, and several 32-row chunks.
+* AUTO dispatch: each choice is bit-identical to the path it names.
 """
 import struct
 
@@ -33,8 +34,9 @@ def _blocks(codes, d=1.0):
     return np.frombuffer(bytes(out), np.uint8).reshape(N, -1)
 
 
+@pytest.mark.parametrize("algo", ["mfma", "skinny"])
 @pytest.mark.parametrize("extreme", [False, True])
-def test_mfma_exactness_window(extreme):
+def test_mfma_exactness_window(extreme, algo):
     M, N, K = 130, 300, 512
     rng = np.random.default_rng(31)
     if extreme:
@@ -49,7 +51,7 @@ def test_mfma_exactness_window(extreme):
     want, terms = full_reference("q4_0", w, y, M, N, K)
     assert terms.max() < 2 ** 24
     wd = upload_weights("q4_0", w, N, K, "repacked")
-    got = to_host(qmm.mul_mat_q4_0(wd, to_dev(y.reshape(-1)), M, N, K, layout="repacked", algo="mfma"))
+    got = to_host(qmm.mul_mat_q4_0(wd, to_dev(y.reshape(-1)), M, N, K, layout="repacked", algo=algo))
     assert np.array_equal(got.astype(np.float64), want)
 
 
@@ -63,11 +65,55 @@ def test_mfma_q4_0(M, N, K):
     assert_close(got, want, terms, f"q4_0 mfma M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 70, 256), (5, 33, 512), (8, 300, 2048), (9, 64, 4608), (17, 1, 256),
+                                   (32, 257, 1024), (40, 100, 2048), (70, 130, 4608)])
+def test_skinny_q4_0(M, N, K):
+    w = oracle.quantize("q4_0", weights_normal([434, M + N], N, K))
+    y = oracle.quantize("q8_0", activations([435, M + N], M, K, outlier_frac=0.01))
+    want, terms = full_reference("q4_0", w, y, M, N, K)
+    wd = upload_weights("q4_0", w, N, K, "repacked")
+    got = to_host(qmm.mul_mat_q4_0(wd, to_dev(y.reshape(-1)), M, N, K, layout="repacked", algo="skinny"))
+    assert_close(got, want, terms, f"q4_0 skinny M={M} N={N} K={K}")
+
+
+def test_skinny_overwrites_and_rejects():
+    """The small-batch kernel writes every output (no accumulation into a
+    stale buffer) and refuses what it does not take: the canonical layout and
+    K not a multiple of 256."""
+    M, N, K = 20, 50, 512
+    w = oracle.quantize("q4_0", weights_normal([436, 1], N, K))
+    y = oracle.quantize("q8_0", activations([437, 1], M, K))
+    want, terms = full_reference("q4_0", w, y, M, N, K)
+    wd = upload_weights("q4_0", w, N, K, "repacked")
+    import torch
+    out = torch.full((M, N), float("nan"), device="cuda")
+    qmm.mul_mat_q4_0(wd, to_dev(y.reshape(-1)), M, N, K, layout="repacked", algo="skinny", out=out)
+    assert_close(to_host(out), want, terms, "q4_0 skinny into a NaN-filled buffer")
+    with pytest.raises(qmm.QmmError):
+        qmm.mul_mat_q4_0(upload_weights("q4_0", w, N, K, "canonical"), to_dev(y.reshape(-1)), M, N, K,
+                         layout="canonical", algo="skinny")
+    K = 288
+    w = oracle.quantize("q4_0", weights_normal([436, 2], N, K))
+    y = oracle.quantize("q8_0", activations([437, 2], M, K))
+    with pytest.raises(qmm.QmmError):
+        qmm.mul_mat_q4_0(upload_weights("q4_0", w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K,
+                         layout="repacked", algo="skinny")
+
+
+def _auto_algo(M, N, K, layout):
+    """The AUTO rule as the library documents it."""
+    if layout == "canonical" or K % 256 != 0 or M == 1 or (M == 2 and N < 8192):
+        return "gemv"
+    return "skinny" if (M + 31) // 32 * N <= 16 * 8192 else "mfma"
+
+
 def test_auto_dispatch():
-    """Every AUTO choice (the GEMV for M = 1 and while M*N <= 30*8192 per 65536
-    columns, for the canonical layout and for K % 256 != 0; the GEMM
-    otherwise) is bit-identical to that path and agrees with the oracle."""
-    for M, N, K in [(8, 70, 1024), (40, 70, 1024), (40, 70, 288), (40, 6200, 1024)]:
+    """Every AUTO choice (the GEMV for M = 1, for M = 2 below 8192 columns, for
+    the canonical layout and for K % 256 != 0; the small-batch kernel while
+    ceil(M/32)*N <= 16*8192; the GEMM above) is bit-identical to that path and
+    agrees with the oracle."""
+    for M, N, K in [(1, 70, 1024), (2, 70, 1024), (2, 8192, 256), (8, 70, 1024), (40, 70, 288),
+                    (40, 6200, 1024), (100, 32768, 256), (161, 26000, 256)]:
         w = oracle.quantize("q4_0", weights_normal([432, M + K], N, K))
         y = oracle.quantize("q8_0", activations([433, M + K], M, K))
         want, terms = full_reference("q4_0", w, y, M, N, K)
@@ -75,11 +121,12 @@ def test_auto_dispatch():
             wd = upload_weights("q4_0", w, N, K, layout)
             got = to_host(qmm.mul_mat_q4_0(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout))
             assert_close(got, want, terms, f"q4_0 auto M={M} K={K} {layout}")
-            gemv = (layout == "canonical" or K % 256 != 0 or M == 1
-                    or M * N <= 30 * 8192 * ((N + 65535) // 65536))
-            ref = to_host(qmm.mul_mat_q4_0(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout,
-                                           algo="gemv" if gemv else "mfma"))
-            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (M, N, K, layout)
+            algo = _auto_algo(M, N, K, layout)
+            ref = to_host(qmm.mul_mat_q4_0(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout, algo=algo))
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (M, N, K, layout, algo)
+    seen = {_auto_algo(M, N, K, "repacked") for M, N, K in [(2, 70, 1024), (2, 8192, 256), (100, 32768, 256),
+                                                              (161, 26000, 256)]}
+    assert seen == {"gemv", "skinny", "mfma"}
     M, N, K = 40, 70, 288                                      # K % 256 != 0: no MFMA path
     w = oracle.quantize("q4_0", weights_normal([432, M + K], N, K))
     y = oracle.quantize("q8_0", activations([433, M + K], M, K))
