@@ -9,12 +9,16 @@
 // A Q4_0 block is one K = 32 chunk of v_mfma_i32_32x32x32_i8, so the codes go
 // straight into the weight operand as the int8 values q - 8 and one MFMA per
 // chunk gives P_b for a 32 x 32 tile.  Unlike the K-quants, both scales change
-// every 32 elements, so every MFMA result needs its own fp32 epilogue (convert,
-// times d_w, fused multiply-add with d_a): three vector instructions per
-// output value per block against one MFMA per 32 x 32 x 32 -- this kernel is
-// bound by that epilogue, not by the matrix cores.  (The ggml-cpu page finds
-// Q4_0 faster than the K-quants for CPU prefill because its unpack is
-// cheaper; on the matrix cores the per-block scale traffic dominates instead.)
+// every 32 elements, so every MFMA result needs its own fp32 epilogue.  The
+// scale products S_b[m][n] = d_a[m,b] * d_w[n,b] of a 32 x 32 tile come from
+// one fp16 MFMA (v_mfma_f32_32x32x16_f16): the A operand holds the eight
+// blocks' d_a of a row in K slots 0..7, the B operand holds d_w of block b in
+// slot b and zeros elsewhere, so S_b is the single product, exact in fp32.
+// The epilogue is then two vector instructions per output value per block
+// (convert P_b, fused multiply-add with S_b) against two MFMAs per 32 x 32 x 32
+// -- still the bound of this kernel, ahead of the matrix cores.  (The ggml-cpu
+// page finds Q4_0 faster than the K-quants for CPU prefill because its unpack
+// is cheaper; on the matrix cores the per-block scale traffic dominates.)
 //
 // Tiling as in the K-quant GEMMs: 512 threads = 8 wavefronts, tile 128 (M) x
 // 256 (N), wavefront w owns the 32-column tile 32w..32w+31 for all four
@@ -24,9 +28,15 @@
 // staged through registers: each thread loads one block pair (68 bytes, four
 // dwordx4 + one dword, one step ahead), realigns the first block's codes with
 // v_alignbyte, and writes codes and d_a to LDS (double-buffered; codes
-// XOR-swizzled by 16-byte piece, d_a block-major so that four consecutive
-// rows are one 8-byte read).  Weights: each lane loads its column's eight
-// 16-byte payloads and eight fp16 d straight into registers, one step ahead.
+// XOR-swizzled by 16-byte piece, d_a row-major so that a row's eight blocks
+// are one 16-byte read).  Weights: each wavefront moves its 32 columns' step
+// (eight 16-byte payloads and 16 bytes of fp16 d per column) with direct
+// global->LDS loads into its own region of the next buffer, one step ahead;
+// piece c of column col sits at slot c ^ (col & 7) of the column's 128 bytes,
+// so the 32 lanes reading one piece of their columns hit distinct banks.  No
+// other wavefront reads that region, so the loads need only this wavefront's
+// wait.  Per step the blocks are the outer loop and the four row tiles the
+// inner one, which keeps one decoded weight operand live.
 #include "mfma_common.h"
 #include "qmm_device.h"
 #include "qmm_launch.h"
@@ -36,17 +46,15 @@ namespace {
 
 constexpr int BM = 128, BN = 256, MT = BM / 32, NWAVE = 8, NTHR = 64 * NWAVE;
 constexpr int A_OFF = 0, A_BYTES = BM * 256;
-constexpr int DA_OFF = A_OFF + A_BYTES, DA_BYTES = 8 * BM * 2;  // fp16 [8 blocks][128 rows]
-constexpr int BUF_BYTES = DA_OFF + DA_BYTES;
-constexpr int LDS_BYTES = 2 * BUF_BYTES;
+constexpr int DA_OFF = A_OFF + A_BYTES, DA_BYTES = 8 * BM * 2;  // fp16 [128 rows][8 blocks]
+constexpr int WP_OFF = DA_OFF + DA_BYTES, WP_WAVE = 32 * 128;    // payloads [wave][32 columns][8 slots]
+constexpr int WD_OFF = WP_OFF + NWAVE * WP_WAVE, WD_WAVE = 32 * 16;  // d_w [wave][32 columns][8 fp16]
+constexpr int BUF_BYTES = WD_OFF + NWAVE * WD_WAVE;
+constexpr int ZERO_OFF = 2 * BUF_BYTES;    // 16 zero bytes: the scale MFMA's K slots 8..15
+constexpr int LDS_BYTES = ZERO_OFF + 16;
 constexpr int kStepBytes = 8 * kQ8_0Bytes;  // 272: one K step of a Q8_0 row
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 static_assert(BN == 32 * NWAVE && 4 * BM == NTHR, "one column tile per wavefront; one block pair per thread");
-
-struct Q40Stage {
-    uint4 pay[8];  // payloads of blocks 8b..8b+7 of this lane's column
-    uint4 d;       // their fp16 d
-};
 
 template <bool GROUPED>
 __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict__ W, int64_t w_bytes,
@@ -94,12 +102,30 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
     };
     const uint32_t a_off = arow(s_row < m_last ? s_row : m_last) + 68 * s_pair;
 
-    // ---- this lane's weight column (columns past N clamped; never stored)
+    // ---- weight DMA of this wavefront's 32 columns (columns past N clamped;
+    // never stored): instruction t moves columns 8t..8t+7, lane l the piece
+    // (l & 7) ^ (col & 7) of column col = 8t + l/8 to slot l & 7; lanes 0..31 of
+    // one more move the 16 bytes of d of column l
     const int64_t NB = N * nb32;
     const int64_t dsec = (2 * NB + 255) / 256 * 256;
-    const int64_t n_lane = n_base + wave * 32 + l32 < N ? n_base + wave * 32 + l32 : N - 1;
-    const uint32_t v_pay = (uint32_t)(dsec + 16 * n_lane * nb32);
-    const uint32_t v_d = (uint32_t)(2 * n_lane * nb32);
+    auto wcol = [&](int col) -> int64_t {
+        const int64_t n = n_base + wave * 32 + col;
+        return n < N ? n : N - 1;
+    };
+    uint32_t wp_goff[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int col = 8 * t + (lane >> 3);
+        wp_goff[t] = (uint32_t)(dsec + 16 * wcol(col) * nb32 + 16 * ((lane & 7) ^ (col & 7)));
+    }
+    const uint32_t wd_goff = (uint32_t)(2 * wcol(l32) * nb32);
+    auto wdma = [&](int64_t b, uint8_t *buf) {
+        const rsrc_t rw = make_rsrc(W, w_bytes);
+        const uint32_t bb = (uint32_t)b;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dma16(rw, wp_goff[t], 128 * bb, buf + WP_OFF + wave * WP_WAVE + 1024 * t);
+        if (lane < 32) dma16(rw, wd_goff, 16 * bb, buf + WD_OFF + wave * WD_WAVE);
+    };
 
     struct ARaw {
         uint4 q[4];
@@ -126,16 +152,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
         *reinterpret_cast<uint4 *>(arow_p + 16 * ((2 * blk0 + 1) ^ (s_row & 15))) = make_uint4(c0[4], c0[5], c0[6], c0[7]);
         *reinterpret_cast<uint4 *>(arow_p + 16 * ((2 * blk1) ^ (s_row & 15))) = make_uint4(w[9], w[10], w[11], w[12]);
         *reinterpret_cast<uint4 *>(arow_p + 16 * ((2 * blk1 + 1) ^ (s_row & 15))) = make_uint4(w[13], w[14], w[15], w[16]);
-        uint16_t *da = reinterpret_cast<uint16_t *>(buf + DA_OFF);
-        da[blk0 * BM + s_row] = (uint16_t)(w[0] & 0xffff);
-        da[blk1 * BM + s_row] = (uint16_t)(w[8] >> 16);
-    };
-    auto wload = [&](int64_t b, Q40Stage &x) {
-        const rsrc_t rw = make_rsrc(W, w_bytes);
-        const uint32_t bb = (uint32_t)b;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) x.pay[c] = bld16(rw, v_pay + 16 * c, 128 * bb);
-        x.d = bld16(rw, v_d, 16 * bb);
+        // d_a of blocks blk0, blk1 of row s_row: adjacent halves
+        *reinterpret_cast<uint32_t *>(buf + DA_OFF + s_row * 16 + 4 * s_pair) = (w[0] & 0xffffu) | (w[8] & 0xffff0000u);
     };
 
     float acc[MT][16];
@@ -145,70 +163,96 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
         for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
     ARaw ar;
-    Q40Stage wx;
     aload(0, ar);
-    wload(0, wx);
+    wdma(0, lds);
+    if (tid == 0) *reinterpret_cast<uint4 *>(lds + ZERO_OFF) = make_uint4(0, 0, 0, 0);  // read after a barrier
+    // scale MFMA A operand: lanes 0..31 read their row's eight d_a (K slots
+    // 0..7), lanes 32..63 the zero bytes (K slots 8..15)
+    const int da_lane = hh ? ZERO_OFF : DA_OFF + l32 * 16;
+    const uint32_t bmask = hh ? 0u : 0xffffffffu;  // B operand: K slots 8..15 are zero
+    const int wp_lane = WP_OFF + wave * WP_WAVE + l32 * 128, wsw = l32 & 7;
+    const int wd_lane = WD_OFF + wave * WD_WAVE + l32 * 16;
 
     for (int64_t b = 0; b < nsteps; ++b) {
         uint8_t *buf = lds + (b & 1) * BUF_BYTES;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of step b
+        // this thread's activation loads and this wavefront's weight DMA of step b
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         acommit(ar, buf);
-
-        // ---------------- decode: lane half hh takes the low (hh = 0) or high
-        // nibbles of each payload (elements 16hh..16hh+15 of the block) as the
-        // int8 values q - 8: ((q | 0x80) - 8) ^ 0x80 per byte, no borrow
-        // crossing bytes
-        v4i bq[8];
-        float dw[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const uint32_t pw[4] = {wx.pay[c].x, wx.pay[c].y, wx.pay[c].z, wx.pay[c].w};
-            uint32_t o[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                o[k] = ((((pw[k] >> (4 * hh)) & 0x0f0f0f0fu) | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
-            bq[c] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-        }
-        {
-            const uint32_t dd[4] = {wx.d.x, wx.d.y, wx.d.z, wx.d.w};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) dw[c] = f16_bits_to_f32((dd[c >> 1] >> (16 * (c & 1))) & 0xffff);
-        }
-
-        __syncthreads();  // every thread's step-b data is in LDS; step b-1 is fully consumed
+        __syncthreads();  // every thread's step-b activations are in LDS; step b-1 is fully consumed
         if (b + 1 < nsteps) {
             aload(b + 1, ar);
-            wload(b + 1, wx);
+            wdma(b + 1, lds + ((b + 1) & 1) * BUF_BYTES);
         }
-        const _Float16 *da = reinterpret_cast<const _Float16 *>(buf + DA_OFF);
+        const uint8_t *da_base = (hh ? lds : buf) + da_lane;  // the zero bytes are outside the buffers
+        v8h a_da[MT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+            a_da[i] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4 *>(da_base + (hh ? 0 : i * 32 * 16)));
+        const uint4 dv = *reinterpret_cast<const uint4 *>(buf + wd_lane);
+        const uint32_t dd[4] = {dv.x & bmask, dv.y & bmask, dv.z & bmask, dv.w & bmask};
 
-        // ---------------- the four row tiles of this column tile
+        // The 32 (block, row tile) pairs run as a pipeline: the two MFMAs of
+        // pair t + 1 are issued before the epilogue of pair t (convert P,
+        // fused multiply-add with S), so the matrix cores work while the
+        // vector ALU does the epilogue; scheduling barriers and the empty asm
+        // statements keep that order.
+        v4i bq[2];
+        v8h b_dw[2];
+        v16i P[2];
+        v16f S[2];
+        uint4 av[2], pv[2];
+        auto read_a = [&](int t) {
+            const int c = t >> 2, row = (t & 3) * 32 + l32;
+            av[t & 1] = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * 256 + 16 * ((2 * c + hh) ^ (row & 15)));
+        };
+        auto read_w = [&](int c) {
+            pv[c & 1] = *reinterpret_cast<const uint4 *>(buf + wp_lane + 16 * (c ^ wsw));
+        };
+        // LDS reads run one pair (codes) or three pairs (payloads) ahead of
+        // the MFMAs that take them
+        auto issue = [&](int t) {
+            const int c = t >> 2, i = t & 3;
+            if (t + 1 < 8 * MT) read_a(t + 1);
+            if (i == 1 && c + 1 < 8) read_w(c + 1);
+            if (i == 0) {
+                // decode: lane half hh takes the low (hh = 0) or high nibbles of
+                // the payload (elements 16hh..16hh+15 of block c) into the high
+                // half of each byte, XOR 0x80: the signed byte 16 * (q - 8).
+                // The factor 16 is removed, exactly, at the store.  d_w of
+                // block c goes to K slot c of the scale MFMA's B operand
+                // (dword c/2, half c%2), zeros elsewhere.
+                const uint32_t pw[4] = {pv[c & 1].x, pv[c & 1].y, pv[c & 1].z, pv[c & 1].w};
+                uint32_t o[4];
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int row = i * 32 + l32;
-            const v16i zero = {};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * 256 +
-                                                                 16 * ((2 * c + hh) ^ (row & 15)));
-                const v16i P = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w},
-                                                                     bq[c], zero, 0, 0, 0);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // d_a of rows 32i + 8q + 4hh .. +3 (one 8-byte read)
-                    const uint2 dq = *reinterpret_cast<const uint2 *>(da + c * BM + i * 32 + 8 * q + 4 * hh);
-                    const _Float16 *dh = reinterpret_cast<const _Float16 *>(&dq);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * q + e;
-                        acc[i][r] = fmaf((float)dh[e], dw[c] * (float)P[r], acc[i][r]);
-                    }
-                }
+                for (int k = 0; k < 4; ++k) o[k] = ((pw[k] << (4 - 4 * hh)) & 0xf0f0f0f0u) ^ 0x80808080u;
+                bq[c & 1] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+                uint32_t bs[4] = {0u, 0u, 0u, 0u};
+                bs[c >> 1] = dd[c >> 1] & ((c & 1) ? 0xffff0000u : 0x0000ffffu);
+                b_dw[c & 1] = __builtin_bit_cast(v8h, make_uint4(bs[0], bs[1], bs[2], bs[3]));
             }
+            const uint4 a = av[t & 1];
+            P[t & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w},
+                                                             bq[c & 1], v16i{}, 0, 0, 0);
+            S[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_da[i], b_dw[c & 1], v16f{}, 0, 0, 0);
+        };
+        read_w(0);
+        read_a(0);
+        issue(0);
+#pragma unroll
+        for (int t = 0; t < 8 * MT; ++t) {
+            if (t + 1 < 8 * MT) issue(t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int i = t & 3;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] = fmaf((float)P[t & 1][r], S[t & 1][r], acc[i][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(acc[i][r]));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
+    // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column
+    // l%32; the weight operand carried 16 * (q - 8), and scaling by 1/16 is exact
     const int64_t n = n_base + wave * 32 + l32;
     if (n < N) {
 #pragma unroll
@@ -217,10 +261,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
             for (int r = 0; r < 16; ++r) {
                 if constexpr (GROUPED) {
                     const int lm = i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (lm <= m_last) out[(int64_t)grp.sorted[r0 + lm] * N + n] = acc[i][r];
+                    if (lm <= m_last) out[(int64_t)grp.sorted[r0 + lm] * N + n] = acc[i][r] * 0.0625f;
                 } else {
                     const int64_t m = m_base + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (m < M) out[m * N + n] = acc[i][r];
+                    if (m < M) out[m * N + n] = acc[i][r] * 0.0625f;
                 }
             }
     }
