@@ -27,13 +27,15 @@
 // but the codes of every other block sit at a 2-byte offset, so the tile is
 // staged through registers: each thread loads one block pair (68 bytes, four
 // dwordx4 + one dword, one step ahead), realigns the first block's codes with
-// v_alignbyte, and writes codes and d_a to LDS (double-buffered; codes
-// XOR-swizzled by 16-byte piece, d_a row-major so that a row's eight blocks
-// are one 16-byte read).  Weights: each wavefront moves its 32 columns' step
+// v_alignbyte, and writes codes and d_a to LDS (double-buffered; code rows
+// padded to 272 bytes, an odd number of 16-byte slots, so the 8, 16 or 32
+// lanes serviced together reading one piece of consecutive rows hit distinct
+// banks; d_a row-major so that a row's eight blocks are one 16-byte read).  Weights: each wavefront moves its 32 columns' step
 // (eight 16-byte payloads and 16 bytes of fp16 d per column) with direct
 // global->LDS loads into its own region of the next buffer, one step ahead;
-// piece c of column col sits at slot c ^ (col & 7) of the column's 128 bytes,
-// so the 32 lanes reading one piece of their columns hit distinct banks.  No
+// piece c of column col sits at slot c ^ (col & 7) ^ ((col >> 3) & 3) of the
+// column's 128 bytes, so 8, 16 or 32 consecutive columns reading one piece
+// fall in distinct 16-byte slots of 128, 256 or 512 bytes.  No
 // other wavefront reads that region, so the loads need only this wavefront's
 // wait.  Per step the blocks are the outer loop and the four row tiles the
 // inner one, which keeps one decoded weight operand live.
@@ -45,7 +47,8 @@ namespace qmm {
 namespace {
 
 constexpr int BM = 128, BN = 256, MT = BM / 32, NWAVE = 8, NTHR = 64 * NWAVE;
-constexpr int A_OFF = 0, A_BYTES = BM * 256;
+constexpr int A_ROW = 272;  // 256 code bytes + 16 bytes of padding per row
+constexpr int A_OFF = 0, A_BYTES = BM * A_ROW;
 constexpr int DA_OFF = A_OFF + A_BYTES, DA_BYTES = 8 * BM * 2;  // fp16 [128 rows][8 blocks]
 constexpr int WP_OFF = DA_OFF + DA_BYTES, WP_WAVE = 32 * 128;    // payloads [wave][32 columns][8 slots]
 constexpr int WD_OFF = WP_OFF + NWAVE * WP_WAVE, WD_WAVE = 32 * 16;  // d_w [wave][32 columns][8 fp16]
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
 
     // ---- weight DMA of this wavefront's 32 columns (columns past N clamped;
     // never stored): instruction t moves columns 8t..8t+7, lane l the piece
-    // (l & 7) ^ (col & 7) of column col = 8t + l/8 to slot l & 7; lanes 0..31 of
+    // (l & 7) ^ wsw(col) of column col = 8t + l/8 to slot l & 7; lanes 0..31 of
     // one more move the 16 bytes of d of column l
     const int64_t NB = N * nb32;
     const int64_t dsec = (2 * NB + 255) / 256 * 256;
@@ -112,11 +115,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
         const int64_t n = n_base + wave * 32 + col;
         return n < N ? n : N - 1;
     };
+    auto wsw_of = [](int col) { return (col & 7) ^ ((col >> 3) & 3); };
     uint32_t wp_goff[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int col = 8 * t + (lane >> 3);
-        wp_goff[t] = (uint32_t)(dsec + 16 * wcol(col) * nb32 + 16 * ((lane & 7) ^ (col & 7)));
+        wp_goff[t] = (uint32_t)(dsec + 16 * wcol(col) * nb32 + 16 * ((lane & 7) ^ wsw_of(col)));
     }
     const uint32_t wd_goff = (uint32_t)(2 * wcol(l32) * nb32);
     auto wdma = [&](int64_t b, uint8_t *buf) {
@@ -146,13 +150,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
         uint32_t c0[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) c0[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], 2);
-        uint8_t *arow_p = buf + A_OFF + s_row * 256;
-        const int blk0 = 2 * s_pair, blk1 = 2 * s_pair + 1;
-        *reinterpret_cast<uint4 *>(arow_p + 16 * ((2 * blk0) ^ (s_row & 15))) = make_uint4(c0[0], c0[1], c0[2], c0[3]);
-        *reinterpret_cast<uint4 *>(arow_p + 16 * ((2 * blk0 + 1) ^ (s_row & 15))) = make_uint4(c0[4], c0[5], c0[6], c0[7]);
-        *reinterpret_cast<uint4 *>(arow_p + 16 * ((2 * blk1) ^ (s_row & 15))) = make_uint4(w[9], w[10], w[11], w[12]);
-        *reinterpret_cast<uint4 *>(arow_p + 16 * ((2 * blk1 + 1) ^ (s_row & 15))) = make_uint4(w[13], w[14], w[15], w[16]);
-        // d_a of blocks blk0, blk1 of row s_row: adjacent halves
+        uint4 *arow_p = reinterpret_cast<uint4 *>(buf + A_OFF + s_row * A_ROW + 64 * s_pair);
+        arow_p[0] = make_uint4(c0[0], c0[1], c0[2], c0[3]);
+        arow_p[1] = make_uint4(c0[4], c0[5], c0[6], c0[7]);
+        arow_p[2] = make_uint4(w[9], w[10], w[11], w[12]);
+        arow_p[3] = make_uint4(w[13], w[14], w[15], w[16]);
+        // d_a of blocks 2 s_pair and 2 s_pair + 1 of row s_row: adjacent halves
         *reinterpret_cast<uint32_t *>(buf + DA_OFF + s_row * 16 + 4 * s_pair) = (w[0] & 0xffffu) | (w[8] & 0xffff0000u);
     };
 
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
     // 0..7), lanes 32..63 the zero bytes (K slots 8..15)
     const int da_lane = hh ? ZERO_OFF : DA_OFF + l32 * 16;
     const uint32_t bmask = hh ? 0u : 0xffffffffu;  // B operand: K slots 8..15 are zero
-    const int wp_lane = WP_OFF + wave * WP_WAVE + l32 * 128, wsw = l32 & 7;
+    const int wp_lane = WP_OFF + wave * WP_WAVE + l32 * 128, wsw = wsw_of(l32);
     const int wd_lane = WD_OFF + wave * WD_WAVE + l32 * 16;
 
     for (int64_t b = 0; b < nsteps; ++b) {
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
         uint4 av[2], pv[2];
         auto read_a = [&](int t) {
             const int c = t >> 2, row = (t & 3) * 32 + l32;
-            av[t & 1] = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * 256 + 16 * ((2 * c + hh) ^ (row & 15)));
+            av[t & 1] = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * A_ROW + 16 * (2 * c + hh));
         };
         auto read_w = [&](int c) {
             pv[c & 1] = *reinterpret_cast<const uint4 *>(buf + wp_lane + 16 * (c ^ wsw));
