@@ -493,6 +493,127 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ W
     }
 }
 
+// ---------------------------------------------------------------------------
+// Q4_0 x Q8_0 with the activation rows staged in LDS (K a multiple of 64 and
+// M * K * 5/4 bytes within the LDS budget).  The workgroup first moves its M
+// activation rows into LDS once, in 68-byte block pairs (dword-aligned because
+// nb is even: four 16-byte loads and one 4-byte load per pair), realigns the
+// first block's codes with v_alignbyte, and stores per block the 32 codes, d_a
+// as fp32 and the code sum sum_i y_i (for the -8 of every weight).  Then each
+// wavefront takes one output row as in k_gemv_q4_0, with the activation
+// operands from LDS instead of 2-byte global loads.  The two 16-byte code reads
+// of block b go in the order (b & 1, 1 - (b & 1)), so 16 consecutive lanes
+// (consecutive blocks) read 16 distinct 16-byte slots; the weight nibbles are
+// paired to match.  Same integer sums and the same fp32 operations, in the
+// same order, as k_gemv_q4_0.
+// ---------------------------------------------------------------------------
+int64_t gemv_q4_0s_lds_bytes(int64_t M, int64_t K) { return M * (K / QK4_0) * (32 + 4 + 4); }
+
+template <int M, bool REPACKED, int MODE, bool ID = false>
+__global__ __launch_bounds__(256) void k_gemv_q4_0s(const uint8_t *__restrict__ W,
+                                                    const uint8_t *__restrict__ Y,
+                                                    void *__restrict__ dst, int64_t N, int64_t K,
+                                                    int64_t dsec, IdRoute route = {}) {
+    bool valid = true;
+    if constexpr (ID) {
+        const IdPair ip = id_route(route);
+        valid = ip.valid;
+        W += ip.w_off;
+        Y += ip.y_off;
+        dst = reinterpret_cast<float *>(dst) + ip.out_row * N;
+    }
+    extern __shared__ __attribute__((aligned(16))) uint8_t ys[];
+    const int64_t nb = K / QK4_0;
+    const int nbi = (int)nb, half = nbi / 2;
+    uint8_t *s_q = ys;                                             // codes [M][nb][32]
+    float *s_d = reinterpret_cast<float *>(ys + (int64_t)M * nb * 32);  // d_a [M][nb]
+    int *s_s = reinterpret_cast<int *>(s_d + M * nb);              // sum of codes [M][nb]
+    const int tid = threadIdx.x;
+
+    // ---- stage the M rows: pair pr of row m is [d0 | 32 codes | d1 | 32 codes]
+    for (int q = tid; q < M * half; q += 256) {
+        const int m = q / half, pr = q - m * half;
+        const int blk = m * nbi + 2 * pr;
+        const uint8_t *src = Y + (int64_t)blk * kQ8_0Bytes;
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = ld_align4<uint4>(src + 16 * k);
+        const uint32_t w[17] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w, v[2].x,
+                                v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w,
+                                ld_align4<uint32_t>(src + 64)};
+        uint32_t c0[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c0[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], 2);
+        uint4 *dq = reinterpret_cast<uint4 *>(s_q + (int64_t)blk * 32);
+        dq[0] = make_uint4(c0[0], c0[1], c0[2], c0[3]);
+        dq[1] = make_uint4(c0[4], c0[5], c0[6], c0[7]);
+        dq[2] = make_uint4(w[9], w[10], w[11], w[12]);
+        dq[3] = make_uint4(w[13], w[14], w[15], w[16]);
+        int s0 = 0, s1 = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            s0 = dot4(0x01010101u, c0[j], s0);
+            s1 = dot4(0x01010101u, w[9 + j], s1);
+        }
+        s_d[blk] = f16_bits_to_f32(w[0] & 0xffff);
+        s_d[blk + 1] = f16_bits_to_f32(w[8] >> 16);
+        s_s[blk] = s0;
+        s_s[blk + 1] = s1;
+    }
+    __syncthreads();
+
+    const int wave = tid >> 6, lane = tid & 63;
+    const int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (n >= N) return;  // uniform per wavefront, after the only barrier
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    for (int64_t b = lane; b < nb; b += kWave) {
+        uint32_t w[4];
+        float dw;
+        if (REPACKED) {
+            const uint4 v = ld16(W + dsec + 16 * (n * nb + b));
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            dw = f16_bits_to_f32(ld_u16(W + 2 * (n * nb + b)));
+        } else {
+            const uint8_t *blk = W + kQ4_0Bytes * (n * nb + b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = ld_u32_a2(blk + 2 + 4 * i);
+            dw = f16_bits_to_f32(ld_u16(blk));
+        }
+        // first read: elements 16*odd .. +15 (nibbles >> 4*odd), second: the other half
+        const int odd = (int)(b & 1), sa = 4 * odd, sb = 4 - sa;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int64_t bi = (int64_t)m * nb + b;
+            const uint8_t *cq = s_q + bi * 32;
+            const uint4 ra = *reinterpret_cast<const uint4 *>(cq + 16 * odd);
+            const uint4 rb = *reinterpret_cast<const uint4 *>(cq + 16 - 16 * odd);
+            const uint32_t ya[4] = {ra.x, ra.y, ra.z, ra.w}, yb[4] = {rb.x, rb.y, rb.z, rb.w};
+            int p = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p = dot4((w[i] >> sa) & 0x0f0f0f0fu, ya[i], p);
+                p = dot4((w[i] >> sb) & 0x0f0f0f0fu, yb[i], p);
+            }
+            p -= 8 * s_s[bi];
+            if (MODE == 0) {
+                acc[m] = fmaf(dw * s_d[bi], (float)p, acc[m]);
+            } else {
+                reinterpret_cast<int32_t *>(dst)[((int64_t)m * N + n) * nb + b] = p;
+            }
+        }
+    }
+    if (MODE == 0) {
+        float *out = reinterpret_cast<float *>(dst);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float v = wave_sum(acc[m]);
+            if (lane == 0) out[(int64_t)m * N + n] = valid ? v : __builtin_nanf("");
+        }
+    }
+}
+
 template <int MODE>
 hipError_t dispatch_q4_K(const uint8_t *w, bool rep, const uint8_t *y, void *dst, int64_t M,
                          int64_t N, int64_t K, hipStream_t s) {
@@ -527,14 +648,23 @@ hipError_t dispatch_q4_0(const uint8_t *w, bool rep, const uint8_t *y, void *dst
                          int64_t N, int64_t K, hipStream_t s) {
     const int64_t dsec = repacked_bytes_q4_0(N, K) - 16 * N * (K / QK4_0);
     const dim3 grid((unsigned)((N + kWavesPerBlock - 1) / kWavesPerBlock));
-#define QMM_GEMV_0(MM)                                                                            \
-    do {                                                                                          \
-        if (rep)                                                                                  \
-            hipLaunchKernelGGL((k_gemv_q4_0<MM, true, MODE>), grid, dim3(256), 0, s, w, y, dst, N, \
-                               K, dsec);                                                          \
-        else                                                                                      \
-            hipLaunchKernelGGL((k_gemv_q4_0<MM, false, MODE>), grid, dim3(256), 0, s, w, y, dst,   \
-                               N, K, dsec);                                                       \
+    // activation rows staged in LDS where they fit, else read per lane
+    const bool staged = gemv_q4_0s_fits(M, K);
+    const unsigned lds = staged ? (unsigned)gemv_q4_0s_lds_bytes(M, K) : 0u;
+#define QMM_GEMV_0(MM)                                                                                   \
+    do {                                                                                                 \
+        if (staged && rep)                                                                               \
+            hipLaunchKernelGGL((k_gemv_q4_0s<MM, true, MODE>), grid, dim3(256), lds, s, w, y, dst, N, K,  \
+                               dsec, IdRoute{});                                                         \
+        else if (staged)                                                                                 \
+            hipLaunchKernelGGL((k_gemv_q4_0s<MM, false, MODE>), grid, dim3(256), lds, s, w, y, dst, N, K, \
+                               dsec, IdRoute{});                                                         \
+        else if (rep)                                                                                    \
+            hipLaunchKernelGGL((k_gemv_q4_0<MM, true, MODE>), grid, dim3(256), 0, s, w, y, dst, N, K,     \
+                               dsec);                                                                    \
+        else                                                                                             \
+            hipLaunchKernelGGL((k_gemv_q4_0<MM, false, MODE>), grid, dim3(256), 0, s, w, y, dst, N, K,    \
+                               dsec);                                                                    \
     } while (0)
     switch (M) {
         case 1: QMM_GEMV_0(1); break;
@@ -552,6 +682,10 @@ hipError_t dispatch_q4_0(const uint8_t *w, bool rep, const uint8_t *y, void *dst
 }
 
 }  // namespace
+
+bool gemv_q4_0s_fits(int64_t M, int64_t K) {
+    return K % 64 == 0 && gemv_q4_0s_lds_bytes(M, K) <= 60 * 1024;
+}
 
 hipError_t launch_gemv_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s) {
@@ -686,12 +820,21 @@ hipError_t launch_gemv_id_q4_0(const uint8_t *w, bool repacked, int64_t w_stride
         const int64_t pp = P - p0 < 65535 ? P - p0 : 65535;
         const dim3 grid((unsigned)((N + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)pp);
         const IdRoute r{ids, p0, U, E, w_stride, (K / QK4_0) * kQ8_0Bytes, y_per_slot};
-        if (repacked)
+        if (gemv_q4_0s_fits(1, K)) {
+            const unsigned lds = (unsigned)gemv_q4_0s_lds_bytes(1, K);
+            if (repacked)
+                hipLaunchKernelGGL((k_gemv_q4_0s<1, true, 0, true>), grid, dim3(256), lds, s, w, y, (void *)out, N,
+                                   K, dsec, r);
+            else
+                hipLaunchKernelGGL((k_gemv_q4_0s<1, false, 0, true>), grid, dim3(256), lds, s, w, y, (void *)out, N,
+                                   K, dsec, r);
+        } else if (repacked) {
             hipLaunchKernelGGL((k_gemv_q4_0<1, true, 0, true>), grid, dim3(256), 0, s, w, y, (void *)out, N, K,
                                dsec, r);
-        else
+        } else {
             hipLaunchKernelGGL((k_gemv_q4_0<1, false, 0, true>), grid, dim3(256), 0, s, w, y, (void *)out, N, K,
                                dsec, r);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
