@@ -648,8 +648,10 @@ hipError_t dispatch_q4_0(const uint8_t *w, bool rep, const uint8_t *y, void *dst
                          int64_t N, int64_t K, hipStream_t s) {
     const int64_t dsec = repacked_bytes_q4_0(N, K) - 16 * N * (K / QK4_0);
     const dim3 grid((unsigned)((N + kWavesPerBlock - 1) / kWavesPerBlock));
-    // activation rows staged in LDS where they fit, else read per lane
-    const bool staged = gemv_q4_0s_fits(M, K);
+    // activation rows staged in LDS where they fit and the matrix is large
+    // enough for the staging latency to pay (N*K >= 2^22; at c1, 256 x 1024,
+    // the per-lane kernel is 0.2 us faster), else read per lane
+    const bool staged = gemv_q4_0s_fits(M, K) && N * K >= (int64_t(1) << 22);
     const unsigned lds = staged ? (unsigned)gemv_q4_0s_lds_bytes(M, K) : 0u;
 #define QMM_GEMV_0(MM)                                                                                   \
     do {                                                                                                 \
@@ -820,7 +822,7 @@ hipError_t launch_gemv_id_q4_0(const uint8_t *w, bool repacked, int64_t w_stride
         const int64_t pp = P - p0 < 65535 ? P - p0 : 65535;
         const dim3 grid((unsigned)((N + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)pp);
         const IdRoute r{ids, p0, U, E, w_stride, (K / QK4_0) * kQ8_0Bytes, y_per_slot};
-        if (gemv_q4_0s_fits(1, K)) {
+        if (gemv_q4_0s_fits(1, K) && N * K >= (int64_t(1) << 22)) {
             const unsigned lds = (unsigned)gemv_q4_0s_lds_bytes(1, K);
             if (repacked)
                 hipLaunchKernelGGL((k_gemv_q4_0s<1, true, 0, true>), grid, dim3(256), lds, s, w, y, (void *)out, N,

@@ -185,6 +185,21 @@ def test_mul_mat_id_formats(fmt, algo, T, layouts, y_per_slot):
         assert_close(got, want, terms, f"{fmt} {algo} {layout} per_slot={y_per_slot}")
 
 
+def test_mul_mat_id_q4_0_staged_gemv():
+    """Q4_0 decode with experts large enough for the GEMV that stages the
+    activation row in LDS (N*K >= 2^22), both layouts."""
+    T, U, E, N, K = 3, 2, 3, 1024, 4096
+    rng = np.random.default_rng(52)
+    w = _stack_fmt("q4_0", E, N, K, 844)
+    y = oracle.quantize("q8_0", activations([845, 0], T, K))
+    ids = _routing(rng, T, U, E, skew=False)
+    want, terms = oracle.mul_mat_id("q4_0", w, E, N, K, y, ids, False)
+    for layout in ("canonical", "repacked"):
+        got = to_host(qmm.mul_mat_id("q4_0", _upload_fmt("q4_0", w, E, N, K, layout), E, to_dev(y.reshape(-1)),
+                                     to_dev(ids), N, K, layout=layout, y_per_slot=False, algo="gemv"))
+        assert_close(got, want, terms, f"q4_0 staged gemv id {layout}")
+
+
 @pytest.mark.parametrize("fmt", OTHER)
 def test_mul_mat_id_formats_bad_ids(fmt):
     T, U, E, N, K = 100, 2, 4, 40, 512

@@ -76,6 +76,25 @@ def test_skinny_q4_0(M, N, K):
     assert_close(got, want, terms, f"q4_0 skinny M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("layout", ["canonical", "repacked"])
+@pytest.mark.parametrize("M,N,K", [(1, 2048, 2048), (1, 4099, 1024), (2, 1031, 4096), (3, 8200, 512),
+                                   (4, 512, 12288)])
+def test_gemv_q4_0_staged(M, N, K, layout):
+    """The GEMV with the activation rows staged in LDS (N*K >= 2^22, K % 64 == 0,
+    M*K*5/4 <= 61440): the smallest staged N*K, ragged N, one block pair per row
+    and the LDS boundary M = 4, K = 12288, both layouts; fp32 outputs against
+    the oracle and the int32 block sums of the same kernel bit-exact."""
+    w = oracle.quantize("q4_0", weights_normal([438, M + N], N, K))
+    y = oracle.quantize("q8_0", activations([439, M + N], M, K, outlier_frac=0.01))
+    want, terms = full_reference("q4_0", w, y, M, N, K)
+    wd = upload_weights("q4_0", w, N, K, layout)
+    yd = to_dev(y.reshape(-1))
+    got = to_host(qmm.mul_mat_q4_0(wd, yd, M, N, K, layout=layout, algo="gemv"))
+    assert_close(got, want, terms, f"q4_0 staged gemv M={M} N={N} K={K} {layout}")
+    sums = to_host(qmm.debug_block_sums("q4_0", wd, yd, M, N, K, layout=layout))
+    assert np.array_equal(sums, oracle.subblock_sums("q4_0", w, y, M, N, K))
+
+
 def test_skinny_overwrites_and_rejects():
     """The small-batch kernel writes every output (no accumulation into a
     stale buffer) and refuses what it does not take: the canonical layout and
