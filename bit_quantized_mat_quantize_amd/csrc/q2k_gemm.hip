@@ -286,13 +286,9 @@ namespace {
 template <bool GROUPED>
 hipError_t launch_t(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M, int64_t N,
                     int64_t K, int tiles_m, const Grouping &g, hipStream_t s) {
-    static bool attr_set = false;  // the LDS budget above 64 KiB must be opted into once
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_q2_K<GROUPED>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};  // the LDS budget above 64 KiB, per device
+    const hipError_t e = ensure_lds_bytes((const void *)k_gemm_q2_K<GROUPED>, LDS_BYTES, lds_set);
+    if (e != hipSuccess) return e;
     const int tiles_n = (int)((N + BN - 1) / BN);
     hipLaunchKernelGGL((k_gemm_q2_K<GROUPED>), dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), LDS_BYTES, s,
                        w, w_bytes, y, out, M, N, K, tiles_m, tiles_n, g);

@@ -240,13 +240,9 @@ int64_t skinny_q4_0_max_m() { return QS_MAX_M; }
 
 hipError_t launch_skinny_q4_0(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M,
                               int64_t N, int64_t K, hipStream_t s) {
-    static bool attr_set = false;  // the LDS budget above 64 KiB must be opted into once
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void *)k_skinny_q4_0,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, QS_LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};  // the LDS budget above 64 KiB, per device
+    const hipError_t e = ensure_lds_bytes((const void *)k_skinny_q4_0, QS_LDS, lds_set);
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + QS_ROWS - 1) / QS_ROWS));
     hipLaunchKernelGGL(k_skinny_q4_0, grid, dim3(QS_THREADS), QS_LDS, s, w, w_bytes, y, out, M, N, K);
     return hipGetLastError();

@@ -6,7 +6,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qmm {
+
+// Opts kernel `func` into `bytes` of dynamic LDS (past the default 64 KiB)
+// once per device: `done` holds one bit per device id below 64 (higher ids
+// set the attribute on every call).  The attribute call is idempotent and the
+// mask atomic, so concurrent first calls from several threads are safe.
+inline hipError_t ensure_lds_bytes(const void *func, int bytes, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 hipError_t launch_quantize_q8_0(const float *x, uint8_t *y, int64_t M, int64_t K, hipStream_t s);
 hipError_t launch_quantize_q8_K(const float *x, uint8_t *y, int64_t M, int64_t K, hipStream_t s);

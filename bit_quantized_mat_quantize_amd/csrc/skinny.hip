@@ -286,14 +286,11 @@ int64_t skinny_max_m() { return SK_MAX_M; }
 
 hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                               int64_t M, int64_t N, int64_t K, hipStream_t s) {
-    static bool attr_set[2] = {false, false};  // the LDS budget above 64 KiB must be opted into once
-    if (!attr_set[repacked]) {
-        const hipError_t e = hipFuncSetAttribute(
-            repacked ? (const void *)k_skinny_q4_K<true, true> : (const void *)k_skinny_q4_K<false, true>,
-            hipFuncAttributeMaxDynamicSharedMemorySize, SK_LDS);
-        if (e != hipSuccess) return e;
-        attr_set[repacked] = true;
-    }
+    static std::atomic<uint64_t> lds_set[2] = {{0}, {0}};  // the LDS budget above 64 KiB, per device
+    const hipError_t e = ensure_lds_bytes(
+        repacked ? (const void *)k_skinny_q4_K<true, true> : (const void *)k_skinny_q4_K<false, true>, SK_LDS,
+        lds_set[repacked]);
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + SK_ROWS - 1) / SK_ROWS)), block(SK_THREADS);
     // up to 8 rows the per-lane operand loads touch few cache lines and beat
     // the LDS staging; more rows are staged
