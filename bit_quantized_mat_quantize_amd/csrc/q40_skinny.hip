@@ -17,15 +17,17 @@
 // fp16 d straight into registers (no other wavefront reads them), one step
 // ahead.  Q8_0 blocks are 34 bytes, so their codes are only 2-byte aligned:
 // each lane loads two 68-byte block pairs of the activation rows (four
-// dwordx4 + one dword each, aligned), also one step ahead, realigns the first
-// block's codes with v_alignbyte and writes codes and d_a into the
-// wavefront's own LDS stage (code rows padded to 272 bytes, so the 32 rows of
-// one block read at a 68-dword stride fall in distinct bank groups and each
-// block's read address is the lane's base plus an immediate; d_a block-major).
-// No other wavefront reads that stage, so no barrier is needed until the
-// final reduction.  Each block is one K = 32 chunk of
-// v_mfma_i32_32x32x32_i8 with q - 8 as the signed weight operand, followed by
-// the per-block fp32 epilogue (convert, times d_w, fused multiply-add with d_a).
+// dwordx4 + one dword each, dword-aligned), also one step ahead.  After the
+// step's MFMAs it realigns the first block's codes with v_alignbyte and writes
+// codes and d_a into the other of its wavefront's two LDS stages (code rows
+// padded to 272 bytes, so the 32 rows of one block read at a 68-dword stride
+// fall in distinct bank groups and each block's read address is the lane's
+// base plus an immediate; d_a block-major).  No other wavefront reads those
+// stages, so a wavefront barrier suffices until the final reduction.  Each
+// block is one K = 32 chunk of v_mfma_i32_32x32x32_i8 with q - 8 as the signed
+// weight operand, followed by the per-block fp32 epilogue (convert, times d_w,
+// fused multiply-add with d_a), which runs after the next block's MFMA is
+// issued.
 //
 // MFMA operand convention (v_mfma_*_32x32xK): lane l supplies row (A) or
 // column (B) l % 32 and the K-slice selected by l / 32; the result register r
