@@ -225,12 +225,14 @@ qmm_status qmm_mul_mat_q4_0_ex(const void *w, size_t w_bytes, qmm_layout l, cons
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     qmm_algo a = algo;
     if (a == QMM_ALGO_AUTO) {
-        // GEMV for M = 1; up to M = 4 while the GEMV stages the rows in LDS
+        // GEMV for M = 1; while the GEMV stages the rows in LDS, up to M = 4
         // (its pass over the weights per row is still cheaper than the
-        // small-batch kernel: 18 against 21 us at M = 4, N = K = 8192); for
-        // M = 2 below 8192 columns, where the small-batch kernel's N/32
-        // workgroups leave CUs idle; and where the MFMA kernels are ruled out
-        if (!mfma_ok || M == 1 || (M <= 4 && qmm::gemv_q4_0s_fits(M, K)) || (M == 2 && N < 8192))
+        // small-batch kernel: 18 against 21 us at M = 4, N = K = 8192) and up
+        // to M*N = 36864 (N < 8192, where the small-batch kernel's N/32
+        // workgroups leave CUs idle: 9.5 against 12.1 us at M = 8, N = 4096);
+        // for M = 2 below 8192 columns; and where the MFMA kernels are ruled out
+        if (!mfma_ok || M == 1 || (qmm::gemv_q4_0s_fits(M, K) && (M <= 4 || M * N <= 36864)) ||
+            (M == 2 && N < 8192))
             a = QMM_ALGO_GEMV;
         else if (skinny_ok && ((M + 31) / 32) * N <= kSkinnyMN_Q4_0) a = QMM_ALGO_SKINNY;
         else a = QMM_ALGO_MFMA;

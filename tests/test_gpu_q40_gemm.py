@@ -122,18 +122,21 @@ def test_skinny_overwrites_and_rejects():
 def _auto_algo(M, N, K, layout):
     """The AUTO rule as the library documents it."""
     staged = K % 64 == 0 and M * K * 5 // 4 <= 61440
-    if layout == "canonical" or K % 256 != 0 or M == 1 or (M <= 4 and staged) or (M == 2 and N < 8192):
+    if (layout == "canonical" or K % 256 != 0 or M == 1 or (staged and (M <= 4 or M * N <= 36864))
+            or (M == 2 and N < 8192)):
         return "gemv"
     return "skinny" if (M + 31) // 32 * N <= 16 * 8192 else "mfma"
 
 
 def test_auto_dispatch():
-    """Every AUTO choice (the GEMV for M = 1, for M <= 4 while the rows fit its
-    LDS staging, for M = 2 below 8192 columns, for the canonical layout and for
-    K % 256 != 0; the small-batch kernel while ceil(M/32)*N <= 16*8192; the GEMM
-    above) is bit-identical to that path and agrees with the oracle."""
+    """Every AUTO choice (the GEMV for M = 1, for M <= 4 or M*N <= 36864 while the
+    rows fit its LDS staging, for M = 2 below 8192 columns, for the canonical
+    layout and for K % 256 != 0; the small-batch kernel while ceil(M/32)*N <=
+    16*8192; the GEMM above) is bit-identical to that path and agrees with the
+    oracle."""
     for M, N, K in [(1, 70, 1024), (2, 70, 1024), (4, 300, 12288), (4, 300, 12544), (2, 8192, 256),
-                    (8, 70, 1024), (40, 70, 288), (40, 6200, 1024), (100, 32768, 256), (161, 26000, 256)]:
+                    (8, 4608, 1024), (8, 4609, 1024), (40, 70, 288), (40, 6200, 1024), (100, 32768, 256),
+                    (161, 26000, 256)]:
         w = oracle.quantize("q4_0", weights_normal([432, M + K], N, K))
         y = oracle.quantize("q8_0", activations([433, M + K], M, K))
         want, terms = full_reference("q4_0", w, y, M, N, K)
