@@ -292,9 +292,11 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, cons
     // K split over its wavefronts) beats the GEMM up to 32 rows, and further
     // while ceil(M/32)*N stays below 9*8192 (measured at K = 8192: up to
     // M ~ 300 for N = 8192, M ~ 80 for N = 28672); K cancels, both scale with it.
+    // At M = 2 below 8192 columns (fewer than 256 small-batch workgroups) the
+    // GEMV is faster: 6.7 against 8.1 us at N = K = 4096.
     if (a == QMM_ALGO_AUTO) {
         const bool skinny_pref = M <= 32 || ((M + 31) / 32) * N <= 9 * 8192;
-        a = M == 1 ? QMM_ALGO_GEMV
+        a = M == 1 || (M == 2 && N < 8192) ? QMM_ALGO_GEMV
                    : (skinny_ok && skinny_pref ? QMM_ALGO_SKINNY
                                                : (M <= qmm::kGemvMaxM || !small ? QMM_ALGO_GEMV : QMM_ALGO_MFMA));
     }

@@ -208,19 +208,19 @@ def test_q4_0(M, N, K, layout):
 
 
 def test_auto_dispatch_and_overwrite():
-    """AUTO picks the GEMV for M = 1, the small-batch kernel up to M = 32 and
-    while ceil(M/32)*N <= 9*8192, the GEMM above, and is bit-identical to that
-    path; `out` is overwritten."""
+    """AUTO picks the GEMV for M = 1 and for M = 2 below 8192 columns, the
+    small-batch kernel up to M = 32 and while ceil(M/32)*N <= 9*8192, the GEMM
+    above, and is bit-identical to that path; `out` is overwritten."""
     import torch
     K = 512
-    for M, N in ((1, 64), (8, 64), (9, 64), (32, 64), (33, 64), (100, 64), (33, 40000)):
+    for M, N in ((1, 64), (2, 64), (2, 8192), (8, 64), (9, 64), (32, 64), (33, 64), (100, 64), (33, 40000)):
         w, x, y, _ = _case("q4_K", M, N, K, 900 + M)
         want, terms = full_reference("q4_K", w, y, M, N, K)
         wd, yd = to_dev(w.reshape(-1)), to_dev(y.reshape(-1))
         out = torch.full((M, N), 1e9, device="cuda")
         qmm.mul_mat_q4_K(wd, yd, M, N, K, out=out)
         assert_close(to_host(out), want, terms, f"auto M={M} N={N}")
-        algo = ("gemv" if M == 1 else
+        algo = ("gemv" if M == 1 or (M == 2 and N < 8192) else
                 "skinny" if M <= 32 or (M + 31) // 32 * N <= 9 * 8192 else "mfma")
         ref = to_host(qmm.mul_mat_q4_K(wd, yd, M, N, K, algo=algo))
         assert np.array_equal(to_host(out).view(np.uint32), ref.view(np.uint32)), (M, N, algo)
