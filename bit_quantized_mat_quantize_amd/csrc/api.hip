@@ -337,16 +337,27 @@ struct GroupedKernels {
                        hipStream_t);
     hipError_t (*gemm)(const uint8_t *, int64_t, const uint8_t *, float *, int64_t, int64_t, int64_t,
                        hipStream_t);
+    // small-batch kernel (repacked layout), or null where the format has none;
+    // AUTO takes it while ceil(M/32)*N <= skinny_mn
+    hipError_t (*skinny)(const uint8_t *, int64_t, const uint8_t *, float *, int64_t, int64_t, int64_t,
+                         hipStream_t);
+    int64_t skinny_max_m, skinny_mn;
 };
 
 qmm_status mul_mat_grouped(qmm_weight_type t, const GroupedKernels &k, const void *w, size_t w_bytes,
                            qmm_layout l, const void *y, size_t y_bytes, float *out, size_t out_bytes,
                            int64_t M, int64_t N, int64_t K, qmm_algo algo, void *stream) {
-    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
-        return fail(QMM_EUNSUPPORTED, "%s takes the GEMV or MFMA path (algo %d)", k.name, (int)algo);
+    if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA &&
+        !(algo == QMM_ALGO_SKINNY && k.skinny))
+        return fail(QMM_EUNSUPPORTED, "%s takes the GEMV%s or MFMA path (algo %d)", k.name,
+                    k.skinny ? ", SKINNY" : "", (int)algo);
     QMM_TRY(mul_mat_common(t, w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K));
     const bool gemv_ok = K <= k.gemv_max_k;
     const bool mfma_ok = l == QMM_LAYOUT_REPACKED && below_4gib(t, l, M, N, K);
+    const bool skinny_ok = k.skinny && mfma_ok && M <= k.skinny_max_m;
+    if (algo == QMM_ALGO_SKINNY && !skinny_ok)
+        return fail(QMM_EUNSUPPORTED, "%s SKINNY path takes the repacked layout, M <= %lld and matrices below 4 GiB",
+                    k.name, (long long)k.skinny_max_m);
     if (algo == QMM_ALGO_GEMV && !gemv_ok)
         return fail(QMM_EUNSUPPORTED, "%s GEMV takes K <= %lld (K = %lld)", k.name,
                     (long long)k.gemv_max_k, (long long)K);
@@ -362,19 +373,34 @@ qmm_status mul_mat_grouped(qmm_weight_type t, const GroupedKernels &k, const voi
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     qmm_algo a = algo;
-    if (a == QMM_ALGO_AUTO)
+    if (a == QMM_ALGO_AUTO && skinny_ok) {
+        // GEMV for M = 1 and for M = 2 below 8192 columns (fewer than 256
+        // small-batch workgroups), the small-batch kernel while its row chunks
+        // cost less than one GEMM K loop, the GEMM above
+        if ((M == 1 || (M == 2 && N < 8192)) && gemv_ok) a = QMM_ALGO_GEMV;
+        else if (((M + 31) / 32) * N <= k.skinny_mn) a = QMM_ALGO_SKINNY;
+        else a = QMM_ALGO_MFMA;
+    } else if (a == QMM_ALGO_AUTO) {
         a = (prefer_gemv(M, N, k.gemv_mn) && gemv_ok) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
+    }
     if (a == QMM_ALGO_GEMV)
         return device_status(k.gemv(wb, l == QMM_LAYOUT_REPACKED, yb, out, M, N, K, s), "mul_mat gemv launch");
+    if (a == QMM_ALGO_SKINNY)
+        return device_status(k.skinny(wb, (int64_t)qmm_weight_bytes(t, l, N, K), yb, out, M, N, K, s),
+                             "mul_mat skinny launch");
     return device_status(k.gemm(wb, (int64_t)qmm_weight_bytes(t, l, N, K), yb, out, M, N, K, s),
                          "mul_mat gemm launch");
 }
 
 GroupedKernels q6_K_kernels() {
-    return GroupedKernels{"Q6_K", qmm::q6_K_max_k(), kGemvMN_Q6_K, qmm::launch_gemv_q6_K, qmm::launch_gemm_q6_K};
+    // small batch measured at N = 4096..28672: 18.9 against 78 us (GEMV) at
+    // M = 8, N = K = 8192; 74 against 77 us (GEMM) at M = 64, N = 28672
+    return GroupedKernels{"Q6_K", qmm::q6_K_max_k(), kGemvMN_Q6_K, qmm::launch_gemv_q6_K, qmm::launch_gemm_q6_K,
+                          qmm::launch_skinny_q6_K, qmm::skinny_q6_K_max_m(), 8 * 8192};
 }
 GroupedKernels q2_K_kernels() {
-    return GroupedKernels{"Q2_K", qmm::q2_K_max_k(), kGemvMN_Q2_K, qmm::launch_gemv_q2_K, qmm::launch_gemm_q2_K};
+    return GroupedKernels{"Q2_K", qmm::q2_K_max_k(), kGemvMN_Q2_K, qmm::launch_gemv_q2_K, qmm::launch_gemm_q2_K,
+                          nullptr, 0, 0};
 }
 
 }  // namespace

@@ -59,21 +59,6 @@ struct Q6KStage {
     uint32_t d;
 };
 
-// Four codes u (bytes in [0, 63]) with the pairs s2 = (s, s) and
-// c2 = (128 - 32s, 128 - 32s) -> the digit bytes of t = s*(u - 32) = 256*hi + lo:
-// t' = t + 128 = s*u + 128 - 32s (one packed 16-bit multiply-add per two codes;
-// |t'| < 2^15), hi = the high byte of t' (floor(t'/256), signed), lo = the low
-// byte of t' minus 128 (its top bit flipped), both in int8 range.
-__device__ __forceinline__ void t_digits(uint32_t u, s16x2 s2, s16x2 c2, uint32_t &hi, uint32_t &lo) {
-    const uint32_t e = __builtin_amdgcn_perm(u, u, 0x0c020c00u);  // u0, u2 in 16-bit lanes
-    const uint32_t o = __builtin_amdgcn_perm(u, u, 0x0c030c01u);  // u1, u3
-    const uint32_t te = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, e) * s2 + c2);
-    const uint32_t to = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, o) * s2 + c2);
-    // bytes 0-3 of the pair are the second operand, 4-7 the first
-    hi = __builtin_amdgcn_perm(to, te, 0x07030501u);
-    lo = __builtin_amdgcn_perm(to, te, 0x06020400u) ^ 0x80808080u;
-}
-
 template <bool GROUPED>
 __global__ __launch_bounds__(NTHR, 1) void k_gemm_q6_K(const uint8_t *__restrict__ W, int64_t w_bytes,
                                                        const uint8_t *__restrict__ Y,

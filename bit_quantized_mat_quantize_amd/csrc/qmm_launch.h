@@ -93,6 +93,11 @@ inline int64_t q8k_group_max_k() { return q6_K_max_k() < q2_K_max_k() ? q6_K_max
 // of w_bytes bytes.
 hipError_t launch_gemm_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
+// Q6_K small batch: repacked layout, M <= skinny_q6_K_max_m(), matrices below
+// 4 GiB; w_bytes is the repacked matrix size.
+int64_t skinny_q6_K_max_m();
+hipError_t launch_skinny_q6_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M,
+                              int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_q6_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,

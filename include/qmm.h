@@ -94,8 +94,8 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
  *   GEMV    vector int8 dot products, one wavefront per output row (Q4_0 and
  *           Q4_K: M <= 8 per launch; Q6_K and Q2_K: any M, K <= 53760)
  *   SKINNY  small-batch int8 MFMA, one 32-column x 32-row tile per workgroup,
- *           K split over its wavefronts (Q4_K; Q4_0 in the repacked layout
- *           with K % 256 == 0; M <= 65535*32)
+ *           K split over its wavefronts (Q4_K; Q6_K in the repacked layout;
+ *           Q4_0 in the repacked layout with K % 256 == 0; M <= 65535*32)
  *   MFMA    prefill GEMM on int8 MFMA, 128 x 256 output tiles (any M; Q6_K,
  *           Q2_K and Q4_0 need the repacked layout, Q4_0 also K % 256 == 0)
  * SKINNY and MFMA address the weight and activation matrices with 32-bit
@@ -106,9 +106,11 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
  * M <= 4 or M*N <= 36864 when K % 64 == 0 and M*K*5/4 <= 61440 (the rows fit
  * the GEMV's LDS staging) and for M = 2 with N < 8192, SKINNY while
  * ceil(M/32)*N <= 16*8192, MFMA above, GEMV where the MFMA kernels are ruled
- * out; for Q6_K and Q2_K it takes GEMV for
- * M = 1 and while M*N <= c*ceil(N/65536) with c = 16*8192 (Q6_K), 26*8192
- * (Q2_K), MFMA above, GEMV where MFMA is ruled out. */
+ * out; for Q6_K in the repacked layout it takes GEMV for M = 1 and for M = 2
+ * with N < 8192, SKINNY while ceil(M/32)*N <= 8*8192, MFMA above; for Q2_K,
+ * and Q6_K in the canonical layout, it takes GEMV for M = 1 and while
+ * M*N <= c*ceil(N/65536) with c = 16*8192 (Q6_K), 26*8192 (Q2_K), MFMA above,
+ * GEMV where MFMA is ruled out. */
 typedef enum {
     QMM_ALGO_AUTO = 0,
     QMM_ALGO_GEMV = 1,
@@ -200,9 +202,9 @@ qmm_status qmm_mul_mat_q6_K(const void *w, size_t w_bytes, qmm_layout l,
                             int64_t M, int64_t N, int64_t K, void *stream);
 
 /* Same as qmm_mul_mat_q6_K with an explicit kernel family: QMM_ALGO_GEMV
- * (K <= 53760) or QMM_ALGO_MFMA (repacked layout, both matrices below 4 GiB);
- * QMM_ALGO_SKINNY and a family whose limits the call exceeds give
- * QMM_EUNSUPPORTED. */
+ * (K <= 53760), QMM_ALGO_SKINNY (repacked layout, M <= 65535*32, both matrices
+ * below 4 GiB) or QMM_ALGO_MFMA (repacked layout, both matrices below 4 GiB);
+ * a family whose limits the call exceeds gives QMM_EUNSUPPORTED. */
 qmm_status qmm_mul_mat_q6_K_ex(const void *w, size_t w_bytes, qmm_layout l,
                                const void *y, size_t y_bytes,
                                float *out, size_t out_bytes,

@@ -169,7 +169,10 @@ def test_q6_K_validation(lib):
     assert "Q6_K GEMV takes K" in _last(lib)
     assert fx(A, big, 0, A, big, A, big, 2, 8, 512, 2, None) == EUNSUP  # MFMA, canonical
     assert "repacked layout" in _last(lib)
-    assert fx(A, big, 1, A, big, A, big, 2, 8, 512, 3, None) == EUNSUP  # SKINNY
+    # SKINNY: repacked layout, M <= 65535*32
+    assert fx(A, big, 0, A, big, A, big, 2, 8, 512, 3, None) == EUNSUP and "SKINNY" in _last(lib)
+    assert fx(A, 2**40, 1, A, 2**40, A, 2**40, 65535 * 32 + 1, 8, 512, 3, None) == EUNSUP
+    assert fx(A, 2**40, 1, A, 2**40, A, 2**40, 65535 * 32, 0, 512, 3, None) == OK
     assert fx(A, big, 1, A, big, A, big, 2, 8, 512, 9, None) == EUNSUP  # unknown
     # 32-bit offsets: a weight matrix of 4 GiB or more rules the MFMA path out
     kk = 1 << 20

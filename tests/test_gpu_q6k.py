@@ -11,7 +11,9 @@
 Shapes: GEMV with one, two and four 16-byte piece units per lane (K <= 8192)
 and two or four half-block units per lane (longer rows, K up to 53760, the last
 with a second pass), ragged N, several activation rows, both layouts; GEMM with
-ragged row and column tiles, K past the GEMV's limit, and AUTO dispatch.
+ragged row and column tiles, K past the GEMV's limit, and AUTO dispatch; the
+small-batch kernel with 8, 16 and 32 staged rows, several 32-row chunks, step
+counts that leave wavefronts idle or uneven, and ragged N.
 """
 import struct
 
@@ -141,9 +143,10 @@ def test_mfma_exactness_window():
     y = oracle.quantize("q8_K", x)
     want, terms = full_reference("q6_K", w, y, M, N, K)
     assert terms.max() < 2 ** 24
-    got = to_host(qmm.mul_mat_q6_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K,
-                                   layout="repacked", algo="mfma"))
-    assert np.array_equal(got.astype(np.float64), want)
+    for algo in ("mfma", "skinny"):
+        got = to_host(qmm.mul_mat_q6_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K,
+                                       layout="repacked", algo=algo))
+        assert np.array_equal(got.astype(np.float64), want), algo
 
 
 def test_mfma_extreme_digits():
@@ -160,7 +163,7 @@ def test_mfma_extreme_digits():
     y = oracle.quantize("q8_K", x)
     want, terms = full_reference("q6_K", w, y, M, N, K)
     assert terms.max() < 2 ** 24
-    for algo in ("mfma", "gemv"):
+    for algo in ("mfma", "gemv", "skinny"):
         got = to_host(qmm.mul_mat_q6_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N,
                                        K, layout="repacked", algo=algo))
         assert np.array_equal(got.astype(np.float64), want), algo
@@ -175,18 +178,52 @@ def test_mul_mat_q6_K_mfma(M, N, K):
     assert_close(got, want, terms, f"q6_K mfma M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 70, 256), (5, 33, 512), (8, 300, 2048), (9, 64, 4608), (16, 40, 1024),
+                                   (17, 1, 256), (32, 257, 1024), (40, 100, 2048), (70, 130, 4608)])
+def test_mul_mat_q6_K_skinny(M, N, K):
+    w, y = _case(M, N, K, 13 * M + N)
+    want, terms = full_reference("q6_K", w, y, M, N, K)
+    got = to_host(qmm.mul_mat_q6_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K,
+                                   layout="repacked", algo="skinny"))
+    assert_close(got, want, terms, f"q6_K skinny M={M} N={N} K={K}")
+
+
+def test_skinny_overwrites_and_rejects():
+    """The small-batch kernel writes every output, and refuses the canonical layout."""
+    import torch
+    M, N, K = 12, 50, 512
+    w, y = _case(M, N, K, 77)
+    want, terms = full_reference("q6_K", w, y, M, N, K)
+    out = torch.full((M, N), float("nan"), device="cuda")
+    qmm.mul_mat_q6_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K, layout="repacked",
+                     algo="skinny", out=out)
+    assert_close(to_host(out), want, terms, "q6_K skinny into a NaN-filled buffer")
+    with pytest.raises(qmm.QmmError):
+        qmm.mul_mat_q6_K(_upload(w, N, K, "canonical"), to_dev(y.reshape(-1)), M, N, K, layout="canonical",
+                         algo="skinny")
+
+
+def _auto_algo(M, N, layout):
+    """The AUTO rule as the library documents it (K within the GEMV's limit)."""
+    if layout == "canonical" or M == 1 or (M == 2 and N < 8192):
+        return "gemv"
+    return "skinny" if (M + 31) // 32 * N <= 8 * 8192 else "mfma"
+
+
 def test_auto_dispatch():
-    """AUTO: the GEMV for M = 1 and while M*N <= 16*8192 (per 65536 columns),
-    the GEMM above (repacked), the GEMV for the canonical layout at any M;
-    AUTO is bit-identical to that path and agrees with the oracle."""
-    K = 2048
-    for M, N in ((1, 96), (8, 96), (64, 96), (64, 2100)):
+    """AUTO (repacked): the GEMV for M = 1 and for M = 2 below 8192 columns, the
+    small-batch kernel while ceil(M/32)*N <= 8*8192, the GEMM above; the GEMV
+    for the canonical layout at any M.  AUTO is bit-identical to that path and
+    agrees with the oracle."""
+    for M, N, K in ((1, 96, 2048), (2, 96, 2048), (2, 8192, 512), (8, 96, 2048), (64, 2100, 2048),
+                    (64, 32768, 256), (65, 22000, 256)):
         w, y = _case(M, N, K, 900 + M)
         want, terms = full_reference("q6_K", w, y, M, N, K)
         for layout in LAYOUTS:
             wd, yd = _upload(w, N, K, layout), to_dev(y.reshape(-1))
             got = to_host(qmm.mul_mat_q6_K(wd, yd, M, N, K, layout=layout))
             assert_close(got, want, terms, f"q6_K auto M={M} N={N} {layout}")
-            gemv = layout == "canonical" or M == 1 or M * N <= 16 * 8192 * ((N + 65535) // 65536)
-            ref = to_host(qmm.mul_mat_q6_K(wd, yd, M, N, K, layout=layout, algo="gemv" if gemv else "mfma"))
-            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (M, N, layout)
+            algo = _auto_algo(M, N, layout)
+            ref = to_host(qmm.mul_mat_q6_K(wd, yd, M, N, K, layout=layout, algo=algo))
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (M, N, layout, algo)
+    assert {_auto_algo(M, N, "repacked") for M, N in ((2, 96), (64, 32768), (65, 22000))} == {"gemv", "skinny", "mfma"}
