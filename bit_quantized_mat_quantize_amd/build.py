@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libqmm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "quantize.hip", "repack.hip", "gemv.hip", "skinny.hip", "q6k.hip", "q6k_gemm.hip", "q6k_skinny.hip",
-           "q2k.hip", "q2k_gemm.hip", "q40_gemm.hip", "q40_skinny.hip", "moe.hip", "gemm.hip"]
+           "q2k.hip", "q2k_gemm.hip", "q2k_skinny.hip", "q40_gemm.hip", "q40_skinny.hip", "moe.hip", "gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

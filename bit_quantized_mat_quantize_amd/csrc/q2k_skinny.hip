@@ -1,0 +1,252 @@
+// q2k_skinny.hip -- Q2_K weights x Q8_K activations for small batches on int8
+// MFMA, gfx950, repacked layout.
+//
+// Format and integer path: ggml-cpu mul_mat page, "更低的比特:Q6_K 与 Q2_K 的取舍"
+// (2-bit codes, 4-bit scale and min per 16-element group, fp16 d and dmin),
+// "正确性:缩放系数可以提到求和号外面" and "min 项与最终归约":
+//   per super-block b, output (m, n):
+//     S  = sum_j s_j * sum_{i in j} q_i y_i,   Mn = sum_j m_j * bsums_j,
+//     acc += d_a * (d * S - dmin * Mn).
+//
+// A few activation rows still read every weight once (BitBLAS page,
+// "调度与自动调优": small batches sit on the memory side of the roofline), but
+// the GEMV repeats its dot products for every row and a single-row-tile GEMM
+// runs too few workgroups.  As in the Q4_K small-batch kernel, a workgroup owns
+// 32 output columns and up to 32 activation rows (more rows take more grid
+// rows, blockIdx.y), and its 8 wavefronts split K: wavefront w takes the
+// super-blocks w, w + 8, ... and the eight partial tiles are summed through LDS.
+//
+// Weights: each lane loads the part of its column's super-block that the Q2_K
+// GEMM's lane loads (qs pieces h and h + 2, the 16 scale/min bytes, d and
+// dmin), and the bsums of its activation row, straight into registers, one
+// step ahead, in two alternating register stages (the loop is unrolled by
+// two).  Decode as in the GEMM: s_j * q <= 45 folded into the int8 weight
+// bytes, one MFMA per 32-element chunk, and the min term as one fp16 MFMA of
+// the mins against the bsums (exact in fp16, |Mn| < 2^24).
+// Activations: the R = 8, 16 or 32 rows M needs of the wavefront's super-block
+// go into its own LDS stage by direct global->LDS loads, 16 lanes per 256-byte
+// row (pieces XOR-swizzled by row), with d_a beside them, one step ahead.
+// Each step reads all of its stage before it issues the next step's loads:
+// the compiler makes an LDS read wait for every direct global->LDS load issued
+// before it, and those would otherwise be the next step's.
+//
+// MFMA operand convention (v_mfma_*_32x32xK): lane l supplies row (A) or
+// column (B) l % 32 and the K-slice selected by l / 32; the result register r
+// of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+#include "mfma_common.h"
+#include "qmm_device.h"
+#include "qmm_launch.h"
+
+namespace qmm {
+namespace {
+
+constexpr int Q2S_WAVES = 8, Q2S_THREADS = 64 * Q2S_WAVES;
+constexpr int Q2S_ROWS = 32;                       // activation rows per workgroup
+constexpr int64_t Q2S_MAX_M = 65535ll * Q2S_ROWS;  // row chunks go to grid.y
+// Per-wavefront LDS stage: codes [32 rows][256] (16-byte piece p of row r at
+// position p ^ (r & 15)), then d_a [64] (rows l % 32 of the loading lane l).
+constexpr int Q2S_A = 0, Q2S_DA = Q2S_ROWS * 256, Q2S_STAGE = Q2S_DA + 64 * 4;
+constexpr int Q2S_LDS = Q2S_WAVES * 2 * Q2S_STAGE;
+constexpr int Q2S_RED = Q2S_WAVES * 16 * 64 * 4;  // the partial tiles at the end
+static_assert(Q2S_LDS <= 160 * 1024 && Q2S_RED <= Q2S_LDS, "LDS budget of a gfx950 CU");
+
+// One super-block for lane (column l % 32, slice h = l / 32): the weight side
+// and the bsums of activation row l % 32 (groups 8h .. 8h + 7).
+struct Q2SW {
+    uint4 qa, qb;  // qs pieces h and h + 2 (four 2-bit fields each)
+    uint4 sc;      // the 16 scale (low nibble) / min (high nibble) bytes
+    uint32_t dm;   // fp16 d | fp16 dmin << 16
+    uint4 bs;      // int16 bsums of the lane's activation row
+};
+
+template <int R>
+__global__ __launch_bounds__(Q2S_THREADS, 1) void k_skinny_q2_K(const uint8_t *__restrict__ W, int64_t w_bytes,
+                                                               const uint8_t *__restrict__ Y,
+                                                               float *__restrict__ out, int64_t M, int64_t N,
+                                                               int64_t K) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    // this workgroup's chunk of at most 32 activation rows (grid.y)
+    const int64_t nb = K / QK_K;
+    const int64_t m0 = (int64_t)blockIdx.y * Q2S_ROWS;
+    Y += m0 * nb * kQ8_KBytes;
+    out += m0 * N;
+    M = M - m0 < Q2S_ROWS ? M - m0 : Q2S_ROWS;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds scalar offsets
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int64_t n_base = (int64_t)blockIdx.x * 32;
+    const int64_t col = n_base + l32 < N ? n_base + l32 : N - 1;  // clamped: loads stay in bounds
+    uint8_t *const my = lds + wave * 2 * Q2S_STAGE;                // this wavefront's two stages
+
+    // weights (repacked Q2_K: d|dmin section of 4 bytes per super-block padded
+    // to 256 bytes, then scales 16 B and qs 64 B per super-block, each section
+    // [N][nb]); offsets relative to the matrix start
+    const int64_t NB = N * nb;
+    const int64_t dsec = (4 * NB + 255) / 256 * 256;
+    const int64_t i0 = col * nb;  // the column's first super-block
+    const uint32_t v_dm = (uint32_t)(4 * i0);
+    const uint32_t v_sc = (uint32_t)(dsec + 16 * i0);
+    const uint32_t v_qs = (uint32_t)(dsec + 16 * NB + 64 * i0 + 16 * hh);
+
+    // activations: rows past M - 1 are clamped to it (loaded, never stored)
+    const int64_t y_bytes = M * nb * kQ8_KBytes;
+    const uint32_t row_stride = (uint32_t)(nb * kQ8_KBytes);
+    auto row_off = [&](int r) -> uint32_t { return (uint32_t)(r < M ? r : M - 1) * row_stride; };
+    // codes: instruction t moves rows 4t .. 4t+3, 16 lanes per 256-byte row
+    const int c_row = lane >> 4, c_pos = lane & 15;
+    uint32_t a_goff[R / 4];
+#pragma unroll
+    for (int t = 0; t < R / 4; ++t) {
+        const int r = 4 * t + c_row;
+        a_goff[t] = row_off(r) + 4 + 16 * (uint32_t)(c_pos ^ (r & 15));
+    }
+    const uint32_t da_off = row_off(l32);
+    // constant offsets go to the scalar offset (a vector add would be hoisted
+    // out of the loop and hold a register per load)
+    auto wload = [&](int64_t b, Q2SW &x) {
+        const rsrc_t rw = make_rsrc(W, w_bytes);
+        const uint32_t bb = (uint32_t)b;
+        x.qa = bld16(rw, v_qs, 64 * bb);
+        x.qb = bld16(rw, v_qs, 64 * bb + 32);
+        x.sc = bld16(rw, v_sc, 16 * bb);
+        x.dm = __builtin_amdgcn_raw_buffer_load_b32(rw, v_dm, 4 * bb, 0);
+        const rsrc_t ry = make_rsrc(Y, y_bytes);
+        x.bs = bld16(ry, da_off + 260 + 16 * hh, (uint32_t)b * kQ8_KBytes);
+    };
+    auto aload = [&](int64_t b, uint8_t *st) {
+        const rsrc_t ry = make_rsrc(Y, y_bytes);
+        const uint32_t sy = (uint32_t)b * kQ8_KBytes;
+#pragma unroll
+        for (int t = 0; t < R / 4; ++t) dma16(ry, a_goff[t], sy, st + Q2S_A + 1024 * t);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void *)(st + Q2S_DA), 4, da_off, sy, 0, 0);
+    };
+    // MFMA row l32 reads staged row l32 & (R - 1) (rows >= M are never stored)
+    const int arow = l32 & (R - 1);
+
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+
+    // One step: wait for this step's data, read the whole stage, start the
+    // next step's loads (a wavefront past its last step reloads that step: in
+    // bounds, unused), then decode, contraction and epilogue.
+    auto step = [&](int64_t b, int si, const Q2SW &cur, Q2SW &nxt) {
+        const int64_t bn = b + Q2S_WAVES < nb ? b + Q2S_WAVES : b;
+        const uint8_t *st = my + si * Q2S_STAGE;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this step's weights and LDS rows
+        uint4 a[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            a[c] = *reinterpret_cast<const uint4 *>(st + Q2S_A + arow * 256 + 16 * ((2 * c + hh) ^ (arow & 15)));
+        float4 d4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d4[q] = *reinterpret_cast<const float4 *>(st + Q2S_DA + 4 * (8 * q + 4 * hh));
+        aload(bn, my + (si ^ 1) * Q2S_STAGE);
+        wload(bn, nxt);
+
+        // chunk c holds group 2c + hh of this lane: qs piece (c/4)*2 + hh,
+        // field c%4 (see the Q2_K GEMM)
+        const float dcol = f16_bits_to_f32(cur.dm & 0xffff);
+        const float dmneg = -f16_bits_to_f32(cur.dm >> 16);
+        const uint32_t sw[4] = {cur.sc.x, cur.sc.y, cur.sc.z, cur.sc.w};
+        const v16i zero = {};
+        v16i as = zero;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint4 pc = c < 4 ? cur.qa : cur.qb;
+            const int sh = 2 * (c & 3);
+            // scale byte 2c + hh: dword c/2, byte 2(c%2) + hh; s_j is its low nibble
+            const uint32_t s2 = ((sw[c >> 1] >> (16 * (c & 1) + 8 * hh)) & 15) * 0x00010001u;
+            const v4i bq = v4i{plane((pc.x >> sh) & 0x03030303u, s2), plane((pc.y >> sh) & 0x03030303u, s2),
+                               plane((pc.z >> sh) & 0x03030303u, s2), plane((pc.w >> sh) & 0x03030303u, s2)};
+            const v4i av = v4i{(int)a[c].x, (int)a[c].y, (int)a[c].z, (int)a[c].w};
+            as = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bq, as, 0, 0, 0);
+        }
+        // min term: mins of groups 8hh..8hh+7 against the row's bsums, both fp16
+        v8h bmn, a_bs;
+        {
+            const uint32_t m_lo = hh ? sw[2] : sw[0], m_hi = hh ? sw[3] : sw[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bmn[e] = (_Float16)(float)((m_lo >> (8 * e + 4)) & 15);
+                bmn[4 + e] = (_Float16)(float)((m_hi >> (8 * e + 4)) & 15);
+            }
+            const uint4 r = cur.bs;
+            const uint4 hv = make_uint4(h2_bits((int16_t)(r.x & 0xffff), (int16_t)(r.x >> 16)),
+                                        h2_bits((int16_t)(r.y & 0xffff), (int16_t)(r.y >> 16)),
+                                        h2_bits((int16_t)(r.z & 0xffff), (int16_t)(r.z >> 16)),
+                                        h2_bits((int16_t)(r.w & 0xffff), (int16_t)(r.w >> 16)));
+            __builtin_memcpy(&a_bs, &hv, 16);
+        }
+        const v16f zf = {};
+        const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_bs, bmn, zf, 0, 0, 0);
+        // epilogue: acc += d_a * (d * S - dmin * Mn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float dv[4] = {d4[q].x, d4[q].y, d4[q].z, d4[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q + e;
+                acc[r] = fmaf(dv[e], fmaf(dcol, (float)as[r], dmneg * mn[r]), acc[r]);
+            }
+        }
+        // the epilogue stays in this step: sunk into the next one it would
+        // keep this step's MFMA results live across that step
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(acc[r]));
+    };
+
+    const int64_t b0 = wave < nb ? wave : nb - 1;
+    Q2SW w0, w1;
+    aload(b0, my);
+    wload(b0, w0);
+    for (int64_t b = wave; b < nb; b += 2 * Q2S_WAVES) {
+        step(b, 0, w0, w1);
+        if (b + Q2S_WAVES < nb) step(b + Q2S_WAVES, 1, w1, w0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no transfer into LDS outlives the loop
+
+    // ---- sum the eight K-split partial tiles (in the stage LDS, now free)
+    // and store the valid outputs
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(lds);  // [Q2S_WAVES][16][64]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+    __syncthreads();
+    for (int o = tid; o < 32 * 32; o += Q2S_THREADS) {
+        const int m = o >> 5, c = o & 31;      // output row m, column n_base + c
+        const int r = 4 * (m >> 3) + (m & 3);  // register holding row m ...
+        const int l = c + 32 * ((m >> 2) & 1); // ... in lane l
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < Q2S_WAVES; ++w) s += red[(w * 16 + r) * 64 + l];
+        if (m < M && n_base + c < N) out[(int64_t)m * N + n_base + c] = s;
+    }
+}
+
+template <int R>
+hipError_t launch_q2s(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M, int64_t N,
+                      int64_t K, hipStream_t s) {
+    static std::atomic<uint64_t> lds_set{0};  // the LDS budget above 64 KiB, per device
+    const hipError_t e = ensure_lds_bytes((const void *)k_skinny_q2_K<R>, Q2S_LDS, lds_set);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + Q2S_ROWS - 1) / Q2S_ROWS));
+    hipLaunchKernelGGL((k_skinny_q2_K<R>), grid, dim3(Q2S_THREADS), Q2S_LDS, s, w, w_bytes, y, out, M, N, K);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t skinny_q2_K_max_m() { return Q2S_MAX_M; }
+
+hipError_t launch_skinny_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M,
+                              int64_t N, int64_t K, hipStream_t s) {
+    // rows staged per super-block: the power of two >= M among 8, 16, 32
+    if (M <= 8) return launch_q2s<8>(w, w_bytes, y, out, M, N, K, s);
+    if (M <= 16) return launch_q2s<16>(w, w_bytes, y, out, M, N, K, s);
+    return launch_q2s<32>(w, w_bytes, y, out, M, N, K, s);
+}
+
+}  // namespace qmm

@@ -102,6 +102,11 @@ hipError_t launch_gemm_q6_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
+// Q2_K small batch: repacked layout, M <= skinny_q2_K_max_m(), matrices below
+// 4 GiB; w_bytes is the repacked matrix size.
+int64_t skinny_q2_K_max_m();
+hipError_t launch_skinny_q2_K(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M,
+                              int64_t N, int64_t K, hipStream_t s);
 // Q4_0 x Q8_0, repacked layout, K a multiple of 256.
 hipError_t launch_gemm_q4_0(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);

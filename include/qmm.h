@@ -94,8 +94,9 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
  *   GEMV    vector int8 dot products, one wavefront per output row (Q4_0 and
  *           Q4_K: M <= 8 per launch; Q6_K and Q2_K: any M, K <= 53760)
  *   SKINNY  small-batch int8 MFMA, one 32-column x 32-row tile per workgroup,
- *           K split over its wavefronts (Q4_K; Q6_K in the repacked layout;
- *           Q4_0 in the repacked layout with K % 256 == 0; M <= 65535*32)
+ *           K split over its wavefronts (Q4_K; Q6_K and Q2_K in the repacked
+ *           layout; Q4_0 in the repacked layout with K % 256 == 0;
+ *           M <= 65535*32)
  *   MFMA    prefill GEMM on int8 MFMA, 128 x 256 output tiles (any M; Q6_K,
  *           Q2_K and Q4_0 need the repacked layout, Q4_0 also K % 256 == 0)
  * SKINNY and MFMA address the weight and activation matrices with 32-bit
@@ -107,10 +108,12 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
  * the GEMV's LDS staging) and for M = 2 with N < 8192, SKINNY while
  * ceil(M/32)*N <= 16*8192, MFMA above, GEMV where the MFMA kernels are ruled
  * out; for Q6_K in the repacked layout it takes GEMV for M = 1 and for M = 2
- * with N < 8192, SKINNY while ceil(M/32)*N <= 8*8192, MFMA above; for Q2_K,
- * and Q6_K in the canonical layout, it takes GEMV for M = 1 and while
- * M*N <= c*ceil(N/65536) with c = 16*8192 (Q6_K), 26*8192 (Q2_K), MFMA above,
- * GEMV where MFMA is ruled out. */
+ * with N < 8192, SKINNY while ceil(M/32)*N <= 8*8192, MFMA above; for Q2_K in
+ * the repacked layout it takes GEMV for M <= 2, SKINNY while
+ * ceil(M/32)*N <= 6*8192, MFMA above; for Q6_K and Q2_K in the canonical
+ * layout it takes GEMV for M = 1 and while M*N <= c*ceil(N/65536) with
+ * c = 16*8192 (Q6_K), 26*8192 (Q2_K), MFMA above, GEMV where MFMA is ruled
+ * out (the canonical layout has only the GEMV). */
 typedef enum {
     QMM_ALGO_AUTO = 0,
     QMM_ALGO_GEMV = 1,
@@ -225,8 +228,8 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l,
  * S = sum_j s_j*P_j, P_j = sum_{i in j} q_i*y_i and Mn = sum_j m_j*bsums[j] over
  * the 16-element groups j (ggml-cpu mul_mat page, "更低的比特:Q6_K 与 Q2_K 的取舍",
  * "正确性:缩放系数可以提到求和号外面", "min 项与最终归约").  fp32 output,
- * overwritten.  w: Q2_K [N,K] in layout l; y: Q8_K [M,K].  Kernel choice and
- * limits as for qmm_mul_mat_q6_K. */
+ * overwritten.  w: Q2_K [N,K] in layout l; y: Q8_K [M,K].  Kernel choice as
+ * qmm_algo states; limits as for qmm_mul_mat_q6_K. */
 qmm_status qmm_mul_mat_q2_K(const void *w, size_t w_bytes, qmm_layout l,
                             const void *y, size_t y_bytes,
                             float *out, size_t out_bytes,

@@ -201,7 +201,10 @@ def test_q2_K_validation(lib):
     assert "Q2_K with K" in _last(lib)
     assert fx(A, big, 1, A, big, A, big, 2, 8, 53760 + 256, 1, None) == EUNSUP  # GEMV
     assert fx(A, big, 0, A, big, A, big, 2, 8, 512, 2, None) == EUNSUP        # MFMA, canonical
-    assert fx(A, big, 1, A, big, A, big, 2, 8, 512, 3, None) == EUNSUP        # SKINNY
+    # SKINNY: repacked layout, M <= 65535*32
+    assert fx(A, big, 0, A, big, A, big, 2, 8, 512, 3, None) == EUNSUP and "SKINNY" in _last(lib)
+    assert fx(A, 2**40, 1, A, 2**40, A, 2**40, 65535 * 32 + 1, 8, 512, 3, None) == EUNSUP
+    assert fx(A, 2**40, 1, A, 2**40, A, 2**40, 65535 * 32, 0, 512, 3, None) == OK
     assert f(A, 8 * 2 * 84 - 1, 0, A, big, A, big, 2, 8, 512, None) == EINVAL
     assert f(A, 256 + 8 * 2 * 80 - 1, 1, A, big, A, big, 2, 8, 512, None) == EINVAL
     assert f(A, big, 1, A, 2 * 2 * 292 - 1, A, big, 2, 8, 512, None) == EINVAL

@@ -10,7 +10,9 @@
 * fp32 outputs: |gpu - oracle| <= 1e-4 * sum_k |w a| for every checked (m, n).
 Shapes: GEMV with one, two and four units per lane (K up to 53760), ragged N,
 several activation rows, both layouts; GEMM with ragged row and column tiles,
-K past the GEMV's limit, and AUTO dispatch.
+K past the GEMV's limit; the small-batch kernel with 8, 16 and 32 staged rows,
+ragged N, K not a multiple of eight super-blocks and several row chunks; and
+AUTO dispatch.
 """
 import struct
 
@@ -84,7 +86,8 @@ def _window(rng, N, K, dmin, scales, mins, codes):
     return np.frombuffer(blocks, np.uint8).reshape(N, -1)
 
 
-@pytest.mark.parametrize("algo,M,N,K", [("gemv", 3, 41, 1024), ("mfma", 130, 300, 1024)])
+@pytest.mark.parametrize("algo,M,N,K", [("gemv", 3, 41, 1024), ("mfma", 130, 300, 1024),
+                                         ("skinny", 20, 70, 2304)])
 @pytest.mark.parametrize("dmin", [0.0, 1.0])
 def test_exactness_window(algo, M, N, K, dmin):
     rng = np.random.default_rng(21)
@@ -112,7 +115,7 @@ def test_saturated_window():
     y = oracle.quantize("q8_K", x)
     want, terms = full_reference("q2_K", w, y, M, N, K)
     assert terms.max() < 2 ** 24
-    for algo in ("gemv", "mfma"):
+    for algo in ("gemv", "mfma", "skinny"):
         got = to_host(qmm.mul_mat_q2_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K,
                                        layout="repacked", algo=algo))
         assert np.array_equal(got.astype(np.float64), want), algo
@@ -138,12 +141,48 @@ def test_mul_mat_q2_K_mfma(M, N, K):
     assert_close(got, want, terms, f"q2_K mfma M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 70, 256), (5, 33, 512), (8, 300, 2048), (9, 64, 4608), (16, 40, 1024),
+                                   (17, 1, 256), (32, 257, 1024), (40, 100, 2048), (70, 130, 4608),
+                                   (3, 20, Q2K_MAX_K + 256)])
+def test_mul_mat_q2_K_skinny(M, N, K):
+    w, y = _case(M, N, K, 13 * M + N)
+    want, terms = full_reference("q2_K", w, y, M, N, K)
+    got = to_host(qmm.mul_mat_q2_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K,
+                                   layout="repacked", algo="skinny"))
+    assert_close(got, want, terms, f"q2_K skinny M={M} N={N} K={K}")
+
+
+def test_skinny_overwrites_and_rejects():
+    """The small-batch kernel writes every output, and refuses the canonical layout."""
+    import torch
+    M, N, K = 12, 50, 512
+    w, y = _case(M, N, K, 77)
+    want, terms = full_reference("q2_K", w, y, M, N, K)
+    out = torch.full((M, N), float("nan"), device="cuda")
+    qmm.mul_mat_q2_K(_upload(w, N, K, "repacked"), to_dev(y.reshape(-1)), M, N, K, layout="repacked",
+                     algo="skinny", out=out)
+    assert_close(to_host(out), want, terms, "q2_K skinny into a NaN-filled buffer")
+    with pytest.raises(qmm.QmmError):
+        qmm.mul_mat_q2_K(_upload(w, N, K, "canonical"), to_dev(y.reshape(-1)), M, N, K, layout="canonical",
+                         algo="skinny")
+
+
+SKINNY_MN = 6 * 8192
+
+
+def _auto_algo(M, N, layout):
+    """The AUTO rule as the library documents it (K within the GEMV's limit)."""
+    if layout == "canonical" or M <= 2:
+        return "gemv"
+    return "skinny" if (M + 31) // 32 * N <= SKINNY_MN else "mfma"
+
+
 def test_auto_dispatch_and_fused():
-    """AUTO picks the GEMV for M = 1 and while M*N <= 26*8192 (per 65536
-    columns), the GEMM above (repacked), the GEMV for the canonical layout, and
-    is bit-identical to that path; quantize_mul_mat equals quantize + mul_mat."""
-    K = 2048
-    for M, N in ((1, 96), (8, 96), (64, 96), (64, 3400)):
+    """AUTO (repacked): the GEMV for M <= 2, the small-batch kernel while ceil(M/32)*N <= SKINNY_MN, the GEMM above; the
+    GEMV for the canonical layout.  AUTO is bit-identical to that path and
+    agrees with the oracle; quantize_mul_mat equals quantize + mul_mat."""
+    for M, N, K in ((1, 96, 2048), (2, 96, 2048), (8, 96, 2048), (64, 96, 2048), (64, 3400, 2048),
+                    (3, 9000, 256), (64, 24576, 256), (65, 16400, 256)):
         w, _ = _case(M, N, K, 900 + M)
         x = activations([703, M], M, K)
         y = oracle.quantize("q8_K", x)
@@ -152,9 +191,8 @@ def test_auto_dispatch_and_fused():
             wd = _upload(w, N, K, layout)
             got = to_host(qmm.mul_mat_q2_K(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout))
             assert_close(got, want, terms, f"q2_K auto M={M} N={N} {layout}")
-            gemv = layout == "canonical" or M == 1 or M * N <= 26 * 8192 * ((N + 65535) // 65536)
             ref = to_host(qmm.mul_mat_q2_K(wd, to_dev(y.reshape(-1)), M, N, K, layout=layout,
-                                           algo="gemv" if gemv else "mfma"))
+                                           algo=_auto_algo(M, N, layout)))
             assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (M, N, layout)
             fused, yq = qmm.quantize_mul_mat("q2_K", wd, to_dev(x), N, layout=layout)
             assert np.array_equal(to_host(yq).reshape(-1), y.reshape(-1))
