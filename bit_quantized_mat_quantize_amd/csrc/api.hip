@@ -338,12 +338,10 @@ struct GroupedKernels {
     hipError_t (*gemm)(const uint8_t *, int64_t, const uint8_t *, float *, int64_t, int64_t, int64_t,
                        hipStream_t);
     // small-batch kernel (repacked layout), or null where the format has none;
-    // AUTO takes it while ceil(M/32)*N <= skinny_mn, and leaves M = 2 to the
-    // GEMV below 8192 columns, or at any N where gemv_m2 is set
+    // AUTO takes it while ceil(M/32)*N <= skinny_mn
     hipError_t (*skinny)(const uint8_t *, int64_t, const uint8_t *, float *, int64_t, int64_t, int64_t,
                          hipStream_t);
     int64_t skinny_max_m, skinny_mn;
-    bool gemv_m2;
 };
 
 qmm_status mul_mat_grouped(qmm_weight_type t, const GroupedKernels &k, const void *w, size_t w_bytes,
@@ -377,9 +375,9 @@ qmm_status mul_mat_grouped(qmm_weight_type t, const GroupedKernels &k, const voi
     qmm_algo a = algo;
     if (a == QMM_ALGO_AUTO && skinny_ok) {
         // GEMV for M = 1 and for M = 2 below 8192 columns (fewer than 256
-        // small-batch workgroups; Q2_K at any N), the small-batch kernel while
-        // its row chunks cost less than one GEMM K loop, the GEMM above
-        if ((M == 1 || (M == 2 && (N < 8192 || k.gemv_m2))) && gemv_ok) a = QMM_ALGO_GEMV;
+        // small-batch workgroups), the small-batch kernel while its row chunks
+        // cost less than one GEMM K loop, the GEMM above
+        if ((M == 1 || (M == 2 && N < 8192)) && gemv_ok) a = QMM_ALGO_GEMV;
         else if (((M + 31) / 32) * N <= k.skinny_mn) a = QMM_ALGO_SKINNY;
         else a = QMM_ALGO_MFMA;
     } else if (a == QMM_ALGO_AUTO) {
@@ -398,15 +396,15 @@ GroupedKernels q6_K_kernels() {
     // small batch measured at N = 4096..28672: 18.9 against 78 us (GEMV) at
     // M = 8, N = K = 8192; 74 against 77 us (GEMM) at M = 64, N = 28672
     return GroupedKernels{"Q6_K", qmm::q6_K_max_k(), kGemvMN_Q6_K, qmm::launch_gemv_q6_K, qmm::launch_gemm_q6_K,
-                          qmm::launch_skinny_q6_K, qmm::skinny_q6_K_max_m(), 8 * 8192, false};
+                          qmm::launch_skinny_q6_K, qmm::skinny_q6_K_max_m(), 8 * 8192};
 }
 GroupedKernels q2_K_kernels() {
-    // small batch measured at N = 4096..28672, K = 4096..14336: 11.9 against
-    // 32.1 us (GEMV) at M = 8, N = K = 8192; at M = 2 the GEMV is as fast or
-    // faster (22.8 against 25.9 us at N = 28672); 54.6 against 50.4 us (GEMM)
-    // at M = 64, N = 28672, 96.6 against 98.9 at M = 256, N = 8192
+    // small batch measured at N = 4096..28672, K = 4096..14336: 11.7 against
+    // 32.1 us (GEMV) at M = 8, N = K = 8192; 19.4 against 22.8 us (GEMV at
+    // M = 2) at M = 3, N = 28672; 54.6 against 50.4 us (GEMM) at M = 64,
+    // N = 28672, 96.6 against 98.9 at M = 256, N = 8192
     return GroupedKernels{"Q2_K", qmm::q2_K_max_k(), kGemvMN_Q2_K, qmm::launch_gemv_q2_K, qmm::launch_gemm_q2_K,
-                          qmm::launch_skinny_q2_K, qmm::skinny_q2_K_max_m(), 6 * 8192, true};
+                          qmm::launch_skinny_q2_K, qmm::skinny_q2_K_max_m(), 6 * 8192};
 }
 
 }  // namespace

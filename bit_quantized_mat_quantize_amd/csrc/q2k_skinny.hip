@@ -43,12 +43,16 @@ namespace {
 constexpr int Q2S_WAVES = 8, Q2S_THREADS = 64 * Q2S_WAVES;
 constexpr int Q2S_ROWS = 32;                       // activation rows per workgroup
 constexpr int64_t Q2S_MAX_M = 65535ll * Q2S_ROWS;  // row chunks go to grid.y
-// Per-wavefront LDS stage: codes [32 rows][256] (16-byte piece p of row r at
-// position p ^ (r & 15)), then d_a [64] (rows l % 32 of the loading lane l).
-constexpr int Q2S_A = 0, Q2S_DA = Q2S_ROWS * 256, Q2S_STAGE = Q2S_DA + 64 * 4;
-constexpr int Q2S_LDS = Q2S_WAVES * 2 * Q2S_STAGE;
+// Per-wavefront LDS stage for R staged rows: codes [R][256] (16-byte piece p
+// of row r at position p ^ (r & 15)), then d_a [64] (rows l % 32 of the loading
+// lane l).  Sized by R, so that at R = 8 several workgroups share a CU.
+constexpr int Q2S_A = 0;
 constexpr int Q2S_RED = Q2S_WAVES * 16 * 64 * 4;  // the partial tiles at the end
-static_assert(Q2S_LDS <= 160 * 1024 && Q2S_RED <= Q2S_LDS, "LDS budget of a gfx950 CU");
+template <int R>
+struct Q2SLds {
+    static constexpr int DA = R * 256, STAGE = DA + 64 * 4, BYTES = Q2S_WAVES * 2 * STAGE;
+    static_assert(BYTES <= 160 * 1024 && Q2S_RED <= BYTES, "LDS budget of a gfx950 CU");
+};
 
 // One super-block for lane (column l % 32, slice h = l / 32): the weight side
 // and the bsums of activation row l % 32 (groups 8h .. 8h + 7).
@@ -59,12 +63,15 @@ struct Q2SW {
     uint4 bs;      // int16 bsums of the lane's activation row
 };
 
+// At least 4 wavefronts per SIMD (at most 128 VGPRs, no spills): with the
+// R = 8 and 16 stages two workgroups then share a CU.
 template <int R>
-__global__ __launch_bounds__(Q2S_THREADS, 1) void k_skinny_q2_K(const uint8_t *__restrict__ W, int64_t w_bytes,
+__global__ __launch_bounds__(Q2S_THREADS, 4) void k_skinny_q2_K(const uint8_t *__restrict__ W, int64_t w_bytes,
                                                                const uint8_t *__restrict__ Y,
                                                                float *__restrict__ out, int64_t M, int64_t N,
                                                                int64_t K) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int STAGE = Q2SLds<R>::STAGE, DA = Q2SLds<R>::DA;
 
     // this workgroup's chunk of at most 32 activation rows (grid.y)
     const int64_t nb = K / QK_K;
@@ -78,7 +85,7 @@ __global__ __launch_bounds__(Q2S_THREADS, 1) void k_skinny_q2_K(const uint8_t *_
     const int l32 = lane & 31, hh = lane >> 5;
     const int64_t n_base = (int64_t)blockIdx.x * 32;
     const int64_t col = n_base + l32 < N ? n_base + l32 : N - 1;  // clamped: loads stay in bounds
-    uint8_t *const my = lds + wave * 2 * Q2S_STAGE;                // this wavefront's two stages
+    uint8_t *const my = lds + wave * 2 * STAGE;                // this wavefront's two stages
 
     // weights (repacked Q2_K: d|dmin section of 4 bytes per super-block padded
     // to 256 bytes, then scales 16 B and qs 64 B per super-block, each section
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(Q2S_THREADS, 1) void k_skinny_q2_K(const uint8_t *_
         const uint32_t sy = (uint32_t)b * kQ8_KBytes;
 #pragma unroll
         for (int t = 0; t < R / 4; ++t) dma16(ry, a_goff[t], sy, st + Q2S_A + 1024 * t);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void *)(st + Q2S_DA), 4, da_off, sy, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void *)(st + DA), 4, da_off, sy, 0, 0);
     };
     // MFMA row l32 reads staged row l32 & (R - 1) (rows >= M are never stored)
     const int arow = l32 & (R - 1);
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(Q2S_THREADS, 1) void k_skinny_q2_K(const uint8_t *_
     // bounds, unused), then decode, contraction and epilogue.
     auto step = [&](int64_t b, int si, const Q2SW &cur, Q2SW &nxt) {
         const int64_t bn = b + Q2S_WAVES < nb ? b + Q2S_WAVES : b;
-        const uint8_t *st = my + si * Q2S_STAGE;
+        const uint8_t *st = my + si * STAGE;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this step's weights and LDS rows
         uint4 a[8];
 #pragma unroll
@@ -142,8 +149,8 @@ __global__ __launch_bounds__(Q2S_THREADS, 1) void k_skinny_q2_K(const uint8_t *_
             a[c] = *reinterpret_cast<const uint4 *>(st + Q2S_A + arow * 256 + 16 * ((2 * c + hh) ^ (arow & 15)));
         float4 d4[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) d4[q] = *reinterpret_cast<const float4 *>(st + Q2S_DA + 4 * (8 * q + 4 * hh));
-        aload(bn, my + (si ^ 1) * Q2S_STAGE);
+        for (int q = 0; q < 4; ++q) d4[q] = *reinterpret_cast<const float4 *>(st + DA + 4 * (8 * q + 4 * hh));
+        aload(bn, my + (si ^ 1) * STAGE);
         wload(bn, nxt);
 
         // chunk c holds group 2c + hh of this lane: qs piece (c/4)*2 + hh,
@@ -230,10 +237,10 @@ template <int R>
 hipError_t launch_q2s(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M, int64_t N,
                       int64_t K, hipStream_t s) {
     static std::atomic<uint64_t> lds_set{0};  // the LDS budget above 64 KiB, per device
-    const hipError_t e = ensure_lds_bytes((const void *)k_skinny_q2_K<R>, Q2S_LDS, lds_set);
+    const hipError_t e = ensure_lds_bytes((const void *)k_skinny_q2_K<R>, Q2SLds<R>::BYTES, lds_set);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + Q2S_ROWS - 1) / Q2S_ROWS));
-    hipLaunchKernelGGL((k_skinny_q2_K<R>), grid, dim3(Q2S_THREADS), Q2S_LDS, s, w, w_bytes, y, out, M, N, K);
+    hipLaunchKernelGGL((k_skinny_q2_K<R>), grid, dim3(Q2S_THREADS), Q2SLds<R>::BYTES, s, w, w_bytes, y, out, M, N, K);
     return hipGetLastError();
 }
 

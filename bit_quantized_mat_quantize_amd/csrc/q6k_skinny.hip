@@ -41,12 +41,16 @@ namespace {
 constexpr int Q6S_WAVES = 8, Q6S_THREADS = 64 * Q6S_WAVES;
 constexpr int Q6S_ROWS = 32;                       // activation rows per workgroup
 constexpr int64_t Q6S_MAX_M = 65535ll * Q6S_ROWS;  // row chunks go to grid.y
-// Per-wavefront LDS stage: codes [32 rows][256] (16-byte piece p of row r at
-// position p ^ (r & 15)), then d_a [64] (rows l % 32 of the loading lane l).
-constexpr int Q6S_A = 0, Q6S_DA = Q6S_ROWS * 256, Q6S_STAGE = Q6S_DA + 64 * 4;
-constexpr int Q6S_LDS = Q6S_WAVES * 2 * Q6S_STAGE;
+// Per-wavefront LDS stage for R staged rows: codes [R][256] (16-byte piece p
+// of row r at position p ^ (r & 15)), then d_a [64] (rows l % 32 of the loading
+// lane l).  Sized by R, so that at R = 8 several workgroups share a CU.
+constexpr int Q6S_A = 0;
 constexpr int Q6S_RED = Q6S_WAVES * 16 * 64 * 4;  // the partial tiles at the end
-static_assert(Q6S_LDS <= 160 * 1024 && Q6S_RED <= Q6S_LDS, "LDS budget of a gfx950 CU");
+template <int R>
+struct Q6SLds {
+    static constexpr int DA = R * 256, STAGE = DA + 64 * 4, BYTES = Q6S_WAVES * 2 * STAGE;
+    static_assert(BYTES <= 160 * 1024 && Q6S_RED <= BYTES, "LDS budget of a gfx950 CU");
+};
 
 // The weight side of one super-block for lane (column l % 32, slice h = l / 32).
 struct Q6SW {
@@ -62,6 +66,7 @@ __global__ __launch_bounds__(Q6S_THREADS, 1) void k_skinny_q6_K(const uint8_t *_
                                                                float *__restrict__ out, int64_t M, int64_t N,
                                                                int64_t K) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int STAGE = Q6SLds<R>::STAGE, DA = Q6SLds<R>::DA;
 
     // this workgroup's chunk of at most 32 activation rows (grid.y)
     const int64_t nb = K / QK_K;
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(Q6S_THREADS, 1) void k_skinny_q6_K(const uint8_t *_
     const int l32 = lane & 31, hh = lane >> 5;
     const int64_t n_base = (int64_t)blockIdx.x * 32;
     const int64_t col = n_base + l32 < N ? n_base + l32 : N - 1;  // clamped: loads stay in bounds
-    uint8_t *const my = lds + wave * 2 * Q6S_STAGE;                // this wavefront's two stages
+    uint8_t *const my = lds + wave * 2 * STAGE;                // this wavefront's two stages
 
     // weights (repacked Q6_K: d section of 2 bytes per super-block padded to
     // 256 bytes, then scales 16 B, ql 128 B and qh 64 B per super-block, each
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(Q6S_THREADS, 1) void k_skinny_q6_K(const uint8_t *_
         const uint32_t sy = (uint32_t)b * kQ8_KBytes;
 #pragma unroll
         for (int t = 0; t < R / 4; ++t) dma16(ry, a_goff[t], sy, st + Q6S_A + 1024 * t);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void *)(st + Q6S_DA), 4, da_off, sy, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void *)(st + DA), 4, da_off, sy, 0, 0);
     };
     // MFMA row l32 reads staged row l32 & (R - 1) (rows >= M are never stored)
     const int arow = l32 & (R - 1);
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(Q6S_THREADS, 1) void k_skinny_q6_K(const uint8_t *_
     // bounds, unused), then decode, contraction and epilogue.
     auto step = [&](int64_t b, int si, const Q6SW &cur, Q6SW &nxt) {
         const int64_t bn = b + Q6S_WAVES < nb ? b + Q6S_WAVES : b;
-        const uint8_t *st = my + si * Q6S_STAGE;
+        const uint8_t *st = my + si * STAGE;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this step's weights and LDS rows
         uint4 a[8];
 #pragma unroll
@@ -140,8 +145,8 @@ __global__ __launch_bounds__(Q6S_THREADS, 1) void k_skinny_q6_K(const uint8_t *_
             a[c] = *reinterpret_cast<const uint4 *>(st + Q6S_A + arow * 256 + 16 * ((2 * c + hh) ^ (arow & 15)));
         float4 d4[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) d4[q] = *reinterpret_cast<const float4 *>(st + Q6S_DA + 4 * (8 * q + 4 * hh));
-        aload(bn, my + (si ^ 1) * Q6S_STAGE);
+        for (int q = 0; q < 4; ++q) d4[q] = *reinterpret_cast<const float4 *>(st + DA + 4 * (8 * q + 4 * hh));
+        aload(bn, my + (si ^ 1) * STAGE);
         wload(bn, nxt);
 
         // chunk c holds group 2c + hh of this lane (see the Q6_K GEMM)
@@ -218,10 +223,10 @@ template <int R>
 hipError_t launch_q6s(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M, int64_t N,
                       int64_t K, hipStream_t s) {
     static std::atomic<uint64_t> lds_set{0};  // the LDS budget above 64 KiB, per device
-    const hipError_t e = ensure_lds_bytes((const void *)k_skinny_q6_K<R>, Q6S_LDS, lds_set);
+    const hipError_t e = ensure_lds_bytes((const void *)k_skinny_q6_K<R>, Q6SLds<R>::BYTES, lds_set);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + Q6S_ROWS - 1) / Q6S_ROWS));
-    hipLaunchKernelGGL((k_skinny_q6_K<R>), grid, dim3(Q6S_THREADS), Q6S_LDS, s, w, w_bytes, y, out, M, N, K);
+    hipLaunchKernelGGL((k_skinny_q6_K<R>), grid, dim3(Q6S_THREADS), Q6SLds<R>::BYTES, s, w, w_bytes, y, out, M, N, K);
     return hipGetLastError();
 }
 

@@ -109,7 +109,7 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
  * ceil(M/32)*N <= 16*8192, MFMA above, GEMV where the MFMA kernels are ruled
  * out; for Q6_K in the repacked layout it takes GEMV for M = 1 and for M = 2
  * with N < 8192, SKINNY while ceil(M/32)*N <= 8*8192, MFMA above; for Q2_K in
- * the repacked layout it takes GEMV for M <= 2, SKINNY while
+ * the repacked layout it takes GEMV for M = 1 and for M = 2 with N < 8192, SKINNY while
  * ceil(M/32)*N <= 6*8192, MFMA above; for Q6_K and Q2_K in the canonical
  * layout it takes GEMV for M = 1 and while M*N <= c*ceil(N/65536) with
  * c = 16*8192 (Q6_K), 26*8192 (Q2_K), MFMA above, GEMV where MFMA is ruled

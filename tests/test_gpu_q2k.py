@@ -172,17 +172,18 @@ SKINNY_MN = 6 * 8192
 
 def _auto_algo(M, N, layout):
     """The AUTO rule as the library documents it (K within the GEMV's limit)."""
-    if layout == "canonical" or M <= 2:
+    if layout == "canonical" or M == 1 or (M == 2 and N < 8192):
         return "gemv"
     return "skinny" if (M + 31) // 32 * N <= SKINNY_MN else "mfma"
 
 
 def test_auto_dispatch_and_fused():
-    """AUTO (repacked): the GEMV for M <= 2, the small-batch kernel while ceil(M/32)*N <= SKINNY_MN, the GEMM above; the
+    """AUTO (repacked): the GEMV for M = 1 and for M = 2 below 8192 columns,
+    the small-batch kernel while ceil(M/32)*N <= SKINNY_MN, the GEMM above; the
     GEMV for the canonical layout.  AUTO is bit-identical to that path and
     agrees with the oracle; quantize_mul_mat equals quantize + mul_mat."""
     for M, N, K in ((1, 96, 2048), (2, 96, 2048), (8, 96, 2048), (64, 96, 2048), (64, 3400, 2048),
-                    (3, 9000, 256), (64, 24576, 256), (65, 16400, 256)):
+                    (2, 9000, 256), (3, 9000, 256), (64, 24576, 256), (65, 16400, 256)):
         w, _ = _case(M, N, K, 900 + M)
         x = activations([703, M], M, K)
         y = oracle.quantize("q8_K", x)
