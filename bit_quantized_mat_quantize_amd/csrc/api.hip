@@ -7,6 +7,7 @@
 // q6k_gemm.hip, q2k.hip, q2k_gemm.hip, q40_gemm.hip and moe.hip.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/qmm.h"
 #include "qmm_launch.h"
@@ -76,6 +77,43 @@ qmm_status check_size(const char *name, size_t have, size_t need) {
 qmm_status device_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return QMM_OK;
     return fail(QMM_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// QMM_LOG set to anything but "" or "0" prints every mul_mat call's kernel
+// choice, with its output tile, to stderr (read once per process).
+bool log_enabled() {
+    static const bool on = [] {
+        const char *v = getenv("QMM_LOG");
+        return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+    }();
+    return on;
+}
+
+const char *algo_name(qmm_algo a) {
+    switch (a) {
+        case QMM_ALGO_AUTO: return "AUTO";
+        case QMM_ALGO_GEMV: return "GEMV";
+        case QMM_ALGO_MFMA: return "MFMA";
+        case QMM_ALGO_SKINNY: return "SKINNY";
+    }
+    return "?";
+}
+
+const char *family_tile(qmm_algo a) {
+    switch (a) {
+        case QMM_ALGO_GEMV: return "one wavefront per output row, up to 8 activation rows per launch";
+        case QMM_ALGO_SKINNY: return "32 x 32 output tile per workgroup, K split over 8 wavefronts";
+        case QMM_ALGO_MFMA: return "128 x 256 output tile per workgroup";
+        default: return "";
+    }
+}
+
+void log_choice(const char *entry, const char *fmt, qmm_layout l, int64_t M, int64_t N, int64_t K,
+                qmm_algo asked, qmm_algo taken) {
+    if (!log_enabled()) return;
+    fprintf(stderr, "qmm: %s %s M=%lld N=%lld K=%lld layout=%s algo=%s -> %s (%s)\n", entry, fmt,
+            (long long)M, (long long)N, (long long)K, l == QMM_LAYOUT_REPACKED ? "repacked" : "canonical",
+            algo_name(asked), algo_name(taken), family_tile(taken));
 }
 
 #define QMM_TRY(expr)                        \
@@ -185,18 +223,6 @@ qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N,
                          "repack_weights launch");
 }
 
-// AUTO between a GEMV and the MFMA GEMM.  The GEMV costs a pass over the
-// weights per activation row (or group of rows); with a single row tile the
-// GEMM runs N/256 workgroups, and as long as that is below the CU count its
-// time is one workgroup's K loop whatever N is.  The GEMV therefore wins while
-// M*N stays below a per-format constant (measured at N = K = 8192 on the
-// weight stream: Q6_K up to M ~ 16, Q2_K ~ 26), which grows with the GEMM's
-// waves of workgroups once N passes 256 column tiles.  M = 1 always takes the
-// GEMV.
-bool prefer_gemv(int64_t M, int64_t N, int64_t mn_limit) {
-    return M == 1 || M * N <= mn_limit * ((N + 65535) / 65536);
-}
-constexpr int64_t kGemvMN_Q6_K = 16 * 8192, kGemvMN_Q2_K = 26 * 8192;
 // Q4_0 small-batch kernel vs GEMM: its time grows with the number of 32-row
 // chunks times N/32 workgroups, the GEMM's stays one K loop while its row
 // tiles fit the CUs; measured on N = 4096..28672, K = 4096..14336 it wins
@@ -237,6 +263,7 @@ qmm_status qmm_mul_mat_q4_0_ex(const void *w, size_t w_bytes, qmm_layout l, cons
         else if (skinny_ok && ((M + 31) / 32) * N <= kSkinnyMN_Q4_0) a = QMM_ALGO_SKINNY;
         else a = QMM_ALGO_MFMA;
     }
+    log_choice("mul_mat", "Q4_0", l, M, N, K, algo, a);
     if (a == QMM_ALGO_SKINNY)
         return device_status(qmm::launch_skinny_q4_0(wb, (int64_t)qmm_weight_bytes(QMM_Q4_0, l, N, K), yb, out,
                                                      M, N, K, s),
@@ -300,6 +327,7 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, cons
                    : (skinny_ok && skinny_pref ? QMM_ALGO_SKINNY
                                                : (M <= qmm::kGemvMaxM || !small ? QMM_ALGO_GEMV : QMM_ALGO_MFMA));
     }
+    log_choice("mul_mat", "Q4_K", l, M, N, K, algo, a);
     if (a == QMM_ALGO_GEMV) {
         // groups of up to 8 activation rows per GEMV launch
         const int64_t rowb = (K / 256) * 292;
@@ -328,11 +356,11 @@ qmm_status qmm_mul_mat_q4_K(const void *w, size_t w_bytes, qmm_layout l, const v
 namespace {
 
 // Q6_K and Q2_K (16-element groups): a GEMV for any M while the activation
-// row fits LDS, and an MFMA GEMM for the repacked layout; AUTO as in
-// prefer_gemv.
+// row fits LDS; for the repacked layout also a small-batch kernel and an MFMA
+// GEMM.
 struct GroupedKernels {
     const char *name;
-    int64_t gemv_max_k, gemv_mn;
+    int64_t gemv_max_k;
     hipError_t (*gemv)(const uint8_t *, bool, const uint8_t *, float *, int64_t, int64_t, int64_t,
                        hipStream_t);
     hipError_t (*gemm)(const uint8_t *, int64_t, const uint8_t *, float *, int64_t, int64_t, int64_t,
@@ -373,16 +401,18 @@ qmm_status mul_mat_grouped(qmm_weight_type t, const GroupedKernels &k, const voi
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     qmm_algo a = algo;
-    if (a == QMM_ALGO_AUTO && skinny_ok) {
-        // GEMV for M = 1 and for M = 2 below 8192 columns (fewer than 256
-        // small-batch workgroups), the small-batch kernel while its row chunks
-        // cost less than one GEMM K loop, the GEMM above
-        if ((M == 1 || (M == 2 && N < 8192)) && gemv_ok) a = QMM_ALGO_GEMV;
-        else if (((M + 31) / 32) * N <= k.skinny_mn) a = QMM_ALGO_SKINNY;
+    if (a == QMM_ALGO_AUTO) {
+        // the canonical layout (and a matrix of 4 GiB or more) has only the
+        // GEMV; otherwise the GEMV for M = 1 and for M = 2 below 8192 columns
+        // (fewer than 256 small-batch workgroups), the small-batch kernel
+        // while its row chunks cost less than one GEMM K loop, the GEMM above.
+        // A K past the GEMV's limit sends M = 1 and 2 down the same rule.
+        if (!mfma_ok) a = QMM_ALGO_GEMV;
+        else if ((M == 1 || (M == 2 && N < 8192)) && gemv_ok) a = QMM_ALGO_GEMV;
+        else if (skinny_ok && ((M + 31) / 32) * N <= k.skinny_mn) a = QMM_ALGO_SKINNY;
         else a = QMM_ALGO_MFMA;
-    } else if (a == QMM_ALGO_AUTO) {
-        a = (prefer_gemv(M, N, k.gemv_mn) && gemv_ok) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
     }
+    log_choice("mul_mat", k.name, l, M, N, K, algo, a);
     if (a == QMM_ALGO_GEMV)
         return device_status(k.gemv(wb, l == QMM_LAYOUT_REPACKED, yb, out, M, N, K, s), "mul_mat gemv launch");
     if (a == QMM_ALGO_SKINNY)
@@ -395,7 +425,7 @@ qmm_status mul_mat_grouped(qmm_weight_type t, const GroupedKernels &k, const voi
 GroupedKernels q6_K_kernels() {
     // small batch measured at N = 4096..28672: 18.9 against 78 us (GEMV) at
     // M = 8, N = K = 8192; 74 against 77 us (GEMM) at M = 64, N = 28672
-    return GroupedKernels{"Q6_K", qmm::q6_K_max_k(), kGemvMN_Q6_K, qmm::launch_gemv_q6_K, qmm::launch_gemm_q6_K,
+    return GroupedKernels{"Q6_K", qmm::q6_K_max_k(), qmm::launch_gemv_q6_K, qmm::launch_gemm_q6_K,
                           qmm::launch_skinny_q6_K, qmm::skinny_q6_K_max_m(), 8 * 8192};
 }
 GroupedKernels q2_K_kernels() {
@@ -403,7 +433,7 @@ GroupedKernels q2_K_kernels() {
     // 32.1 us (GEMV) at M = 8, N = K = 8192; 19.4 against 22.8 us (GEMV at
     // M = 2) at M = 3, N = 28672; 54.6 against 50.4 us (GEMM) at M = 64,
     // N = 28672, 96.6 against 98.9 at M = 256, N = 8192
-    return GroupedKernels{"Q2_K", qmm::q2_K_max_k(), kGemvMN_Q2_K, qmm::launch_gemv_q2_K, qmm::launch_gemm_q2_K,
+    return GroupedKernels{"Q2_K", qmm::q2_K_max_k(), qmm::launch_gemv_q2_K, qmm::launch_gemm_q2_K,
                           qmm::launch_skinny_q2_K, qmm::skinny_q2_K_max_m(), 6 * 8192};
 }
 
@@ -541,6 +571,13 @@ qmm_status qmm_mul_mat_id(qmm_weight_type t, const void *w, size_t w_bytes, int6
     // sparse.  Measured on eight 14336 x 4096 Q4_K experts the two cross between
     // 32 and 48 pairs, i.e. near four pairs per expert.
     if (a == QMM_ALGO_AUTO) a = (P <= 4 * E && gemv_ok) || !mfma_ok ? QMM_ALGO_GEMV : QMM_ALGO_MFMA;
+    if (log_enabled())
+        fprintf(stderr, "qmm: mul_mat_id %s E=%lld T=%lld U=%lld N=%lld K=%lld layout=%s algo=%s -> %s (%s)\n",
+                t == QMM_Q4_0 ? "Q4_0" : t == QMM_Q4_K ? "Q4_K" : t == QMM_Q6_K ? "Q6_K" : "Q2_K", (long long)E,
+                (long long)T, (long long)U, (long long)N, (long long)K,
+                l == QMM_LAYOUT_REPACKED ? "repacked" : "canonical", algo_name(algo), algo_name(a),
+                a == QMM_ALGO_GEMV ? "one M = 1 GEMV per (token, slot)"
+                                   : "expert grouping, then 128 x 256 tiles of each expert's rows");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
@@ -586,11 +623,16 @@ qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t *yb = static_cast<uint8_t *>(y);
-    if (t == QMM_Q4_K && M == 1 && N > 0 && K <= qmm::gemv1_fused_max_k())
+    if (t == QMM_Q4_K && M == 1 && N > 0 && K <= qmm::gemv1_fused_max_k()) {
+        if (log_enabled())
+            fprintf(stderr, "qmm: quantize_mul_mat Q4_K M=1 N=%lld K=%lld layout=%s -> fused quantize + GEMV "
+                    "(one launch, one wavefront per output row)\n", (long long)N, (long long)K,
+                    l == QMM_LAYOUT_REPACKED ? "repacked" : "canonical");
         return device_status(qmm::launch_gemv1_fused_q4_K(static_cast<const uint8_t *>(w),
                                                           l == QMM_LAYOUT_REPACKED, x, yb, out, N,
                                                           K, s),
                              "quantize_mul_mat fused launch");
+    }
     QMM_TRY(qmm_quantize_row_q8(at, x, M, K, y, y_bytes, stream));
     if (N == 0) return QMM_OK;
     if (t == QMM_Q6_K) return qmm_mul_mat_q6_K(w, w_bytes, l, y, y_bytes, out, out_bytes, M, N, K, stream);

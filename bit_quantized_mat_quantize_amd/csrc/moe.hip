@@ -1,8 +1,8 @@
 // moe.hip -- expert grouping for mul_mat_id on gfx950.
 //
 // mul_mat_id is mul_mat with one more level, the grouping by expert id
-// (ggml-cpu mul_mat page, closing list of follow-ups: "mul_mat_id(MoE 专家路由
-// 下的矩阵乘)").  For prefill-sized batches the (token, slot) pairs routed to
+// (ggml-cpu mul_mat page, "本篇没有覆盖的部分", the list of follow-up topics
+// that names the expert-routed matrix product of MoE models).  For prefill-sized batches the (token, slot) pairs routed to
 // the same expert become the rows of one GEMM against that expert's matrix,
 // so the pairs are sorted by expert on the device (the ids come from a router
 // kernel and never visit the host) and cut into row tiles of the GEMM.

@@ -110,10 +110,10 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
  * out; for Q6_K in the repacked layout it takes GEMV for M = 1 and for M = 2
  * with N < 8192, SKINNY while ceil(M/32)*N <= 8*8192, MFMA above; for Q2_K in
  * the repacked layout it takes GEMV for M = 1 and for M = 2 with N < 8192, SKINNY while
- * ceil(M/32)*N <= 6*8192, MFMA above; for Q6_K and Q2_K in the canonical
- * layout it takes GEMV for M = 1 and while M*N <= c*ceil(N/65536) with
- * c = 16*8192 (Q6_K), 26*8192 (Q2_K), MFMA above, GEMV where MFMA is ruled
- * out (the canonical layout has only the GEMV). */
+ * ceil(M/32)*N <= 6*8192, MFMA above.  For Q6_K and Q2_K, a K above the
+ * GEMV's limit (53760) sends M = 1 and M = 2 to SKINNY or MFMA by the same
+ * ceil(M/32)*N rule.  The canonical layout of Q6_K and Q2_K, and a matrix of
+ * 4 GiB or more, have only the GEMV: AUTO takes it for every M. */
 typedef enum {
     QMM_ALGO_AUTO = 0,
     QMM_ALGO_GEMV = 1,
@@ -158,15 +158,25 @@ qmm_status qmm_quantize_row_q8(qmm_act_type t, const float *x, int64_t M, int64_
 qmm_status qmm_quantize_weights(qmm_weight_type t, const float *w, int64_t N, int64_t K,
                                 void *out, size_t out_bytes, void *stream);
 
-/* Permute canonical weight blocks into QMM_LAYOUT_REPACKED (load time, once
- * per weight matrix; the canonical bytes stay the source of truth).
- * w_canon and w_repacked must not overlap. */
+/* Permute canonical weight blocks into QMM_LAYOUT_REPACKED (BitBLAS page,
+ * "Ladder Permutation": an offline, lossless reordering of static weights into
+ * the order the kernel reads them; same page, "4. 权重变换只做一次": the
+ * transform runs once at load time and the original quantized blocks stay the
+ * source of truth; GGML memory/quantization page, "量化:热路径是点积,不是反量化":
+ * a load-time layout change that leaves the file's blocks untouched).  The byte map of each format is given at the top of this header.
+ * w_canon: device, qmm_weight_bytes(t, CANONICAL, N, K) bytes; w_repacked:
+ * device, out_bytes >= qmm_weight_bytes(t, REPACKED, N, K), fully written
+ * (padding zeroed).  The two must not overlap (QMM_EINVAL). */
 qmm_status qmm_repack_weights(qmm_weight_type t, const void *w_canon, int64_t N, int64_t K,
                               void *w_repacked, size_t out_bytes, void *stream);
 
-/* out[m*N+n] = sum over blocks b of d_w*d_a*sum_i (q_i-8)*y_i  (fp32 output,
- * overwritten).  w: Q4_0 [N,K] in layout l; y: Q8_0 [M,K] from
- * qmm_quantize_row_q8.  Kernel choice as QMM_ALGO_AUTO describes. */
+/* out[m*N+n] = sum over blocks b of d_w*d_a*sum_i (q_i-8)*y_i  (ggml-cpu
+ * mul_mat page, "最基础的两块:Q4_0 与 Q8_0": a Q4_0 block decodes to
+ * d*(q-8) and a Q8_0 block to d*y, so a block pair's dot product is the int32
+ * sum of (q-8)*y scaled once by both fp16 d's; "正确性:缩放系数可以提到求和号外面"
+ * for pulling the scales out of the sum).  fp32 output, overwritten.
+ * w: Q4_0 [N,K] in layout l; y: Q8_0 [M,K] from qmm_quantize_row_q8.
+ * Kernel choice as QMM_ALGO_AUTO describes. */
 qmm_status qmm_mul_mat_q4_0(const void *w, size_t w_bytes, qmm_layout l,
                             const void *y, size_t y_bytes,
                             float *out, size_t out_bytes,
@@ -249,8 +259,8 @@ qmm_status qmm_mul_mat_q2_K_ex(const void *w, size_t w_bytes, qmm_layout l,
  * Returns 0 for invalid arguments (U < 1, E outside [1, 4096], T*U >= 2^31). */
 size_t qmm_mul_mat_id_workspace_bytes(int64_t T, int64_t U, int64_t E);
 
-/* mul_mat_id (ggml-cpu mul_mat page, closing list of follow-ups: mul_mat with
- * one more level, the grouping by expert id).  For every token t < T and slot
+/* mul_mat_id (ggml-cpu mul_mat page, "本篇没有覆盖的部分", the follow-up
+ * topics: mul_mat with one more level, the grouping by expert id).  For every token t < T and slot
  * u < U, with e = ids[t*U + u]:
  *     out[(t*U + u)*N + n] = mul_mat_q4_K(W_e, y_row)[n]
  * where W_e is expert e's Q4_K [N,K] matrix -- w holds the E matrices one

@@ -101,32 +101,64 @@ static int16_t rd_i16(const uint8_t *p) {
 
 /* ------------------------------------------------------------------------ */
 /* Q4_K 12-byte scale field.  P1 "6-bit 参数是怎么塞进 12 字节的": the decode  */
-/* rule there fixes all 96 bits.  Sub-blocks j<4: s_j = low 6 bits of byte j, */
-/* m_j = low 6 bits of byte j+4.  j>=4: the low 4 bits of s_j / m_j are the  */
-/* low / high nibble of byte j+4, their top 2 bits sit in the top 2 bits of  */
-/* byte j-4 (for s_j) and byte j (for m_j).  (The prose of that section puts */
-/* the two nibbles the other way round; the decode rule is followed.)        */
+/* rule there fixes all 96 bits.  This project's statement of that layout,   */
+/* as bit pieces (byte, first bit, width), low piece first:                  */
+/*                                                                          */
+/*   field        low piece            high piece                           */
+/*   s_j, j<4     byte j,   bit 0, 6   -                                    */
+/*   m_j, j<4     byte j+4, bit 0, 6   -                                    */
+/*   s_j, j>=4    byte j+4, bit 0, 4   byte j-4, bit 6, 2                    */
+/*   m_j, j>=4    byte j+4, bit 4, 4   byte j,   bit 6, 2                    */
+/*                                                                          */
+/* (The prose of that section puts the two nibbles of bytes 8..11 the other  */
+/* way round; the decode rule is followed.)  Decoding reads the pieces and   */
+/* joins them; packing writes them.  Every one of the 96 bits belongs to     */
+/* exactly one piece, which the exhaustive round-trip test relies on.        */
 /* ------------------------------------------------------------------------ */
-void orc_q4_K_get_scale_min(const uint8_t *q, int j, uint8_t *s, uint8_t *m) {
+typedef struct { int byte, bit, width; } bit_piece;
+
+/* the pieces of field `which` (0 = scale s_j, 1 = min m_j) of sub-block j;  */
+/* returns the number of pieces (1 or 2), low piece first                    */
+static int scale_field_pieces(int j, int which, bit_piece pc[2]) {
     if (j < 4) {
-        *s = q[j] & 63;
-        *m = q[j + 4] & 63;
-    } else {
-        *s = (uint8_t)((q[j + 4] & 0x0f) | ((q[j - 4] >> 6) << 4));
-        *m = (uint8_t)((q[j + 4] >> 4) | ((q[j] >> 6) << 4));
+        pc[0] = (bit_piece){ j + 4 * which, 0, 6 };
+        return 1;
     }
+    pc[0] = (bit_piece){ j + 4, 4 * which, 4 };
+    pc[1] = (bit_piece){ which ? j : j - 4, 6, 2 };
+    return 2;
+}
+
+static uint8_t read_field(const uint8_t *q, int j, int which) {
+    bit_piece pc[2];
+    int n = scale_field_pieces(j, which, pc), v = 0, at = 0;
+    for (int i = 0; i < n; ++i) {
+        v |= ((q[pc[i].byte] >> pc[i].bit) & ((1 << pc[i].width) - 1)) << at;
+        at += pc[i].width;
+    }
+    return (uint8_t)v;
+}
+
+static void write_field(uint8_t *q, int j, int which, int v) {
+    bit_piece pc[2];
+    int n = scale_field_pieces(j, which, pc);
+    for (int i = 0; i < n; ++i) {
+        int mask = (1 << pc[i].width) - 1;
+        q[pc[i].byte] = (uint8_t)((q[pc[i].byte] & ~(mask << pc[i].bit)) | ((v & mask) << pc[i].bit));
+        v >>= pc[i].width;
+    }
+}
+
+void orc_q4_K_get_scale_min(const uint8_t *q, int j, uint8_t *s, uint8_t *m) {
+    *s = read_field(q, j, 0);
+    *m = read_field(q, j, 1);
 }
 
 void orc_q4_K_pack_scales(const uint8_t s[8], const uint8_t m[8], uint8_t out[12]) {
     memset(out, 0, 12);
-    for (int j = 0; j < 4; ++j) {
-        out[j] = (uint8_t)(s[j] & 63);
-        out[j + 4] = (uint8_t)(m[j] & 63);
-    }
-    for (int j = 4; j < 8; ++j) {
-        out[j + 4] = (uint8_t)((s[j] & 0x0f) | ((m[j] & 0x0f) << 4));
-        out[j - 4] |= (uint8_t)(((s[j] >> 4) & 3) << 6);
-        out[j] |= (uint8_t)(((m[j] >> 4) & 3) << 6);
+    for (int j = 0; j < 8; ++j) {
+        write_field(out, j, 0, s[j] & 63);
+        write_field(out, j, 1, m[j] & 63);
     }
 }
 
@@ -870,8 +902,9 @@ void orc_repack_q2_K(const uint8_t *canon, int64_t N, int64_t K, uint8_t *out) {
 }
 
 /* ======================================================================== */
-/* mul_mat_id.  P1 closing list of follow-ups ("mul_mat_id(MoE 专家路由下的  */
-/* 矩阵乘)"): mul_mat with one more level, the grouping by expert id.        */
+/* mul_mat_id.  P1 "本篇没有覆盖的部分" (its list of follow-up topics names   */
+/* the expert-routed product of MoE models): mul_mat with one more level,    */
+/* the grouping by expert id.                                                */
 /* Reading: a stack of E weight matrices [E][N][K] (expert e's rows start at */
 /* e*N rows), a token-by-slot table ids[T][U] of expert ids, and activation  */
 /* rows either one per token (y_per_slot = 0: row t serves every slot of     */

@@ -81,6 +81,11 @@ def test_scale_field_word_parallel_rule(orc):
         word = ((w2 >> 4) & 0x0F0F0F0F) | (((w1 >> 6) & 0x03030303) << 4)
         mins_hi = [(word >> (8 * i)) & 0xFF for i in range(4)]
         assert mins_hi == [orc.get_scale_min(f, 4 + i)[1] for i in range(4)]
+        # the scales of sub-blocks 4..7: low nibbles of bytes 8..11 joined with
+        # the top two bits of bytes 0..3
+        word = (w2 & 0x0F0F0F0F) | (((w0 >> 6) & 0x03030303) << 4)
+        scales_hi = [(word >> (8 * i)) & 0xFF for i in range(4)]
+        assert scales_hi == [orc.get_scale_min(f, 4 + i)[0] for i in range(4)]
         # and the first four: low six bits of bytes 0..3 (scales), 4..7 (mins)
         assert [orc.get_scale_min(f, i)[0] for i in range(4)] == [b & 63 for b in f[:4]]
         assert [orc.get_scale_min(f, i)[1] for i in range(4)] == [b & 63 for b in f[4:8]]
@@ -330,6 +335,28 @@ def test_q4_0_integer_path_vs_brute_force(orc, M, N, K):
     bf, terms = orc.brute_force(orc.dequantize("q4_0", w, N, K), orc.dequantize("q8_0", y, M, K))
     out = orc.mul_mat("q4_0", w, y, M, N, K)
     assert np.all(np.abs(out - bf) <= 1e-12 * terms + 1e-300)
+    # the sampler, asked for every (m, n) in a shuffled order, returns the same
+    # outputs and the brute-force sum|w a|: a wrong activation or weight stride
+    # in the sampler picks another row and fails here
+    perm = np.random.default_rng(M * 131 + N).permutation(M * N)
+    ms, ns = perm // N, perm % N
+    so, st = orc.sample("q4_0", w, y, M, N, K, ms, ns)
+    assert np.array_equal(so, out[ms, ns])
+    assert np.allclose(st, terms[ms, ns], rtol=1e-12, atol=0)
+    # the block sums equal sum (q - 8) y over each 32-block, with the codes read
+    # straight from the block bytes (d first, then element l low / l+16 high)
+    P = orc.subblock_sums("q4_0", w, y, M, N, K)
+    nb = K // 32
+    qw = np.zeros((N, K), np.int64)
+    for n in range(N):
+        for b in range(nb):
+            qs = w[n, 18 * b + 2:18 * b + 18].astype(np.int64)
+            qw[n, 32 * b:32 * b + 16] = (qs & 15) - 8
+            qw[n, 32 * b + 16:32 * b + 32] = (qs >> 4) - 8
+    qy = np.stack([np.concatenate([y[m, 34 * b + 2:34 * b + 34].view(np.int8) for b in range(nb)])
+                   for m in range(M)]).astype(np.int64)
+    want = (qy[:, None, :] * qw[None, :, :]).reshape(M, N, nb, 32).sum(-1)
+    assert np.array_equal(P, want)
 
 
 def test_special_cases(orc):
