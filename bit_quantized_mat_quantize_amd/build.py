@@ -20,6 +20,8 @@ OUT = os.path.join(PKG, "libqmm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "quantize.hip", "repack.hip", "gemv.hip", "skinny.hip", "q6k.hip", "q6k_gemm.hip", "q6k_skinny.hip",
            "q2k.hip", "q2k_gemm.hip", "q2k_skinny.hip", "q40_gemm.hip", "q40_skinny.hip", "moe.hip", "gemm.hip"]
+PROBE_SOURCES = ["probe.hip"]
+PROBE_OUT = os.path.join(PKG, "libqmm_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -47,16 +49,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """libqmm.so (the method) and libqmm_probe.so (the calibration probes the
+    benchmark reports beside it)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], OUT, verbose)
+    _link(objs[len(SOURCES):], PROBE_OUT, verbose)
     return OUT
 
 

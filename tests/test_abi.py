@@ -39,6 +39,28 @@ def test_header_symbols_exported(lib):
     assert exported == names
 
 
+def test_probe_header_symbols_exported():
+    """libqmm_probe.so exports exactly what include/qmm_probe.h declares, and
+    its argument checks answer without a GPU."""
+    import subprocess
+    from bit_quantized_mat_quantize_amd import _probe
+    plib = _probe.load()
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qmm_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(qmm_[A-Za-z0-9_]+)\s*\(", src)))
+    out = subprocess.run(["nm", "-D", "--defined-only", plib._name], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if re.search(r" T qmm_", l)})
+    assert exported == names and len(names) == 4
+    assert plib.qmm_probe_mfma_sink_bytes() == 256 * 8 * 256 * 4
+    assert plib.qmm_probe_mfma_ops(1) == 256 * 8 * 4 * 4 * 2 * 32 ** 3
+    P = ctypes.c_void_p
+    assert plib.qmm_probe_read(None, 16, 4, P(16), None) == 1      # null buffer
+    assert plib.qmm_probe_read(P(16), 24, 4, P(16), None) == 1     # not a multiple of 16
+    assert plib.qmm_probe_read(P(16), 32, 3, P(16), None) == 1     # unsupported loads per thread
+    assert plib.qmm_probe_read(P(8), 32, 4, P(16), None) == 1      # misaligned
+    assert plib.qmm_probe_mfma_i8(P(16), 16, 8, 0, None) == 1      # sink too small
+
+
 def test_size_helpers(lib):
     assert lib.qmm_act_bytes(0, 3, 64) == 3 * 2 * 34
     assert lib.qmm_act_bytes(1, 3, 512) == 3 * 2 * 292
