@@ -62,6 +62,7 @@ def load() -> ctypes.CDLL:
         "qmm_mul_mat_id_workspace_bytes": (SZ, [I64, I64, I64]),
         "qmm_mul_mat_id_q4_K": (I, [P, SZ, I64, I, P, SZ, I, P, I64, I64, P, SZ, I64, I64, P, SZ, I, P]),
         "qmm_mul_mat_id": (I, [I, P, SZ, I64, I, P, SZ, I, P, I64, I64, P, SZ, I64, I64, P, SZ, I, P]),
+        "qmm_mul_mat_id_noalloc": (I, [I, P, SZ, I64, I, P, SZ, I, P, I64, I64, P, SZ, I64, I64, I, P]),
         "qmm_mul_mat_q2_K_ex": (I, [P, SZ, I, P, SZ, P, SZ, I64, I64, I64, I, P]),
         "qmm_quantize_mul_mat": (I, [I, P, SZ, I, P, P, SZ, P, SZ, I64, I64, I64, P]),
         "qmm_debug_block_sums": (I, [I, P, SZ, I, P, SZ, P, SZ, I64, I64, I64, P]),
@@ -250,6 +251,26 @@ def mul_mat_id(wfmt: str, w, E: int, y, ids, N: int, K: int, layout: str = "cano
     _check(load().qmm_mul_mat_id(_WEIGHT[wfmt], pw, nw, E, _LAYOUT[layout], py, ny, int(bool(y_per_slot)), pi,
                                  T, U, po, no, N, K, pws, nws, _ALGO[algo], _stream(stream)),
            "qmm_mul_mat_id")
+    return out
+
+
+def mul_mat_id_noalloc(wfmt: str, w, E: int, y, ids, N: int, K: int, layout: str = "canonical",
+                       y_per_slot: bool = False, algo: str = "auto", out=None, stream=None):
+    """mul_mat_id with the expert grouping in the library's own per-GPU scratch
+    (no workspace argument; see qmm_mul_mat_id_noalloc)."""
+    import torch
+    T, U = ids.shape
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    if out is None:
+        out = torch.empty((T, U, N), dtype=torch.float32, device=ids.device)
+    pw, nw = _dev(w, "w")
+    py, ny = _dev(y, "y")
+    pi, _ = _dev(ids, "ids")
+    po, no = _dev(out, "out")
+    _check(load().qmm_mul_mat_id_noalloc(_WEIGHT[wfmt], pw, nw, E, _LAYOUT[layout], py, ny, int(bool(y_per_slot)),
+                                         pi, T, U, po, no, N, K, _ALGO[algo], _stream(stream)),
+           "qmm_mul_mat_id_noalloc")
     return out
 
 

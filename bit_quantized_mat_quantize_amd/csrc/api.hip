@@ -523,10 +523,16 @@ size_t qmm_mul_mat_id_workspace_bytes(int64_t T, int64_t U, int64_t E) {
     return (size_t)qmm::moe_group_layout(T * U, E, qmm::gemm_tile_rows()).words * 4;
 }
 
-qmm_status qmm_mul_mat_id(qmm_weight_type t, const void *w, size_t w_bytes, int64_t E, qmm_layout l,
-                          const void *y, size_t y_bytes, int y_per_slot, const int32_t *ids, int64_t T,
-                          int64_t U, float *out, size_t out_bytes, int64_t N, int64_t K, void *workspace,
-                          size_t ws_bytes, qmm_algo algo, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// mul_mat_id with the grouping tables in the caller's workspace
+// (own_scratch = false) or in the library's per-GPU scratch array.
+qmm_status mul_mat_id_impl(qmm_weight_type t, const void *w, size_t w_bytes, int64_t E, qmm_layout l,
+                           const void *y, size_t y_bytes, int y_per_slot, const int32_t *ids, int64_t T,
+                           int64_t U, float *out, size_t out_bytes, int64_t N, int64_t K, void *workspace,
+                           size_t ws_bytes, bool own_scratch, qmm_algo algo, void *stream) {
     IdKernels kk;
     if (!id_kernels(t, kk)) return fail(QMM_EUNSUPPORTED, "unknown weight type %d", (int)t);
     if (algo != QMM_ALGO_AUTO && algo != QMM_ALGO_GEMV && algo != QMM_ALGO_MFMA)
@@ -585,12 +591,45 @@ qmm_status qmm_mul_mat_id(qmm_weight_type t, const void *w, size_t w_bytes, int6
     if (a == QMM_ALGO_GEMV)
         return device_status(kk.gemv(wb, rep, (int64_t)w_one, yb, y_per_slot, ids, P, U, E, out, N, K, s),
                              "mul_mat_id gemv launch");
-    QMM_TRY(check_ptr("workspace", workspace));
-    QMM_TRY(check_size("workspace", ws_bytes, qmm_mul_mat_id_workspace_bytes(T, U, E)));
-    int32_t *ws = static_cast<int32_t *>(workspace);
+    int32_t *ws = nullptr;
+    if (own_scratch) {
+        QMM_TRY(device_status(qmm::noalloc_scratch(s, &ws), "mul_mat_id scratch address"));
+    } else {
+        QMM_TRY(check_ptr("workspace", workspace));
+        QMM_TRY(check_size("workspace", ws_bytes, qmm_mul_mat_id_workspace_bytes(T, U, E)));
+        ws = static_cast<int32_t *>(workspace);
+    }
     QMM_TRY(device_status(qmm::launch_moe_group_ids(ids, P, E, ws, out, N, s), "mul_mat_id grouping launch"));
     return device_status(kk.gemm(wb, rep, (int64_t)w_one, yb, y_rows, y_per_slot, U, ws, E, P, out, N, K, s),
                          "mul_mat_id gemm launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+qmm_status qmm_mul_mat_id(qmm_weight_type t, const void *w, size_t w_bytes, int64_t E, qmm_layout l,
+                          const void *y, size_t y_bytes, int y_per_slot, const int32_t *ids, int64_t T,
+                          int64_t U, float *out, size_t out_bytes, int64_t N, int64_t K, void *workspace,
+                          size_t ws_bytes, qmm_algo algo, void *stream) {
+    return mul_mat_id_impl(t, w, w_bytes, E, l, y, y_bytes, y_per_slot, ids, T, U, out, out_bytes, N, K,
+                           workspace, ws_bytes, false, algo, stream);
+}
+
+qmm_status qmm_mul_mat_id_noalloc(qmm_weight_type t, const void *w, size_t w_bytes, int64_t E, qmm_layout l,
+                                  const void *y, size_t y_bytes, int y_per_slot, const int32_t *ids,
+                                  int64_t T, int64_t U, float *out, size_t out_bytes, int64_t N, int64_t K,
+                                  qmm_algo algo, void *stream) {
+    // the grouping must fit the library's scratch array (checked before any
+    // HIP call; only the per-pair GEMV path needs no grouping)
+    const size_t need = qmm_mul_mat_id_workspace_bytes(T, U, E);
+    if (algo != QMM_ALGO_GEMV && need > qmm::kNoAllocScratchBytes)
+        return fail(QMM_EUNSUPPORTED,
+                    "mul_mat_id_noalloc: the expert grouping of T = %lld, U = %lld, E = %lld needs %zu bytes; "
+                    "the library's scratch holds %zu (use qmm_mul_mat_id with a workspace, or QMM_ALGO_GEMV)",
+                    (long long)T, (long long)U, (long long)E, need, qmm::kNoAllocScratchBytes);
+    return mul_mat_id_impl(t, w, w_bytes, E, l, y, y_bytes, y_per_slot, ids, T, U, out, out_bytes, N, K,
+                           nullptr, 0, true, algo, stream);
 }
 
 qmm_status qmm_mul_mat_id_q4_K(const void *w, size_t w_bytes, int64_t E, qmm_layout l, const void *y,

@@ -13,11 +13,30 @@
 // scatter of the pair indices to their expert's range.  The order of pairs
 // inside an expert's range is whatever the atomics give: every output row is
 // computed from its own pair alone, so the results do not depend on it.
+//
+// The grouping tables normally live in a workspace the caller passes.  For
+// callers that cannot allocate device memory, the library also keeps one
+// grouping area of its own per GPU: the file-scope array `scratch` below
+// (kNoAllocScratchBytes, held by each GPU the library runs on until the
+// process ends).  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): noalloc_scratch() looks up its
+// device address once per device with hipGetSymbolAddress, with that device
+// current, and every use goes through that address.  The grouping kernel
+// writes every word the GEMMs read (start, the tile table, the tile count and
+// the sorted pairs), so nothing has to be cleared between calls.
+#include <mutex>
+
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
 namespace qmm {
 namespace {
+
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int kGroupThreads = 1024;
 
@@ -99,6 +118,36 @@ __global__ __launch_bounds__(kGroupThreads) void k_moe_group_ids(const int32_t *
 }
 
 }  // namespace
+
+hipError_t noalloc_scratch(hipStream_t stream, int32_t **ptr) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream != nullptr) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(stream, &sd);
+        if (e != hipSuccess) return e;
+        dev = (int)sd;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        // the symbol's address on `dev`, looked up with `dev` current
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<int32_t *>(p);
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_moe_group_ids(const int32_t *ids, int64_t P, int64_t E, int32_t *ws, float *out,
                                 int64_t N, hipStream_t s) {

@@ -137,6 +137,11 @@ inline MoeGroupLayout moe_group_layout(int64_t P, int64_t E, int64_t bm) {
 constexpr int kMoeMaxExperts = 4096;
 int gemm_tile_rows();  // BM of the Q4_K GEMM
 int64_t gemv1_max_k();
+// The library's own grouping area for callers that cannot allocate: device
+// address of a static array of kNoAllocScratchBytes on the device of `stream`
+// (the current device for the null stream), looked up once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(2) << 20;
+hipError_t noalloc_scratch(hipStream_t stream, int32_t **ptr);
 // Build the grouping for pairs p < P with expert ids[p] (ids outside [0, E)
 // are left out, and their output rows are filled with NaN).
 hipError_t launch_moe_group_ids(const int32_t *ids, int64_t P, int64_t E, int32_t *ws, float *out,

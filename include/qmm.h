@@ -297,6 +297,24 @@ qmm_status qmm_mul_mat_id(qmm_weight_type t, const void *w, size_t w_bytes, int6
                           void *workspace, size_t ws_bytes, qmm_algo algo,
                           void *stream);
 
+/* qmm_mul_mat_id without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same contract, kernels and results as
+ * qmm_mul_mat_id; its MFMA path keeps the expert grouping in a scratch array
+ * the library holds in device memory: 2 MiB per GPU, kept until the process
+ * ends.  A call that may take the grouped path (algo AUTO or MFMA) and whose
+ * grouping needs more than that (qmm_mul_mat_id_workspace_bytes(T, U, E) >
+ * 2097152) gives QMM_EUNSUPPORTED before any HIP call.  Every call on one GPU
+ * shares that GPU's array and leaves its tables in it (each call rewrites all
+ * it reads, so nothing needs clearing): calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and must
+ * be serialized by the caller.  Allocates nothing. */
+qmm_status qmm_mul_mat_id_noalloc(qmm_weight_type t, const void *w, size_t w_bytes, int64_t E,
+                                  qmm_layout l, const void *y, size_t y_bytes, int y_per_slot,
+                                  const int32_t *ids, int64_t T, int64_t U,
+                                  float *out, size_t out_bytes, int64_t N, int64_t K,
+                                  qmm_algo algo, void *stream);
+
 /* Quantize-and-multiply in one call: y = quantize_row_q8(x) (Q8_0 for t = Q4_0,
  * Q8_K for t = Q4_K, Q6_K and Q2_K), then out = mul_mat(w, y).  The ggml-cpu mul_mat page
  * ("激活量化重复与融合") notes that quantizing the activations once at the

@@ -307,6 +307,36 @@ def test_mul_mat_id_generic_validation(lib):
     assert call(1, algo=1, K=53760 + 256) == EUNSUP
 
 
+def test_mul_mat_id_noalloc_validation(lib):
+    """The no-workspace variant refuses, before any HIP call, a grouping that
+    does not fit the library's 2 MiB scratch (unless the call is forced onto
+    the per-pair GEMV, which needs none), and validates like qmm_mul_mat_id."""
+    f = lib.qmm_mul_mat_id_noalloc
+    big = 10**12
+    wsb = lib.qmm_mul_mat_id_workspace_bytes
+
+    def call(t, **kw):
+        a = dict(w=A, wb=big, E=8, l=1, y=A, yb=big, yps=0, ids=A, T=3, U=2, o=A, ob=big, N=8, K=512, algo=0)
+        a.update(kw)
+        return f(t, a["w"], a["wb"], a["E"], a["l"], a["y"], a["yb"], a["yps"], a["ids"], a["T"], a["U"],
+                 a["o"], a["ob"], a["N"], a["K"], a["algo"], None)
+
+    limit = 2 << 20
+    T_fit = 1
+    while wsb(2 * T_fit, 2, 8) <= limit:
+        T_fit *= 2
+    while wsb(T_fit + 1, 2, 8) <= limit:
+        T_fit += 1
+    assert wsb(T_fit, 2, 8) <= limit < wsb(T_fit + 1, 2, 8)
+    for algo in (0, 2):                                   # AUTO, MFMA
+        assert call(1, T=T_fit + 1, algo=algo) == EUNSUP and "scratch" in _last(lib)
+    assert call(7) == EUNSUP and "weight type" in _last(lib)
+    assert call(1, algo=2, l=1, ids=None) == EINVAL
+    assert call(0, K=96, algo=2) == EUNSUP               # MFMA path steps K by 256
+    assert call(1, U=9) == EINVAL                        # U > E
+    assert call(1, T=0, w=None, y=None, ids=None, o=None) == OK
+
+
 def test_other_validation(lib):
     assert lib.qmm_quantize_weights(1, A, 4, 100, A, 10**6, None) == EUNSUP
     assert lib.qmm_quantize_weights(0, A, 4, 64, A, 4 * 2 * 18 - 1, None) == EINVAL
