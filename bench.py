@@ -267,19 +267,24 @@ def time_steps(prep, steps: int, only=None, min_replays: int = 3):
 
 
 # ------------------------------------------------------------- rooflines
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemv_q4_K.md")
-TRAFFIC_SOURCES = ("bit_quantized_mat_quantize_amd/csrc/gemv.hip",
-                   "bit_quantized_mat_quantize_amd/csrc/qmm_device.h",
-                   "bit_quantized_mat_quantize_amd/csrc/skinny.hip",
-                   "bit_quantized_mat_quantize_amd/csrc/gemm.hip",
-                   "bit_quantized_mat_quantize_amd/csrc/mfma_common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_q4_K.md")
+_CSRC = "bit_quantized_mat_quantize_amd/csrc/"
+KERNEL_SOURCES = {  # the files that define each kernel the counters were taken for
+    "k_gemv1_fused_q4_K": ("gemv.hip", "qmm_device.h"),
+    "k_gemv1_q4_K": ("gemv.hip", "qmm_device.h"),
+    "k_gemv_q4_0": ("gemv.hip", "qmm_device.h"),
+    "k_skinny_q4_K": ("skinny.hip", "mfma_common.h", "qmm_device.h"),
+    "k_gemm_q4_K": ("gemm.hip", "mfma_common.h", "qmm_device.h"),
+}
 
 
-def sources_sha() -> str:
+def sources_sha(kernel: str):
     import hashlib
+    if kernel not in KERNEL_SOURCES:
+        return None
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, _CSRC + f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -290,9 +295,9 @@ def profiled_traffic(kernel: str, workload: str):
     size), or None when no such measurement exists or the kernel sources have
     changed since it was taken."""
     import re
-    if not os.path.exists(TRAFFIC_FILE):
+    sha = sources_sha(kernel)
+    if sha is None or not os.path.exists(TRAFFIC_FILE):
         return None
-    sha = sources_sha()
     pat = re.compile(r"traffic kernel=(\S+) workload=(\S+) bytes_per_launch=(\d+) sources_sha256_16=(\w+)")
     with open(TRAFFIC_FILE) as fh:
         for line in fh:
@@ -351,7 +356,7 @@ def measure_config(key: str, layout: str, steps: int, forms=(False, True), probe
     if prefill:
         achieved = dom["ops"] / (dom["us"] * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None}
+                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": profiled_traffic(kern, key)}
     else:
         achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
         wl_tag = key + ("_gate_up" if "||" in dom["call"] else "")

@@ -44,6 +44,9 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m bit_quantized_mat_quantize_amd.build`")
+    # torch first: its HIP runtime must be the one libqmm binds to (loading
+    # libqmm first would bring in the system runtime under the same soname)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     sigs = {

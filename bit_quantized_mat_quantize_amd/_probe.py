@@ -19,6 +19,9 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(PROBE_LIB_PATH):
         raise ImportError(f"{PROBE_LIB_PATH} is missing: build it with "
                           "`python -m bit_quantized_mat_quantize_amd.build`")
+    # torch first: its HIP runtime must be the one libqmm binds to (loading
+    # libqmm first would bring in the system runtime under the same soname)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(PROBE_LIB_PATH)
     P, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     for name, res, args in (("qmm_probe_read", I, [P, SZ, I, P, P]),

@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libqmm.so")
-BUILD_DIR = os.path.join(ROOT, "_build")
+BUILD_DIR = os.path.join(ROOT, "_build_asan" if os.environ.get("QMM_ASAN") else "_build")
 SOURCES = ["api.hip", "quantize.hip", "repack.hip", "gemv.hip", "skinny.hip", "q6k.hip", "q6k_gemm.hip", "q6k_skinny.hip",
            "q2k.hip", "q2k_gemm.hip", "q2k_skinny.hip", "q40_gemm.hip", "q40_skinny.hip", "moe.hip", "gemm.hip"]
 PROBE_SOURCES = ["probe.hip"]
@@ -33,9 +33,16 @@ FLAGS = [
 ]
 
 
+# QMM_ASAN=1: AddressSanitizer on the host code only (argument validation,
+# dispatch, launch set-up), for the CPU test run of tests/asan_cpu.sh; the GPU
+# code is built as usual.
+ASAN = bool(os.environ.get("QMM_ASAN"))
+HOST_ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *(HOST_ASAN if ASAN else []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,7 +58,8 @@ def _compile(src: str, verbose: bool) -> str:
 
 def _link(objs, out: str, verbose: bool) -> None:
     tmp = out + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *(["-shared-libsan", "-fsanitize=address"] if ASAN else []),
+           "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

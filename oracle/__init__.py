@@ -32,6 +32,8 @@ def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
            "-o", _LIB + ".tmp", _SRC, "-lm"]
+    if os.environ.get("ORACLE_ASAN"):  # AddressSanitizer build (tests/asan_cpu.sh)
+        cmd[1:1] = ["-fsanitize=address", "-fno-omit-frame-pointer"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
