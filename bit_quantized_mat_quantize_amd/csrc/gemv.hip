@@ -330,16 +330,16 @@ __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ 
 // Fused M = 1 path: the fp32 activation row is quantized to Q8_K inside the
 // GEMV, straight into LDS, so one launch covers quantize + mul_mat.
 // Quantization costs vector-ALU work that every workgroup repeats, so the
-// grid holds one or two 16-wavefront workgroups per CU and each workgroup
-// loops over rows (wavefront w of workgroup g takes rows g*16 + w, then
-// + 16*gridDim.x, ...).  A wavefront first issues the fp32 loads of up to kXB
-// of its activation blocks (b = wave + 16i) and the loads of its first row,
-// then quantizes while the weights are in flight; in the row loop the next
-// row's pieces are loaded before the current row is reduced when the row
-// takes at most two pieces per lane (longer rows load it right after).  Rows
-// are one pass: K <= 8192, at most four pieces per lane.  Workgroup 0 also stores the Q8_K bytes to Yq, byte-identical to the
-// stand-alone quantizer (same device routine), so another projection of the
-// same input can reuse them.
+// grid holds one 16-wavefront workgroup per CU and each workgroup loops over
+// rows (wavefront w of workgroup g takes rows g*16 + w, then + 16*gridDim.x,
+// ...).  A wavefront first issues the fp32 loads of up to kXB of its
+// activation blocks (b = wave + 16i) and the loads of its first row, then
+// quantizes while the weights are in flight; in the row loop the next row's
+// pieces are loaded before the current row is reduced when the row takes at
+// most two pieces per lane (longer rows load it right after).  Rows are one
+// pass: K <= 8192, at most four pieces per lane.  Workgroup 0 also stores
+// the Q8_K bytes to Yq, byte-identical to the stand-alone quantizer (same
+// device routine), so another projection of the same input can reuse them.
 // ---------------------------------------------------------------------------
 constexpr int kFusedWaves = 16;
 
@@ -392,27 +392,41 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
     uint4 pw[kNit], hw[gemv1_subs<kNit>()];
     // a wavefront without rows loads a valid row and stores nothing
     gemv1_load<REPACKED, kNit>(A, row < N ? row : N - 1, 0, nchunk, lane, hw, pw);
+    // and every weight load ahead of the quantization: left to itself the
+    // scheduler issues part of them after the first block's reduction, which
+    // waits for its x load, so that part of the stream starts one round trip late
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kXB; ++i) quantize_block(xv[i], wave + kFusedWaves * i);
     __syncthreads();
 
-    for (; row < N; row += stride) {
-        const bool more = row + stride < N;
-        float acc = 0.0f;
-        if constexpr (kNit <= 2) {  // rows of one pass; registers for a second row
-            uint4 pn[kNit], hn[gemv1_subs<kNit>()];
-            if (more) gemv1_load<REPACKED, kNit>(A, row + stride, 0, nchunk, lane, hn, pn);
-            acc = gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, acc);
-#pragma unroll
-            for (int sp = 0; sp < gemv1_subs<kNit>(); ++sp) hw[sp] = hn[sp];
-#pragma unroll
-            for (int it = 0; it < kNit; ++it) pw[it] = pn[it];
-        } else {
-            acc = gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, acc);
-            if (more) gemv1_load<REPACKED, kNit>(A, row + stride, 0, nchunk, lane, hw, pw);
-        }
+    auto finish = [&](int64_t r, float acc) {
         acc = wave_sum(acc);
-        if (lane == 0) out[row] = acc;
+        if (lane == 0) out[r] = acc;
+    };
+    if constexpr (kNit <= 2) {
+        // Rows of one pass, two register stages: the next row's pieces are
+        // requested before the current row is reduced.  Every load is
+        // unconditional (past the last row it fetches row N - 1 again and
+        // drops it), so the wait before a reduction covers only the older
+        // stage; a conditional prefetch would make it wait for both.
+        uint4 pn[kNit], hn[gemv1_subs<kNit>()];
+        for (; row < N; row += 2 * stride) {
+            const int64_t r1 = row + stride, r2 = r1 + stride;
+            gemv1_load<REPACKED, kNit>(A, r1 < N ? r1 : N - 1, 0, nchunk, lane, hn, pn);
+            finish(row, gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, 0.0f));
+            if (r1 >= N) break;
+            gemv1_load<REPACKED, kNit>(A, r2 < N ? r2 : N - 1, 0, nchunk, lane, hw, pw);
+            finish(r1, gemv1_accumulate<kNit>(hn, pn, 0, nchunk, lane, s_qs, s_bs, s_d, 0.0f));
+        }
+    } else {
+        // longer rows: the first row's pieces are in flight already; it is
+        // reduced outside the loop, so its waits follow the pieces in order
+        if (row < N) finish(row, gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, 0.0f));
+        for (row += stride; row < N; row += stride) {
+            gemv1_load<REPACKED, kNit>(A, row, 0, nchunk, lane, hw, pw);
+            finish(row, gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, 0.0f));
+        }
     }
 }
 
@@ -750,9 +764,9 @@ hipError_t launch_gemv_id_q4_K(const uint8_t *w, bool repacked, int64_t w_stride
 }
 
 int64_t gemv1_fused_max_k() {
-    // rows of up to four 16-byte pieces per lane (K <= 8192): longer rows
-    // need more registers than a 16-wavefront workgroup leaves per lane, and
-    // their weight stream is long enough to hide a separate quantize launch
+    // rows of up to four 16-byte pieces per lane (K <= 8192).  Eight pieces
+    // (K <= 16384) fit in the registers too, but measured no faster than the
+    // two launches at N = 4096, K = 14336 (11.4 us either way)
     return 4 * 64 / 8 * QK_K;
 }
 
@@ -773,13 +787,13 @@ hipError_t launch_gemv1_fused_q4_K(const uint8_t *w, bool repacked, const float 
                                    float *out, int64_t N, int64_t K, hipStream_t s) {
     const int64_t lds = gemv1_lds_bytes(K);
     const int64_t nit = (K / QK_K * 8 + 63) / 64;
-    // one workgroup per CU; two (the register budget allows two 16-wavefront
-    // workgroups per CU) when each wavefront would still loop over at least
-    // two rows, so more of the weight stream is in flight
+    // at most one workgroup per CU: every extra workgroup repeats the
+    // quantization, and 16 wavefronts per CU, each with two rows in flight,
+    // keep the weight stream full (measured: a second 16-wavefront workgroup
+    // per CU, or a third register stage, made N = 28672, K = 4096 slower)
     const int64_t groups = (N + kFusedWaves - 1) / kFusedWaves;
     const int64_t cus = cu_count();
-    const int64_t cap = groups >= 4 * cus ? 2 * cus : cus;
-    const dim3 grid((unsigned)(groups < cap ? groups : cap)), block(kFusedWaves * 64);
+    const dim3 grid((unsigned)(groups < cus ? groups : cus)), block(kFusedWaves * 64);
 #define QMM_FUSED1(NIT, XB)                                                                        \
     do {                                                                                           \
         if (repacked)                                                                              \
