@@ -274,6 +274,7 @@ KERNEL_SOURCES = {  # the files that define each kernel the counters were taken 
     "k_gemv1_q4_K": ("gemv.hip", "qmm_device.h"),
     "k_gemv_q4_0": ("gemv.hip", "qmm_device.h"),
     "k_skinny_q4_K": ("skinny.hip", "mfma_common.h", "qmm_device.h"),
+    "k_skinny16_q4_K": ("skinny16.hip", "mfma_common.h", "qmm_device.h"),
     "k_gemm_q4_K": ("gemm.hip", "mfma_common.h", "qmm_device.h"),
 }
 
@@ -318,7 +319,7 @@ def kernel_of(key: str, call_name: str, fused: bool) -> str:
     if wfmt == "q4_K":
         if M == 1:
             return "k_gemv1_fused_q4_K" if fused and K <= 8192 else "k_gemv1_q4_K"
-        return "k_skinny_q4_K" if M <= 32 else "k_gemm_q4_K"
+        return "k_skinny16_q4_K" if M <= 16 else ("k_skinny_q4_K" if M <= 32 else "k_gemm_q4_K")
     fam = {"q6_K": "q6_K", "q2_K": "q2_K"}[wfmt]
     return f"k_gemv_{fam}" if M == 1 else (f"k_skinny_{fam}" if M <= 32 else f"k_gemm_{fam}")
 

@@ -26,6 +26,11 @@ qmm_status fail(qmm_status st, const char *fmt, ...) {
 
 constexpr int64_t kMaxRows = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 20;
+// Q4_K small batches of at most this many rows take the 16 x 16-tile kernel
+// (skinny16.hip): from 3 to 16 rows it was as fast as the 32 x 32 kernel or
+// faster on every shape measured (N = 4096 .. 28672, K = 4096 .. 14336), up
+// to 1.6x where N / 32 is below the CU count.
+constexpr int64_t kSkinny16MaxM = 16;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -315,15 +320,16 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, cons
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const uint8_t *yb = static_cast<const uint8_t *>(y);
     qmm_algo a = algo;
-    // AUTO: the small-batch kernel (one workgroup per 32 columns and 32 rows,
-    // K split over its wavefronts) beats the GEMM up to 32 rows, and further
-    // while ceil(M/32)*N stays below 9*8192 (measured at K = 8192: up to
-    // M ~ 300 for N = 8192, M ~ 80 for N = 28672); K cancels, both scale with it.
-    // At M = 2 below 8192 columns (fewer than 256 small-batch workgroups) the
-    // GEMV is faster: 6.7 against 8.1 us at N = K = 4096.
+    // AUTO: the small-batch kernels (K split over the wavefronts of a
+    // workgroup; 16 x 16 tiles up to 16 rows, 32 x 32 above) beat the GEMM up
+    // to 32 rows, and further while ceil(M/32)*N stays below 9*8192 (measured
+    // at K = 8192: up to M ~ 300 for N = 8192, M ~ 80 for N = 28672); K
+    // cancels, both scale with it.  From M = 2 on the 16 x 16 kernel is as
+    // fast as the GEMV or faster (N = K = 4096: 5.6 against 6.3 us; N = 4096,
+    // K = 14336: 11.6 against 17.2 us), whose vector work grows with M.
     if (a == QMM_ALGO_AUTO) {
         const bool skinny_pref = M <= 32 || ((M + 31) / 32) * N <= 9 * 8192;
-        a = M == 1 || (M == 2 && N < 8192) ? QMM_ALGO_GEMV
+        a = M == 1 ? QMM_ALGO_GEMV
                    : (skinny_ok && skinny_pref ? QMM_ALGO_SKINNY
                                                : (M <= qmm::kGemvMaxM || !small ? QMM_ALGO_GEMV : QMM_ALGO_MFMA));
     }
@@ -338,6 +344,10 @@ qmm_status qmm_mul_mat_q4_K_ex(const void *w, size_t w_bytes, qmm_layout l, cons
         }
         return QMM_OK;
     }
+    // the small-batch family: 16 x 16 tiles up to 16 rows, 32 x 32 above
+    if (a == QMM_ALGO_SKINNY && M <= kSkinny16MaxM)
+        return device_status(qmm::launch_skinny16_q4_K(wb, rep, yb, out, M, N, K, s),
+                             "mul_mat_q4_K skinny launch");
     if (a == QMM_ALGO_SKINNY)
         return device_status(qmm::launch_skinny_q4_K(wb, rep, yb, out, M, N, K, s),
                              "mul_mat_q4_K skinny launch");

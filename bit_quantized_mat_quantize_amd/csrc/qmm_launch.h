@@ -56,6 +56,11 @@ hipError_t launch_block_sums_q4_K(const uint8_t *w, bool repacked, const uint8_t
 int64_t skinny_max_m();
 hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                               int64_t M, int64_t N, int64_t K, hipStream_t s);
+// The same on 16 x 16 MFMA tiles (workgroups of 16 rows and 16 or 32
+// columns): M <= skinny16_max_m(), matrices below 4 GiB.
+int64_t skinny16_max_m();
+hipError_t launch_skinny16_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
+                                int64_t M, int64_t N, int64_t K, hipStream_t s);
 // Q4_0 small batch: repacked layout, K % 256 == 0, M <= skinny_q4_0_max_m(),
 // matrices below 4 GiB; w_bytes is the repacked matrix size.
 // Q4_0 GEMV with the M activation rows staged in LDS: K % 64 == 0 and

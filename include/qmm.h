@@ -101,9 +101,9 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
  *           Q2_K and Q4_0 need the repacked layout, Q4_0 also K % 256 == 0)
  * SKINNY and MFMA address the weight and activation matrices with 32-bit
  * offsets, so both must be below 4 GiB.  AUTO follows measured crossovers:
- * for Q4_K it takes GEMV for M = 1 and for M = 2 with N < 8192, SKINNY for
- * the other M <= 32 and while ceil(M/32)*N <= 9*8192, MFMA above (GEMV in
- * groups of 8 rows where the size limit rules the MFMA kernels out); for Q4_0 it takes GEMV for M = 1, for
+ * for Q4_K it takes GEMV for M = 1, SKINNY for the other M <= 32 and while
+ * ceil(M/32)*N <= 9*8192, MFMA above (GEMV in groups of 8 rows where the
+ * size limit rules the MFMA kernels out); for Q4_0 it takes GEMV for M = 1, for
  * M <= 4 or M*N <= 36864 when K % 64 == 0 and M*K*5/4 <= 61440 (the rows fit
  * the GEMV's LDS staging) and for M = 2 with N < 8192, SKINNY while
  * ceil(M/32)*N <= 16*8192, MFMA above, GEMV where the MFMA kernels are ruled

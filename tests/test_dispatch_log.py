@@ -44,7 +44,7 @@ CASES = [
     # M = 32 and while ceil(M/32)*N <= 9*8192; GEMM above
     ("q4_K", 1, 1, 4096, 4096, "GEMV"),
     ("q4_K", 0, 1, 4096, 4096, "GEMV"),
-    ("q4_K", 1, 2, 4096, 4096, "GEMV"),
+    ("q4_K", 1, 2, 4096, 4096, "SKINNY"),
     ("q4_K", 1, 2, 8192, 8192, "SKINNY"),
     ("q4_K", 1, 4, 8192, 8192, "SKINNY"),
     ("q4_K", 1, 32, 28672, 8192, "SKINNY"),

@@ -85,7 +85,7 @@ def _window_weights(N, K, rng, dmin_one=True, smax=3, qmax=15, mmax=7):
 @pytest.mark.parametrize("algo,M,N,K", [("gemv", 1, 70, 1024), ("gemv", 8, 33, 2048),
                                         ("mfma", 1, 130, 512), ("mfma", 40, 257, 1024),
                                         ("mfma", 129, 64, 2048), ("skinny", 2, 70, 1024),
-                                        ("skinny", 32, 33, 4608)])
+                                        ("skinny", 16, 8230, 512), ("skinny", 32, 33, 4608)])
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_exactness_window_q4_K(algo, M, N, K, layout):
     rng = np.random.default_rng(M * 7 + N)
@@ -146,7 +146,7 @@ def test_special_scale_cases():
     y = oracle.quantize("q8_K", activations(78, M, K))
     want, terms = full_reference("q4_K", w, y, M, N, K)
     yd = to_dev(y.reshape(-1))
-    for algo, mm in (("gemv", 8), ("mfma", M), ("skinny", 32)):
+    for algo, mm in (("gemv", 8), ("mfma", M), ("skinny", 16), ("skinny", 32)):
         got = to_host(qmm.mul_mat_q4_K(to_dev(w.reshape(-1)), yd, mm, N, K, algo=algo))
         assert_close(got, want[:mm], terms[:mm], f"special {algo}")
 
@@ -178,12 +178,13 @@ def test_mfma_q4_K(M, N, K, layout):
 @pytest.mark.parametrize("M,N,K", [(2, 1, 256), (2, 33, 512), (3, 100, 2304), (5, 64, 4096),
                                    (8, 257, 6144), (9, 40, 1536), (16, 64, 2560), (17, 45, 1024),
                                    (32, 96, 3840), (1, 70, 2048), (40, 50, 1024), (65, 33, 512),
-                                   (97, 70, 2304)])
+                                   (97, 70, 2304), (4, 8200, 768), (13, 8192, 512), (16, 9000, 1280)])
 def test_skinny_q4_K(M, N, K, layout):
-    """Small-batch MFMA path: ragged N, K splits of 1..3 super-blocks per
-    wavefront (odd and even counts, wavefronts without work), 8, 16 and 32
-    staged activation rows, and several 32-row chunks (grid.y) with a ragged
-    last chunk."""
+    """Small-batch MFMA paths: ragged N, K splits of 1..3 super-blocks per
+    wavefront (odd and even counts, wavefronts without work); up to 16 rows
+    the 16 x 16-tile kernel (8 wavefronts per 16 columns below N = 8192),
+    above it the 32 x 32 kernel with 8, 16 and 32 staged activation rows and
+    several 32-row chunks (grid.y) with a ragged last chunk."""
     w, x, y, _ = _case("q4_K", M, N, K, 7 * M + N)
     want, terms = full_reference("q4_K", w, y, M, N, K)
     wd = upload_weights("q4_K", w, N, K, layout)
@@ -208,9 +209,9 @@ def test_q4_0(M, N, K, layout):
 
 
 def test_auto_dispatch_and_overwrite():
-    """AUTO picks the GEMV for M = 1 and for M = 2 below 8192 columns, the
-    small-batch kernel up to M = 32 and while ceil(M/32)*N <= 9*8192, the GEMM
-    above, and is bit-identical to that path; `out` is overwritten."""
+    """AUTO picks the GEMV for M = 1, the small-batch kernels up to M = 32
+    and while ceil(M/32)*N <= 9*8192, the GEMM above, and is bit-identical to
+    that path; `out` is overwritten."""
     import torch
     K = 512
     for M, N in ((1, 64), (2, 64), (2, 8192), (8, 64), (9, 64), (32, 64), (33, 64), (100, 64), (33, 40000)):
@@ -220,7 +221,7 @@ def test_auto_dispatch_and_overwrite():
         out = torch.full((M, N), 1e9, device="cuda")
         qmm.mul_mat_q4_K(wd, yd, M, N, K, out=out)
         assert_close(to_host(out), want, terms, f"auto M={M} N={N}")
-        algo = ("gemv" if M == 1 or (M == 2 and N < 8192) else
+        algo = ("gemv" if M == 1 else
                 "skinny" if M <= 32 or (M + 31) // 32 * N <= 9 * 8192 else "mfma")
         ref = to_host(qmm.mul_mat_q4_K(wd, yd, M, N, K, algo=algo))
         assert np.array_equal(to_host(out).view(np.uint32), ref.view(np.uint32)), (M, N, algo)
