@@ -112,6 +112,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
     // last valid one (their results are never stored), so every load is in
     // bounds and none is predicated.
     const int m_last = GROUPED ? m_last_g : (int)(M - 1 - m_base < BM - 1 ? M - 1 - m_base : BM - 1);
+    const int mt_used = m_last / 32 + 1;  // 32-row tiles holding valid rows
     const int n_last = (int)(N - 1 - n_base < BN - 1 ? N - 1 - n_base : BN - 1);
     const uint32_t a_rowstride = (uint32_t)(nb * kQ8_KBytes);
     const int64_t a_first = m_base * nb * kQ8_KBytes;
@@ -266,6 +267,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
         };
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
+            // row tiles past the last valid row (a short tail tile, or an
+            // expert's remainder rows under mul_mat_id) are skipped; row tile 0
+            // always runs (it builds the planes and requests the next weights)
+            if (i > 0 && i >= mt_used) continue;  // wavefront-uniform
             const int row = i * 32 + l32;
             const v16i zero = {};
             v16i ah, al;
@@ -296,7 +301,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) s_prev[r] = (ah[r] << 3) + al[r];
         }
-        tail(MT - 1, s_prev, bs_prev);
+        // the tail of the last row tile run
+        if (mt_used == MT) tail(MT - 1, s_prev, bs_prev);
+#pragma unroll
+        for (int i = 0; i < MT - 1; ++i)
+            if (mt_used == i + 1) tail(i, s_prev, bs_prev);
     }
 
     // ---- store: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
