@@ -360,8 +360,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
     const Q4KAddr<REPACKED> A{W, N, nb};
     const bool store_q = blockIdx.x == 0;
 
-    // one 256-value block per wavefront and step: quantize, write LDS (+ Yq);
-    // an invalid block (b >= nb) is quantized too and stored to the trash slot
+    // one 256-value block per wavefront and step: quantize, write LDS; an
+    // invalid block (b >= nb) is quantized too and stored to the trash slot
     auto quantize_block = [&](const float4 v, int b) {
         const bool valid = b < nb;
         const Q8KLane r = q8K_quantize_lane(v);
@@ -371,12 +371,6 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
             *reinterpret_cast<int16_t *>(valid ? reinterpret_cast<uint8_t *>(s_bs + 16 * b + (lane >> 2))
                                                : s_trash) = (int16_t)r.bsum;
         if (lane == 0) *reinterpret_cast<float *>(valid ? reinterpret_cast<uint8_t *>(s_d + b) : s_trash) = r.d;
-        if (store_q && valid) {
-            uint8_t *o = Yq + (int64_t)b * kQ8_KBytes;
-            *reinterpret_cast<uint32_t *>(o + 4 + 4 * lane) = packed;
-            if ((lane & 3) == 0) *reinterpret_cast<int16_t *>(o + 260 + 2 * (lane >> 2)) = (int16_t)r.bsum;
-            if (lane == 0) *reinterpret_cast<float *>(o) = r.d;
-        }
     };
 
     // the launcher guarantees nb <= 16 * kXB; block indices past the row end
@@ -426,6 +420,18 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
         for (row += stride; row < N; row += stride) {
             gemv1_load<REPACKED, kNit>(A, row, 0, nchunk, lane, hw, pw);
             finish(row, gemv1_accumulate<kNit>(hw, pw, 0, nchunk, lane, s_qs, s_bs, s_d, 0.0f));
+        }
+    }
+    // Workgroup 0 copies the Q8_K row to Yq last: stores issued before the
+    // row loop would sit in the same in-order counter as the weight loads and
+    // make the first reduction wait for all of them.
+    if (store_q) {
+        for (int i = tid; i < nb * (kQ8_KBytes / 4); i += kFusedWaves * 64) {
+            const int b = i / (kQ8_KBytes / 4), w = i - b * (kQ8_KBytes / 4);  // dword w of block b
+            const uint32_t v = w == 0 ? __float_as_uint(s_d[b])
+                             : w <= QK_K / 4 ? *reinterpret_cast<const uint32_t *>(s_qs + b * QK_K + 4 * (w - 1))
+                                             : *reinterpret_cast<const uint32_t *>(s_bs + 16 * b + 2 * (w - 1 - QK_K / 4));
+            *reinterpret_cast<uint32_t *>(Yq + (int64_t)b * kQ8_KBytes + 4 * w) = v;
         }
     }
 }
@@ -766,7 +772,7 @@ hipError_t launch_gemv_id_q4_K(const uint8_t *w, bool repacked, int64_t w_stride
 int64_t gemv1_fused_max_k() {
     // rows of up to four 16-byte pieces per lane (K <= 8192).  Eight pieces
     // (K <= 16384) fit in the registers too, but measured no faster than the
-    // two launches at N = 4096, K = 14336 (11.4 us either way)
+    // two launches at N = 4096, K = 14336 (10.3 us either way, eager)
     return 4 * 64 / 8 * QK_K;
 }
 
