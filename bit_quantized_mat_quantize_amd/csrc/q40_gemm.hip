@@ -27,10 +27,15 @@
 // but the codes of every other block sit at a 2-byte offset, so the tile is
 // staged through registers: each thread loads one block pair (68 bytes, four
 // dwordx4 + one dword, one step ahead), realigns the first block's codes with
-// v_alignbyte, and writes codes and d_a to LDS (double-buffered; code rows
-// padded to 272 bytes, an odd number of 16-byte slots, so the 8, 16 or 32
-// lanes serviced together reading one piece of consecutive rows hit distinct
-// banks; d_a row-major so that a row's eight blocks are one 16-byte read).  Weights: each wavefront moves its 32 columns' step
+// v_alignbyte, and writes codes and d_a to LDS (double-buffered; d_a
+// row-major so that a row's eight blocks are one 16-byte read).  Code rows
+// are padded to 272 bytes, an odd number of 16-byte slots, so the lanes
+// reading one piece of consecutive rows hit distinct banks.  Within a row,
+// piece k (16 bytes) of block pair p sits at slot 8*(k/2) + 2p + k%2: a
+// 16-byte store serves 8 lanes together (two rows, four pairs, one piece k),
+// and their slots are then the four even and the four odd ones modulo 8 --
+// with pairs at 64-byte strides, pairs 0 and 2 of a row would share banks.
+// Weights: each wavefront moves its 32 columns' step
 // (eight 16-byte payloads and 16 bytes of fp16 d per column) with direct
 // global->LDS loads into its own region of the next buffer, one step ahead;
 // piece c of column col sits at slot c ^ (col & 7) ^ ((col >> 3) & 3) of the
@@ -150,11 +155,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
         uint32_t c0[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) c0[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], 2);
-        uint4 *arow_p = reinterpret_cast<uint4 *>(buf + A_OFF + s_row * A_ROW + 64 * s_pair);
+        uint4 *arow_p = reinterpret_cast<uint4 *>(buf + A_OFF + s_row * A_ROW + 32 * s_pair);
         arow_p[0] = make_uint4(c0[0], c0[1], c0[2], c0[3]);
         arow_p[1] = make_uint4(c0[4], c0[5], c0[6], c0[7]);
-        arow_p[2] = make_uint4(w[9], w[10], w[11], w[12]);
-        arow_p[3] = make_uint4(w[13], w[14], w[15], w[16]);
+        arow_p[8] = make_uint4(w[9], w[10], w[11], w[12]);
+        arow_p[9] = make_uint4(w[13], w[14], w[15], w[16]);
         // d_a of blocks 2 s_pair and 2 s_pair + 1 of row s_row: adjacent halves
         *reinterpret_cast<uint32_t *>(buf + DA_OFF + s_row * 16 + 4 * s_pair) = (w[0] & 0xffffu) | (w[8] & 0xffff0000u);
     };
@@ -206,7 +211,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_0(const uint8_t *__restrict
         uint4 av[2], pv[2];
         auto read_a = [&](int t) {
             const int c = t >> 2, row = (t & 3) * 32 + l32;
-            av[t & 1] = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * A_ROW + 16 * (2 * c + hh));
+            av[t & 1] = *reinterpret_cast<const uint4 *>(buf + A_OFF + row * A_ROW + 128 * (c & 1) + 32 * (c >> 1) +
+                                                         16 * hh);
         };
         auto read_w = [&](int c) {
             pv[c & 1] = *reinterpret_cast<const uint4 *>(buf + wp_lane + 16 * (c ^ wsw));
