@@ -332,9 +332,9 @@ __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ 
 // Quantization costs vector-ALU work that every workgroup repeats, so the
 // grid holds one 16-wavefront workgroup per CU and each workgroup loops over
 // rows (wavefront w of workgroup g takes rows g*16 + w, then + 16*gridDim.x,
-// ...).  A wavefront first issues the fp32 loads of up to kXB of its
-// activation blocks (b = wave + 16i) and the loads of its first row, then
-// quantizes while the weights are in flight; in the row loop the next row's
+// ...).  A wavefront first loads up to kXB of its fp32 activation blocks
+// (b = wave + 16i), then issues the loads of its first row and quantizes
+// while the weights are in flight; in the row loop the next row's
 // pieces are loaded before the current row is reduced when the row takes at
 // most two pieces per lane (longer rows load it right after).  Rows are one
 // pass: K <= 8192, at most four pieces per lane.  Workgroup 0 also stores
@@ -382,13 +382,20 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
         const int b = b0 < nb ? b0 : (int)nb - 1;
         xv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane);
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
+    // With at most two rows per wavefront the activation loads complete before
+    // any weight load is issued: queued behind the weight stream of the whole
+    // chip they would arrive late, and the quantization, the barrier and every
+    // reduction would wait for them (measured: N = K = 4096 4.2 against
+    // 4.7 us; N = 4096, K = 8192 6.3 against 6.8 us).  With more rows the
+    // first rows' weights are better requested at once (N = 28672, K = 4096:
+    // 13.5 against 13.8 us).
+    if (N <= 2 * stride) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // uniform
+    __builtin_amdgcn_sched_barrier(0);
     uint4 pw[kNit], hw[gemv1_subs<kNit>()];
     // a wavefront without rows loads a valid row and stores nothing
     gemv1_load<REPACKED, kNit>(A, row < N ? row : N - 1, 0, nchunk, lane, hw, pw);
     // and every weight load ahead of the quantization: left to itself the
-    // scheduler issues part of them after the first block's reduction, which
-    // waits for its x load, so that part of the stream starts one round trip late
+    // scheduler issues part of them after the first block's arithmetic
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kXB; ++i) quantize_block(xv[i], wave + kFusedWaves * i);

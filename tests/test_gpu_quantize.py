@@ -10,8 +10,9 @@ from gpu_helpers import to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def _special_rows(K, rng):
-    """Rows that exercise the rounding and clamping decisions."""
+def _special_rows(K, rng, scale_edges=False):
+    """Rows that exercise the rounding and clamping decisions (with
+    scale_edges, also subnormal and near-overflow activation scales)."""
     rows = []
     z = np.zeros(K, np.float32)
     rows.append(z)                                       # all-zero blocks
@@ -25,6 +26,12 @@ def _special_rows(K, rng):
     rows.append(np.full(K, -3.0, np.float32))            # constant negative blocks
     rows.append((rng.standard_normal(K) * 1e-30).astype(np.float32))   # tiny scales
     rows.append((rng.standard_normal(K) * 1e30).astype(np.float32))    # huge scales
+    if scale_edges:
+        rows.append((rng.standard_normal(K) * 3e-37).astype(np.float32))   # subnormal d, finite 1/d
+        sub = (rng.uniform(-1.0, 1.0, K) * 1.1e-38).astype(np.float32)      # subnormal inputs ...
+        sub[::32] = 1.4e-36                                                  # ... with a normal max per block
+        rows.append(sub)
+        rows.append((rng.standard_normal(K) * 3e38).clip(-3.4e38, 3.4e38).astype(np.float32))  # near FLT_MAX
     sp = np.zeros(K, np.float32)
     sp[rng.choice(K, K // 50, replace=False)] = rng.standard_normal(K // 50).astype(np.float32)
     rows.append(sp)                                      # sparse
@@ -37,7 +44,8 @@ def _special_rows(K, rng):
 def test_quantize_row_q8_bit_exact(fmt, K, M):
     x = activations([200, M, K], M, K, outlier_frac=0.01)
     if M == 37:
-        x = np.concatenate([x[:-6], _special_rows(K, np.random.default_rng(M))])
+        sp = _special_rows(K, np.random.default_rng(M), scale_edges=True)
+        x = np.concatenate([x[:M - sp.shape[0]], sp])
     want = oracle.quantize(fmt, x)
     got = to_host(qmm.quantize_row_q8(to_dev(x), fmt))
     assert got.size == want.size
