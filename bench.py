@@ -275,6 +275,7 @@ KERNEL_SOURCES = {  # the files that define each kernel the counters were taken 
     "k_gemv_q4_0": ("gemv.hip", "qmm_device.h"),
     "k_skinny_q4_K": ("skinny.hip", "mfma_common.h", "qmm_device.h"),
     "k_skinny16_q4_K": ("skinny16.hip", "mfma_common.h", "qmm_device.h"),
+    "k_skinny16r_q4_K": ("skinny16r.hip", "mfma_common.h", "qmm_device.h"),
     "k_gemm_q4_K": ("gemm.hip", "mfma_common.h", "qmm_device.h"),
 }
 
@@ -308,7 +309,7 @@ def profiled_traffic(kernel: str, workload: str):
     return None
 
 
-def kernel_of(key: str, call_name: str, fused: bool) -> str:
+def kernel_of(key: str, call_name: str, fused: bool, layout: str = "repacked") -> str:
     """The kernel the automatic dispatch runs for a measured call (the AUTO
     rules for these shapes are pinned by tests/test_dispatch_log.py)."""
     wfmt = call_name.split()[2]
@@ -319,6 +320,8 @@ def kernel_of(key: str, call_name: str, fused: bool) -> str:
     if wfmt == "q4_K":
         if M == 1:
             return "k_gemv1_fused_q4_K" if fused and K <= 8192 else "k_gemv1_q4_K"
+        if M <= 8 and layout == "repacked":
+            return "k_skinny16r_q4_K"
         return "k_skinny16_q4_K" if M <= 16 else ("k_skinny_q4_K" if M <= 32 else "k_gemm_q4_K")
     fam = {"q6_K": "q6_K", "q2_K": "q2_K"}[wfmt]
     return f"k_gemv_{fam}" if M == 1 else (f"k_skinny_{fam}" if M <= 32 else f"k_gemm_{fam}")
@@ -352,7 +355,7 @@ def measure_config(key: str, layout: str, steps: int, forms=(False, True), probe
     res["best"] = best
     r = res[best]
     dom = max(r["calls"], key=lambda c: (c["bytes"], c["ops"]))
-    kern = kernel_of(key, dom["call"], best == "fused")
+    kern = kernel_of(key, dom["call"], best == "fused", layout)
     prefill = res["M"] > 32
     if prefill:
         achieved = dom["ops"] / (dom["us"] * 1e-6) / 1e12

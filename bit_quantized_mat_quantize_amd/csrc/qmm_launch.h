@@ -59,6 +59,12 @@ hipError_t launch_skinny_q4_K(const uint8_t *w, bool repacked, const uint8_t *y,
 // The same on 16 x 16 MFMA tiles (workgroups of 16 rows and 16 or 32
 // columns): M <= skinny16_max_m(), matrices below 4 GiB.
 int64_t skinny16_max_m();
+// compute units of the current device (queried once per device)
+int cu_count();
+// Q4_K small batch, repacked layout, 1 <= M <= 8 (skinny16r.hip): producer
+// wavefront streaming through an LDS ring, four consumer wavefronts.
+hipError_t launch_skinny16r_q4_K(const uint8_t *w, const uint8_t *y, float *out, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t s);
 hipError_t launch_skinny16_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                                 int64_t M, int64_t N, int64_t K, hipStream_t s);
 // Q4_0 small batch: repacked layout, K % 256 == 0, M <= skinny_q4_0_max_m(),
