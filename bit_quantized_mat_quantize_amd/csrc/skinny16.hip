@@ -247,7 +247,7 @@ int64_t skinny16_max_m() { return S16_MAX_M; }
 hipError_t launch_skinny16_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                                 int64_t M, int64_t N, int64_t K, hipStream_t s) {
     // Up to 8 rows of the repacked layout the producer/consumer kernel of
-    // skinny16r.hip streams the weights faster (N = K = 8192: 11.8 / 12.1
+    // skinny16r.hip streams the weights faster (N = K = 8192: 11.6 / 12.1
     // against 14.0 / 14.2 us at M = 4 / 8; 5-25% on the other shapes).
     if (repacked && M <= 8) return launch_skinny16r_q4_K(w, y, out, M, N, K, s);
     // Below 8192 columns (fewer than 256 tiles of 32) 8 wavefronts per

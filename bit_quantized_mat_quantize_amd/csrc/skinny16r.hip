@@ -37,7 +37,9 @@
 // Ring slot (16 columns, super-blocks 4S .. 4S + 3, 4*RG activation rows;
 // every region a whole number of 64-lane load instructions):
 //   HDR  1 KB      header of super-block l / 16, column l % 16 at 16 l
-//   PAY  8 KB      super-block b, payload piece p of column c at 16 (128 b + 16 p + c)
+//   PAY  8 KB      super-block b, payload piece p of column c at 16 (128 b + 8 c + (p ^ (c & 7)))
+//                  (each load instruction fetches eight whole 128-byte payloads; the
+//                  XOR spreads the reads down 8 columns over distinct banks)
 //   ACT  4 KB x RG row group g, super-block b, row r: code piece q at
 //                  4096 g + 1024 b + 16 (16 (r & 3) + (q ^ r))   (XOR: rows read
 //                  down 16 lanes hit distinct banks)
@@ -124,9 +126,11 @@ __global__ __launch_bounds__(kRingThreads, 1) void k_skinny16r_q4_K(const uint8_
             const rsrc_t ra = make_rsrc(Y, y_bytes);
             dma16(rw, (uint32_t)(16 * (col * nb + clamp_b(4 * S + g))), 0, base + RS::HDR);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {  // super-block k / 2, pieces 4 (k % 2) .. + 3
-                const int p = 4 * (k & 1) + (lane >> 4);
-                dma16(rw, (uint32_t)(16 * N * nb + 128 * (col * nb + clamp_b(4 * S + (k >> 1))) + 16 * p), 0,
+            for (int k = 0; k < 8; ++k) {  // super-block k / 2, columns 8 (k % 2) .. + 7
+                const int cc = 8 * (k & 1) + (lane >> 3);
+                const int64_t ck = n_base + cc < N ? n_base + cc : N - 1;
+                const int p = (lane & 7) ^ (cc & 7);  // the piece stored at position lane
+                dma16(rw, (uint32_t)(16 * N * nb + 128 * (ck * nb + clamp_b(4 * S + (k >> 1))) + 16 * p), 0,
                       base + RS::PAY + 1024 * k);
             }
 #pragma unroll
@@ -164,8 +168,9 @@ __global__ __launch_bounds__(kRingThreads, 1) void k_skinny16r_q4_K(const uint8_
             if (4 * S + c < nb) {  // wavefront-uniform
                 const uint8_t *base = lds + (S % RS::R) * RS::STAGE;
                 const uint4 hd = *reinterpret_cast<const uint4 *>(base + RS::HDR + 16 * (16 * c + l16));
-                const uint4 p0 = *reinterpret_cast<const uint4 *>(base + RS::PAY + 16 * (128 * c + 32 * h + l16));
-                const uint4 p1 = *reinterpret_cast<const uint4 *>(base + RS::PAY + 16 * (128 * c + 32 * h + 16 + l16));
+                const int pb = RS::PAY + 16 * (128 * c + 8 * l16);
+                const uint4 p0 = *reinterpret_cast<const uint4 *>(base + pb + 16 * ((2 * h) ^ (l16 & 7)));
+                const uint4 p1 = *reinterpret_cast<const uint4 *>(base + pb + 16 * ((2 * h + 1) ^ (l16 & 7)));
                 const uint8_t *arow = base + RS::ACT + 4096 * (rr >> 2) + 1024 * c + 256 * (rr & 3);
                 uint4 av[4];
 #pragma unroll
