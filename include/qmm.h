@@ -96,7 +96,9 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
  *   SKINNY  small-batch int8 MFMA, one 32-column x 32-row tile per workgroup,
  *           K split over its wavefronts (Q4_K; Q6_K and Q2_K in the repacked
  *           layout; Q4_0 in the repacked layout with K % 256 == 0;
- *           M <= 65535*32)
+ *           M <= 65535*32).  For Q4_K up to 16 rows the tiles are 16 x 16,
+ *           and up to 8 rows of the repacked layout one wavefront per
+ *           workgroup streams the weights into LDS for four that compute
  *   MFMA    prefill GEMM on int8 MFMA, 128 x 256 output tiles (any M; Q6_K,
  *           Q2_K and Q4_0 need the repacked layout, Q4_0 also K % 256 == 0)
  * SKINNY and MFMA address the weight and activation matrices with 32-bit
