@@ -206,14 +206,18 @@ __global__ __launch_bounds__(256) void k_gemv_q2_K(const uint8_t *__restrict__ W
     const int nunits = (int)(4 * nb);
     const Q2KAddr<REPACKED> A{W, N * nb, REPACKED ? (4 * N * nb + 255) / 256 * 256 : 0};
 
-    // this row's first units: issue the weight loads, then stage the activations
+    // the activation row's first pieces, then this row's first units, then
+    // the activations into LDS (the wait before the stores covers only them)
+    const uint8_t *yrow = Y + m * nb * kQ8_KBytes;
+    const Q8KRowHead yh = load_q8k_row_head(yrow, K);
+    __builtin_amdgcn_sched_barrier(0);
     Q2KUnit x[kNit];
 #pragma unroll
     for (int it = 0; it < kNit; ++it) {
         const int u = lane + 64 * it;
         q2k_load<REPACKED>(A, nn, nb, u < nunits ? u : nunits - 1, x[it]);
     }
-    const Q8KRowLds row = stage_q8k_row<256>(Y + m * nb * kQ8_KBytes, K, ys);
+    const Q8KRowLds row = commit_q8k_row(yh, yrow, K, ys);
 
     float acc = 0.0f;
     for (int base = 0; base < nunits; base += 64 * kNit) {

@@ -317,14 +317,18 @@ __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W
         else q6k_load_half<REPACKED>(A, nn, nb, u, x);
     };
 
-    // this row's first units: issue the weight loads, then stage the activations
+    // the activation row's first pieces, then this row's first units, then
+    // the activations into LDS (the wait before the stores covers only them)
+    const uint8_t *yrow = Y + m * nb * kQ8_KBytes;
+    const Q8KRowHead yh = load_q8k_row_head(yrow, K);
+    __builtin_amdgcn_sched_barrier(0);
     Unit x[kNit];
 #pragma unroll
     for (int it = 0; it < kNit; ++it) {
         const int u = lane + 64 * it;
         load(u < nunits ? u : nunits - 1, x[it]);
     }
-    const Q8KRowLds row = stage_q8k_row<256>(Y + m * nb * kQ8_KBytes, K, ys);
+    const Q8KRowLds row = commit_q8k_row(yh, yrow, K, ys);
     const uint8_t *s_qs = row.qs;
     const float *s_d = row.d;
     const int16_t *s_bs = row.bsums;

@@ -26,6 +26,51 @@ struct Q8KRowLds {
     const int16_t *bsums;
 };
 
+// The first part of a row for 256 threads, held in registers between the
+// two halves of a staging: with these loads issued ahead of a wavefront's
+// weight loads, the wait that precedes the LDS stores covers only them (loads
+// complete in issue order), not the weights as well.
+struct Q8KRowHead {
+    uint4 q;   // code piece tid (16 codes)
+    uint4 bs;  // bsums piece tid (8 sums)
+    float d;   // d of block tid
+};
+__device__ __forceinline__ Q8KRowHead load_q8k_row_head(const uint8_t *__restrict__ Yrow, int64_t K) {
+    const int64_t nb = K / QK_K;
+    const int nq = (int)(K / 16), nbs = (int)(nb * 2);
+    const int tid = threadIdx.x;
+    const int pc = tid < nq ? tid : nq - 1, qb = tid < nbs ? tid : nbs - 1, qd = tid < nb ? tid : (int)nb - 1;
+    Q8KRowHead h;
+    h.q = ld_align4<uint4>(Yrow + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
+    h.bs = ld_align4<uint4>(Yrow + (qb >> 1) * kQ8_KBytes + 260 + 16 * (qb & 1));
+    h.d = ld_align4<float>(Yrow + qd * kQ8_KBytes);
+    return h;
+}
+// Store the head (threads past the row's pieces write the trash slot), stage
+// the rest of the row, then barrier.  256 threads.
+__device__ __forceinline__ Q8KRowLds commit_q8k_row(const Q8KRowHead &h, const uint8_t *__restrict__ Yrow,
+                                                    int64_t K, uint8_t *ys) {
+    const int64_t nb = K / QK_K;
+    const int nq = (int)(K / 16), nbs = (int)(nb * 2);
+    uint8_t *s_qs = ys;
+    uint8_t *s_d = ys + K;
+    uint8_t *s_bs = ys + K + (nb * 4 + 15) / 16 * 16;
+    uint8_t *trash = s_bs + nb * 32;
+    const int tid = threadIdx.x;
+    *reinterpret_cast<uint4 *>(tid < nq ? s_qs + 16 * tid : trash) = h.q;
+    *reinterpret_cast<uint4 *>(tid < nbs ? s_bs + 16 * tid : trash) = h.bs;
+    *reinterpret_cast<float *>(tid < nb ? s_d + 4 * tid : trash) = h.d;
+    for (int pc = tid + 256; pc < nq; pc += 256)
+        *reinterpret_cast<uint4 *>(s_qs + 16 * pc) =
+            ld_align4<uint4>(Yrow + (pc >> 4) * kQ8_KBytes + 4 + 16 * (pc & 15));
+    for (int q = tid + 256; q < nbs; q += 256)
+        *reinterpret_cast<uint4 *>(s_bs + 16 * q) = ld_align4<uint4>(Yrow + (q >> 1) * kQ8_KBytes + 260 + 16 * (q & 1));
+    for (int q = tid + 256; q < nb; q += 256)
+        *reinterpret_cast<float *>(s_d + 4 * q) = ld_align4<float>(Yrow + q * kQ8_KBytes);
+    __syncthreads();
+    return Q8KRowLds{s_qs, reinterpret_cast<const float *>(s_d), reinterpret_cast<const int16_t *>(s_bs)};
+}
+
 // Stage activation row Yrow into ys with `nthreads` threads (branch-free
 // loads, 16 bytes per thread and trip), then barrier.
 template <int kThreads>
