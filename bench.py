@@ -7,7 +7,7 @@ A step is one pass of the hot path over one batch: quantize the fp32
 activations to int8 blocks and multiply them with the packed weights, for every
 projection of the workload.  Two forms are timed for the M = 1 workloads: the
 two-call form (quantize_row_q8, then mul_mat per projection) and the fused form
-(quantize_mul_mat per input; for Q4_K at M = 1 and K <= 8192 the quantization
+(quantize_mul_mat per input; for Q4_K at M = 1 and K <= 16384 the quantization
 runs inside the GEMV launch, and gate||up is one concatenated matrix).  The
 faster form is the workload's figure; the other is reported beside it.
 
@@ -319,7 +319,7 @@ def kernel_of(key: str, call_name: str, fused: bool, layout: str = "repacked") -
         return "k_gemv_q4_0" if M == 1 else ("k_skinny_q4_0" if M <= 32 else "k_gemm_q4_0")
     if wfmt == "q4_K":
         if M == 1:
-            return "k_gemv1_fused_q4_K" if fused and K <= 8192 else "k_gemv1_q4_K"
+            return "k_gemv1_fused_q4_K" if fused and K <= 16384 else "k_gemv1_q4_K"
         if M <= 8 and layout == "repacked":
             return "k_skinny16r_q4_K"
         return "k_skinny16_q4_K" if M <= 16 else ("k_skinny_q4_K" if M <= 32 else "k_gemm_q4_K")
@@ -732,7 +732,7 @@ def main():
             "weight_bytes": head["weight_bytes"], "weight_copies_rotated": head["copies"],
             "rotation_bytes": head["rotation_bytes"],
             "step": ("quantize_mul_mat per input (gate||up concatenated; Q8_K quantization inside the GEMV "
-                     "launch where K <= 8192)" if best == "fused" else "quantize_row_q8 + mul_mat per projection")
+                     "launch where K <= 16384)" if best == "fused" else "quantize_row_q8 + mul_mat per projection")
                     + ", HIP graph replay of exactly `steps` steps",
             "parallelism": "single GPU"}
         line["roofline"] = head["roofline"]

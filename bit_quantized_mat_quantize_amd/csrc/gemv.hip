@@ -165,13 +165,14 @@ constexpr int gemv1_kp() { return kNit >= 2 ? 2 : 1; }
 template <int kNit>
 constexpr int gemv1_subs() { return kNit / gemv1_kp<kNit>(); }
 
-template <bool REPACKED, int kNit>
+// Sub-passes SP0 .. SP1 - 1 only (the fused kernel splits a row's requests).
+template <bool REPACKED, int kNit, int SP0 = 0, int SP1 = gemv1_subs<kNit>()>
 __device__ __forceinline__ void gemv1_load(const Q4KAddr<REPACKED> &A, int64_t nn, int base,
                                            int nchunk, int lane, uint4 (&hw)[gemv1_subs<kNit>()],
                                            uint4 (&pw)[kNit]) {
     constexpr int kP = gemv1_kp<kNit>();
 #pragma unroll
-    for (int sp = 0; sp < gemv1_subs<kNit>(); ++sp) {
+    for (int sp = SP0; sp < SP1; ++sp) {
         const int c0 = base + 64 * kP * sp + kP * lane;
         const int c = c0 < nchunk ? c0 : nchunk - kP;
         const int b = c >> 3, cc = c & 7;
@@ -337,7 +338,14 @@ __global__ __launch_bounds__(256) void k_gemv1_q4_K(const uint8_t *__restrict__ 
 // while the weights are in flight; in the row loop the next row's
 // pieces are loaded before the current row is reduced when the row takes at
 // most two pieces per lane (longer rows load it right after).  Rows are one
-// pass: K <= 8192, at most four pieces per lane.  Workgroup 0 also stores
+// pass: K <= 16384, at most eight pieces per lane.  With eight pieces a
+// wavefront requests only the first two of its four sub-passes before
+// quantizing and the other two after the barrier: the memory pipeline takes
+// requests at the rate it delivers, so a wavefront issuing all twelve loads
+// first reached its quantization, and the whole workgroup its barrier, late,
+// and every row was then reduced at once after the barrier (N = 4096,
+// K = 14336: 9.35 against 10.6 us for this kernel with all requests first, or
+// for the two launches).  Workgroup 0 also stores
 // the Q8_K bytes to Yq, byte-identical to the stand-alone quantizer (same
 // device routine), so another projection of the same input can reuse them.
 // ---------------------------------------------------------------------------
@@ -389,17 +397,26 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
     // 4.7 us; N = 4096, K = 8192 6.3 against 6.8 us).  With more rows the
     // first rows' weights are better requested at once (N = 28672, K = 4096:
     // 13.5 against 13.8 us).
-    if (N <= 2 * stride) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // uniform
+    // Rows of eight pieces issue only part of the row first (below), so there
+    // the x loads need no head start (9.35 against 9.45 us at N = 4096,
+    // K = 14336).
+    if (kNit < 8 && N <= 2 * stride) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // uniform
     __builtin_amdgcn_sched_barrier(0);
     uint4 pw[kNit], hw[gemv1_subs<kNit>()];
+    // sub-passes of the first row requested before quantizing: all, or two of
+    // four for rows of eight pieces (one or three measured slower: 9.7 and
+    // 10.0 us at N = 4096, K = 14336)
+    constexpr int kFirst = kNit >= 8 ? 2 : gemv1_subs<kNit>();
     // a wavefront without rows loads a valid row and stores nothing
-    gemv1_load<REPACKED, kNit>(A, row < N ? row : N - 1, 0, nchunk, lane, hw, pw);
+    gemv1_load<REPACKED, kNit, 0, kFirst>(A, row < N ? row : N - 1, 0, nchunk, lane, hw, pw);
     // and every weight load ahead of the quantization: left to itself the
     // scheduler issues part of them after the first block's arithmetic
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kXB; ++i) quantize_block(xv[i], wave + kFusedWaves * i);
     __syncthreads();
+    // the rest of the first row, requested once the activation row is in LDS
+    gemv1_load<REPACKED, kNit, kFirst>(A, row < N ? row : N - 1, 0, nchunk, lane, hw, pw);
 
     auto finish = [&](int64_t r, float acc) {
         acc = wave_sum(acc);
@@ -777,10 +794,9 @@ hipError_t launch_gemv_id_q4_K(const uint8_t *w, bool repacked, int64_t w_stride
 }
 
 int64_t gemv1_fused_max_k() {
-    // rows of up to four 16-byte pieces per lane (K <= 8192).  Eight pieces
-    // (K <= 16384) fit in the registers too, but measured no faster than the
-    // two launches at N = 4096, K = 14336 (10.3 us either way, eager)
-    return 4 * 64 / 8 * QK_K;
+    // rows of up to eight 16-byte pieces per lane (K <= 16384, 104-117
+    // registers); longer rows take two launches (quantize, then the GEMV)
+    return 8 * 64 / 8 * QK_K;
 }
 
 int cu_count() {
@@ -819,7 +835,8 @@ hipError_t launch_gemv1_fused_q4_K(const uint8_t *w, bool repacked, const float 
     // kXB = activation blocks per wavefront: ceil(nb / 16) (nb <= 8 * kNit <= 16 * kXB)
     if (nit <= 1) QMM_FUSED1(1, 1);
     else if (nit <= 2) QMM_FUSED1(2, 1);
-    else QMM_FUSED1(4, 2);
+    else if (nit <= 4) QMM_FUSED1(4, 2);
+    else QMM_FUSED1(8, 4);
 #undef QMM_FUSED1
     return hipGetLastError();
 }

@@ -6,9 +6,11 @@ Checks, on the same seeded inputs:
 * the fp32 outputs are within 1e-4 * sum_k |w a| of the oracle;
 * the outputs equal, bit for bit, those of quantize_row_q8 followed by
   mul_mat (the same per-row arithmetic in the same order).
-Shapes cover one, two and four pieces per lane, rows looped over by the
-persistent workgroups (N above 16 rows per CU), ragged N tails, the largest K
-of the one-launch kernel and K above it (two-launch path), M > 1 and Q4_0.
+Shapes cover one, two, four and eight pieces per lane (eight: the first row's
+requests split around the quantization), rows looped over by the persistent
+workgroups (N above 16 rows per CU, also with eight pieces), ragged N tails,
+the largest K of the one-launch kernel and K above it (two-launch path),
+M > 1 and Q4_0.
 """
 import numpy as np
 import pytest
@@ -20,7 +22,7 @@ from gpu_helpers import assert_close, full_reference, to_dev, to_host, upload_we
 
 pytestmark = pytest.mark.gpu
 
-FUSED_MAX_K = 8192  # largest K of the one-launch path (four 16-byte pieces per lane)
+FUSED_MAX_K = 16384  # largest K of the one-launch path (eight 16-byte pieces per lane)
 
 
 def _inputs(wfmt, M, N, K, seed):
@@ -63,7 +65,8 @@ def _check(wfmt, M, N, K, layout, seed, sample=None):
 
 @pytest.mark.parametrize("layout", ["canonical", "repacked"])
 @pytest.mark.parametrize("N,K", [(1, 256), (7, 512), (131, 2048), (64, 4096), (77, 8192),
-                                 (45, 14336), (19, 20480), (9000, 1024), (5003, 4096)])
+                                 (45, 14336), (19, 20480), (9000, 1024), (5003, 4096), (4500, 16384),
+                                 (4200, 12288)])
 def test_fused_q4_K_m1(N, K, layout):
     _check("q4_K", 1, N, K, layout, seed=N * 7 + K)
 
