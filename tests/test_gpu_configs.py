@@ -4,7 +4,11 @@ benchmark times (repacked weights, automatic GEMV/MFMA dispatch).
 The weights are encoded on the GPU exactly as the benchmark does it and must be
 byte-identical to the oracle's encoding; activations likewise.  Outputs are
 compared element by element with the oracle for the GEMV workloads and on a
-sample of (m, n) pairs (all tile corners plus random ones) for the prefill GEMM.
+sample of (m, n) pairs for the prefill GEMM: one whole 128 x 256 workgroup
+tile (every lane and result register of all eight wavefronts and four row
+tiles), tile corners and random pairs.  The Q4_K M = 1 workloads also run
+through quantize_mul_mat (the fused form the benchmark times), which must give
+the same Q8_K bytes and the same outputs bit for bit.
 """
 import numpy as np
 import pytest
@@ -29,6 +33,10 @@ def _run_projection(p, full: bool):
     assert np.array_equal(to_host(y_gpu), y_orc.reshape(-1)), f"{p.name}: activation bytes differ"
     wr = qmm.repack_weights(w_gpu, p.wfmt, p.N, p.K)
     got = to_host(qmm.mul_mat(p.wfmt, wr, y_gpu, p.M, p.N, p.K, layout="repacked"))
+    if p.wfmt == "q4_K" and p.M == 1:
+        out_f, y_f = qmm.quantize_mul_mat(p.wfmt, wr, to_dev(x), p.N, layout="repacked")
+        assert np.array_equal(to_host(y_f).reshape(-1), y_orc.reshape(-1)), f"{p.name}: fused Q8_K bytes differ"
+        assert np.array_equal(to_host(out_f).view(np.uint32), got.view(np.uint32)), f"{p.name}: fused != two-call"
     if full:
         want, terms = full_reference(p.wfmt, w_orc, y_orc, p.M, p.N, p.K)
         assert_close(got, want, terms, p.name)
@@ -38,6 +46,12 @@ def _run_projection(p, full: bool):
         ns = [0, p.N - 1] + [127, 128, 129, 255] + list(rng.integers(0, p.N, 2000))
         ms = np.array([m for m in ms if m < p.M][: len(ns)], np.int64)
         ns = np.array(ns[: len(ms)], np.int64)
+        # one whole workgroup tile of the last row tile: rows 128 t .. + 127, columns 256 c .. + 255
+        t, c = (p.M - 1) // 128, int(rng.integers(0, p.N // 256))
+        tm, tn = np.meshgrid(np.arange(128 * t, min(128 * t + 128, p.M)), np.arange(256 * c, 256 * c + 256),
+                             indexing="ij")
+        ms = np.concatenate([ms, tm.ravel()])
+        ns = np.concatenate([ns, tn.ravel()])
         want, terms = oracle.sample(p.wfmt, w_orc, y_orc, p.M, p.N, p.K, ms, ns)
         assert_close(got[ms, ns], want, terms, p.name + " (sampled)")
 
