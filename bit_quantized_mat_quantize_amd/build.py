@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libqmm.so")
 BUILD_DIR = os.path.join(ROOT, "_build_asan" if os.environ.get("QMM_ASAN") else "_build")
-SOURCES = ["api.hip", "quantize.hip", "repack.hip", "gemv.hip", "skinny.hip", "skinny16.hip", "skinny16r.hip", "q6k.hip", "q6k_gemm.hip", "q6k_skinny.hip",
+SOURCES = ["api.hip", "quantize.hip", "repack.hip", "gemv.hip", "skinny.hip", "skinny16.hip", "skinny16r.hip", "skinny32r.hip", "q6k.hip", "q6k_gemm.hip", "q6k_skinny.hip",
            "q2k.hip", "q2k_gemm.hip", "q2k_skinny.hip", "q40_gemm.hip", "q40_skinny.hip", "moe.hip", "gemm.hip"]
 PROBE_SOURCES = ["probe.hip"]
 PROBE_OUT = os.path.join(PKG, "libqmm_probe.so")

@@ -107,7 +107,9 @@ const char *algo_name(qmm_algo a) {
 const char *family_tile(qmm_algo a) {
     switch (a) {
         case QMM_ALGO_GEMV: return "one wavefront per output row, up to 8 activation rows per launch";
-        case QMM_ALGO_SKINNY: return "32 x 32 output tile per workgroup, K split over 8 wavefronts";
+        case QMM_ALGO_SKINNY:
+            return "small-batch MFMA kernel: 16 or 32 columns per workgroup, K split inside the workgroup, "
+                   "weights read once per 32-row chunk";
         case QMM_ALGO_MFMA: return "128 x 256 output tile per workgroup";
         default: return "";
     }
