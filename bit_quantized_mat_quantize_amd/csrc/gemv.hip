@@ -553,6 +553,67 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ W
 // ---------------------------------------------------------------------------
 int64_t gemv_q4_0s_lds_bytes(int64_t M, int64_t K) { return M * (K / QK4_0) * (32 + 4 + 4); }
 
+// Rows of a Q4_0 GEMV against activation rows staged in LDS (codes [M][nb][32],
+// d_a [M][nb] as fp32, code sums [M][nb]): wavefront w of the workgroup takes
+// output row blockIdx.x * 4 + w (the compute half of k_gemv_q4_0s, shared with
+// the fused quantize + GEMV kernel).
+template <int M, bool REPACKED, int MODE>
+__device__ __forceinline__ void gemv_q4_0_lds_rows(const uint8_t *__restrict__ W, void *__restrict__ dst,
+                                                   int64_t N, int64_t nb, int64_t dsec, const uint8_t *s_q,
+                                                   const float *s_d, const int *s_s, bool valid) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (n >= N) return;  // uniform per wavefront; the caller's barrier is behind it
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    for (int64_t b = lane; b < nb; b += kWave) {
+        uint32_t w[4];
+        float dw;
+        if (REPACKED) {
+            const uint4 v = ld16(W + dsec + 16 * (n * nb + b));
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            dw = f16_bits_to_f32(ld_u16(W + 2 * (n * nb + b)));
+        } else {
+            const uint8_t *blk = W + kQ4_0Bytes * (n * nb + b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = ld_u32_a2(blk + 2 + 4 * i);
+            dw = f16_bits_to_f32(ld_u16(blk));
+        }
+        // first read: elements 16*odd .. +15 (nibbles >> 4*odd), second: the other half
+        const int odd = (int)(b & 1), sa = 4 * odd, sb = 4 - sa;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int64_t bi = (int64_t)m * nb + b;
+            const uint8_t *cq = s_q + bi * 32;
+            const uint4 ra = *reinterpret_cast<const uint4 *>(cq + 16 * odd);
+            const uint4 rb = *reinterpret_cast<const uint4 *>(cq + 16 - 16 * odd);
+            const uint32_t ya[4] = {ra.x, ra.y, ra.z, ra.w}, yb[4] = {rb.x, rb.y, rb.z, rb.w};
+            int p = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p = dot4((w[i] >> sa) & 0x0f0f0f0fu, ya[i], p);
+                p = dot4((w[i] >> sb) & 0x0f0f0f0fu, yb[i], p);
+            }
+            p -= 8 * s_s[bi];
+            if (MODE == 0) {
+                acc[m] = fmaf(dw * s_d[bi], (float)p, acc[m]);
+            } else {
+                reinterpret_cast<int32_t *>(dst)[((int64_t)m * N + n) * nb + b] = p;
+            }
+        }
+    }
+    if (MODE == 0) {
+        float *out = reinterpret_cast<float *>(dst);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float v = wave_sum(acc[m]);
+            if (lane == 0) out[(int64_t)m * N + n] = valid ? v : __builtin_nanf("");
+        }
+    }
+}
+
 template <int M, bool REPACKED, int MODE, bool ID = false>
 __global__ __launch_bounds__(256) void k_gemv_q4_0s(const uint8_t *__restrict__ W,
                                                     const uint8_t *__restrict__ Y,
@@ -605,57 +666,57 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0s(const uint8_t *__restrict__ 
         s_s[blk + 1] = s1;
     }
     __syncthreads();
+    gemv_q4_0_lds_rows<M, REPACKED, MODE>(W, dst, N, nb, dsec, s_q, s_d, s_s, valid);
+}
 
-    const int wave = tid >> 6, lane = tid & 63;
-    const int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (n >= N) return;  // uniform per wavefront, after the only barrier
-    float acc[M];
+// ---------------------------------------------------------------------------
+// Fused M = 1 path for Q4_0 on small matrices, where a second launch costs
+// more than the work: every workgroup quantizes the fp32 row into Q8_0 codes
+// in LDS, in the staged layout above, with the stand-alone quantizer's block
+// routine (8 lanes per 32-value block); workgroup 0 also stores the Q8_0
+// bytes to Yq, byte-identical to quantize_row_q8.  Then each wavefront takes
+// one output row (gemv_q4_0_lds_rows): the same integer sums and fp32
+// operations, in the same order, as quantize_row_q8 followed by either Q4_0
+// GEMV.
+// ---------------------------------------------------------------------------
+template <bool REPACKED>
+__global__ __launch_bounds__(256) void k_gemv_fused_q4_0(const uint8_t *__restrict__ W,
+                                                         const float *__restrict__ X, uint8_t *__restrict__ Yq,
+                                                         float *__restrict__ out, int64_t N, int64_t K,
+                                                         int64_t dsec) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t ys[];
+    const int64_t nb = K / QK4_0;
+    uint8_t *s_q = ys;                                   // codes [nb][32]
+    float *s_d = reinterpret_cast<float *>(ys + nb * 32);  // d_a [nb] (the fp16 value)
+    int *s_s = reinterpret_cast<int *>(s_d + nb);         // sum of codes [nb]
+    const int tid = threadIdx.x, sub = tid & 7;
+    for (int64_t base = 0; base < nb; base += 32) {  // 32 blocks per pass, every lane in each pass
+        const int64_t blk = base + (tid >> 3);
+        const bool live = blk < nb;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live) v = *reinterpret_cast<const float4 *>(X + blk * QK4_0 + sub * 4);
+        const Q80Part r = q8_0_quantize_part(v);
+        int cs = dot4(0x01010101u, r.q, 0);  // the block's code sum over its 8 lanes
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-    for (int64_t b = lane; b < nb; b += kWave) {
-        uint32_t w[4];
-        float dw;
-        if (REPACKED) {
-            const uint4 v = ld16(W + dsec + 16 * (n * nb + b));
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-            dw = f16_bits_to_f32(ld_u16(W + 2 * (n * nb + b)));
-        } else {
-            const uint8_t *blk = W + kQ4_0Bytes * (n * nb + b);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = ld_u32_a2(blk + 2 + 4 * i);
-            dw = f16_bits_to_f32(ld_u16(blk));
-        }
-        // first read: elements 16*odd .. +15 (nibbles >> 4*odd), second: the other half
-        const int odd = (int)(b & 1), sa = 4 * odd, sb = 4 - sa;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const int64_t bi = (int64_t)m * nb + b;
-            const uint8_t *cq = s_q + bi * 32;
-            const uint4 ra = *reinterpret_cast<const uint4 *>(cq + 16 * odd);
-            const uint4 rb = *reinterpret_cast<const uint4 *>(cq + 16 - 16 * odd);
-            const uint32_t ya[4] = {ra.x, ra.y, ra.z, ra.w}, yb[4] = {rb.x, rb.y, rb.z, rb.w};
-            int p = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p = dot4((w[i] >> sa) & 0x0f0f0f0fu, ya[i], p);
-                p = dot4((w[i] >> sb) & 0x0f0f0f0fu, yb[i], p);
+        for (int o = 4; o > 0; o >>= 1) cs += __shfl_xor(cs, o, kWave);
+        if (live) {
+            const uint32_t d16 = f32_to_f16_bits(r.d);
+            *reinterpret_cast<uint32_t *>(s_q + blk * 32 + 4 * sub) = r.q;
+            if (sub == 0) {
+                s_d[blk] = f16_bits_to_f32(d16);
+                s_s[blk] = cs;
             }
-            p -= 8 * s_s[bi];
-            if (MODE == 0) {
-                acc[m] = fmaf(dw * s_d[bi], (float)p, acc[m]);
-            } else {
-                reinterpret_cast<int32_t *>(dst)[((int64_t)m * N + n) * nb + b] = p;
+            if (blockIdx.x == 0) {
+                uint8_t *o = Yq + blk * kQ8_0Bytes;
+                uint16_t *o16 = reinterpret_cast<uint16_t *>(o + 2 + sub * 4);
+                o16[0] = (uint16_t)(r.q & 0xffff);
+                o16[1] = (uint16_t)(r.q >> 16);
+                if (sub == 0) *reinterpret_cast<uint16_t *>(o) = (uint16_t)d16;
             }
         }
     }
-    if (MODE == 0) {
-        float *out = reinterpret_cast<float *>(dst);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float v = wave_sum(acc[m]);
-            if (lane == 0) out[(int64_t)m * N + n] = valid ? v : __builtin_nanf("");
-        }
-    }
+    __syncthreads();
+    gemv_q4_0_lds_rows<1, REPACKED, 0>(W, out, N, nb, dsec, s_q, s_d, s_s, true);
 }
 
 template <int MODE>
@@ -856,6 +917,25 @@ hipError_t launch_block_sums_q4_K(const uint8_t *w, bool repacked, const uint8_t
 hipError_t launch_gemv_q4_0(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                             int64_t M, int64_t N, int64_t K, hipStream_t s) {
     return dispatch_q4_0<0>(w, repacked, y, out, M, N, K, s);
+}
+
+bool gemv_fused_q4_0_ok(int64_t N, int64_t K) {
+    // small matrices only: each of the N/4 workgroups repeats the quantization
+    constexpr int64_t kFusedQ40MaxK = 16384, kFusedQ40MaxNK = int64_t(1) << 22;
+    return K % 64 == 0 && K <= kFusedQ40MaxK && N * K <= kFusedQ40MaxNK;
+}
+
+hipError_t launch_gemv_fused_q4_0(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
+                                  int64_t N, int64_t K, hipStream_t s) {
+    if (!gemv_fused_q4_0_ok(N, K)) return hipErrorInvalidValue;
+    const int64_t dsec = repacked_bytes_q4_0(N, K) - 16 * N * (K / QK4_0);
+    const dim3 grid((unsigned)((N + kWavesPerBlock - 1) / kWavesPerBlock));
+    const unsigned lds = (unsigned)gemv_q4_0s_lds_bytes(1, K);
+    if (repacked)
+        hipLaunchKernelGGL((k_gemv_fused_q4_0<true>), grid, dim3(256), lds, s, w, x, yq, out, N, K, dsec);
+    else
+        hipLaunchKernelGGL((k_gemv_fused_q4_0<false>), grid, dim3(256), lds, s, w, x, yq, out, N, K, dsec);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_id_q4_0(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,

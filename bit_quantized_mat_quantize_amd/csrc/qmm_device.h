@@ -137,6 +137,28 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xff) << 24);
 }
 
+// ---- Q8_0 quantization of one 32-value block held by 8 consecutive lanes,
+// four consecutive values per lane (lane 8k + s holds elements 4s .. 4s + 3):
+// amax over the 8 lanes, d = amax/127, id = d ? 1/d : 0, q = rint(x*id)
+// clamped to [-127, 127] (ggml-cpu mul_mat page, "最基础的两块:Q4_0 与 Q8_0").
+// Every lane of the wavefront must call it (the lanes exchange their maxima);
+// d is returned in fp32, the block stores it as fp16.
+struct Q80Part {
+    uint32_t q;  // this lane's four codes, packed
+    float d;
+};
+__device__ __forceinline__ Q80Part q8_0_quantize_part(const float4 v) {
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int o = 4; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+    Q80Part r;
+    r.d = a / 127.0f;
+    const float id = r.d != 0.0f ? 1.0f / r.d : 0.0f;
+    r.q = pack4_i8(clamp127((int)rintf(v.x * id)), clamp127((int)rintf(v.y * id)),
+                   clamp127((int)rintf(v.z * id)), clamp127((int)rintf(v.w * id)));
+    return r;
+}
+
 // ---- mul_mat_id routing for the per-pair GEMVs: blockIdx.y is the (token,
 // slot) pair p0 + y; its expert id selects the weight matrix, its token (or the
 // pair itself) the activation row, and the pair the output row.  An id outside

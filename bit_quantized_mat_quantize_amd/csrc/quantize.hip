@@ -50,22 +50,13 @@ __global__ __launch_bounds__(256) void k_quantize_q8_0(const float *__restrict__
     const int64_t row = bb / nb_row, b = bb - row * nb_row;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live) v = *reinterpret_cast<const float4 *>(x + row * K + b * QK4_0 + sub * 4);
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-    for (int o = 4; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+    const Q80Part r = q8_0_quantize_part(v);  // all lanes: they exchange their maxima
     if (!live) return;
-    const float d = a / 127.0f;
-    const float id = d != 0.0f ? 1.0f / d : 0.0f;
-    const int q0 = clampi((int)rintf(v.x * id), -127, 127);
-    const int q1 = clampi((int)rintf(v.y * id), -127, 127);
-    const int q2 = clampi((int)rintf(v.z * id), -127, 127);
-    const int q3 = clampi((int)rintf(v.w * id), -127, 127);
     uint8_t *out = y + blk * kQ8_0Bytes;
-    const uint32_t p = pack4_i8(q0, q1, q2, q3);
     uint16_t *o16 = reinterpret_cast<uint16_t *>(out + 2 + sub * 4);
-    o16[0] = (uint16_t)(p & 0xffff);
-    o16[1] = (uint16_t)(p >> 16);
-    if (sub == 0) *reinterpret_cast<uint16_t *>(out) = (uint16_t)f32_to_f16_bits(d);
+    o16[0] = (uint16_t)(r.q & 0xffff);
+    o16[1] = (uint16_t)(r.q >> 16);
+    if (sub == 0) *reinterpret_cast<uint16_t *>(out) = (uint16_t)f32_to_f16_bits(r.d);
 }
 
 // ---------------------------------------------------------------------------

@@ -87,6 +87,15 @@ def test_quantize_mul_mat_q4_0(M, N, K):
     _check("q4_0", M, N, K, "repacked", seed=M * 13 + N)
 
 
+@pytest.mark.parametrize("layout", ["canonical", "repacked"])
+@pytest.mark.parametrize("N,K", [(77, 64), (3, 16384), (4096, 1024), (4097, 1024), (10, 96), (1, 16448)])
+def test_fused_q4_0_m1(N, K, layout):
+    """Q4_0 at M = 1: one launch (quantization in every workgroup) for K % 64 == 0,
+    K <= 16384 and N*K <= 2^22 -- one and many 32-block quantization passes, the
+    N*K limit itself -- and two launches just past those limits."""
+    _check("q4_0", 1, N, K, layout, seed=N * 3 + K)
+
+
 def test_fused_full_size_headline_shape():
     """N = K = 4096, M = 1 (the decode shape) on sampled outputs."""
     _check("q4_K", 1, 4096, 4096, "repacked", seed=4096, sample=3000)
