@@ -273,6 +273,7 @@ KERNEL_SOURCES = {  # the files that define each kernel the counters were taken 
     "k_gemv1_fused_q4_K": ("gemv.hip", "qmm_device.h"),
     "k_gemv1_q4_K": ("gemv.hip", "qmm_device.h"),
     "k_gemv_q4_0": ("gemv.hip", "qmm_device.h"),
+    "k_gemv_fused_q4_0": ("gemv.hip", "qmm_device.h"),
     "k_skinny_q4_K": ("skinny.hip", "mfma_common.h", "qmm_device.h"),
     "k_skinny16_q4_K": ("skinny16.hip", "mfma_common.h", "qmm_device.h"),
     "k_skinny16r_q4_K": ("skinny16r.hip", "mfma_common.h", "qmm_device.h"),
