@@ -327,10 +327,12 @@ def kernel_of(key: str, call_name: str, fused: bool, layout: str = "repacked") -
             return "k_gemv1_fused_q4_K" if fused and K <= 16384 else "k_gemv1_q4_K"
         if M <= 8 and layout == "repacked":
             return "k_skinny16r_q4_K"
+        if M <= 32 and layout == "repacked":
+            return "k_skinny32r_q4_K"
         if M <= 16:
             return "k_skinny16_q4_K"
         if M <= 32:
-            return "k_skinny32r_q4_K" if layout == "repacked" else "k_skinny_q4_K"
+            return "k_skinny_q4_K"
         return "k_gemm_q4_K"
     fam = {"q6_K": "q6_K", "q2_K": "q2_K"}[wfmt]
     return f"k_gemv_{fam}" if M == 1 else (f"k_skinny_{fam}" if M <= 32 else f"k_gemm_{fam}")

@@ -65,7 +65,7 @@ int cu_count();
 // wavefront streaming through an LDS ring, four consumer wavefronts.
 hipError_t launch_skinny16r_q4_K(const uint8_t *w, const uint8_t *y, float *out, int64_t M, int64_t N,
                                  int64_t K, hipStream_t s);
-// Q4_K small batch, repacked layout, 1 <= M <= 32 (skinny32r.hip): three
+// Q4_K small batch, repacked layout, 1 <= M <= 32 (skinny32r.hip): two or three
 // producer wavefronts streaming through an LDS ring, four consumer wavefronts.
 hipError_t launch_skinny32r_q4_K(const uint8_t *w, const uint8_t *y, float *out, int64_t M, int64_t N,
                                  int64_t K, hipStream_t s);

@@ -250,6 +250,10 @@ hipError_t launch_skinny16_q4_K(const uint8_t *w, bool repacked, const uint8_t *
     // skinny16r.hip streams the weights faster (N = K = 8192: 11.6 / 12.1
     // against 14.0 / 14.2 us at M = 4 / 8; 5-25% on the other shapes).
     if (repacked && M <= 8) return launch_skinny16r_q4_K(w, y, out, M, N, K, s);
+    // 9 to 16 rows of the repacked layout: the three-producer ring with one
+    // 16-row block (skinny32r.hip; M = 16, N = K = 8192: 13.6 against 16.6 us
+    // here, N = 28672, K = 4096: 21.7 against 28.8 us)
+    if (repacked) return launch_skinny32r_q4_K(w, y, out, M, N, K, s);
     // Below 8192 columns (fewer than 256 tiles of 32) 8 wavefronts per
     // 16-column tile give twice the workgroups; wider matrices take 4
     // wavefronts per 32 columns, whose workgroups share a CU three at a time.

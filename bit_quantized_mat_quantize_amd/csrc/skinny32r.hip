@@ -1,7 +1,8 @@
 // skinny32r.hip -- Q4_K weights (repacked layout) x Q8_K activations for
-// batches of 17 to 32 rows, gfx950: the producer/consumer LDS ring of
-// skinny16r.hip, widened to 32 activation rows (two 16-row MFMA blocks),
-// with three producer wavefronts.
+// batches of 9 to 32 rows, gfx950: the producer/consumer LDS ring of
+// skinny16r.hip, widened to RB = 1 or 2 blocks of 16 activation rows (16 or
+// 32 rows), with one producer wavefront for the weights and one per row block
+// for the activation codes.
 //
 // A small batch reads every weight once, so the weight stream bounds it
 // (BitBLAS page, "调度与自动调优": small-M shapes sit on the memory side of the
@@ -12,20 +13,22 @@
 // twice the weight bytes), else 16, and a stage holds SB = 64 / COLS
 // super-blocks (one 64-lane load of headers).  A stage is 28 (COLS = 32) or
 // 47 (COLS = 16) load instructions of 64 lanes, more than one wavefront's
-// in-order load counter (63) holds for two stages in flight, so three
-// producer wavefronts share them: producer 0 the headers, payloads, bsums and
-// d_a, producers 1 and 2 the codes of rows 0-15 and 16-31.  Each waits for its
-// own part of the oldest stage (loads complete in issue order), then every
-// wavefront meets at one workgroup barrier, which releases the stage to the
-// four consumers; consumer c contracts super-block SB S + c % SB of stage S for
-// the 16 columns 16 (c / SB) .. + 15 and both 16-row blocks.  D stages are in
-// flight: two with one workgroup per CU, one where the grid gives two per CU
-// (two 55.8 KB rings fit the CU's LDS, three 27.9 KB slots each).  Measured
-// against the 32 x 32-tile kernel (skinny.hip) at M = 32: N = K = 8192 17.0
-// against 20.7 us, N = 28672, K = 4096 27.0 against 36.9, N = 4096,
-// K = 14336 18.4 against 28.4 (16 columns; with 32 only half the CUs get a
-// workgroup).  Deeper rings were slower (N = K = 8192, 32 columns: 17.4 us
-// with D = 3, 18.2 with D = 4).
+// in-order load counter (63) holds for two stages in flight, so the loads are
+// shared: producer 0 takes the headers, payloads, bsums and d_a, producer 1
+// the codes of rows 0-15 and (RB = 2) producer 2 those of rows 16-31.  Each
+// waits for its own part of the oldest stage (loads complete in issue order),
+// then every wavefront meets at one workgroup barrier, which releases the
+// stage to the four consumers; consumer c contracts super-block SB S + c % SB
+// of stage S for the 16 columns 16 (c / SB) .. + 15 and every row block.  D
+// stages are in flight: two with one workgroup per CU, one where the grid
+// gives two per CU (their rings share the LDS).  Measured at M = 32 against
+// the 32 x 32-tile kernel (skinny.hip): N = K = 8192 17.0 against 20.7 us,
+// N = 28672, K = 4096 27.0 against 36.9, N = 4096, K = 14336 18.4 against
+// 28.4 (16 columns; with 32 only half the CUs get a workgroup); deeper rings
+// were slower (N = K = 8192, 32 columns: 17.4 us with D = 3, 18.2 with D = 4).
+// At M = 16 (RB = 1) against the 16 x 16-tile kernel (skinny16.hip): 13.6
+// against 16.6 us at N = K = 8192, 21.7 against 28.8 at N = 28672, K = 4096,
+// 13.2 against 17.2 at N = 4096, K = 14336.
 //
 // Arithmetic, per super-block and output (m, n), as in skinny16r.hip (ggml-cpu
 // mul_mat page, "正确性:缩放系数可以提到求和号外面" and "min 项与最终归约"):
@@ -61,26 +64,31 @@ typedef _Float16 v8h32r __attribute__((ext_vector_type(8)));
 typedef int v4i32r __attribute__((ext_vector_type(4)));
 typedef float v4f32r __attribute__((ext_vector_type(4)));
 
-constexpr int kR32Consumers = 4, kR32Producers = 3;
-constexpr int kR32Threads = 64 * (kR32Consumers + kR32Producers);
-constexpr int kR32Rows = 32;
+constexpr int kR32Consumers = 4;
+// RB row blocks of 16 activation rows: one producer for the weights, bsums and
+// d_a and one per row block for the codes
+template <int RB>
+constexpr int r32_threads() { return 64 * (kR32Consumers + 1 + RB); }
 
 // Geometry for COLS columns per workgroup (16 or 32): a stage holds SB =
 // 64 / COLS super-blocks, so its headers are one 64-lane load.
-template <int COLS>
+template <int COLS, int RB>
 struct R32 {
     static_assert(COLS == 16 || COLS == 32, "16 or 32 columns per workgroup");
+    static_assert(RB == 1 || RB == 2, "16 or 32 activation rows");
     static constexpr int SB = 64 / COLS;      // super-blocks per stage
     static constexpr int RPB = 32 / SB;       // rows per bsums load (8 or 16)
     static constexpr int RPD = 64 / SB;       // rows per d_a load (16 or 32)
-    static constexpr int HDR = 0, PAY = 1024, ACT = PAY + 8192, BSM = ACT + 8192 * SB, DA = BSM + 1024 * SB;
-    static constexpr int STAGE = DA + 128 * SB;
-    static constexpr int L0 = 1 + 8 + SB + SB / 2;  // producer 0: header, payloads, bsums, d_a
-    static constexpr int L1 = 4 * SB;               // producers 1 and 2: codes of 16 rows
+    static constexpr int NBS = 16 * RB / RPB;               // bsums loads
+    static constexpr int NDA = (16 * RB + RPD - 1) / RPD;   // d_a loads
+    static constexpr int HDR = 0, PAY = 1024, ACT = PAY + 8192, BSM = ACT + 4096 * SB * RB, DA = BSM + 1024 * NBS;
+    static constexpr int STAGE = DA + 256 * NDA;
+    static constexpr int L0 = 1 + 8 + NBS + NDA;  // producer 0: header, payloads, bsums, d_a
+    static constexpr int L1 = 4 * SB;             // producers 1 (and 2): codes of 16 rows
 };
-template <int COLS, int D>
+template <int COLS, int D, int RB>
 struct R32Ring {
-    using G = R32<COLS>;
+    using G = R32<COLS, RB>;
     static_assert(D >= 1 && D * G::L0 <= 63 && D * G::L1 <= 63, "the wait counter holds 63 loads");
     static constexpr int R = D + 1;  // slots: D in flight, one being contracted
     static constexpr int BYTES = R * G::STAGE;
@@ -112,19 +120,20 @@ __device__ __forceinline__ void r32_dma4(rsrc_t r, uint32_t voff, uint32_t soff,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 4, voff, soff, 0, 0);
 }
 
-template <int COLS, int D>
-__global__ __launch_bounds__(kR32Threads, 1) void k_skinny32r_q4_K(const uint8_t *__restrict__ W,
+template <int COLS, int D, int RB>
+__global__ __launch_bounds__(r32_threads<RB>(), 1) void k_skinny32r_q4_K(const uint8_t *__restrict__ W,
                                                                   const uint8_t *__restrict__ Y,
                                                                   float *__restrict__ out, int64_t M,
                                                                   int64_t N, int64_t K) {
-    using RS = R32Ring<COLS, D>;
-    using G = R32<COLS>;
+    using RS = R32Ring<COLS, D, RB>;
+    using G = R32<COLS, RB>;
+    constexpr int kRows = 16 * RB, kThreads = r32_threads<RB>();
     constexpr int SB = G::SB;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int Mc = (int)M;  // 1 <= M <= 32
+    const int Mc = (int)M;  // 1 <= M <= 16 RB
     const int nb = (int)(K / QK_K), nst = (nb + SB - 1) / SB;
     const int64_t n_base = (int64_t)blockIdx.x * COLS;
 
@@ -153,14 +162,14 @@ __global__ __launch_bounds__(kR32Threads, 1) void k_skinny32r_q4_K(const uint8_t
                           base + G::PAY + 1024 * k);
                 }
 #pragma unroll
-                for (int j = 0; j < SB; ++j) {  // bsums of rows RPB j .. + RPB - 1
+                for (int j = 0; j < G::NBS; ++j) {  // bsums of rows RPB j .. + RPB - 1
                     const int gb = lane / (2 * G::RPB);
                     const int rr = clamp_r(G::RPB * j + ((lane >> 1) % G::RPB));
                     dma16(ra, (uint32_t)rr * rowb + (uint32_t)clamp_b(SB * S + gb) * kQ8_KBytes + 260 + 16 * (lane & 1),
                           0, base + G::BSM + 1024 * j);
                 }
 #pragma unroll
-                for (int j = 0; j < SB / 2; ++j) {  // d_a of rows RPD j .. + RPD - 1
+                for (int j = 0; j < G::NDA; ++j) {  // d_a of rows RPD j .. + RPD - 1
                     const int gd = lane / G::RPD;
                     const int rr = clamp_r(G::RPD * j + lane % G::RPD);
                     r32_dma4(ra, (uint32_t)rr * rowb + (uint32_t)clamp_b(SB * S + gd) * kQ8_KBytes, 0,
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void k_skinny32r_q4_K(const uint8_t
         // ---------------- consumer c: super-block SB S + c % SB of every stage S, columns 16 (c / SB) .. + 15
         const int c = wave, gsb = c % SB, l16 = lane & 15, h = lane >> 4;
         const int cl = 16 * (c / SB) + l16;  // this lane's column of the workgroup's COLS
-        v4f32r acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        v4f32r acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};  // row blocks 0, 1
         for (int S = 0; S < nst; ++S) {
             r32_barrier();
             if (SB * S + gsb < nb) {  // wavefront-uniform
@@ -209,11 +218,11 @@ __global__ __launch_bounds__(kR32Threads, 1) void k_skinny32r_q4_K(const uint8_t
                 const uint4 p0 = *reinterpret_cast<const uint4 *>(base + pb + 16 * ((2 * h) ^ (l16 & 7)));
                 const uint4 p1 = *reinterpret_cast<const uint4 *>(base + pb + 16 * ((2 * h + 1) ^ (l16 & 7)));
                 // rows l16 (block 0) and 16 + l16 (block 1)
-                uint32_t aw[2][16];
-                uint4 bsr[2];
-                float dv[2][4];
+                uint32_t aw[RB][16];
+                uint4 bsr[RB];
+                float dv[RB][4];
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk) {
+                for (int blk = 0; blk < RB; ++blk) {
                     const int rr = 16 * blk + l16;
                     const uint8_t *arow = base + G::ACT + 1024 * SB * (rr >> 2) + 1024 * gsb + 256 * (rr & 3);
 #pragma unroll
@@ -254,12 +263,14 @@ __global__ __launch_bounds__(kR32Threads, 1) void k_skinny32r_q4_K(const uint8_t
                     const v4i32r bl = {plane(q0, la), plane(q1, la), plane(q2, lb), plane(q3, lb)};
                     const v4i32r a0 = {(int)aw[0][2 * t], (int)aw[0][2 * t + 1], (int)aw[0][8 + 2 * t],
                                        (int)aw[0][9 + 2 * t]};
-                    const v4i32r a1 = {(int)aw[1][2 * t], (int)aw[1][2 * t + 1], (int)aw[1][8 + 2 * t],
-                                       (int)aw[1][9 + 2 * t]};
                     ah0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bh, ah0, 0, 0, 0);
                     al0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bl, al0, 0, 0, 0);
-                    ah1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bh, ah1, 0, 0, 0);
-                    al1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bl, al1, 0, 0, 0);
+                    if constexpr (RB == 2) {
+                        const v4i32r a1 = {(int)aw[RB - 1][2 * t], (int)aw[RB - 1][2 * t + 1],
+                                           (int)aw[RB - 1][8 + 2 * t], (int)aw[RB - 1][9 + 2 * t]};
+                        ah1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bh, ah1, 0, 0, 0);
+                        al1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bl, al1, 0, 0, 0);
+                    }
                 }
                 // min term: bsums 8 (h & 1) .. + 7 of the row against the hi (h < 2)
                 // or lo part of -dmin * m_j of sub-blocks 4 (h & 1) .. + 3
@@ -278,7 +289,7 @@ __global__ __launch_bounds__(kR32Threads, 1) void k_skinny32r_q4_K(const uint8_t
                 }
                 const v4f32r zf = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk) {
+                for (int blk = 0; blk < RB; ++blk) {
                     v8h32r a_bs;
                     {
                         const uint4 bv = bsr[blk];
@@ -307,19 +318,19 @@ __global__ __launch_bounds__(kR32Threads, 1) void k_skinny32r_q4_K(const uint8_t
         float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            red[((c * 2 + 0) * 4 + r) * 64 + lane] = acc0[r];
-            red[((c * 2 + 1) * 4 + r) * 64 + lane] = acc1[r];
+            red[((c * RB + 0) * 4 + r) * 64 + lane] = acc0[r];
+            if constexpr (RB == 2) red[((c * RB + 1) * 4 + r) * 64 + lane] = acc1[r];
         }
     }
     __syncthreads();
     // output (m, col): column group cg = col / 16, block m / 16, register m % 4 of
     // lane col % 16 + 16 ((m % 16) / 4) of consumers SB cg .. SB cg + SB - 1
     const float *red = reinterpret_cast<const float *>(lds);
-    for (int o = tid; o < kR32Rows * COLS; o += kR32Threads) {
+    for (int o = tid; o < kRows * COLS; o += kThreads) {
         const int m = o / COLS, col = o % COLS;
         const int cg = col >> 4, blk = m >> 4, mm = m & 15;
         const int r = mm & 3, l = (col & 15) + 16 * (mm >> 2);
-        auto at = [&](int cons) { return red[((cons * 2 + blk) * 4 + r) * 64 + l]; };
+        auto at = [&](int cons) { return red[((cons * RB + blk) * 4 + r) * 64 + l]; };
         float v = at(SB * cg);
 #pragma unroll
         for (int k = 1; k < SB; ++k) v += at(SB * cg + k);
@@ -327,31 +338,40 @@ __global__ __launch_bounds__(kR32Threads, 1) void k_skinny32r_q4_K(const uint8_t
     }
 }
 
-template <int COLS, int D>
+template <int COLS, int D, int RB>
 hipError_t launch_r32(const uint8_t *w, const uint8_t *y, float *out, int64_t M, int64_t N, int64_t K,
                       hipStream_t s) {
     static std::atomic<uint64_t> lds_set{0};  // the LDS budget above 64 KiB, per device
-    const int bytes = R32Ring<COLS, D>::BYTES;
+    const int bytes = R32Ring<COLS, D, RB>::BYTES;
     if (bytes > 64 * 1024) {
-        const hipError_t e = ensure_lds_bytes((const void *)k_skinny32r_q4_K<COLS, D>, bytes, lds_set);
+        const hipError_t e = ensure_lds_bytes((const void *)k_skinny32r_q4_K<COLS, D, RB>, bytes, lds_set);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_skinny32r_q4_K<COLS, D>), dim3((unsigned)((N + COLS - 1) / COLS)), dim3(kR32Threads),
-                       (unsigned)bytes, s, w, y, out, M, N, K);
+    hipLaunchKernelGGL((k_skinny32r_q4_K<COLS, D, RB>), dim3((unsigned)((N + COLS - 1) / COLS)),
+                       dim3(r32_threads<RB>()), (unsigned)bytes, s, w, y, out, M, N, K);
     return hipGetLastError();
+}
+
+template <int RB>
+hipError_t launch_rb(const uint8_t *w, const uint8_t *y, float *out, int64_t M, int64_t N, int64_t K,
+                     hipStream_t s) {
+    // 32 columns per workgroup once every CU gets one, and one stage in flight
+    // once the grid gives two workgroups per CU (their rings share the LDS)
+    const int64_t cus = cu_count();
+#ifdef R32_COLS
+    return launch_r32<R32_COLS, R32_DEPTH, RB>(w, y, out, M, N, K, s);
+#endif
+    if (N < 32 * cus) return launch_r32<16, 2, RB>(w, y, out, M, N, K, s);
+    return (N + 31) / 32 >= 2 * cus ? launch_r32<32, 1, RB>(w, y, out, M, N, K, s)
+                                    : launch_r32<32, 2, RB>(w, y, out, M, N, K, s);
 }
 
 }  // namespace
 
 hipError_t launch_skinny32r_q4_K(const uint8_t *w, const uint8_t *y, float *out, int64_t M, int64_t N,
                                  int64_t K, hipStream_t s) {
-    if (M < 1 || M > kR32Rows) return hipErrorInvalidValue;
-    // 32 columns per workgroup once every CU gets one, and one stage in flight
-    // once the grid gives two workgroups per CU (their rings share the LDS)
-    const int64_t cus = cu_count();
-    if (N < 32 * cus) return launch_r32<16, 2>(w, y, out, M, N, K, s);
-    return (N + 31) / 32 >= 2 * cus ? launch_r32<32, 1>(w, y, out, M, N, K, s)
-                                    : launch_r32<32, 2>(w, y, out, M, N, K, s);
+    if (M < 1 || M > 32) return hipErrorInvalidValue;
+    return M <= 16 ? launch_rb<1>(w, y, out, M, N, K, s) : launch_rb<2>(w, y, out, M, N, K, s);
 }
 
 }  // namespace qmm

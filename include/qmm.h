@@ -99,7 +99,7 @@ typedef enum { QMM_LAYOUT_CANONICAL = 0, QMM_LAYOUT_REPACKED = 1 } qmm_layout;
  *           M <= 65535*32).  For Q4_K up to 16 rows the tiles are 16 x 16,
  *           and up to 8 rows of the repacked layout one wavefront per
  *           workgroup streams the weights into LDS for four that compute;
- *           from 17 to 32 rows of the repacked layout three wavefronts
+ *           from 9 to 32 rows of the repacked layout two or three wavefronts
  *           stream weights and activation rows for four that compute
  *   MFMA    prefill GEMM on int8 MFMA, 128 x 256 output tiles (any M; Q6_K,
  *           Q2_K and Q4_0 need the repacked layout, Q4_0 also K % 256 == 0)

@@ -180,19 +180,20 @@ def test_mfma_q4_K(M, N, K, layout):
                                    (32, 96, 3840), (1, 70, 2048), (40, 50, 1024), (65, 33, 512),
                                    (97, 70, 2304), (4, 8200, 768), (13, 8192, 512), (16, 9000, 1280),
                                    (7, 6000, 1280), (6, 17, 3328), (1, 4100, 512), (32, 8200, 768),
-                                   (20, 16400, 512), (25, 4100, 1280), (31, 33, 2304), (32, 8192, 256)])
+                                   (20, 16400, 512), (25, 4100, 1280), (31, 33, 2304), (32, 8192, 256),
+                                   (12, 16400, 512), (10, 4100, 1280)])
 def test_skinny_q4_K(M, N, K, layout):
     """Small-batch MFMA paths: ragged N, K splits of 1..3 super-blocks per
     wavefront (odd and even counts, wavefronts without work); up to 8 rows
     of the repacked layout the producer/consumer ring kernel (stages of four
     super-blocks with 1..3 of them past K; one, two and three or more
-    workgroups per CU, i.e. 3, 2 and 1 stages in flight), up to 16 rows the
-    16 x 16-tile kernel (8 wavefronts per 16 columns below N = 8192), from 17
-    to 32 rows of the repacked layout the three-producer ring (16 columns per
-    workgroup below N = 8192, 32 from there; one or two stages in flight;
-    stages with super-blocks past K), otherwise the 32 x 32 kernel with 8, 16
-    and 32 staged activation rows and several 32-row chunks (grid.y) with a
-    ragged last chunk."""
+    workgroups per CU, i.e. 3, 2 and 1 stages in flight), from 9 to 32 rows
+    of the repacked layout the ring with one or two 16-row blocks (16 columns
+    per workgroup below N = 8192, 32 from there; one or two stages in flight;
+    stages with super-blocks past K), the 16 x 16-tile kernel up to 16 rows of
+    the canonical layout (8 wavefronts per 16 columns below N = 8192), and the
+    32 x 32 kernel above with 8, 16 and 32 staged activation rows and several
+    32-row chunks (grid.y) with a ragged last chunk."""
     w, x, y, _ = _case("q4_K", M, N, K, 7 * M + N)
     want, terms = full_reference("q4_K", w, y, M, N, K)
     wd = upload_weights("q4_K", w, N, K, layout)
