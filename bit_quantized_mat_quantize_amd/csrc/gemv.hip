@@ -18,6 +18,7 @@
 //   partial = d_a * (d * (s_2g*P_lo + s_2g+1*P_hi) - dmin * (m_2g*B_lo + m_2g+1*B_hi))
 // Summed over the 8 pieces of a block this is d_a*(d*S - dmin*Mn) of the
 // ggml-cpu page ("正确性" and "min 项与最终归约").
+#include "q8k_row.h"
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
@@ -361,25 +362,15 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
     uint8_t *s_qs = ys;
     float *s_d = reinterpret_cast<float *>(ys + K);
     int16_t *s_bs = reinterpret_cast<int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
-    uint8_t *s_trash = ys + K + (nb * 4 + 15) / 16 * 16 + nb * 32;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t stride = (int64_t)gridDim.x * kFusedWaves;
     int64_t row = (int64_t)blockIdx.x * kFusedWaves + wave;  // uniform per wavefront
     const Q4KAddr<REPACKED> A{W, N, nb};
     const bool store_q = blockIdx.x == 0;
 
-    // one 256-value block per wavefront and step: quantize, write LDS; an
-    // invalid block (b >= nb) is quantized too and stored to the trash slot
-    auto quantize_block = [&](const float4 v, int b) {
-        const bool valid = b < nb;
-        const Q8KLane r = q8K_quantize_lane(v);
-        const uint32_t packed = pack4_i8(r.q[0], r.q[1], r.q[2], r.q[3]);
-        *reinterpret_cast<uint32_t *>(valid ? s_qs + b * QK_K + 4 * lane : s_trash) = packed;
-        if ((lane & 3) == 0)
-            *reinterpret_cast<int16_t *>(valid ? reinterpret_cast<uint8_t *>(s_bs + 16 * b + (lane >> 2))
-                                               : s_trash) = (int16_t)r.bsum;
-        if (lane == 0) *reinterpret_cast<float *>(valid ? reinterpret_cast<uint8_t *>(s_d + b) : s_trash) = r.d;
-    };
+    // one 256-value block per wavefront and step: quantize, write LDS (a block
+    // past the row goes to the trash slot)
+    auto quantize_block = [&](const float4 v, int b) { q8k_quantize_block_lds(v, b, K, ys, lane); };
 
     // the launcher guarantees nb <= 16 * kXB; block indices past the row end
     // load the last block again (branch-free loads)
@@ -449,15 +440,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv1_fused_q4_K(
     // Workgroup 0 copies the Q8_K row to Yq last: stores issued before the
     // row loop would sit in the same in-order counter as the weight loads and
     // make the first reduction wait for all of them.
-    if (store_q) {
-        for (int i = tid; i < nb * (kQ8_KBytes / 4); i += kFusedWaves * 64) {
-            const int b = i / (kQ8_KBytes / 4), w = i - b * (kQ8_KBytes / 4);  // dword w of block b
-            const uint32_t v = w == 0 ? __float_as_uint(s_d[b])
-                             : w <= QK_K / 4 ? *reinterpret_cast<const uint32_t *>(s_qs + b * QK_K + 4 * (w - 1))
-                                             : *reinterpret_cast<const uint32_t *>(s_bs + 16 * b + 2 * (w - 1 - QK_K / 4));
-            *reinterpret_cast<uint32_t *>(Yq + (int64_t)b * kQ8_KBytes + 4 * w) = v;
-        }
-    }
+    if (store_q) q8k_store_row<kFusedWaves * 64>(Yq, ys, K);
 }
 
 // ---------------------------------------------------------------------------

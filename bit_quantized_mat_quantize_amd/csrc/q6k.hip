@@ -391,6 +391,86 @@ __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused M = 1 path for Q6_K (rows of up to four piece units per lane, at most
+// two rows per wavefront): the fp32 row is quantized to Q8_K inside the GEMV,
+// straight into LDS, so one launch covers quantize + mul_mat.  As in the Q4_K
+// fused kernel every workgroup quantizes the whole row, so the grid holds one
+// 16-wavefront workgroup per CU and wavefront w of workgroup g takes rows
+// g*16 + w and g*16 + w + 16*gridDim.x.  A wavefront first loads its fp32
+// activation blocks (b = wave + 16i), waits for them, issues its first row's
+// units and quantizes while they are in flight; its second row (if any) is
+// requested after the barrier, before the first is reduced.  Workgroup 0 also
+// stores the Q8_K bytes to Yq.  Per row the same integer sums and fp32
+// operations, in the same order, as k_gemv_q6_K.
+// ---------------------------------------------------------------------------
+constexpr int kQ6FusedWaves = 16;
+
+template <bool REPACKED, int kNit, int kXB>
+__global__ __launch_bounds__(kQ6FusedWaves * 64) void k_gemv_fused_q6_K(
+    const uint8_t *__restrict__ W, const float *__restrict__ X, uint8_t *__restrict__ Yq,
+    float *__restrict__ out, int64_t N, int64_t K) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t ys[];
+    const int64_t nb = K / QK_K;
+    const int nunits = (int)(8 * nb);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t stride = (int64_t)gridDim.x * kQ6FusedWaves;
+    const int64_t row = (int64_t)blockIdx.x * kQ6FusedWaves + wave, row2 = row + stride;  // uniform
+    const Q6KAddr<REPACKED> A{W, N * nb, REPACKED ? (2 * N * nb + 255) / 256 * 256 : 0};
+    auto load_row = [&](int64_t r, Q6KUnit (&x)[kNit]) {
+        const int64_t rr = r < N ? r : N - 1;  // past the last row: a valid row, never stored
+#pragma unroll
+        for (int it = 0; it < kNit; ++it) {
+            const int u = lane + 64 * it;
+            q6k_load<REPACKED>(A, rr, nb, u < nunits ? u : nunits - 1, x[it]);
+        }
+    };
+    float4 xv[kXB];
+#pragma unroll
+    for (int i = 0; i < kXB; ++i) {  // block indices past the row load the last block again
+        const int b0 = wave + kQ6FusedWaves * i;
+        const int b = b0 < nb ? b0 : (int)nb - 1;
+        xv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane);
+    }
+    // the activation loads complete before any weight load is issued (queued
+    // behind the chip's weight stream they would arrive late)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    Q6KUnit x[kNit], x2[kNit];
+    load_row(row, x);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kXB; ++i) q8k_quantize_block_lds(xv[i], wave + kQ6FusedWaves * i, K, ys, lane);
+    __syncthreads();
+    const uint8_t *s_qs = ys;
+    const float *s_d = reinterpret_cast<const float *>(ys + K);
+    const int16_t *s_bs = reinterpret_cast<const int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
+    const bool two = row2 < N;  // wavefront-uniform
+    if (two) load_row(row2, x2);
+    auto reduce = [&](int64_t r, const Q6KUnit (&xx)[kNit]) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int it = 0; it < kNit; ++it) {
+            const int u = lane + 64 * it;
+            if (u >= nunits) continue;
+            int P[2];
+            q6k_group_sums(xx[it], u, s_qs, s_bs, P);
+            const int b = u >> 3, p = u & 7, h = p & 1;
+            const int s_lo = (int)(int8_t)(xx[it].sc >> (8 * h));
+            const int s_hi = (int)(int8_t)(xx[it].sc >> (8 * (2 + h)));
+            const int S = s_lo * P[0] + s_hi * P[1];
+            acc = fmaf(s_d[b], f16_bits_to_f32(xx[it].d) * (float)S, acc);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0 && r < N) out[r] = acc;
+    };
+    reduce(row, x);
+    if (two) reduce(row2, x2);
+    // workgroup 0 copies the Q8_K row to Yq last (stores issued earlier would
+    // sit in the in-order counter ahead of the weight loads)
+    if (blockIdx.x == 0) q8k_store_row<kQ6FusedWaves * 64>(Yq, ys, K);
+}
+
 template <int MODE>
 hipError_t dispatch_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, void *dst, int64_t M,
                          int64_t N, int64_t K, hipStream_t s) {
@@ -451,6 +531,35 @@ hipError_t launch_gemv_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, f
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+bool gemv_fused_q6_K_ok(int64_t N, int64_t K) {
+    // rows of up to four piece units per lane (K <= 8192) and at most two rows
+    // per wavefront; each workgroup repeats the quantization
+    return K <= 8192 && N <= 2 * (int64_t)kQ6FusedWaves * cu_count() &&
+           q8k_row_lds_bytes(K) <= 60 * 1024;
+}
+
+hipError_t launch_gemv_fused_q6_K(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
+                                  int64_t N, int64_t K, hipStream_t s) {
+    if (!gemv_fused_q6_K_ok(N, K)) return hipErrorInvalidValue;
+    const int64_t nit = (8 * (K / QK_K) + 63) / 64;
+    const int64_t groups = (N + kQ6FusedWaves - 1) / kQ6FusedWaves, cus = cu_count();
+    const dim3 grid((unsigned)(groups < cus ? groups : cus)), block(kQ6FusedWaves * 64);
+    const unsigned lds = (unsigned)q8k_row_lds_bytes(K);
+#define QMM_Q6F(NIT, XB)                                                                                  \
+    do {                                                                                                  \
+        if (repacked)                                                                                     \
+            hipLaunchKernelGGL((k_gemv_fused_q6_K<true, NIT, XB>), grid, block, lds, s, w, x, yq, out, N, K);  \
+        else                                                                                              \
+            hipLaunchKernelGGL((k_gemv_fused_q6_K<false, NIT, XB>), grid, block, lds, s, w, x, yq, out, N, K); \
+    } while (0)
+    // kXB = activation blocks per wavefront: ceil(nb / 16) (nb <= 8 * kNit <= 16 * kXB)
+    if (nit <= 1) QMM_Q6F(1, 1);
+    else if (nit <= 2) QMM_Q6F(2, 1);
+    else QMM_Q6F(4, 2);
+#undef QMM_Q6F
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_id_q6_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,

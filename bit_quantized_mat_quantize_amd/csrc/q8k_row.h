@@ -94,4 +94,40 @@ __device__ __forceinline__ Q8KRowLds stage_q8k_row(const uint8_t *__restrict__ Y
     return Q8KRowLds{s_qs, reinterpret_cast<const float *>(s_d), reinterpret_cast<const int16_t *>(s_bs)};
 }
 
+// ---- Fused quantize + GEMV kernels: the fp32 row quantized to Q8_K straight
+// into the staged layout above, one 256-value block per wavefront call (four
+// consecutive values per lane, the stand-alone quantizer's routine).  A block
+// index past the row (b >= nb) is quantized too and stored to the trash slot,
+// so the call stays branch-free.
+__device__ __forceinline__ void q8k_quantize_block_lds(const float4 v, int b, int64_t K, uint8_t *ys, int lane) {
+    const int64_t nb = K / QK_K;
+    uint8_t *s_qs = ys;
+    uint8_t *s_d = ys + K;
+    uint8_t *s_bs = ys + K + (nb * 4 + 15) / 16 * 16;
+    uint8_t *trash = s_bs + nb * 32;
+    const bool valid = b < nb;
+    const Q8KLane r = q8K_quantize_lane(v);
+    const uint32_t packed = pack4_i8(r.q[0], r.q[1], r.q[2], r.q[3]);
+    *reinterpret_cast<uint32_t *>(valid ? s_qs + b * QK_K + 4 * lane : trash) = packed;
+    if ((lane & 3) == 0)
+        *reinterpret_cast<int16_t *>(valid ? s_bs + 32 * b + 2 * (lane >> 2) : trash) = (int16_t)r.bsum;
+    if (lane == 0) *reinterpret_cast<float *>(valid ? s_d + 4 * b : trash) = r.d;
+}
+// Copy the staged row to Yq in the Q8_K byte layout (d | 256 codes | 16 bsums
+// per block), byte-identical to the stand-alone quantizer; kThreads threads.
+template <int kThreads>
+__device__ __forceinline__ void q8k_store_row(uint8_t *__restrict__ Yq, const uint8_t *ys, int64_t K) {
+    const int64_t nb = K / QK_K;
+    const uint8_t *s_qs = ys;
+    const float *s_d = reinterpret_cast<const float *>(ys + K);
+    const int16_t *s_bs = reinterpret_cast<const int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
+    for (int i = threadIdx.x; i < nb * (kQ8_KBytes / 4); i += kThreads) {
+        const int b = i / (kQ8_KBytes / 4), w = i - b * (kQ8_KBytes / 4);  // dword w of block b
+        const uint32_t v = w == 0 ? __float_as_uint(s_d[b])
+                         : w <= QK_K / 4 ? *reinterpret_cast<const uint32_t *>(s_qs + b * QK_K + 4 * (w - 1))
+                                         : *reinterpret_cast<const uint32_t *>(s_bs + 16 * b + 2 * (w - 1 - QK_K / 4));
+        *reinterpret_cast<uint32_t *>(Yq + (int64_t)b * kQ8_KBytes + 4 * w) = v;
+    }
+}
+
 }  // namespace qmm

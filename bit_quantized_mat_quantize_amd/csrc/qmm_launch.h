@@ -76,6 +76,10 @@ hipError_t launch_skinny16_q4_K(const uint8_t *w, bool repacked, const uint8_t *
 // Q4_0 GEMV with the M activation rows staged in LDS: K % 64 == 0 and
 // M * K * 5/4 bytes <= 60 KiB (other shapes read the rows per lane).
 // Q4_0, M = 1, small matrices (gemv_fused_q4_0_ok): quantize + GEMV in one launch
+// Q6_K, M = 1, K <= 8192, N <= 32 * CUs (gemv_fused_q6_K_ok): quantize + GEMV in one launch
+bool gemv_fused_q6_K_ok(int64_t N, int64_t K);
+hipError_t launch_gemv_fused_q6_K(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
+                                  int64_t N, int64_t K, hipStream_t s);
 bool gemv_fused_q4_0_ok(int64_t N, int64_t K);
 hipError_t launch_gemv_fused_q4_0(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
                                   int64_t N, int64_t K, hipStream_t s);

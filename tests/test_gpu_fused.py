@@ -26,8 +26,8 @@ FUSED_MAX_K = 16384  # largest K of the one-launch path (eight 16-byte pieces pe
 
 
 def _inputs(wfmt, M, N, K, seed):
-    if wfmt == "q4_K":
-        w = oracle.quantize("q4_K", weights_t4_skewed([500, seed], N, K))
+    if wfmt in ("q4_K", "q6_K"):
+        w = oracle.quantize(wfmt, weights_t4_skewed([500, seed], N, K))
         x = activations([501, seed], M, K, outlier_frac=0.01)
     else:
         w = oracle.quantize("q4_0", weights_normal([502, seed], N, K))
@@ -37,7 +37,7 @@ def _inputs(wfmt, M, N, K, seed):
 
 def _check(wfmt, M, N, K, layout, seed, sample=None):
     import torch
-    afmt = "q8_K" if wfmt == "q4_K" else "q8_0"
+    afmt = "q8_0" if wfmt == "q4_0" else "q8_K"
     w, x = _inputs(wfmt, M, N, K, seed)
     y_want = oracle.quantize(afmt, x)
     wd = upload_weights(wfmt, w, N, K, layout)
@@ -47,8 +47,7 @@ def _check(wfmt, M, N, K, layout, seed, sample=None):
     assert np.array_equal(got_y.reshape(-1), y_want.reshape(-1)), "Q8 bytes differ from the oracle"
     # the two-call path on the same device bytes
     y2 = qmm.quantize_row_q8(xd, afmt)
-    mm = qmm.mul_mat_q4_K if wfmt == "q4_K" else qmm.mul_mat_q4_0
-    ref = to_host(mm(wd, y2, M, N, K, layout=layout))
+    ref = to_host(qmm.mul_mat(wfmt, wd, y2, M, N, K, layout=layout))
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), "fused != quantize + mul_mat"
     if sample is None:
         want, terms = full_reference(wfmt, w, y_want, M, N, K)
@@ -165,3 +164,13 @@ def test_fused_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(to_host(out).view(np.uint32), eager.view(np.uint32))
+
+
+@pytest.mark.parametrize("layout", ["canonical", "repacked"])
+@pytest.mark.parametrize("N,K", [(77, 256), (4096, 4096), (8192, 1024), (100, 8192), (8193, 1024), (3, 8448)])
+def test_fused_q6_K_m1(N, K, layout):
+    """Q6_K at M = 1: one launch (quantization in every workgroup) for K <= 8192
+    and N <= 32 rows per CU -- one and two rows per wavefront, one to four
+    piece units per lane -- and two launches just past those limits."""
+    sample = 3000 if N * K > (1 << 24) else None
+    _check("q6_K", 1, N, K, layout, seed=N * 5 + K, sample=sample)
