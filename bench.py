@@ -270,7 +270,7 @@ def time_steps(prep, steps: int, only=None, min_replays: int = 3):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_q4_K.md")
 _CSRC = "bit_quantized_mat_quantize_amd/csrc/"
 KERNEL_SOURCES = {  # the files that define each kernel the counters were taken for
-    "k_gemv1_fused_q4_K": ("gemv.hip", "qmm_device.h"),
+    "k_gemv1_fused_q4_K": ("gemv.hip", "q8k_row.h", "qmm_device.h"),
     "k_gemv1_q4_K": ("gemv.hip", "qmm_device.h"),
     "k_gemv_q4_0": ("gemv.hip", "qmm_device.h"),
     "k_gemv_fused_q4_0": ("gemv.hip", "qmm_device.h"),
