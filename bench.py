@@ -335,8 +335,10 @@ def kernel_of(key: str, call_name: str, fused: bool, layout: str = "repacked") -
             return "k_skinny_q4_K"
         return "k_gemm_q4_K"
     fam = {"q6_K": "q6_K", "q2_K": "q2_K"}[wfmt]
-    if M == 1 and fused and wfmt == "q6_K" and K <= 8192 and int(call_name.split("N=")[1].split()[0]) <= 8192:
-        return "k_gemv_fused_q6_K"
+    N = int(call_name.split("N=")[1].split()[0])
+    fused_ok = (K <= 4096 and N <= 8192) or (K <= 8192 and N <= 4096) if wfmt == "q6_K" else (K <= 16384 and N <= 8192)
+    if M == 1 and fused and fused_ok:
+        return f"k_gemv_fused_{fam}"
     return f"k_gemv_{fam}" if M == 1 else (f"k_skinny_{fam}" if M <= 32 else f"k_gemm_{fam}")
 
 
@@ -726,15 +728,15 @@ def main():
     nxt = {}
     if not a.no_next and only is None:
         for k in NEXT_DECODE + NEXT_PREFILL:
-            # Q6_K fuses the quantization into its M = 1 GEMV (Q2_K does not)
-            r = measure_config(k, a.layout, steps, forms=(False, True) if k == "q6K_c2" else (False,),
+            # Q6_K and Q2_K fuse the quantization into their M = 1 GEMVs
+            r = measure_config(k, a.layout, steps, forms=(False, True) if k in NEXT_DECODE else (False,),
                                probe=probe)
             nxt[k] = summary(r)
         nxt["mul_mat_id_q4_K"] = measure_moe(steps)
     elif only is not None:
         for k in [k for k in NEXT_DECODE + NEXT_PREFILL + ALL_EXTRA if k in only and k not in results]:
             nxt[k] = summary(measure_config(k, a.layout, steps,
-                                            forms=(False, True) if k in ("q6K_c2", "q6K_down") else (False,),
+                                            forms=(False, True) if k in NEXT_DECODE + ("q6K_down",) else (False,),
                                             probe=probe))
 
     head = results.get(HEADLINE) or (results[main_keys[0]] if main_keys else None)

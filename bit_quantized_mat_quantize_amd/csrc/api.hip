@@ -693,6 +693,15 @@ qmm_status qmm_quantize_mul_mat(qmm_weight_type t, const void *w, size_t w_bytes
                                                          l == QMM_LAYOUT_REPACKED, x, yb, out, N, K, s),
                              "quantize_mul_mat fused launch");
     }
+    if (t == QMM_Q2_K && M == 1 && N > 0 && qmm::gemv_fused_q2_K_ok(N, K)) {
+        if (log_enabled())
+            fprintf(stderr, "qmm: quantize_mul_mat Q2_K M=1 N=%lld K=%lld layout=%s -> fused quantize + GEMV "
+                    "(one launch, one wavefront per output row)\n", (long long)N, (long long)K,
+                    l == QMM_LAYOUT_REPACKED ? "repacked" : "canonical");
+        return device_status(qmm::launch_gemv_fused_q2_K(static_cast<const uint8_t *>(w),
+                                                         l == QMM_LAYOUT_REPACKED, x, yb, out, N, K, s),
+                             "quantize_mul_mat fused launch");
+    }
     if (t == QMM_Q4_0 && M == 1 && N > 0 && qmm::gemv_fused_q4_0_ok(N, K)) {
         if (log_enabled())
             fprintf(stderr, "qmm: quantize_mul_mat Q4_0 M=1 N=%lld K=%lld layout=%s -> fused quantize + GEMV "

@@ -179,6 +179,28 @@ __device__ __forceinline__ void q2k_group_sums(const Q2KUnit &x, int u, const ui
     }
 }
 
+// acc + d_a * (d * S - dmin * Mn) for one unit (the Q4_K-style min term, over
+// the unit's four groups).
+__device__ __forceinline__ float q2k_unit_accum(const Q2KUnit &x, int u, const uint8_t *s_qs,
+                                                const float *s_d, const int16_t *s_bs, float acc) {
+    int P[4];
+    q2k_group_sums(x, u, s_qs, P);
+    const int b = u >> 2, p = u & 3;
+    // scale bytes of groups 8(p/2) + 2s + (p%2): byte 2s + (p%2) of x.sc
+    const uint32_t sw[2] = {x.sc.x, x.sc.y};
+    const int16_t *bs = s_bs + 16 * b + 8 * (p >> 1) + (p & 1);
+    int S = 0, Mn = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t byte = (sw[s >> 1] >> (16 * (s & 1) + 8 * (p & 1))) & 0xff;
+        S += (int)(byte & 15) * P[s];
+        Mn += (int)(byte >> 4) * (int)bs[2 * s];
+    }
+    const float d = f16_bits_to_f32(x.dm & 0xffff);
+    const float dmin = f16_bits_to_f32(x.dm >> 16);
+    return fmaf(s_d[b], d * (float)S - dmin * (float)Mn, acc);
+}
+
 constexpr int kQ2Waves = 4;
 
 // MODE 0: out[m*N + n] (fp32).  MODE 1: P[m][n][K/16] (int32 group sums).
@@ -232,24 +254,12 @@ __global__ __launch_bounds__(256) void k_gemv_q2_K(const uint8_t *__restrict__ W
         for (int it = 0; it < kNit; ++it) {
             const int u = base + lane + 64 * it;
             if (u < nunits) {
-                int P[4];
-                q2k_group_sums(x[it], u, row.qs, P);
-                const int b = u >> 2, p = u & 3;
                 if (MODE == 0) {
-                    // scale bytes of groups 8(p/2) + 2s + (p%2): byte 2s + (p%2) of x.sc
-                    const uint32_t sw[2] = {x[it].sc.x, x[it].sc.y};
-                    const int16_t *bs = row.bsums + 16 * b + 8 * (p >> 1) + (p & 1);
-                    int S = 0, Mn = 0;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const uint32_t byte = (sw[s >> 1] >> (16 * (s & 1) + 8 * (p & 1))) & 0xff;
-                        S += (int)(byte & 15) * P[s];
-                        Mn += (int)(byte >> 4) * (int)bs[2 * s];
-                    }
-                    const float d = f16_bits_to_f32(x[it].dm & 0xffff);
-                    const float dmin = f16_bits_to_f32(x[it].dm >> 16);
-                    acc = fmaf(row.d[b], d * (float)S - dmin * (float)Mn, acc);
+                    acc = q2k_unit_accum(x[it], u, row.qs, row.d, row.bsums, acc);
                 } else if (n < N) {
+                    int P[4];
+                    q2k_group_sums(x[it], u, row.qs, P);
+                    const int b = u >> 2, p = u & 3;
                     int32_t *Pout = reinterpret_cast<int32_t *>(dst) + (m * N + n) * (K / 16) + 16 * b;
 #pragma unroll
                     for (int s = 0; s < 4; ++s) Pout[8 * (p >> 1) + 2 * s + (p & 1)] = P[s];
@@ -261,6 +271,79 @@ __global__ __launch_bounds__(256) void k_gemv_q2_K(const uint8_t *__restrict__ W
         acc = wave_sum(acc);
         if (lane == 0 && n < N) reinterpret_cast<float *>(dst)[m_out * N + n] = valid ? acc : __builtin_nanf("");
     }
+}
+
+// ---------------------------------------------------------------------------
+// Fused M = 1 path (rows of up to four units per lane, K <= 16384, at most two
+// rows per wavefront): the fp32 row is quantized to Q8_K inside the GEMV,
+// straight into LDS, so one launch covers quantize + mul_mat.  Every
+// workgroup quantizes the whole row, so the grid holds one 16-wavefront
+// workgroup per CU; wavefront w of workgroup g takes rows g*16 + w and
+// g*16 + w + 16*gridDim.x.  A wavefront loads its fp32 activation blocks
+// (b = wave + 16i) and waits for them, requests its first row's units,
+// quantizes while they are in flight, and requests its second row (if any)
+// after the barrier.  Workgroup 0 also stores the Q8_K bytes to Yq.  Per row
+// the same integer sums and fp32 operations, in the same order, as
+// k_gemv_q2_K.
+// ---------------------------------------------------------------------------
+constexpr int kQ2FusedWaves = 16;
+
+template <bool REPACKED, int kNit, int kXB>
+__global__ __launch_bounds__(kQ2FusedWaves * 64) void k_gemv_fused_q2_K(
+    const uint8_t *__restrict__ W, const float *__restrict__ X, uint8_t *__restrict__ Yq,
+    float *__restrict__ out, int64_t N, int64_t K) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t ys[];
+    const int64_t nb = K / QK_K;
+    const int nunits = (int)(4 * nb);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t stride = (int64_t)gridDim.x * kQ2FusedWaves;
+    const int64_t row = (int64_t)blockIdx.x * kQ2FusedWaves + wave, row2 = row + stride;  // uniform
+    const Q2KAddr<REPACKED> A{W, N * nb, REPACKED ? (4 * N * nb + 255) / 256 * 256 : 0};
+    auto load_row = [&](int64_t r, Q2KUnit (&x)[kNit]) {
+        const int64_t rr = r < N ? r : N - 1;  // past the last row: a valid row, never stored
+#pragma unroll
+        for (int it = 0; it < kNit; ++it) {
+            const int u = lane + 64 * it;
+            q2k_load<REPACKED>(A, rr, nb, u < nunits ? u : nunits - 1, x[it]);
+        }
+    };
+    float4 xv[kXB];
+#pragma unroll
+    for (int i = 0; i < kXB; ++i) {  // block indices past the row load the last block again
+        const int b0 = wave + kQ2FusedWaves * i;
+        const int b = b0 < nb ? b0 : (int)nb - 1;
+        xv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * QK_K + 4 * lane);
+    }
+    // the activation loads complete before any weight load is issued (queued
+    // behind the chip's weight stream they would arrive late)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    Q2KUnit x[kNit], x2[kNit];
+    load_row(row, x);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kXB; ++i) q8k_quantize_block_lds(xv[i], wave + kQ2FusedWaves * i, K, ys, lane);
+    __syncthreads();
+    const uint8_t *s_qs = ys;
+    const float *s_d = reinterpret_cast<const float *>(ys + K);
+    const int16_t *s_bs = reinterpret_cast<const int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
+    const bool two = row2 < N;  // wavefront-uniform
+    if (two) load_row(row2, x2);
+    auto reduce = [&](int64_t r, const Q2KUnit (&xx)[kNit]) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int it = 0; it < kNit; ++it) {
+            const int u = lane + 64 * it;
+            if (u < nunits) acc = q2k_unit_accum(xx[it], u, s_qs, s_d, s_bs, acc);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0 && r < N) out[r] = acc;
+    };
+    reduce(row, x);
+    if (two) reduce(row2, x2);
+    // workgroup 0 copies the Q8_K row to Yq last (stores issued earlier would
+    // sit in the in-order counter ahead of the weight loads)
+    if (blockIdx.x == 0) q8k_store_row<kQ2FusedWaves * 64>(Yq, ys, K);
 }
 
 template <int MODE>
@@ -319,6 +402,34 @@ hipError_t launch_gemv_q2_K(const uint8_t *w, bool repacked, const uint8_t *y, f
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+bool gemv_fused_q2_K_ok(int64_t N, int64_t K) {
+    // rows of up to four units per lane (K <= 16384) and at most two rows per
+    // wavefront; each workgroup repeats the quantization
+    return K <= 16384 && N <= 2 * (int64_t)kQ2FusedWaves * cu_count();
+}
+
+hipError_t launch_gemv_fused_q2_K(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
+                                  int64_t N, int64_t K, hipStream_t s) {
+    if (!gemv_fused_q2_K_ok(N, K)) return hipErrorInvalidValue;
+    const int64_t nit = (4 * (K / QK_K) + 63) / 64;
+    const int64_t groups = (N + kQ2FusedWaves - 1) / kQ2FusedWaves, cus = cu_count();
+    const dim3 grid((unsigned)(groups < cus ? groups : cus)), block(kQ2FusedWaves * 64);
+    const unsigned lds = (unsigned)q8k_row_lds_bytes(K);
+#define QMM_Q2F(NIT, XB)                                                                                  \
+    do {                                                                                                  \
+        if (repacked)                                                                                     \
+            hipLaunchKernelGGL((k_gemv_fused_q2_K<true, NIT, XB>), grid, block, lds, s, w, x, yq, out, N, K);  \
+        else                                                                                              \
+            hipLaunchKernelGGL((k_gemv_fused_q2_K<false, NIT, XB>), grid, block, lds, s, w, x, yq, out, N, K); \
+    } while (0)
+    // kXB = activation blocks per wavefront: ceil(nb / 16) (nb <= 16 * kNit = 16 * kXB)
+    if (nit <= 1) QMM_Q2F(1, 1);
+    else if (nit <= 2) QMM_Q2F(2, 2);
+    else QMM_Q2F(4, 4);
+#undef QMM_Q2F
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_id_q2_K(const uint8_t *w, bool repacked, int64_t w_stride, const uint8_t *y,

@@ -392,12 +392,14 @@ __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W
 }
 
 // ---------------------------------------------------------------------------
-// Fused M = 1 path for Q6_K (rows of up to four piece units per lane, at most
-// two rows per wavefront): the fp32 row is quantized to Q8_K inside the GEMV,
+// Fused M = 1 path for Q6_K (rows of up to four piece units per lane; two rows
+// per wavefront at most, one where a row takes four units per lane, as two
+// rows of four would not fit the 128 VGPRs of a 1024-thread workgroup without
+// spills): the fp32 row is quantized to Q8_K inside the GEMV,
 // straight into LDS, so one launch covers quantize + mul_mat.  As in the Q4_K
 // fused kernel every workgroup quantizes the whole row, so the grid holds one
 // 16-wavefront workgroup per CU and wavefront w of workgroup g takes rows
-// g*16 + w and g*16 + w + 16*gridDim.x.  A wavefront first loads its fp32
+// g*16 + w and (kRows = 2) g*16 + w + 16*gridDim.x.  A wavefront first loads its fp32
 // activation blocks (b = wave + 16i), waits for them, issues its first row's
 // units and quantizes while they are in flight; its second row (if any) is
 // requested after the barrier, before the first is reduced.  Workgroup 0 also
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(256) void k_gemv_q6_K(const uint8_t *__restrict__ W
 // ---------------------------------------------------------------------------
 constexpr int kQ6FusedWaves = 16;
 
-template <bool REPACKED, int kNit, int kXB>
+template <bool REPACKED, int kNit, int kXB, int kRows>
 __global__ __launch_bounds__(kQ6FusedWaves * 64) void k_gemv_fused_q6_K(
     const uint8_t *__restrict__ W, const float *__restrict__ X, uint8_t *__restrict__ Yq,
     float *__restrict__ out, int64_t N, int64_t K) {
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(kQ6FusedWaves * 64) void k_gemv_fused_q6_K(
     // behind the chip's weight stream they would arrive late)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    Q6KUnit x[kNit], x2[kNit];
+    Q6KUnit x[kNit], x2[kRows == 2 ? kNit : 1];
     load_row(row, x);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -445,8 +447,9 @@ __global__ __launch_bounds__(kQ6FusedWaves * 64) void k_gemv_fused_q6_K(
     const uint8_t *s_qs = ys;
     const float *s_d = reinterpret_cast<const float *>(ys + K);
     const int16_t *s_bs = reinterpret_cast<const int16_t *>(ys + K + (nb * 4 + 15) / 16 * 16);
-    const bool two = row2 < N;  // wavefront-uniform
-    if (two) load_row(row2, x2);
+    const bool two = kRows == 2 && row2 < N;  // wavefront-uniform
+    if constexpr (kRows == 2)
+        if (two) load_row(row2, x2);
     auto reduce = [&](int64_t r, const Q6KUnit (&xx)[kNit]) {
         float acc = 0.0f;
 #pragma unroll
@@ -465,7 +468,8 @@ __global__ __launch_bounds__(kQ6FusedWaves * 64) void k_gemv_fused_q6_K(
         if (lane == 0 && r < N) out[r] = acc;
     };
     reduce(row, x);
-    if (two) reduce(row2, x2);
+    if constexpr (kRows == 2)
+        if (two) reduce(row2, x2);
     // workgroup 0 copies the Q8_K row to Yq last (stores issued earlier would
     // sit in the in-order counter ahead of the weight loads)
     if (blockIdx.x == 0) q8k_store_row<kQ6FusedWaves * 64>(Yq, ys, K);
@@ -534,10 +538,11 @@ hipError_t launch_gemv_q6_K(const uint8_t *w, bool repacked, const uint8_t *y, f
 }
 
 bool gemv_fused_q6_K_ok(int64_t N, int64_t K) {
-    // rows of up to four piece units per lane (K <= 8192) and at most two rows
-    // per wavefront; each workgroup repeats the quantization
-    return K <= 8192 && N <= 2 * (int64_t)kQ6FusedWaves * cu_count() &&
-           q8k_row_lds_bytes(K) <= 60 * 1024;
+    // rows of up to four piece units per lane (K <= 8192); two rows per
+    // wavefront at most, one at four units; each workgroup repeats the
+    // quantization
+    const int64_t rows = K <= 4096 ? 2 : 1;
+    return K <= 8192 && N <= rows * kQ6FusedWaves * cu_count() && q8k_row_lds_bytes(K) <= 60 * 1024;
 }
 
 hipError_t launch_gemv_fused_q6_K(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
@@ -547,17 +552,17 @@ hipError_t launch_gemv_fused_q6_K(const uint8_t *w, bool repacked, const float *
     const int64_t groups = (N + kQ6FusedWaves - 1) / kQ6FusedWaves, cus = cu_count();
     const dim3 grid((unsigned)(groups < cus ? groups : cus)), block(kQ6FusedWaves * 64);
     const unsigned lds = (unsigned)q8k_row_lds_bytes(K);
-#define QMM_Q6F(NIT, XB)                                                                                  \
-    do {                                                                                                  \
-        if (repacked)                                                                                     \
-            hipLaunchKernelGGL((k_gemv_fused_q6_K<true, NIT, XB>), grid, block, lds, s, w, x, yq, out, N, K);  \
-        else                                                                                              \
-            hipLaunchKernelGGL((k_gemv_fused_q6_K<false, NIT, XB>), grid, block, lds, s, w, x, yq, out, N, K); \
+#define QMM_Q6F(NIT, XB, ROWS)                                                                                  \
+    do {                                                                                                        \
+        if (repacked)                                                                                           \
+            hipLaunchKernelGGL((k_gemv_fused_q6_K<true, NIT, XB, ROWS>), grid, block, lds, s, w, x, yq, out, N, K);  \
+        else                                                                                                    \
+            hipLaunchKernelGGL((k_gemv_fused_q6_K<false, NIT, XB, ROWS>), grid, block, lds, s, w, x, yq, out, N, K); \
     } while (0)
     // kXB = activation blocks per wavefront: ceil(nb / 16) (nb <= 8 * kNit <= 16 * kXB)
-    if (nit <= 1) QMM_Q6F(1, 1);
-    else if (nit <= 2) QMM_Q6F(2, 1);
-    else QMM_Q6F(4, 2);
+    if (nit <= 1) QMM_Q6F(1, 1, 2);
+    else if (nit <= 2) QMM_Q6F(2, 1, 2);
+    else QMM_Q6F(4, 2, 1);
 #undef QMM_Q6F
     return hipGetLastError();
 }

@@ -71,19 +71,23 @@ hipError_t launch_skinny32r_q4_K(const uint8_t *w, const uint8_t *y, float *out,
                                  int64_t K, hipStream_t s);
 hipError_t launch_skinny16_q4_K(const uint8_t *w, bool repacked, const uint8_t *y, float *out,
                                 int64_t M, int64_t N, int64_t K, hipStream_t s);
-// Q4_0 small batch: repacked layout, K % 256 == 0, M <= skinny_q4_0_max_m(),
-// matrices below 4 GiB; w_bytes is the repacked matrix size.
-// Q4_0 GEMV with the M activation rows staged in LDS: K % 64 == 0 and
-// M * K * 5/4 bytes <= 60 KiB (other shapes read the rows per lane).
 // Q4_0, M = 1, small matrices (gemv_fused_q4_0_ok): quantize + GEMV in one launch
+bool gemv_fused_q4_0_ok(int64_t N, int64_t K);
+hipError_t launch_gemv_fused_q4_0(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
+                                  int64_t N, int64_t K, hipStream_t s);
 // Q6_K, M = 1, K <= 8192, N <= 32 * CUs (gemv_fused_q6_K_ok): quantize + GEMV in one launch
 bool gemv_fused_q6_K_ok(int64_t N, int64_t K);
 hipError_t launch_gemv_fused_q6_K(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
                                   int64_t N, int64_t K, hipStream_t s);
-bool gemv_fused_q4_0_ok(int64_t N, int64_t K);
-hipError_t launch_gemv_fused_q4_0(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
+// Q2_K, M = 1, K <= 16384, N <= 32 * CUs (gemv_fused_q2_K_ok): quantize + GEMV in one launch
+bool gemv_fused_q2_K_ok(int64_t N, int64_t K);
+hipError_t launch_gemv_fused_q2_K(const uint8_t *w, bool repacked, const float *x, uint8_t *yq, float *out,
                                   int64_t N, int64_t K, hipStream_t s);
+// Q4_0 GEMV with the M activation rows staged in LDS: K % 64 == 0 and
+// M * K * 5/4 bytes <= 60 KiB (other shapes read the rows per lane).
 bool gemv_q4_0s_fits(int64_t M, int64_t K);
+// Q4_0 small batch: repacked layout, K % 256 == 0, M <= skinny_q4_0_max_m(),
+// matrices below 4 GiB; w_bytes is the repacked matrix size.
 int64_t skinny_q4_0_max_m();
 hipError_t launch_skinny_q4_0(const uint8_t *w, int64_t w_bytes, const uint8_t *y, float *out, int64_t M,
                               int64_t N, int64_t K, hipStream_t s);

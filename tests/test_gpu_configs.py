@@ -6,9 +6,9 @@ byte-identical to the oracle's encoding; activations likewise.  Outputs are
 compared element by element with the oracle for the GEMV workloads and on a
 sample of (m, n) pairs for the prefill GEMM: one whole 128 x 256 workgroup
 tile (every lane and result register of all eight wavefronts and four row
-tiles), tile corners and random pairs.  The Q4_K M = 1 workloads also run
-through quantize_mul_mat (the fused form the benchmark times), which must give
-the same Q8_K bytes and the same outputs bit for bit.
+tiles), tile corners and random pairs.  The M = 1 workloads also run through
+quantize_mul_mat (the fused form the benchmark times), which must give the
+same Q8 bytes and the same outputs bit for bit.
 """
 import numpy as np
 import pytest
@@ -33,9 +33,9 @@ def _run_projection(p, full: bool):
     assert np.array_equal(to_host(y_gpu), y_orc.reshape(-1)), f"{p.name}: activation bytes differ"
     wr = qmm.repack_weights(w_gpu, p.wfmt, p.N, p.K)
     got = to_host(qmm.mul_mat(p.wfmt, wr, y_gpu, p.M, p.N, p.K, layout="repacked"))
-    if p.wfmt == "q4_K" and p.M == 1:
+    if p.M == 1:
         out_f, y_f = qmm.quantize_mul_mat(p.wfmt, wr, to_dev(x), p.N, layout="repacked")
-        assert np.array_equal(to_host(y_f).reshape(-1), y_orc.reshape(-1)), f"{p.name}: fused Q8_K bytes differ"
+        assert np.array_equal(to_host(y_f).reshape(-1), y_orc.reshape(-1)), f"{p.name}: fused Q8 bytes differ"
         assert np.array_equal(to_host(out_f).view(np.uint32), got.view(np.uint32)), f"{p.name}: fused != two-call"
     if full:
         want, terms = full_reference(p.wfmt, w_orc, y_orc, p.M, p.N, p.K)

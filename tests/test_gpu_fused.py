@@ -10,7 +10,7 @@ Shapes cover one, two, four and eight pieces per lane (eight: the first row's
 requests split around the quantization), rows looped over by the persistent
 workgroups (N above 16 rows per CU, also with eight pieces), ragged N tails,
 the largest K of the one-launch kernel and K above it (two-launch path),
-M > 1 and Q4_0.
+M > 1, and the one-launch kernels of Q4_0, Q6_K and Q2_K.
 """
 import numpy as np
 import pytest
@@ -26,7 +26,7 @@ FUSED_MAX_K = 16384  # largest K of the one-launch path (eight 16-byte pieces pe
 
 
 def _inputs(wfmt, M, N, K, seed):
-    if wfmt in ("q4_K", "q6_K"):
+    if wfmt in ("q4_K", "q6_K", "q2_K"):
         w = oracle.quantize(wfmt, weights_t4_skewed([500, seed], N, K))
         x = activations([501, seed], M, K, outlier_frac=0.01)
     else:
@@ -167,10 +167,23 @@ def test_fused_graph_replay():
 
 
 @pytest.mark.parametrize("layout", ["canonical", "repacked"])
-@pytest.mark.parametrize("N,K", [(77, 256), (4096, 4096), (8192, 1024), (100, 8192), (8193, 1024), (3, 8448)])
+@pytest.mark.parametrize("N,K", [(77, 256), (4096, 4096), (8192, 1024), (100, 8192), (4096, 8192),
+                                 (8193, 1024), (4097, 8192), (3, 8448)])
 def test_fused_q6_K_m1(N, K, layout):
-    """Q6_K at M = 1: one launch (quantization in every workgroup) for K <= 8192
-    and N <= 32 rows per CU -- one and two rows per wavefront, one to four
-    piece units per lane -- and two launches just past those limits."""
+    """Q6_K at M = 1: one launch (quantization in every workgroup) for K <= 4096
+    and N <= 32 rows per CU (one or two rows per wavefront, one or two piece
+    units per lane) and for K <= 8192 and N <= 16 rows per CU (one row of four
+    units), and two launches just past those limits."""
     sample = 3000 if N * K > (1 << 24) else None
     _check("q6_K", 1, N, K, layout, seed=N * 5 + K, sample=sample)
+
+
+@pytest.mark.parametrize("layout", ["canonical", "repacked"])
+@pytest.mark.parametrize("N,K", [(77, 256), (4096, 4096), (8192, 1024), (100, 8192), (4100, 12288),
+                                 (5, 16384), (8193, 1024), (3, 16640)])
+def test_fused_q2_K_m1(N, K, layout):
+    """Q2_K at M = 1: one launch (quantization in every workgroup) for K <= 16384
+    and N <= 32 rows per CU -- one and two rows per wavefront, one, two and
+    four units per lane -- and two launches just past those limits."""
+    sample = 3000 if N * K > (1 << 24) else None
+    _check("q2_K", 1, N, K, layout, seed=N * 7 + K, sample=sample)
