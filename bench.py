@@ -320,7 +320,7 @@ def kernel_of(key: str, call_name: str, fused: bool, layout: str = "repacked") -
     if wfmt == "q4_0":
         N = int(call_name.split("N=")[1].split()[0])
         if M == 1:
-            return "k_gemv_fused_q4_0" if fused and K % 64 == 0 and K <= 16384 and N * K <= 1 << 22 else "k_gemv_q4_0"
+            return "k_gemv_fused_q4_0" if fused and K % 64 == 0 and K <= 4096 and N * K <= 1 << 22 else "k_gemv_q4_0"
         return "k_skinny_q4_0" if M <= 32 else "k_gemm_q4_0"
     if wfmt == "q4_K":
         if M == 1:

@@ -324,7 +324,7 @@ qmm_status qmm_mul_mat_id_noalloc(qmm_weight_type t, const void *w, size_t w_byt
  * ("激活量化重复与融合") notes that quantizing the activations once at the
  * start of a fused node saves both the launch and the repeated conversion;
  * here, for Q4_K with M == 1 and K <= 16384 (for Q4_0 with M == 1, K % 64 ==
- * 0, K <= 16384 and N*K <= 2^22; for Q6_K with M == 1 and either K <= 4096 and
+ * 0, K <= 4096 and N*K <= 2^22; for Q6_K with M == 1 and either K <= 4096 and
  * N at most 32 rows per compute unit or K <= 8192 and N at most 16 rows per
  * compute unit; for Q2_K with M == 1, K <= 16384 and N at most 32 rows per
  * compute unit), the quantization runs inside the

@@ -87,11 +87,14 @@ def test_quantize_mul_mat_q4_0(M, N, K):
 
 
 @pytest.mark.parametrize("layout", ["canonical", "repacked"])
-@pytest.mark.parametrize("N,K", [(77, 64), (3, 16384), (4096, 1024), (4097, 1024), (10, 96), (1, 16448)])
+@pytest.mark.parametrize("N,K", [(77, 64), (3, 4096), (1024, 4096), (4096, 1024), (4097, 1024), (10, 96),
+                                 (1, 4160), (3, 16384)])
 def test_fused_q4_0_m1(N, K, layout):
     """Q4_0 at M = 1: one launch (quantization in every workgroup) for K % 64 == 0,
-    K <= 16384 and N*K <= 2^22 -- one and many 32-block quantization passes, the
-    N*K limit itself -- and two launches just past those limits."""
+    K <= 4096 and N*K <= 2^22 -- one to four 32-block quantization passes (the
+    first with its values and each lane's first weight block requested ahead),
+    fewer than 32 blocks, the N*K limit itself -- and two launches past those
+    limits."""
     _check("q4_0", 1, N, K, layout, seed=N * 3 + K)
 
 
