@@ -81,6 +81,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // scalar: a uniform branch
 
     // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
     // each XCD gets a contiguous range of the index v; v walks groups of GM
@@ -267,6 +268,16 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_q4_K(const uint8_t *__restrict
         };
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
+            // The two wavefronts of a SIMD (w and w + 4) take turns at high issue
+            // priority, one row tile each, so one issues its MFMAs while the other's
+            // vector work fills the gaps (c5, alternating runs: M = 2048 1045 against
+            // 1085-1096 us, M = 512 317-322 against 321-326 us; priority for the
+            // plane-building row tile only, or for the MFMAs against the tails, gained
+            // about half of that).  Priority changes no result.
+            if (((wave_u >> 2) ^ i) & 1)
+                __builtin_amdgcn_s_setprio(0);
+            else
+                __builtin_amdgcn_s_setprio(2);
             // row tiles past the last valid row (a short tail tile, or an
             // expert's remainder rows under mul_mat_id) are skipped; row tile 0
             // always runs (it builds the planes and requests the next weights)
